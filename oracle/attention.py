@@ -1,0 +1,344 @@
+"""Plain, slow, float64 CPU oracle for exact attention -- TEST INFRASTRUCTURE.
+
+Only the test suite, the package smoke check and the CPU-baseline leg of the
+benchmark may import this module. The GPU library never calls it, and it
+shares no code with the GPU library: it takes numpy arrays and uses numpy
+only (a matmul is the one library primitive it leans on).
+
+What is computed (the pages state the operation, not its formulas; the
+readings taken are listed next to each function):
+
+* the result is exact attention softmax(Q K^T) V -- "FlashAttention" abstract
+  page (exact, not approximate attention) and the DistFlashAttn reviews page,
+  review 1 summary, which writes the operation out;
+* the per-row logsumexp is the saved statistic -- FlashAttention-2 reviews
+  page, reviewer 2 summary, point 2 (save logsumexp instead of max and sum);
+* a causal mask halves the work -- DistFlashAttn reviews page, review 1
+  summary, point 1; FlashAttention-2 reviews page, reviewer 4 (block skipping
+  for causal masking, section 3.1);
+* grouped-query attention shares one K/V head among several query heads --
+  FlashAttention-2 reviews page, reviewer 1 (the MQA/GQA paragraph of the
+  backward-pass section); DistFlashAttn reviews page, review 3 (GQA setting);
+* partial results over key chunks are combined -- DistFlashAttn reviews page,
+  reviews 1 and 4 (chunks of the attention computation spread over workers);
+  BurstAttention rebuttal page (RingAttention vs. online softmax).
+
+Readings where the pages are silent (each also listed in the design notes):
+scores are scale * Q K^T with a caller-given scale; causal keeps key position
+<= query position (absolute positions, so a chunk pair can be masked by its
+offsets); LSE is the natural-log logsumexp of the scaled, masked scores;
+head h reads K/V head h // (H / Hkv); layouts are Q,O,dO [B, N, H, d],
+K,V [B, N, Hkv, d], LSE [B, H, N]; the backward is the gradient of
+sum(dO * O) with respect to Q, K, V.
+
+Every function here is pinned in tests/test_oracle.py against things other
+than its own formula: hand-worked values (tests/golden), closed forms,
+invariants, finite differences and torch's float64 CPU attention.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "scores", "forward", "backward", "merge", "tiled_forward",
+    "forward_rows", "backward_dq_rows", "backward_dkdv_rows", "probs",
+]
+
+
+# ---------------------------------------------------------------------------
+# the definition, one (batch, query head) at a time
+# ---------------------------------------------------------------------------
+
+def scores(q_h, k_g, scale, causal, q_pos=None, k_pos=None):
+    """S[i, j] = scale * q_i . k_j, and -inf where a causal mask forbids j.
+
+    q_h: [Nq, d], k_g: [Nk, d] float64. Positions default to 0..N-1; key j is
+    allowed for query i iff k_pos[j] <= q_pos[i] under the causal mask.
+    """
+    s = scale * (q_h @ k_g.T)
+    if causal:
+        if q_pos is None:
+            q_pos = np.arange(q_h.shape[0])
+        if k_pos is None:
+            k_pos = np.arange(k_g.shape[0])
+        s = np.where(k_pos[None, :] <= q_pos[:, None], s, -np.inf)
+    return s
+
+
+def _softmax_rows(s):
+    """Exact two-pass softmax of each row: returns (P, lse).
+
+    lse = m + ln(sum_j exp(s_j - m)) with m the row max; P = exp(s - lse).
+    A row with every entry -inf gets P = 0 and lse = -inf.
+    """
+    m = np.max(s, axis=1)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    e = np.exp(s - m_safe[:, None])
+    tot = np.sum(e, axis=1)
+    with np.errstate(divide="ignore"):
+        lse = m_safe + np.log(tot)
+    lse = np.where(tot > 0, lse, -np.inf)
+    p = np.where(tot[:, None] > 0, e / np.where(tot > 0, tot, 1.0)[:, None], 0.0)
+    return p, lse
+
+
+def probs(q, k, scale, causal, b=0, h=0):
+    """The full attention matrix P of one (batch, query head): [Nq, Nk]."""
+    G = q.shape[2] // k.shape[2]
+    s = scores(np.asarray(q[b, :, h], np.float64),
+               np.asarray(k[b, :, h // G], np.float64), scale, causal)
+    return _softmax_rows(s)[0]
+
+
+def _check(q, k, v):
+    B, N, H, d = q.shape
+    Bk, Nk, Hkv, dk = k.shape
+    if v.shape != k.shape or Bk != B or dk != d or H % Hkv:
+        raise ValueError("shape mismatch: q %s k %s v %s" % (q.shape, k.shape, v.shape))
+    return B, N, H, Hkv, d, Nk
+
+
+def _row_blocks(n, blk):
+    for r0 in range(0, n, blk):
+        yield r0, min(n, r0 + blk)
+
+
+# ---------------------------------------------------------------------------
+# forward
+# ---------------------------------------------------------------------------
+
+def forward(q, k, v, causal, scale, q_offset=0, k_offset=0, row_block=512):
+    """O and LSE of exact attention.
+
+    q: [B, Nq, H, d]; k, v: [B, Nk, Hkv, d] (any float dtype, used as float64).
+    Returns o [B, Nq, H, d] float64 and lse [B, H, Nq] float64.
+
+    Query rows are processed in blocks; each block's score rows are
+    materialised at full key width and normalised exactly (max, then sum), so
+    no online rescaling is involved. ``q_offset``/``k_offset`` are the absolute
+    positions of row 0 of q and of k, used only by the causal mask.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    B, Nq, H, Hkv, d, Nk = _check(q, k, v)
+    G = H // Hkv
+    o = np.zeros((B, Nq, H, d))
+    lse = np.zeros((B, H, Nq))
+    k_pos = k_offset + np.arange(Nk)
+    for b in range(B):
+        for h in range(H):
+            g = h // G
+            for r0, r1 in _row_blocks(Nq, row_block):
+                q_pos = q_offset + np.arange(r0, r1)
+                s = scores(q[b, r0:r1, h], k[b, :, g], scale, causal, q_pos, k_pos)
+                p, l = _softmax_rows(s)
+                o[b, r0:r1, h] = p @ v[b, :, g]
+                lse[b, h, r0:r1] = l
+    return o, lse
+
+
+def forward_rows(q, k, v, causal, scale, b, h, rows):
+    """O[b, rows, h] and LSE[b, h, rows] for selected query rows only.
+
+    The same definition as ``forward``, evaluated one row at a time so it can
+    check sampled outputs of very long sequences.
+    """
+    G = q.shape[2] // k.shape[2]
+    g = h // G
+    kg = np.asarray(k[b, :, g], np.float64)
+    vg = np.asarray(v[b, :, g], np.float64)
+    rows = np.asarray(rows)
+    out_o = np.zeros((len(rows), q.shape[3]))
+    out_l = np.zeros(len(rows))
+    for t, i in enumerate(rows):
+        n_allowed = (i + 1) if causal else kg.shape[0]
+        s = scale * (kg[:n_allowed] @ np.asarray(q[b, i, h], np.float64))
+        p, l = _softmax_rows(s[None, :])
+        out_o[t] = p[0] @ vg[:n_allowed]
+        out_l[t] = l[0]
+    return out_o, out_l
+
+
+# ---------------------------------------------------------------------------
+# backward
+# ---------------------------------------------------------------------------
+
+def backward(q, k, v, do, causal, scale, row_block=512):
+    """dQ, dK, dV: gradients of sum(dO * O) through exact attention.
+
+    With P the softmax of the masked scaled scores (recomputed exactly here):
+      dV_j  = sum_i P_ij dO_i
+      dP_ij = dO_i . V_j
+      dS_ij = P_ij (dP_ij - sum_l P_il dP_il)
+      dQ_i  = scale * sum_j dS_ij K_j
+      dK_j  = scale * sum_i dS_ij Q_i
+    dK and dV of a K/V head are summed over the query heads that read it.
+    Returns float64 arrays shaped like q, k, v.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    do = np.asarray(do, np.float64)
+    B, N, H, Hkv, d, Nk = _check(q, k, v)
+    G = H // Hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            g = h // G
+            for r0, r1 in _row_blocks(N, row_block):
+                s = scores(q[b, r0:r1, h], k[b, :, g], scale, causal,
+                           np.arange(r0, r1), np.arange(Nk))
+                p, _ = _softmax_rows(s)
+                dob = do[b, r0:r1, h]
+                dv[b, :, g] += p.T @ dob
+                dp = dob @ v[b, :, g].T
+                rowdot = np.sum(p * dp, axis=1)
+                ds = p * (dp - rowdot[:, None])
+                dq[b, r0:r1, h] = scale * (ds @ k[b, :, g])
+                dk[b, :, g] += scale * (ds.T @ q[b, r0:r1, h])
+    return dq, dk, dv
+
+
+def _lse_all_rows(qh, kg, scale, causal, row_block=1024):
+    n = qh.shape[0]
+    out = np.zeros(n)
+    for r0, r1 in _row_blocks(n, row_block):
+        hi = r1 if causal else kg.shape[0]
+        s = scores(qh[r0:r1], kg[:hi], scale, causal, np.arange(r0, r1), np.arange(hi))
+        out[r0:r1] = _softmax_rows(s)[1]
+    return out
+
+
+def backward_dq_rows(q, k, v, do, causal, scale, b, h, rows):
+    """dQ[b, rows, h] for selected query rows (the same definition as
+    ``backward``, one row at a time)."""
+    G = q.shape[2] // k.shape[2]
+    g = h // G
+    kg = np.asarray(k[b, :, g], np.float64)
+    vg = np.asarray(v[b, :, g], np.float64)
+    out = np.zeros((len(rows), q.shape[3]))
+    for t, i in enumerate(np.asarray(rows)):
+        n_allowed = (i + 1) if causal else kg.shape[0]
+        s = scale * (kg[:n_allowed] @ np.asarray(q[b, i, h], np.float64))
+        p, _ = _softmax_rows(s[None, :])
+        p = p[0]
+        dp = vg[:n_allowed] @ np.asarray(do[b, i, h], np.float64)
+        ds = p * (dp - np.dot(p, dp))
+        out[t] = scale * (ds @ kg[:n_allowed])
+    return out
+
+
+def backward_dkdv_rows(q, k, v, do, causal, scale, b, g, cols, row_block=1024):
+    """dK[b, cols, g] and dV[b, cols, g] for selected key rows of K/V head g,
+    summed over the query heads of its group.
+
+    A key row's gradient needs P[i, j] for every query i, so each query
+    head's row logsumexps are computed first (exactly, at full key width)."""
+    H, Hkv = q.shape[2], k.shape[2]
+    G = H // Hkv
+    kg = np.asarray(k[b, :, g], np.float64)
+    vg = np.asarray(v[b, :, g], np.float64)
+    cols = np.asarray(cols)
+    N = q.shape[1]
+    dk = np.zeros((len(cols), q.shape[3]))
+    dv = np.zeros((len(cols), q.shape[3]))
+    for h in range(g * G, (g + 1) * G):
+        qh = np.asarray(q[b, :, h], np.float64)
+        doh = np.asarray(do[b, :, h], np.float64)
+        lse = _lse_all_rows(qh, kg, scale, causal)
+        for r0, r1 in _row_blocks(N, row_block):
+            # P[i, cols] and dP[i, cols] for this block of queries
+            s = scores(qh[r0:r1], kg[cols], scale, causal, np.arange(r0, r1), cols)
+            p = np.exp(s - lse[r0:r1, None])
+            dp = doh[r0:r1] @ vg[cols].T
+            # D_i = sum_j P_ij dP_ij over all keys of row i (full width)
+            hi = r1 if causal else kg.shape[0]
+            s_full = scores(qh[r0:r1], kg[:hi], scale, causal, np.arange(r0, r1), np.arange(hi))
+            p_full = np.exp(s_full - lse[r0:r1, None])
+            dp_full = doh[r0:r1] @ vg[:hi].T
+            rowdot = np.sum(p_full * dp_full, axis=1)
+            ds = p * (dp - rowdot[:, None])
+            dv += p.T @ doh[r0:r1]
+            dk += scale * (ds.T @ qh[r0:r1])
+    return dk, dv
+
+
+# ---------------------------------------------------------------------------
+# merge of partial results over disjoint key sets
+# ---------------------------------------------------------------------------
+
+def merge(o_a, lse_a, o_b, lse_b):
+    """Combine attention over key set A and over a disjoint key set B into
+    attention over A u B.
+
+    Softmax over a union: the new normaliser is e^{lse_a} + e^{lse_b}, so
+      lse = M + ln(e^{lse_a - M} + e^{lse_b - M}),  M = max(lse_a, lse_b)
+      o   = e^{lse_a - lse} o_a + e^{lse_b - lse} o_b
+    Rows where both sides are empty (lse = -inf) give lse = -inf, o = 0.
+    o_*: [B, N, H, d]; lse_*: [B, H, N].
+    """
+    o_a = np.asarray(o_a, np.float64)
+    o_b = np.asarray(o_b, np.float64)
+    lse_a = np.asarray(lse_a, np.float64)
+    lse_b = np.asarray(lse_b, np.float64)
+    m = np.maximum(lse_a, lse_b)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    tot = np.exp(lse_a - m_safe) + np.exp(lse_b - m_safe)
+    with np.errstate(divide="ignore"):
+        lse = np.where(tot > 0, m_safe + np.log(np.where(tot > 0, tot, 1.0)), -np.inf)
+    lse_fin = np.where(np.isfinite(lse), lse, 0.0)
+    wa = np.where(np.isfinite(lse), np.exp(lse_a - lse_fin), 0.0)
+    wb = np.where(np.isfinite(lse), np.exp(lse_b - lse_fin), 0.0)
+    # [B, H, N] weights -> [B, N, H, 1]
+    wa = np.transpose(wa, (0, 2, 1))[..., None]
+    wb = np.transpose(wb, (0, 2, 1))[..., None]
+    return wa * o_a + wb * o_b, lse
+
+
+# ---------------------------------------------------------------------------
+# the tiled online-softmax algorithm (to pin that it equals the definition)
+# ---------------------------------------------------------------------------
+
+def tiled_forward(q, k, v, causal, scale, br, bc):
+    """FlashAttention's tiled forward with online softmax, in float64.
+
+    For each block of ``br`` query rows, keys are visited ``bc`` at a time
+    with a running row max m, an un-normalised running sum l and an
+    un-normalised accumulator; when the max grows both are rescaled by
+    e^{m_old - m_new}, and the division by l happens once at the end
+    (FlashAttention-2 reviews page, reviewer 2, point 1: deferred scaling;
+    point 2: the saved statistic is m + ln l). Key tiles lying entirely
+    above the diagonal are skipped under a causal mask.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    B, N, H, Hkv, d, Nk = _check(q, k, v)
+    G = H // Hkv
+    o = np.zeros((B, N, H, d))
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            g = h // G
+            for r0, r1 in _row_blocks(N, br):
+                m = np.full(r1 - r0, -np.inf)
+                l = np.zeros(r1 - r0)
+                acc = np.zeros((r1 - r0, d))
+                for c0, c1 in _row_blocks(Nk, bc):
+                    if causal and c0 > r1 - 1:
+                        break  # every key of this tile is after every query row
+                    s = scores(q[b, r0:r1, h], k[b, c0:c1, g], scale, causal,
+                               np.arange(r0, r1), np.arange(c0, c1))
+                    m_new = np.maximum(m, np.max(s, axis=1))
+                    m_use = np.where(np.isfinite(m_new), m_new, 0.0)
+                    alpha = np.exp(m - m_use)       # e^{-inf} = 0 on the first tile
+                    p = np.exp(s - m_use[:, None])
+                    l = alpha * l + np.sum(p, axis=1)
+                    acc = alpha[:, None] * acc + p @ v[b, c0:c1, g]
+                    m = m_new
+                o[b, r0:r1, h] = acc / l[:, None]
+                lse[b, h, r0:r1] = m + np.log(l)
+    return o, lse

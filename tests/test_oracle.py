@@ -1,0 +1,346 @@
+"""Pins for the float64 CPU oracle.
+
+Each test ties the oracle to something other than its own formula:
+hand-derived values, closed forms of special cases, invariants of the
+definition, central finite differences, and torch's float64 CPU attention
+(independent library code). A dropped scale, a wrong sign, a transposed
+operand, a wrong causal direction, a wrong head grouping or a missing max
+subtraction each fails at least one of them (see test_oracle_mutations.py).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import logsumexp
+
+import oracle
+from workloads import draw, as_f64
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+TIGHT = 1e-12
+
+
+def rnd(B, H, Hkv, N, d, seed, gain=1.0, Nk=None):
+    rng = np.random.default_rng(seed)
+    Nk = N if Nk is None else Nk
+    q = rng.standard_normal((B, N, H, d)) * gain
+    k = rng.standard_normal((B, Nk, Hkv, d))
+    v = rng.standard_normal((B, Nk, Hkv, d))
+    do = rng.standard_normal((B, N, H, d))
+    return q, k, v, do
+
+
+def load_golden():
+    with open(os.path.join(HERE, "golden", "hand_worked.json")) as f:
+        return json.load(f)["cases"]
+
+
+# ---------------------------------------------------------------- hand-worked
+
+@pytest.mark.parametrize("case", load_golden(), ids=lambda c: c["name"])
+def test_hand_worked_forward_backward(case):
+    a = {k: np.array(case[k], np.float64) for k in ("q", "k", "v", "do", "o", "lse", "dq", "dk", "dv")}
+    o, lse = oracle.forward(a["q"], a["k"], a["v"], case["causal"], case["scale"])
+    np.testing.assert_allclose(o, a["o"], atol=1e-14)
+    np.testing.assert_allclose(lse, a["lse"], atol=1e-14)
+    dq, dk, dv = oracle.backward(a["q"], a["k"], a["v"], a["do"], case["causal"], case["scale"])
+    np.testing.assert_allclose(dq, a["dq"], atol=1e-14)
+    np.testing.assert_allclose(dk, a["dk"], atol=1e-14)
+    np.testing.assert_allclose(dv, a["dv"], atol=1e-14)
+
+
+# ---------------------------------------------------------------- forward invariants
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_rows_sum_to_one(causal):
+    q, k, v, _ = rnd(1, 2, 2, 37, 8, 11)
+    for h in range(2):
+        p = oracle.probs(q, k, 0.3, causal, 0, h)
+        np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-14)
+        assert np.all(p >= 0)
+        if causal:
+            assert np.all(np.triu(p, 1) == 0.0)
+            assert np.all(np.diag(p) > 0)
+
+
+def test_causal_row0_returns_v0():
+    q, k, v, _ = rnd(2, 4, 2, 19, 16, 12)
+    scale = 1 / 4
+    o, lse = oracle.forward(q, k, v, True, scale)
+    for b in range(2):
+        for h in range(4):
+            g = h // 2
+            np.testing.assert_array_equal(o[b, 0, h], v[b, 0, g])
+            assert lse[b, h, 0] == pytest.approx(scale * np.dot(q[b, 0, h], k[b, 0, g]), abs=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_keys_give_mean_of_values(causal):
+    q, k, v, do = rnd(1, 2, 1, 23, 8, 13)
+    k[:] = k[:, :1]                      # every key row equal to row 0
+    scale = 0.7
+    o, lse = oracle.forward(q, k, v, causal, scale)
+    N = q.shape[1]
+    for h in range(2):
+        for i in range(N):
+            cnt = i + 1 if causal else N
+            np.testing.assert_allclose(o[0, i, h], v[0, :cnt, 0].mean(axis=0), atol=1e-13)
+            s = scale * np.dot(q[0, i, h], k[0, 0, 0])
+            assert lse[0, h, i] == pytest.approx(s + math.log(cnt), abs=1e-13)
+    # uniform rows do not depend on q: the query gradient vanishes
+    dq, _, _ = oracle.backward(q, k, v, do, causal, scale)
+    np.testing.assert_allclose(dq, 0.0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_scale_is_uniform(causal):
+    q, k, v, _ = rnd(1, 1, 1, 17, 4, 14)
+    o, lse = oracle.forward(q, k, v, causal, 0.0)
+    for i in range(17):
+        cnt = i + 1 if causal else 17
+        np.testing.assert_allclose(o[0, i, 0], v[0, :cnt, 0].mean(axis=0), atol=1e-14)
+        assert lse[0, 0, i] == pytest.approx(math.log(cnt), abs=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_shift_moves_only_lse(causal):
+    q, k, v, _ = rnd(1, 2, 2, 21, 8, 15)
+    u = np.random.default_rng(1).standard_normal(8)
+    scale = 0.35
+    o1, l1 = oracle.forward(q, k, v, causal, scale)
+    o2, l2 = oracle.forward(q, k + u, v, causal, scale)
+    np.testing.assert_allclose(o2, o1, atol=1e-12)
+    shift = scale * np.einsum("bnhd,d->bhn", q, u)
+    np.testing.assert_allclose(l2, l1 + shift, atol=1e-12)
+
+
+def test_noncausal_key_permutation_invariance():
+    q, k, v, _ = rnd(1, 2, 2, 29, 8, 16)
+    perm = np.random.default_rng(2).permutation(29)
+    o1, l1 = oracle.forward(q, k, v, False, 0.4)
+    o2, l2 = oracle.forward(q, k[:, perm], v[:, perm], False, 0.4)
+    np.testing.assert_allclose(o2, o1, atol=1e-13)
+    np.testing.assert_allclose(l2, l1, atol=1e-13)
+
+
+@pytest.mark.parametrize("gain", [1.0, 60.0, 1000.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_lse_matches_scipy_logsumexp(causal, gain):
+    # gain 1000 makes scores of magnitude ~1e3-1e4: exp without max-subtraction overflows
+    q, k, v, _ = rnd(1, 1, 1, 33, 16, 17, gain=gain)
+    scale = 0.25
+    _, lse = oracle.forward(q, k, v, causal, scale)
+    s = scale * q[0, :, 0] @ k[0, :, 0].T
+    for i in range(33):
+        row = s[i, : i + 1] if causal else s[i]
+        assert lse[0, 0, i] == pytest.approx(logsumexp(row), rel=1e-14, abs=1e-12)
+    assert np.all(np.isfinite(lse))
+
+
+def test_peaked_row_selects_one_value():
+    # one key aligned with the query at a huge score: O is that key's value
+    q, k, v, _ = rnd(1, 1, 1, 9, 4, 18)
+    k[0, 5, 0] = q[0, 8, 0] * 1e3
+    o, _ = oracle.forward(q, k, v, False, 1.0)
+    np.testing.assert_allclose(o[0, 8, 0], v[0, 5, 0], atol=1e-12)
+
+
+# ---------------------------------------------------------------- library cross-check
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,Hkv", [(2, 2), (4, 2), (4, 1)])
+def test_matches_torch_float64_attention(causal, H, Hkv):
+    q, k, v, do = rnd(2, H, Hkv, 24, 8, 19)
+    scale = 0.3
+    o, lse = oracle.forward(q, k, v, causal, scale)
+    dq, dk, dv = oracle.backward(q, k, v, do, causal, scale)
+
+    G = H // Hkv
+    tq = torch.tensor(q).permute(0, 2, 1, 3).requires_grad_(True)
+    tk = torch.tensor(k).permute(0, 2, 1, 3).requires_grad_(True)
+    tv = torch.tensor(v).permute(0, 2, 1, 3).requires_grad_(True)
+    kk = tk.repeat_interleave(G, dim=1)
+    vv = tv.repeat_interleave(G, dim=1)
+    to = torch.nn.functional.scaled_dot_product_attention(tq, kk, vv, is_causal=causal, scale=scale)
+    to.backward(torch.tensor(do).permute(0, 2, 1, 3))
+    np.testing.assert_allclose(o, to.detach().permute(0, 2, 1, 3).numpy(), atol=1e-12)
+    np.testing.assert_allclose(dq, tq.grad.permute(0, 2, 1, 3).numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.permute(0, 2, 1, 3).numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.permute(0, 2, 1, 3).numpy(), atol=1e-12)
+    s = torch.matmul(tq.detach(), kk.detach().transpose(-1, -2)) * scale
+    if causal:
+        s = s.masked_fill(torch.ones(24, 24, dtype=torch.bool).triu(1), float("-inf"))
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), atol=1e-12)
+
+
+# ---------------------------------------------------------------- backward
+
+def _loss(q, k, v, do, causal, scale):
+    o, _ = oracle.forward(q, k, v, causal, scale)
+    return float(np.sum(o * do))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,Hkv", [(2, 2), (4, 2)])
+def test_backward_matches_finite_differences(causal, H, Hkv):
+    q, k, v, do = rnd(1, H, Hkv, 7, 4, 20)
+    scale = 0.45
+    dq, dk, dv = oracle.backward(q, k, v, do, causal, scale)
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            old = x[idx]
+            x[idx] = old + eps
+            fp = _loss(q, k, v, do, causal, scale)
+            x[idx] = old - eps
+            fm = _loss(q, k, v, do, causal, scale)
+            x[idx] = old
+            num[idx] = (fp - fm) / (2 * eps)
+        np.testing.assert_allclose(g, num, atol=2e-8, err_msg=name)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_identities(causal):
+    q, k, v, do = rnd(2, 4, 2, 31, 8, 21)
+    scale = 0.3
+    dq, dk, dv = oracle.backward(q, k, v, do, causal, scale)
+    # rows of dS sum to zero, so the key gradients of a K/V head sum to zero
+    np.testing.assert_allclose(dk.sum(axis=1), 0.0, atol=1e-12)
+    # rows of P sum to one, so the value gradients sum to the group's dO
+    grp = do.reshape(2, 31, 2, 2, 8).sum(axis=3)
+    np.testing.assert_allclose(dv.sum(axis=1), grp.sum(axis=1), atol=1e-12)
+    if causal:
+        # the first query sees one key only: its softmax is constant
+        np.testing.assert_allclose(dq[:, 0], 0.0, atol=1e-14)
+    # sum_j P_ij dP_ij equals dO_i . O_i
+    o, _ = oracle.forward(q, k, v, causal, scale)
+    for h in range(4):
+        p = oracle.probs(q, k, scale, causal, 1, h)
+        dp = do[1, :, h] @ v[1, :, h // 2].T
+        np.testing.assert_allclose((p * dp).sum(axis=1), np.sum(do[1, :, h] * o[1, :, h], axis=1), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_heads_equal_repeated_kv(causal):
+    q, k, v, do = rnd(1, 6, 2, 13, 8, 22)
+    G = 3
+    kr = np.repeat(k, G, axis=2)          # head h -> kv head h // G
+    vr = np.repeat(v, G, axis=2)
+    o1, l1 = oracle.forward(q, k, v, causal, 0.5)
+    o2, l2 = oracle.forward(q, kr, vr, causal, 0.5)
+    np.testing.assert_allclose(o1, o2, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, atol=1e-14)
+    dq1, dk1, dv1 = oracle.backward(q, k, v, do, causal, 0.5)
+    dq2, dk2, dv2 = oracle.backward(q, kr, vr, do, causal, 0.5)
+    np.testing.assert_allclose(dq1, dq2, atol=1e-13)
+    np.testing.assert_allclose(dk1, dk2.reshape(1, 13, 2, G, 8).sum(axis=3), atol=1e-13)
+    np.testing.assert_allclose(dv1, dv2.reshape(1, 13, 2, G, 8).sum(axis=3), atol=1e-13)
+
+
+# ---------------------------------------------------------------- merge
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_merge_of_two_key_chunks_equals_full(causal):
+    q, k, v, _ = rnd(2, 2, 2, 40, 8, 23)
+    scale = 0.33
+    o, lse = oracle.forward(q, k, v, causal, scale)
+    cut = 17
+    # query rows [cut, 40) against keys [0, cut) and [cut, 40)
+    qa = q[:, cut:]
+    oa, la = oracle.forward(qa, k[:, :cut], v[:, :cut], causal, scale, q_offset=cut, k_offset=0)
+    ob, lb = oracle.forward(qa, k[:, cut:], v[:, cut:], causal, scale, q_offset=cut, k_offset=cut)
+    om, lm = oracle.merge(oa, la, ob, lb)
+    np.testing.assert_allclose(om, o[:, cut:], atol=1e-13)
+    np.testing.assert_allclose(lm, lse[:, :, cut:], atol=1e-13)
+    # order independence
+    om2, lm2 = oracle.merge(ob, lb, oa, la)
+    np.testing.assert_allclose(om2, om, atol=1e-15)
+    np.testing.assert_allclose(lm2, lm, atol=1e-15)
+
+
+def test_merge_associative_and_identity():
+    q, k, v, _ = rnd(1, 1, 1, 30, 4, 24)
+    parts = [oracle.forward(q, k[:, a:b], v[:, a:b], False, 0.6)
+             for a, b in ((0, 7), (7, 19), (19, 30))]
+    (o0, l0), (o1, l1), (o2, l2) = parts
+    left = oracle.merge(*oracle.merge(o0, l0, o1, l1), o2, l2)
+    right = oracle.merge(o0, l0, *oracle.merge(o1, l1, o2, l2))
+    full = oracle.forward(q, k, v, False, 0.6)
+    for a, b in zip(left, right):
+        np.testing.assert_allclose(a, b, atol=1e-13)
+    np.testing.assert_allclose(left[0], full[0], atol=1e-13)
+    np.testing.assert_allclose(left[1], full[1], atol=1e-13)
+    # the empty partial (o = 0, lse = -inf) is the identity; two empties stay empty
+    zo = np.zeros_like(o0)
+    zl = np.full_like(l0, -np.inf)
+    om, lm = oracle.merge(o0, l0, zo, zl)
+    np.testing.assert_array_equal(om, o0)
+    np.testing.assert_array_equal(lm, l0)
+    oe, le = oracle.merge(zo, zl, zo, zl)
+    assert np.all(oe == 0) and np.all(le == -np.inf)
+
+
+def test_chunk_pairs_merge_to_full_causal():
+    # every causal chunk pair (i, j<=i) of P chunks, merged per query chunk
+    q, k, v, _ = rnd(1, 2, 1, 48, 8, 25)
+    P, R = 4, 12
+    o, lse = oracle.forward(q, k, v, True, 0.4)
+    for i in range(P):
+        qi = q[:, i * R:(i + 1) * R]
+        acc = None
+        for j in range(i + 1):
+            part = oracle.forward(qi, k[:, j * R:(j + 1) * R], v[:, j * R:(j + 1) * R],
+                                  i == j, 0.4, q_offset=i * R, k_offset=j * R)
+            acc = part if acc is None else oracle.merge(*acc, *part)
+        np.testing.assert_allclose(acc[0], o[:, i * R:(i + 1) * R], atol=1e-13)
+        np.testing.assert_allclose(acc[1], lse[:, :, i * R:(i + 1) * R], atol=1e-13)
+
+
+# ---------------------------------------------------------------- tiled online softmax
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("br,bc", [(16, 16), (8, 32), (32, 8), (13, 7), (64, 64)])
+def test_tiled_online_softmax_equals_naive(causal, br, bc):
+    q, k, v, _ = rnd(1, 2, 1, 45, 8, 26, gain=3.0)
+    o1, l1 = oracle.forward(q, k, v, causal, 0.4)
+    o2, l2 = oracle.tiled_forward(q, k, v, causal, 0.4, br, bc)
+    np.testing.assert_allclose(o2, o1, atol=TIGHT)
+    np.testing.assert_allclose(l2, l1, atol=TIGHT)
+
+
+# ---------------------------------------------------------------- sampled-row helpers
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_row_helpers_match_full(causal):
+    q, k, v, do = rnd(2, 4, 2, 50, 8, 27)
+    scale = 0.3
+    o, lse = oracle.forward(q, k, v, causal, scale)
+    dq, dk, dv = oracle.backward(q, k, v, do, causal, scale)
+    rows = np.array([0, 1, 17, 49])
+    for b, h in ((0, 0), (1, 3)):
+        ro, rl = oracle.forward_rows(q, k, v, causal, scale, b, h, rows)
+        np.testing.assert_allclose(ro, o[b, rows, h], atol=1e-13)
+        np.testing.assert_allclose(rl, lse[b, h, rows], atol=1e-13)
+        np.testing.assert_allclose(oracle.backward_dq_rows(q, k, v, do, causal, scale, b, h, rows),
+                                   dq[b, rows, h], atol=1e-13)
+    for b, g in ((0, 1), (1, 0)):
+        rk, rv = oracle.backward_dkdv_rows(q, k, v, do, causal, scale, b, g, rows, row_block=16)
+        np.testing.assert_allclose(rk, dk[b, rows, g], atol=1e-12)
+        np.testing.assert_allclose(rv, dv[b, rows, g], atol=1e-12)
+
+
+def test_workload_draws_are_seeded_and_rounded():
+    a = draw(1, 2, 1, 8, 4, seed=3)
+    b = draw(1, 2, 1, 8, 4, seed=3)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+        assert x.dtype == torch.bfloat16
+    # the oracle consumes the rounded values exactly
+    q = as_f64(a[0])
+    assert np.array_equal(q, a[0].float().double().numpy())

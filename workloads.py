@@ -1,0 +1,102 @@
+"""Seeded synthetic inputs for the attention hot path.
+
+This module only draws and casts numbers; it holds none of the attention
+arithmetic. Both the oracle-side tests and the GPU path take their inputs from
+here, so the two sides see bit-identical values.
+
+Workloads (shapes of the models the pages train, with iid N(0,1) data standing
+in for real activations -- the pages' datasets and weights are not used):
+
+* ``tiny``     -- exactness case, fp32, N=128, d=64.
+* ``gpt2``     -- GPT-2-small attention shape at sequence length 1K (the
+  FlashAttention abstract's GPT-2 workload), bf16, causal.
+* ``bert``     -- BERT-large attention shape at sequence length 512 (the
+  FlashAttention abstract's BERT-large workload), bf16, non-causal.
+* ``llama16k`` -- Llama-7B heads (DistFlashAttn reviews, the Llama-7B
+  experiments) at a 16K context, bf16, causal; also run as 4 KV chunks.
+* ``gqa64k``   -- grouped-query attention (DistFlashAttn reviews, the GQA
+  setting) with 32 query heads over 8 K/V heads at a 64K context, bf16,
+  causal, processed as 8 chunks.
+
+Draw order (fixed): ``torch.Generator('cpu').manual_seed(seed)``, then
+``randn`` in float32 for Q, K, V, dO at their [B, N, heads, d] shapes, then a
+round-to-nearest-even cast to the compute dtype.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    Hkv: int
+    N: int
+    d: int
+    dtype: str                 # "f32" or "bf16"
+    causal: tuple              # mask settings the workload is run with
+    chunks: int = 1            # KV chunks for the chunked driver (1 = single pass)
+    seed: int = 1
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    @property
+    def G(self) -> int:
+        return self.H // self.Hkv
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 2, 2, 128, 64, "f32", (False, True), 1, seed=1),
+    "gpt2": Workload("gpt2", 8, 12, 12, 1024, 64, "bf16", (True,), 1, seed=2),
+    "bert": Workload("bert", 32, 16, 16, 512, 64, "bf16", (False,), 1, seed=3),
+    "llama16k": Workload("llama16k", 1, 32, 32, 16384, 128, "bf16", (True,), 4, seed=4),
+    "gqa64k": Workload("gqa64k", 1, 32, 8, 65536, 128, "bf16", (True,), 8, seed=5),
+}
+
+
+def draw(B: int, H: int, Hkv: int, N: int, d: int, seed: int,
+         dtype: torch.dtype = torch.bfloat16, q_gain: float = 1.0):
+    """Return (q, k, v, do) as CPU tensors of ``dtype`` in [B, N, heads, d].
+
+    ``q_gain`` multiplies the fp32 Q draw before the cast; a gain well above 1
+    gives peaked softmax rows (stress inputs), 0 gives uniform rows.
+    """
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    q = torch.randn((B, N, H, d), generator=g, dtype=torch.float32)
+    k = torch.randn((B, N, Hkv, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, N, Hkv, d), generator=g, dtype=torch.float32)
+    do = torch.randn((B, N, H, d), generator=g, dtype=torch.float32)
+    if q_gain != 1.0:
+        q = q * q_gain
+    return tuple(t.to(dtype) for t in (q, k, v, do))
+
+
+def draw_workload(w: Workload, seed: int | None = None, N: int | None = None):
+    """Inputs for workload ``w`` (optionally at a shorter sequence length)."""
+    return draw(w.B, w.H, w.Hkv, w.N if N is None else N, w.d,
+                w.seed if seed is None else seed, w.torch_dtype)
+
+
+def as_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact upcast of a CPU tensor (bf16 or fp32) to a float64 numpy array."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def flops(B: int, H: int, N: int, d: int, causal: bool) -> tuple[float, float]:
+    """Algorithmic FLOPs (forward, backward) under the 4*N^2*d convention.
+
+    Forward counts the two N x N x d products (2 FLOP per multiply-add each),
+    halved under a causal mask; backward counts 2.5x the forward.
+    H is the number of query heads, also under grouped-query attention.
+    """
+    f = 4.0 * B * H * N * N * d
+    if causal:
+        f *= 0.5
+    return f, 2.5 * f
