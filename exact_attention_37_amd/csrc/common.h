@@ -1,0 +1,53 @@
+// Shared device/host definitions of libmiattn (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace miattn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// One attention call on a rectangular block of the problem: query rows
+// [q_start, q_start + Nq) against key rows [k_start, k_start + Nk) of a
+// sequence of length N. Every tensor (including chunk scratch buffers) has
+// the full-sequence layout, so a row is always addressed by its absolute
+// position: q/o/dout/dq row i at q_start + i, k/v/dk/dv row j at k_start + j,
+// lse/dsum entry (b, h, q_start + i).
+struct Params {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;           // forward output; backward: the forward's o (read)
+  float* lse;        // [B, H, N]
+  const void* dout;  // backward only
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsum;       // backward: rowsum(dout * o), [B, H, N]
+  int B, H, Hkv, G;
+  int N;             // full sequence length: row strides and [B,H,N] strides
+  int Nq, Nk;        // rows of this block
+  int q_start, k_start;
+  int d;
+  int causal;        // mask keys whose absolute position exceeds the query's
+  float scale;
+  int accumulate;        // backward: add into float32 dq/dk/dv
+};
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
+
+}  // namespace miattn

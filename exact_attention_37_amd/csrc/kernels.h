@@ -1,0 +1,33 @@
+// Launchers of the libmiattn kernels (host side). Each returns the HIP error
+// of its launch(es); none synchronises.
+#pragma once
+
+#include "common.h"
+
+namespace miattn {
+
+// float32 / vector-ALU kernels (dtype 0 = float32, 1 = bf16 inputs).
+hipError_t launch_fwd_simt(const Params& p, int dtype, bool out_f32, hipStream_t s);
+hipError_t launch_bwd_simt(const Params& p, int dtype, hipStream_t s);
+
+// bf16 matrix-core kernels (gfx950 MFMA).
+hipError_t launch_fwd_mfma(const Params& p, bool out_f32, hipStream_t s);
+hipError_t launch_bwd_mfma(const Params& p, float* dq_acc, hipStream_t s);
+
+// rowsum(dout * o) for query rows [row0, row0 + nrows) of every (b, h).
+hipError_t launch_bwd_pre(const void* o, const void* dout, float* dsum, int B, int H, int N,
+                          int d, int row0, int nrows, int dtype, hipStream_t s);
+
+// LSE merge over rows [row0, row0 + nrows); all buffers full-sequence layout.
+// ta/tb/to: element types of o_a, o_b, o (0 = float32, 1 = bf16).
+hipError_t launch_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                        void* o, float* lse, int B, int H, int N, int d, int row0, int nrows,
+                        int ta, int tb, int to, hipStream_t s);
+
+// dst[i] = (bf16 or float) src[i] for n float32 elements.
+hipError_t launch_convert(const float* src, void* dst, long long n, int dtype, hipStream_t s);
+
+// dst[i] = value for n float32 elements (a kernel, so it can sit in a graph).
+hipError_t launch_fill(float* dst, long long n, float value, hipStream_t s);
+
+}  // namespace miattn

@@ -1,0 +1,359 @@
+// C ABI of libmiattn: argument validation, kernel selection, scratch
+// management and the chunk-pair driver. No entry point synchronises the host.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../../include/miattn.h"
+#include "common.h"
+#include "kernels.h"
+
+using miattn::Params;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return MIATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+Range span(const void* p, long long bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return {a, a + (uintptr_t)bytes};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int check_common(int B, int H, int Hkv, int N, int d, int dtype) {
+  if (B < 1 || H < 1 || Hkv < 1 || N < 1)
+    return fail(MIATTN_EINVAL, "B, H, Hkv and N must be >= 1");
+  if (H % Hkv != 0) return fail(MIATTN_EINVAL, "H must be a multiple of Hkv");
+  if (d != 64 && d != 128) return fail(MIATTN_EUNSUPPORTED, "head dimension d must be 64 or 128");
+  if (dtype != MIATTN_F32 && dtype != MIATTN_BF16) return fail(MIATTN_EUNSUPPORTED, "dtype must be MIATTN_F32 or MIATTN_BF16");
+  if (B > 65535 || H > 65535) return fail(MIATTN_EUNSUPPORTED, "B and H must be <= 65535");
+  // [B, H, N] statistics and row positions are indexed with 32-bit ints
+  if ((long long)B * H * N >= (1LL << 31) || (long long)N * H * d >= (1LL << 31))
+    return fail(MIATTN_EUNSUPPORTED, "problem too large for 32-bit row indexing");
+  return MIATTN_OK;
+}
+
+int check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* p : ps) {
+    if (p == nullptr) return fail(MIATTN_EINVAL, "null pointer argument");
+    if (!aligned16(p)) return fail(MIATTN_EINVAL, "pointer not 16-byte aligned");
+  }
+  return MIATTN_OK;
+}
+
+int launch_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MIATTN_OK;
+  return fail(MIATTN_ELAUNCH, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+size_t esize(int dtype) { return dtype == MIATTN_F32 ? 4 : 2; }
+
+Params make_params(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
+                   int N, int d, int causal, float scale) {
+  Params p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.H = H;
+  p.Hkv = Hkv;
+  p.G = H / Hkv;
+  p.N = N;
+  p.Nq = N;
+  p.Nk = N;
+  p.q_start = 0;
+  p.k_start = 0;
+  p.d = d;
+  p.causal = causal;
+  p.scale = scale;
+  return p;
+}
+
+// One forward block (rows and offsets in p). out_f32: o is float32.
+hipError_t fwd_block(const Params& p, int dtype, bool out_f32, hipStream_t s) {
+  return miattn::launch_fwd_simt(p, dtype, out_f32, s);
+}
+
+// One backward block: p.dsum must hold rowsum(dout * o) of these rows.
+// dq_acc: float32 scratch the bf16 kernels accumulate dQ into (zeroed by the
+// caller), or null when p.accumulate already makes p.dq a float32 buffer.
+hipError_t bwd_block(const Params& p, int dtype, float* dq_acc, hipStream_t s) {
+  (void)dq_acc;
+  return miattn::launch_bwd_simt(p, dtype, s);
+}
+
+struct Scratch {
+  std::vector<void*> ptrs;
+  hipStream_t s;
+  explicit Scratch(hipStream_t st) : s(st) {}
+  void* get(size_t bytes) {
+    void* p = nullptr;
+    if (hipMallocAsync(&p, bytes, s) != hipSuccess) return nullptr;
+    ptrs.push_back(p);
+    return p;
+  }
+  ~Scratch() {
+    for (void* p : ptrs) (void)hipFreeAsync(p, s);
+  }
+};
+
+// Balanced rounds of causal chunk pairs (i, j), j <= i, for P chunks.
+// Round 0: the diagonal pairs and the pairs at distance P/2; round t
+// (1 <= t < P/2): the pairs at distance t and at distance P - t. With a
+// diagonal pair counted as half a pair, every round holds P pairs of work.
+std::vector<std::vector<std::pair<int, int>>> balanced_rounds(int P) {
+  std::vector<std::vector<std::pair<int, int>>> rounds;
+  if (P == 1) {
+    rounds.push_back({{0, 0}});
+    return rounds;
+  }
+  std::vector<std::pair<int, int>> r0;
+  for (int i = 0; i < P; ++i) r0.push_back({i, i});
+  for (int i = P / 2; i < P; ++i) r0.push_back({i, i - P / 2});
+  rounds.push_back(r0);
+  for (int t = 1; t < P / 2; ++t) {
+    std::vector<std::pair<int, int>> r;
+    for (int i = t; i < P; ++i) r.push_back({i, i - t});
+    for (int i = P - t; i < P; ++i) r.push_back({i, i - (P - t)});
+    rounds.push_back(r);
+  }
+  return rounds;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_last_error(void) { return g_err.c_str(); }
+
+const char* attn_version(void) { return "libmiattn 0.1 (gfx950)"; }
+
+int attn_chunk_schedule(int nchunks, int* round_of, int* q_chunk, int* k_chunk, int capacity) {
+  if (nchunks < 1 || (nchunks > 1 && nchunks % 2 != 0)) return -1;
+  const int npairs = nchunks * (nchunks + 1) / 2;
+  if (capacity < npairs || !round_of || !q_chunk || !k_chunk) return -1;
+  int n = 0, r = 0;
+  for (const auto& round : balanced_rounds(nchunks)) {
+    for (const auto& pr : round) {
+      round_of[n] = r;
+      q_chunk[n] = pr.first;
+      k_chunk[n] = pr.second;
+      ++n;
+    }
+    ++r;
+  }
+  return n;
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
+             int d, int causal, float scale, void* stream, int dtype) {
+  int st = check_common(B, H, Hkv, N, d, dtype);
+  if (st) return st;
+  if ((st = check_ptrs({q, k, v, o, lse}))) return st;
+  if (causal != 0 && causal != 1) return fail(MIATTN_EINVAL, "causal must be 0 or 1");
+  if (!std::isfinite(scale)) return fail(MIATTN_EINVAL, "scale must be finite");
+  const long long qb = (long long)B * N * H * d * esize(dtype);
+  const long long kb = (long long)B * N * Hkv * d * esize(dtype);
+  const Range ro = span(o, qb), rl = span(lse, (long long)B * H * N * 4);
+  for (Range r : {span(q, qb), span(k, kb), span(v, kb)})
+    if (overlap(ro, r) || overlap(rl, r)) return fail(MIATTN_EINVAL, "o/lse must not alias q, k or v");
+  if (overlap(ro, rl)) return fail(MIATTN_EINVAL, "o and lse must not overlap");
+  Params p = make_params(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale);
+  if ((st = launch_status(fwd_block(p, dtype, dtype == MIATTN_F32, (hipStream_t)stream), "attn_fwd"))) return st;
+  return ok();
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
+             int Hkv, int N, int d, int causal, float scale, void* stream, const void* dout, void* dq, void* dk,
+             void* dv, int dtype, int accumulate) {
+  int st = check_common(B, H, Hkv, N, d, dtype);
+  if (st) return st;
+  if ((st = check_ptrs({q, k, v, o, lse, dout, dq, dk, dv}))) return st;
+  if (causal != 0 && causal != 1) return fail(MIATTN_EINVAL, "causal must be 0 or 1");
+  if (accumulate != 0 && accumulate != 1) return fail(MIATTN_EINVAL, "accumulate must be 0 or 1");
+  if (!std::isfinite(scale)) return fail(MIATTN_EINVAL, "scale must be finite");
+  const size_t ge = accumulate ? 4 : esize(dtype);
+  const long long qb = (long long)B * N * H * d * esize(dtype), kb = (long long)B * N * Hkv * d * esize(dtype);
+  const Range rdq = span(dq, (long long)B * N * H * d * ge), rdk = span(dk, (long long)B * N * Hkv * d * ge),
+              rdv = span(dv, (long long)B * N * Hkv * d * ge);
+  for (Range out : {rdq, rdk, rdv})
+    for (Range in : {span(q, qb), span(k, kb), span(v, kb), span(o, qb), span(dout, qb),
+                     span(lse, (long long)B * H * N * 4)})
+      if (overlap(out, in)) return fail(MIATTN_EINVAL, "dq/dk/dv must not alias an input");
+  if (overlap(rdq, rdk) || overlap(rdq, rdv) || overlap(rdk, rdv))
+    return fail(MIATTN_EINVAL, "dq, dk and dv must not overlap");
+
+  hipStream_t s = (hipStream_t)stream;
+  Scratch scratch(s);
+  float* dsum = (float*)scratch.get((size_t)B * H * N * 4);
+  if (!dsum) return fail(MIATTN_ENOMEM, "hipMallocAsync failed for the rowsum vector");
+  Params p = make_params(q, k, v, const_cast<void*>(o), const_cast<float*>(lse), B, H, Hkv, N, d, causal, scale);
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.dsum = dsum;
+  p.accumulate = accumulate;
+  if ((st = launch_status(miattn::launch_bwd_pre(o, dout, dsum, B, H, N, d, 0, N, dtype, s), "bwd preprocess")))
+    return st;
+  float* dq_acc = nullptr;
+  const long long nq = (long long)B * N * H * d;
+  if (false && dtype == MIATTN_BF16 && !accumulate) {
+    dq_acc = (float*)scratch.get((size_t)nq * 4);
+    if (!dq_acc) return fail(MIATTN_ENOMEM, "hipMallocAsync failed for the dq accumulator");
+    if ((st = launch_status(miattn::launch_fill(dq_acc, nq, 0.f, s), "dq clear"))) return st;
+  }
+  if ((st = launch_status(bwd_block(p, dtype, dq_acc, s), "attn_bwd"))) return st;
+  if (dq_acc && (st = launch_status(miattn::launch_convert(dq_acc, dq, nq, dtype, s), "dq convert"))) return st;
+  return ok();
+}
+
+int attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* o, float* lse, int B,
+               int H, int N, int d, int dtype, void* stream) {
+  int st = check_common(B, H, H, N, d, dtype);
+  if (st) return st;
+  if ((st = check_ptrs({o_a, lse_a, o_b, lse_b, o, lse}))) return st;
+  const int t = dtype == MIATTN_BF16 ? 1 : 0;
+  if ((st = launch_status(miattn::launch_merge(o_a, lse_a, o_b, lse_b, o, lse, B, H, N, d, 0, N, t, t, t,
+                                               (hipStream_t)stream),
+                          "attn_merge")))
+    return st;
+  return ok();
+}
+
+int attn_fwd_chunked(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
+                     int d, float scale, void* stream, int dtype, int nchunks) {
+  int st = check_common(B, H, Hkv, N, d, dtype);
+  if (st) return st;
+  if ((st = check_ptrs({q, k, v, o, lse}))) return st;
+  if (!std::isfinite(scale)) return fail(MIATTN_EINVAL, "scale must be finite");
+  if (nchunks < 1 || N % nchunks != 0 || (nchunks > 1 && nchunks % 2 != 0))
+    return fail(MIATTN_EINVAL, "nchunks must be 1 or an even divisor of N");
+  const long long qb = (long long)B * N * H * d * esize(dtype), kb = (long long)B * N * Hkv * d * esize(dtype);
+  const Range ro = span(o, qb), rl = span(lse, (long long)B * H * N * 4);
+  for (Range r : {span(q, qb), span(k, kb), span(v, kb)})
+    if (overlap(ro, r) || overlap(rl, r)) return fail(MIATTN_EINVAL, "o/lse must not alias q, k or v");
+
+  hipStream_t s = (hipStream_t)stream;
+  const int R = N / nchunks;
+  const long long no = (long long)B * N * H * d, nl = (long long)B * H * N;
+  Scratch scratch(s);
+  // running (merged-so-far) result per query chunk, and one partial per pair
+  float* run_o = (float*)scratch.get(no * 4);
+  float* run_l = (float*)scratch.get(nl * 4);
+  float* part_o = (float*)scratch.get(no * 4);
+  float* part_l = (float*)scratch.get(nl * 4);
+  if (!run_o || !run_l || !part_o || !part_l) return fail(MIATTN_ENOMEM, "hipMallocAsync failed for chunk partials");
+
+  std::vector<int> done(nchunks, 0);   // pairs merged into each query chunk so far
+  for (const auto& round : balanced_rounds(nchunks)) {
+    for (const auto& pr : round) {
+      const int i = pr.first, j = pr.second;
+      const bool last = done[i] == i;   // the query chunk's final pair
+      Params p = make_params(q, k, v, nullptr, nullptr, B, H, Hkv, N, d, i == j, scale);
+      p.Nq = R;
+      p.Nk = R;
+      p.q_start = i * R;
+      p.k_start = j * R;
+      if (done[i] == 0 && last) {
+        // a single pair (query chunk 0): write the result directly
+        p.o = o;
+        p.lse = lse;
+        if ((st = launch_status(fwd_block(p, dtype, dtype == MIATTN_F32, s), "chunk forward"))) return st;
+      } else if (done[i] == 0) {
+        p.o = run_o;
+        p.lse = run_l;
+        if ((st = launch_status(fwd_block(p, dtype, true, s), "chunk forward"))) return st;
+      } else {
+        p.o = part_o;
+        p.lse = part_l;
+        if ((st = launch_status(fwd_block(p, dtype, true, s), "chunk forward"))) return st;
+        const int tout = last ? (dtype == MIATTN_BF16 ? 1 : 0) : 0;
+        void* dst_o = last ? o : (void*)run_o;
+        float* dst_l = last ? lse : run_l;
+        if ((st = launch_status(miattn::launch_merge(run_o, run_l, part_o, part_l, dst_o, dst_l, B, H, N, d, i * R,
+                                                     R, 0, 0, tout, s),
+                                "chunk merge")))
+          return st;
+      }
+      done[i] += 1;
+    }
+  }
+  return ok();
+}
+
+int attn_bwd_chunked(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
+                     int Hkv, int N, int d, float scale, void* stream, const void* dout, void* dq, void* dk, void* dv,
+                     int dtype, int nchunks) {
+  int st = check_common(B, H, Hkv, N, d, dtype);
+  if (st) return st;
+  if ((st = check_ptrs({q, k, v, o, lse, dout, dq, dk, dv}))) return st;
+  if (!std::isfinite(scale)) return fail(MIATTN_EINVAL, "scale must be finite");
+  if (nchunks < 1 || N % nchunks != 0 || (nchunks > 1 && nchunks % 2 != 0))
+    return fail(MIATTN_EINVAL, "nchunks must be 1 or an even divisor of N");
+  const long long qb = (long long)B * N * H * d * esize(dtype), kb = (long long)B * N * Hkv * d * esize(dtype);
+  const Range rdq = span(dq, qb), rdk = span(dk, kb), rdv = span(dv, kb);
+  for (Range out : {rdq, rdk, rdv})
+    for (Range in : {span(q, qb), span(k, kb), span(v, kb), span(o, qb), span(dout, qb),
+                     span(lse, (long long)B * H * N * 4)})
+      if (overlap(out, in)) return fail(MIATTN_EINVAL, "dq/dk/dv must not alias an input");
+
+  hipStream_t s = (hipStream_t)stream;
+  const int R = N / nchunks;
+  const long long nq = (long long)B * N * H * d, nk = (long long)B * N * Hkv * d;
+  Scratch scratch(s);
+  float* dsum = (float*)scratch.get((size_t)B * H * N * 4);
+  float* aq = (float*)scratch.get(nq * 4);
+  float* ak = (float*)scratch.get(nk * 4);
+  float* av = (float*)scratch.get(nk * 4);
+  if (!dsum || !aq || !ak || !av) return fail(MIATTN_ENOMEM, "hipMallocAsync failed for gradient accumulators");
+  if ((st = launch_status(miattn::launch_fill(aq, nq, 0.f, s), "clear"))) return st;
+  if ((st = launch_status(miattn::launch_fill(ak, nk, 0.f, s), "clear"))) return st;
+  if ((st = launch_status(miattn::launch_fill(av, nk, 0.f, s), "clear"))) return st;
+  if ((st = launch_status(miattn::launch_bwd_pre(o, dout, dsum, B, H, N, d, 0, N, dtype, s), "bwd preprocess")))
+    return st;
+  for (const auto& round : balanced_rounds(nchunks)) {
+    for (const auto& pr : round) {
+      const int i = pr.first, j = pr.second;
+      Params p = make_params(q, k, v, const_cast<void*>(o), const_cast<float*>(lse), B, H, Hkv, N, d, i == j, scale);
+      p.Nq = R;
+      p.Nk = R;
+      p.q_start = i * R;
+      p.k_start = j * R;
+      p.dout = dout;
+      p.dq = aq;
+      p.dk = ak;
+      p.dv = av;
+      p.dsum = dsum;
+      p.accumulate = 1;
+      if ((st = launch_status(bwd_block(p, dtype, nullptr, s), "chunk backward"))) return st;
+    }
+  }
+  if ((st = launch_status(miattn::launch_convert(aq, dq, nq, dtype, s), "dq convert"))) return st;
+  if ((st = launch_status(miattn::launch_convert(ak, dk, nk, dtype, s), "dk convert"))) return st;
+  if ((st = launch_status(miattn::launch_convert(av, dv, nk, dtype, s), "dv convert"))) return st;
+  return ok();
+}
+
+}  // extern "C"

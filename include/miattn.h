@@ -1,0 +1,147 @@
+/* libmiattn -- exact attention for one AMD Instinct MI355X (gfx950) GPU.
+ *
+ * C ABI only: plain pointers, ints and floats. Device pointers are HIP
+ * device memory; `stream` is a hipStream_t passed as void* (NULL = the
+ * default stream). Every call only enqueues work on `stream` and returns; no
+ * call synchronises the host. Kernel faults surface at the caller's next
+ * synchronisation, not as a return code.
+ *
+ * Operation (all entry points): exact attention
+ *     O = softmax(scale * Q K^T  [+ causal mask]) V
+ * as written out on the DistFlashAttn reviews page (review 1 summary) and
+ * called exact, not approximate, on the FlashAttention abstract page; the
+ * saved per-row statistic is the logsumexp (FlashAttention-2 reviews page,
+ * reviewer 2, point 2).
+ *
+ * Tensor layouts (all contiguous, row-major):
+ *   q, o, dout, dq : [B, N, H,   d]   element type `dtype`
+ *   k, v, dk, dv   : [B, N, Hkv, d]   element type `dtype`
+ *   lse            : [B, H, N]        float32, natural-log logsumexp of the
+ *                                     scaled, masked scores of each row
+ * Query head h reads K/V head h / (H / Hkv) (grouped-query attention; the
+ * FlashAttention-2 reviews page, reviewer 1, MQA/GQA paragraph of the
+ * backward section). Under `causal`, key j is visible to query i iff j <= i.
+ *
+ * Status codes: every entry point returns MIATTN_OK or an error code and
+ * leaves a message for attn_last_error() (per host thread). Arguments are
+ * validated before anything is enqueued; on error nothing is enqueued.
+ *   MIATTN_EINVAL       null pointer, B/H/Hkv/N < 1, H % Hkv != 0, causal not
+ *                       0/1, non-finite scale, pointer not 16-byte aligned,
+ *                       nchunks not a positive divisor of N (chunked calls),
+ *                       outputs aliasing inputs where forbidden.
+ *   MIATTN_EUNSUPPORTED d not 64 or 128, unknown dtype, or a size whose
+ *                       element count does not fit the 32-bit row indexing.
+ *   MIATTN_ELAUNCH      the HIP runtime reported an error at launch.
+ *   MIATTN_ENOMEM       a stream-ordered scratch allocation failed.
+ *
+ * Ownership: the caller allocates and owns every buffer passed in. The
+ * library keeps no pointer after a call returns beyond the work enqueued on
+ * `stream`. Scratch that a call needs is taken with hipMallocAsync on
+ * `stream` and released with hipFreeAsync on the same stream.
+ */
+#ifndef MIATTN_H
+#define MIATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MIATTN_OK = 0,
+  MIATTN_EINVAL = 1,
+  MIATTN_EUNSUPPORTED = 2,
+  MIATTN_ELAUNCH = 3,
+  MIATTN_ENOMEM = 4
+} miattn_status;
+
+typedef enum {
+  MIATTN_F32 = 0,   /* float32 in and out; float32 arithmetic */
+  MIATTN_BF16 = 1   /* bfloat16 in and out; bf16 matrix products with float32 accumulation */
+} miattn_dtype;
+
+/* Forward pass: writes o and lse.
+ * A tiled pass with online-softmax rescaling (FlashAttention abstract page:
+ * tiling between HBM and on-chip memory; FlashAttention-2 reviews page,
+ * reviewer 2, points 1-3: deferred rescaling, logsumexp saved, parallelism
+ * over the sequence). Key tiles entirely above the diagonal are skipped
+ * under `causal` (FlashAttention-2 reviews page, reviewer 4, section 3.1).
+ * o and lse must not alias q, k or v. */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int Hkv, int N, int d, int causal, float scale,
+             void* stream, int dtype);
+
+/* Backward pass: from q, k, v, the forward's o and lse, and dout = dL/dO,
+ * produces dq, dk, dv without forming the N x N matrix. The forward is not
+ * re-run: P is rebuilt tile by tile from the saved lse (DistFlashAttn
+ * reviews page, review 1 point 3: the backward needs no recomputation of the
+ * forward). dk and dv of a K/V head are summed over the query heads that
+ * read it.
+ *   accumulate = 0: dq, dk, dv have element type `dtype` and are overwritten.
+ *   accumulate = 1: dq, dk, dv are float32 buffers and the gradients are
+ *                   added to their contents.
+ * Scratch: one float32 [B, H, N] vector (rowsum(dout * o)) and, for
+ * accumulate = 0 with bf16, a float32 dq accumulator.
+ * Outputs must not alias any input or each other. */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             int B, int H, int Hkv, int N, int d, int causal, float scale,
+             void* stream, const void* dout, void* dq, void* dk, void* dv,
+             int dtype, int accumulate);
+
+/* Merge of two partial results of the same query rows over disjoint key
+ * sets a and b into the result over a u b (DistFlashAttn reviews page,
+ * reviews 1 and 4: partial chunk results are combined; BurstAttention
+ * rebuttal page: partial softmax results are combined across devices):
+ *     lse = ln(e^lse_a + e^lse_b)  (computed with the max factored out)
+ *     o   = e^(lse_a - lse) o_a + e^(lse_b - lse) o_b
+ * Rows where both lse are -inf give o = 0, lse = -inf.
+ * o_a, o_b, o: [B, N, H, d] of `dtype`; lse_a, lse_b, lse: [B, H, N] float32.
+ * In-place use is allowed: o may equal o_a or o_b, lse may equal lse_a or
+ * lse_b (each element is read before it is written by the same thread). */
+int attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+               void* o, float* lse, int B, int H, int N, int d, int dtype, void* stream);
+
+/* Forward pass of causal attention computed as nchunks x nchunks chunk
+ * pairs: the sequence is cut into nchunks chunks of N / nchunks rows; pair
+ * (i, j), j <= i, is attention of query chunk i over key chunk j (masked
+ * only when i == j), and the partials of a query chunk are combined with the
+ * merge above. Pairs are processed in balanced rounds: one round holds the
+ * diagonal pairs and the pairs at chunk distance nchunks/2, and round t
+ * (t = 1 .. nchunks/2 - 1) holds the pairs at distances t and nchunks - t,
+ * so every round carries the same amount of work (the DistFlashAttn reviews
+ * page, review 1 point 1 and review 3: redistributing causal work from later
+ * to earlier workers). nchunks must be even (or 1) and divide N.
+ * Same arguments and outputs as attn_fwd with causal = 1. Scratch: float32
+ * partial and running outputs, [B, N, H, d] and [B, H, N] each. */
+int attn_fwd_chunked(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int Hkv, int N, int d, float scale,
+                     void* stream, int dtype, int nchunks);
+
+/* Backward pass over the same chunk pairs and rounds as attn_fwd_chunked:
+ * every pair's gradients are taken with the final o and lse of its query
+ * chunk and summed in float32. Same arguments and outputs as attn_bwd with
+ * causal = 1 and accumulate = 0. Scratch: float32 dq, dk, dv accumulators
+ * and the [B, H, N] rowsum vector. */
+int attn_bwd_chunked(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     int B, int H, int Hkv, int N, int d, float scale,
+                     void* stream, const void* dout, void* dq, void* dk, void* dv,
+                     int dtype, int nchunks);
+
+/* The pair order used by the chunked entry points, for inspection (host
+ * only, no GPU work). Writes up to `capacity` entries: pair p belongs to
+ * round round_of[p] and is query chunk q_chunk[p] over key chunk k_chunk[p].
+ * Returns the number of pairs, nchunks * (nchunks + 1) / 2, or -1 if
+ * nchunks is not 1 or a positive even number or capacity is too small. */
+int attn_chunk_schedule(int nchunks, int* round_of, int* q_chunk, int* k_chunk, int capacity);
+
+/* Message of the last error on this host thread ("" after success). The
+ * pointer stays valid until the next call on this thread. */
+const char* attn_last_error(void);
+
+/* Library version string. */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIATTN_H */

@@ -202,10 +202,12 @@ def backward(q, k, v, do, causal, scale, row_block=512):
     return dq, dk, dv
 
 
-def _lse_all_rows(qh, kg, scale, causal, row_block=1024):
+def _lse_rows_from(qh, kg, scale, causal, row_lo, row_block=512):
+    """Logsumexp of query rows [row_lo, Nq) (entries below row_lo are unused)."""
     n = qh.shape[0]
     out = np.zeros(n)
-    for r0, r1 in _row_blocks(n, row_block):
+    for r0, r1 in _row_blocks(n - row_lo, row_block):
+        r0, r1 = r0 + row_lo, r1 + row_lo
         hi = r1 if causal else kg.shape[0]
         s = scores(qh[r0:r1], kg[:hi], scale, causal, np.arange(r0, r1), np.arange(hi))
         out[r0:r1] = _softmax_rows(s)[1]
@@ -231,12 +233,14 @@ def backward_dq_rows(q, k, v, do, causal, scale, b, h, rows):
     return out
 
 
-def backward_dkdv_rows(q, k, v, do, causal, scale, b, g, cols, row_block=1024):
+def backward_dkdv_rows(q, k, v, do, causal, scale, b, g, cols, row_block=512):
     """dK[b, cols, g] and dV[b, cols, g] for selected key rows of K/V head g,
     summed over the query heads of its group.
 
-    A key row's gradient needs P[i, j] for every query i, so each query
-    head's row logsumexps are computed first (exactly, at full key width)."""
+    A key row's gradient needs P[i, j] for every query i that sees it, so each
+    query head's row logsumexps are computed first (exactly, at full key
+    width). Under the causal mask only queries i >= min(cols) see any of the
+    selected keys; rows above that contribute exactly zero and are skipped."""
     H, Hkv = q.shape[2], k.shape[2]
     G = H // Hkv
     kg = np.asarray(k[b, :, g], np.float64)
@@ -245,11 +249,13 @@ def backward_dkdv_rows(q, k, v, do, causal, scale, b, g, cols, row_block=1024):
     N = q.shape[1]
     dk = np.zeros((len(cols), q.shape[3]))
     dv = np.zeros((len(cols), q.shape[3]))
+    row_lo = int(np.min(cols)) if causal else 0
     for h in range(g * G, (g + 1) * G):
         qh = np.asarray(q[b, :, h], np.float64)
         doh = np.asarray(do[b, :, h], np.float64)
-        lse = _lse_all_rows(qh, kg, scale, causal)
-        for r0, r1 in _row_blocks(N, row_block):
+        lse = _lse_rows_from(qh, kg, scale, causal, row_lo)
+        for r0, r1 in _row_blocks(N - row_lo, row_block):
+            r0, r1 = r0 + row_lo, r1 + row_lo
             # P[i, cols] and dP[i, cols] for this block of queries
             s = scores(qh[r0:r1], kg[cols], scale, causal, np.arange(r0, r1), cols)
             p = np.exp(s - lse[r0:r1, None])

@@ -1,0 +1,124 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+the header declares, rejects bad arguments before enqueuing anything, and
+its chunk-pair schedule covers every causal pair once in balanced rounds."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_37_amd as mi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "miattn.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(attn_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_loads_and_exports_header_symbols():
+    L = mi.lib()
+    names = header_functions()
+    assert {"attn_fwd", "attn_bwd", "attn_merge", "attn_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), "libmiattn.so does not export %s" % n
+    assert L.attn_version().startswith(b"libmiattn")
+
+
+def test_export_table_matches_header():
+    # nm-style check on the ELF dynamic symbol table (no GPU involved)
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", mi.library_path], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (attn_\w+)", out))
+    assert set(header_functions()) <= exported
+
+
+FAKE = 1 << 20          # a 16-byte aligned non-null address; never dereferenced
+vp = ctypes.c_void_p
+
+
+def fwd_call(**kw):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, o=FAKE * 4, lse=FAKE * 5, B=1, H=2, Hkv=2, N=4, d=64,
+             causal=0, scale=0.125, dtype=1)
+    a.update(kw)
+    return mi.lib().attn_fwd(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["o"]), vp(a["lse"]), a["B"], a["H"],
+                             a["Hkv"], a["N"], a["d"], a["causal"], a["scale"], None, a["dtype"])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(q=0), 1, "null"),
+    (dict(o=0), 1, "null"),
+    (dict(k=FAKE * 2 + 8), 1, "aligned"),
+    (dict(B=0), 1, ">= 1"),
+    (dict(N=0), 1, ">= 1"),
+    (dict(H=3, Hkv=2), 1, "multiple"),
+    (dict(d=96), 2, "64 or 128"),
+    (dict(d=32), 2, "64 or 128"),
+    (dict(dtype=7), 2, "dtype"),
+    (dict(causal=2), 1, "causal"),
+    (dict(scale=float("nan")), 1, "finite"),
+    (dict(scale=float("inf")), 1, "finite"),
+    (dict(o=FAKE), 1, "alias"),
+    (dict(lse=FAKE * 3), 1, "alias"),
+    (dict(N=1 << 24, H=256), 2, "too large"),
+])
+def test_fwd_rejects_bad_arguments(kw, code, msg):
+    assert fwd_call(**kw) == code
+    assert msg in mi.lib().attn_last_error().decode()
+
+
+def test_bwd_rejects_bad_arguments():
+    L = mi.lib()
+    base = [vp(FAKE * i) for i in range(1, 6)]
+    args = lambda dq, acc=0, d=64: base + [1, 2, 2, 4, d, 0, 0.1, None, vp(FAKE * 6), vp(dq), vp(FAKE * 8),
+                                         vp(FAKE * 9), 1, acc]
+    # every call below must be refused before anything is enqueued
+    assert L.attn_bwd(*args(FAKE)) == 1
+    assert b"alias" in L.attn_last_error()
+    assert L.attn_bwd(*args(FAKE * 7, acc=2)) == 1
+    assert L.attn_bwd(*args(FAKE * 7, d=80)) == 2
+    assert L.attn_bwd(*args(0)) == 1
+
+
+def test_merge_and_chunked_reject_bad_arguments():
+    L = mi.lib()
+    p = [vp(FAKE * i) for i in range(1, 7)]
+    assert L.attn_merge(*p, 1, 2, 4, 100, 1, None) == 2
+    assert L.attn_merge(vp(0), *p[1:], 1, 2, 4, 64, 1, None) == 1
+    q = [vp(FAKE * i) for i in range(1, 6)]
+    assert L.attn_fwd_chunked(*q, 1, 2, 2, 12, 64, 0.1, None, 1, 5) == 1      # 5 does not divide 12
+    assert L.attn_fwd_chunked(*q, 1, 2, 2, 12, 64, 0.1, None, 1, 3) == 1      # odd chunk count
+    assert L.attn_fwd_chunked(*q, 1, 2, 2, 12, 64, 0.1, None, 1, 0) == 1
+    b = [vp(FAKE * i) for i in range(1, 6)]
+    assert L.attn_bwd_chunked(*b, 1, 2, 2, 12, 64, 0.1, None, vp(FAKE * 6), vp(FAKE * 7), vp(FAKE * 8),
+                              vp(FAKE * 9), 1, 7) == 1
+
+
+@pytest.mark.parametrize("P", [1, 2, 4, 6, 8, 16])
+def test_chunk_schedule_covers_causal_pairs_in_balanced_rounds(P):
+    rounds = mi.balanced_rounds(P)
+    pairs = [pr for r in rounds for pr in r]
+    expect = {(i, j) for i in range(P) for j in range(i + 1)}
+    assert len(pairs) == len(expect) == P * (P + 1) // 2
+    assert set(pairs) == expect
+    if P > 1:
+        assert len(rounds) == P // 2
+        for r in rounds:
+            # a diagonal pair is half the work of an off-diagonal pair
+            work = sum(0.5 if i == j else 1.0 for i, j in r)
+            assert work == P
+            # a round holds pairs of at most two chunk distances (P/2 with the
+            # diagonal, or t and P - t), so no query chunk appears more than twice
+            from collections import Counter
+            assert max(Counter(i for i, _ in r).values()) <= 2
+
+
+def test_chunk_schedule_rejects_bad_counts():
+    arr = (ctypes.c_int * 64)()
+    L = mi.lib()
+    assert L.attn_chunk_schedule(3, arr, arr, arr, 64) == -1
+    assert L.attn_chunk_schedule(0, arr, arr, arr, 64) == -1
+    assert L.attn_chunk_schedule(8, arr, arr, arr, 10) == -1

@@ -1,0 +1,264 @@
+"""GPU parity: libmiattn (through its C ABI) against the float64 CPU oracle on
+the same seeded inputs.
+
+Small and medium workloads are compared element by element over every output;
+the long-context workloads (16K and 64K rows) are compared on sampled rows the
+oracle computes one at a time, plus properties that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_37_amd as mi
+import oracle
+from workloads import WORKLOADS, draw, draw_workload, as_f64
+from tests.helpers import (check_bf16, check_abs, check_rel, f64, default_scale,
+                           BF16_LSE_ABS)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def to_dev(*ts):
+    return [t.to(DEV) for t in ts]
+
+
+def run_fwd_bwd(q, k, v, do, causal, scale):
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    o, lse = mi.fwd(qd, kd, vd, causal, scale)
+    dq, dk, dv = mi.bwd(qd, kd, vd, o, lse, dod, causal, scale)
+    torch.cuda.synchronize()
+    return [f64(t) for t in (o, lse, dq, dk, dv)]
+
+
+def oracle_full(q, k, v, do, causal, scale):
+    qq, kk, vv, dd = (as_f64(t) for t in (q, k, v, do))
+    o, lse = oracle.forward(qq, kk, vv, causal, scale)
+    dq, dk, dv = oracle.backward(qq, kk, vv, dd, causal, scale)
+    return o, lse, dq, dk, dv
+
+
+def compare_full(gpu, ref, dtype):
+    names = ("o", "lse", "dq", "dk", "dv")
+    errs = {}
+    for n, g, r in zip(names, gpu, ref):
+        if dtype == torch.float32:
+            errs[n] = check_rel(n, g, r)
+        elif n == "lse":
+            errs[n] = check_abs(n, g, r, BF16_LSE_ABS)
+        else:
+            errs[n] = check_bf16(n, g, r)
+    print("errors", {k: "%.3g" % v for k, v in errs.items()}, flush=True)
+    return errs
+
+
+# ---------------------------------------------------------------- tiny fp32 exactness
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_tiny_fp32_matches_oracle(causal):
+    w = WORKLOADS["tiny"]
+    q, k, v, do = draw_workload(w)
+    scale = default_scale(w.d)
+    compare_full(run_fwd_bwd(q, k, v, do, causal, scale), oracle_full(q, k, v, do, causal, scale), torch.float32)
+
+
+# ---------------------------------------------------------------- small shapes: tiles, ragged tails, GQA
+
+SMALL = [
+    # B, H, Hkv, N, d
+    (1, 1, 1, 1, 64),
+    (1, 2, 2, 17, 64),
+    (2, 2, 1, 127, 64),
+    (1, 4, 2, 129, 128),
+    (2, 4, 1, 200, 128),
+    (1, 8, 2, 300, 64),
+    (1, 2, 2, 520, 128),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B%dH%dKV%dN%dd%d" % s)
+def test_small_shapes_match_oracle(shape, causal, dtype):
+    B, H, Hkv, N, d = shape
+    q, k, v, do = draw(B, H, Hkv, N, d, seed=100 + N, dtype=dtype)
+    scale = default_scale(d)
+    compare_full(run_fwd_bwd(q, k, v, do, causal, scale), oracle_full(q, k, v, do, causal, scale), dtype)
+
+
+@pytest.mark.parametrize("gain", [0.0, 8.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_uniform_and_peaked_rows(gain, causal):
+    # gain 0: every score is 0 (uniform rows); gain 8: scores of magnitude ~8*sqrt(d)*scale,
+    # so the running max changes often and the max subtraction matters
+    q, k, v, do = draw(1, 4, 2, 333, 128, seed=7, dtype=torch.bfloat16, q_gain=gain)
+    scale = default_scale(128)
+    compare_full(run_fwd_bwd(q, k, v, do, causal, scale), oracle_full(q, k, v, do, causal, scale), torch.bfloat16)
+
+
+def test_identical_keys_give_mean_of_values_on_gpu():
+    q, k, v, do = draw(1, 2, 2, 256, 64, seed=8, dtype=torch.bfloat16)
+    k = k[:, :1].expand(-1, 256, -1, -1).contiguous()
+    o, lse, dq, _, _ = run_fwd_bwd(q, k, v, do, True, 0.125)
+    vv = as_f64(v)
+    mean = np.cumsum(vv, axis=1) / np.arange(1, 257)[None, :, None, None]
+    check_bf16("o", o, mean)
+    check_bf16("dq", dq, np.zeros_like(dq))
+
+
+# ---------------------------------------------------------------- medium workloads, every output
+
+@pytest.mark.parametrize("name", ["gpt2", "bert"])
+def test_workload_matches_oracle_everywhere(name):
+    w = WORKLOADS[name]
+    q, k, v, do = draw_workload(w)
+    scale = default_scale(w.d)
+    causal = w.causal[0]
+    compare_full(run_fwd_bwd(q, k, v, do, causal, scale), oracle_full(q, k, v, do, causal, scale), w.torch_dtype)
+
+
+# ---------------------------------------------------------------- long context, sampled
+
+def sampled_check(q, k, v, do, o, lse, dq, dk, dv, scale, heads, kv_heads, rows, cols, b=0):
+    """Compare GPU outputs on selected rows with the oracle's row-by-row values."""
+    for h in heads:
+        ro, rl = oracle.forward_rows(q, k, v, True, scale, b, h, rows)
+        check_bf16("o[h=%d]" % h, f64(o[b, rows, h]), ro)
+        check_abs("lse[h=%d]" % h, f64(lse[b, h, rows]), rl, BF16_LSE_ABS)
+        rq = oracle.backward_dq_rows(q, k, v, do, True, scale, b, h, rows)
+        check_bf16("dq[h=%d]" % h, f64(dq[b, rows, h]), rq)
+    for g in kv_heads:
+        rk, rv = oracle.backward_dkdv_rows(q, k, v, do, True, scale, b, g, cols)
+        check_bf16("dk[g=%d]" % g, f64(dk[b, cols, g]), rk)
+        check_bf16("dv[g=%d]" % g, f64(dv[b, cols, g]), rv)
+
+
+def gradient_sum_properties(dk, dv, do, G):
+    """Any size: the key gradients of a K/V head sum to zero (rows of dS sum
+    to zero) and its value gradients sum to the group's summed dO (rows of P
+    sum to one). Each bf16 output element carries at most 2^-8 of its
+    magnitude from the final cast, so the sums are allowed twice that, summed
+    over the elements."""
+    dk, dv, do = dk.double(), dv.double(), do.double()
+    B, N, H, d = do.shape
+    sk = dk.sum(dim=1)
+    bound_k = 2.0 ** -7 * dk.abs().sum(dim=1)
+    assert torch.all(sk.abs() <= bound_k), float((sk.abs() - bound_k).max())
+    sdo = do.reshape(B, N, H // G, G, d).sum(dim=(1, 3))
+    sv = dv.sum(dim=1)
+    bound_v = 2.0 ** -7 * dv.abs().sum(dim=1)
+    assert torch.all((sv - sdo).abs() <= bound_v), float(((sv - sdo).abs() - bound_v).max())
+
+
+@pytest.mark.slow
+def test_llama16k_single_pass_sampled():
+    w = WORKLOADS["llama16k"]
+    q, k, v, do = draw_workload(w)
+    scale = default_scale(w.d)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    o, lse = mi.fwd(qd, kd, vd, True, scale)
+    dq, dk, dv = mi.bwd(qd, kd, vd, o, lse, dod, True, scale)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 63, 64, 4095, 8191, 12000, w.N - 1])
+    cols = np.array([0, 5, 127, 128, 9000, w.N - 2, w.N - 1])
+    qq, kk, vv, dd = (as_f64(t) for t in (q, k, v, do))
+    sampled_check(qq, kk, vv, dd, o, lse, dq, dk, dv, scale, heads=(0, 31), kv_heads=(17,), rows=rows, cols=cols)
+    gradient_sum_properties(dk.cpu(), dv.cpu(), do, w.G)
+
+
+@pytest.mark.slow
+def test_llama16k_chunked_equals_single_pass():
+    w = WORKLOADS["llama16k"]
+    q, k, v, do = draw_workload(w)
+    scale = default_scale(w.d)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    o1, l1 = mi.fwd(qd, kd, vd, True, scale)
+    o4, l4 = mi.fwd_chunked(qd, kd, vd, w.chunks, scale)
+    dq1, dk1, dv1 = mi.bwd(qd, kd, vd, o1, l1, dod, True, scale)
+    dq4, dk4, dv4 = mi.bwd_chunked(qd, kd, vd, o4, l4, dod, w.chunks, scale)
+    torch.cuda.synchronize()
+    check_bf16("o chunked vs single", f64(o4), f64(o1))
+    check_abs("lse chunked vs single", f64(l4), f64(l1), BF16_LSE_ABS)
+    for n, a, b in (("dq", dq4, dq1), ("dk", dk4, dk1), ("dv", dv4, dv1)):
+        check_bf16(n + " chunked vs single", f64(a), f64(b))
+
+
+@pytest.mark.slow
+def test_gqa64k_chunked_sampled():
+    w = WORKLOADS["gqa64k"]
+    q, k, v, do = draw_workload(w)
+    scale = default_scale(w.d)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    o, lse = mi.fwd_chunked(qd, kd, vd, w.chunks, scale)
+    dq, dk, dv = mi.bwd_chunked(qd, kd, vd, o, lse, dod, w.chunks, scale)
+    torch.cuda.synchronize()
+    N = w.N
+    rows = np.array([0, 8191, 8192, 30000, 57344, N - 1])
+    # key rows in the last chunk keep the oracle's column work bounded (queries >= key)
+    cols = np.array([N - 8192, N - 4097, N - 2, N - 1])
+    qq, kk, vv, dd = (as_f64(t) for t in (q, k, v, do))
+    sampled_check(qq, kk, vv, dd, o, lse, dq, dk, dv, scale, heads=(0, 13, 31), kv_heads=(7,), rows=rows, cols=cols)
+    gradient_sum_properties(dk.cpu(), dv.cpu(), do, w.G)
+
+
+# ---------------------------------------------------------------- merge
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_merge_matches_oracle_and_full_attention(dtype):
+    B, H, N, d = 2, 4, 96, 64
+    q, k, v, _ = draw(B, H, H, N, d, seed=31, dtype=dtype)
+    scale = default_scale(d)
+    cut = 40
+    # partials of every query row over keys [0, cut) and [cut, N), from the
+    # oracle, rounded to the dtype the merge consumes
+    qq, kk, vv = (as_f64(t) for t in (q, k, v))
+    oa, la = oracle.forward(qq, kk[:, :cut], vv[:, :cut], False, scale)
+    ob, lb = oracle.forward(qq, kk[:, cut:], vv[:, cut:], False, scale)
+    t = lambda x, dt: torch.tensor(x, dtype=dt, device=DEV).contiguous()
+    goa, gob = t(oa, dtype), t(ob, dtype)
+    gla, glb = t(la, torch.float32), t(lb, torch.float32)
+    ref_o, ref_l = oracle.merge(f64(goa), f64(gla), f64(gob), f64(glb))
+    go, gl = mi.merge(goa, gla, gob, glb)
+    mi.merge(goa, gla, gob, glb, out=goa, out_lse=gla)      # in place into a
+    torch.cuda.synchronize()
+    for got_o, got_l in ((go, gl), (goa, gla)):
+        if dtype == torch.float32:
+            check_rel("merged o", f64(got_o), ref_o, 1e-6)
+        else:
+            check_bf16("merged o", f64(got_o), ref_o, 1e-6)
+        check_abs("merged lse", f64(got_l), ref_l, 1e-5)
+    # the merge of the two partials is attention over every key
+    full_o, full_l = oracle.forward(qq, kk, vv, False, scale)
+    check_abs("merged lse vs full", f64(gl), full_l, 1e-5)
+    if dtype == torch.float32:
+        check_rel("merged o vs full", f64(go), full_o, 1e-6)
+
+
+def test_merge_empty_partials():
+    B, H, N, d = 1, 2, 8, 64
+    o_a = torch.randn(B, N, H, d, device=DEV, dtype=torch.bfloat16)
+    l_a = torch.randn(B, H, N, device=DEV)
+    empty_o = torch.zeros_like(o_a)
+    empty_l = torch.full_like(l_a, float("-inf"))
+    o, l = mi.merge(o_a, l_a, empty_o, empty_l)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_a) and torch.equal(l, l_a)
+    o2, l2 = mi.merge(empty_o, empty_l, empty_o, empty_l)
+    torch.cuda.synchronize()
+    assert torch.all(o2 == 0) and torch.all(torch.isneginf(l2))
+
+
+# ---------------------------------------------------------------- accumulate mode
+
+def test_backward_accumulate_adds_float32_gradients():
+    q, k, v, do = draw(1, 4, 2, 160, 128, seed=41, dtype=torch.bfloat16)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    scale = default_scale(128)
+    o, lse = mi.fwd(qd, kd, vd, True, scale)
+    dq, dk, dv = mi.bwd(qd, kd, vd, o, lse, dod, True, scale, accumulate=True)
+    mi.bwd(qd, kd, vd, o, lse, dod, True, scale, accumulate=True, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    ref = oracle_full(q, k, v, do, True, scale)
+    for n, g, r in (("dq", dq, ref[2]), ("dk", dk, ref[3]), ("dv", dv, ref[4])):
+        assert g.dtype == torch.float32
+        check_abs(n + " x2", f64(g), 2 * r, 2e-2)
