@@ -1,0 +1,168 @@
+#!/usr/bin/env python3
+"""Benchmark: causal bf16 attention forward + backward on one MI355X.
+
+One step = one forward (attn_fwd) and one backward (attn_bwd) of causal
+exact attention over the Llama-7B-shaped 16K workload (B=1, H=Hkv=32,
+N=16384, d=128, bf16, iid N(0,1) synthetic inputs resident in HBM). Prints
+one JSON line. FLOPs: forward 4*B*H*N^2*d halved for the causal mask,
+backward 2.5x the forward.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--extra]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline leg")
+    ap.add_argument("--extra", action="store_true", help="also time the chunked workloads")
+    ap.add_argument("--workload", default="llama16k")
+    return ap.parse_args()
+
+
+def cpu_baseline(workload, heads=1):
+    """The float64 oracle, untouched, on a bounded sample of the workload:
+    `heads` query heads at the full sequence length, forward + backward."""
+    import numpy as np
+    import oracle
+    from workloads import draw, as_f64, flops
+    w = workload
+    q, k, v, do = draw(1, heads, heads, w.N, w.d, seed=w.seed, dtype=w.torch_dtype)
+    qq, kk, vv, dd = (as_f64(t) for t in (q, k, v, do))
+    scale = w.d ** -0.5
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        threads = os.cpu_count()
+    t0 = time.perf_counter()
+    oracle.forward(qq, kk, vv, True, scale)
+    oracle.backward(qq, kk, vv, dd, True, scale)
+    dt = time.perf_counter() - t0
+    ff, fb = flops(1, heads, w.N, w.d, True)
+    return {"value": round((ff + fb) / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": "%d query heads (B=1, N=%d, d=%d, causal) fwd+bwd in float64; "
+                      "FLOPs counted as for the GPU" % (heads, w.N, w.d)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import exact_attention_37_amd as mi
+    from workloads import WORKLOADS, draw_workload, flops
+
+    w = WORKLOADS[args.workload]
+    causal = True
+    scale = w.d ** -0.5
+    q, k, v, do = [t.to("cuda:0") for t in draw_workload(w)]
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        mi.fwd(q, k, v, causal, scale, out=o, out_lse=lse)
+        if ev is not None:
+            ev[1].record()
+        mi.bwd(q, k, v, o, lse, do, causal, scale, dq=dq, dk=dk, dv=dv)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ms = wall * 1e3 / args.steps
+
+    ff, fb = flops(w.B, w.H, w.N, w.d, causal)
+    value = (ff + fb) / (ms * 1e-3) / 1e12
+    fwd_tf = ff / (fwd_ms * 1e-3) / 1e12
+    bwd_tf = fb / (bwd_ms * 1e-3) / 1e12
+    # dominant kernel: the one with the larger share of the step
+    dom = "bwd" if bwd_ms >= fwd_ms else "fwd"
+    ach = bwd_tf if dom == "bwd" else fwd_tf
+    out = {
+        "metric": "causal bf16 attention fwd+bwd TFLOP/s on 1 GPU and % of bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: B=%d H=%d Hkv=%d N=%d d=%d causal, fwd+bwd" % (w.name, w.B, w.H, w.Hkv, w.N, w.d),
+                   "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)"},
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+        "fwd_tflops": round(fwd_tf, 2), "bwd_tflops": round(bwd_tf, 2),
+        "roofline": {"bound": "mfma", "kernel": "attn_%s call" % dom, "achieved": round(ach, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
+    if args.extra:
+        extra = {}
+        for name in ("llama16k", "gqa64k"):
+            we = WORKLOADS[name]
+            tq, tk, tv, tdo = [t.to("cuda:0") for t in draw_workload(we)]
+            sc = we.d ** -0.5
+            for _ in range(2):
+                oo, ll = mi.fwd_chunked(tq, tk, tv, we.chunks, sc)
+                mi.bwd_chunked(tq, tk, tv, oo, ll, tdo, we.chunks, sc)
+            torch.cuda.synchronize()
+            reps = 3
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            f_ms = b_ms = 0.0
+            for _ in range(reps):
+                e0.record()
+                oo, ll = mi.fwd_chunked(tq, tk, tv, we.chunks, sc)
+                e1.record()
+                mi.bwd_chunked(tq, tk, tv, oo, ll, tdo, we.chunks, sc)
+                e2.record()
+                torch.cuda.synchronize()
+                f_ms += e0.elapsed_time(e1) / reps
+                b_ms += e1.elapsed_time(e2) / reps
+            a, bb = flops(we.B, we.H, we.N, we.d, True)
+            extra[name + "_chunked%d" % we.chunks] = {
+                "fwd_ms": round(f_ms, 3), "bwd_ms": round(b_ms, 3),
+                "tflops": round((a + bb) / ((f_ms + b_ms) * 1e-3) / 1e12, 2)}
+            del tq, tk, tv, tdo, oo, ll
+        out["extra"] = extra
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

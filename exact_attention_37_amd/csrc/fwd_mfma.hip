@@ -1,0 +1,350 @@
+// bf16 forward pass on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16).
+//
+// The method is FlashAttention's tiled forward with online softmax
+// (FlashAttention abstract page: tiles of K and V move through on-chip
+// memory; FlashAttention-2 reviews page, reviewer 2, points 1-3: rescaling
+// deferred to one division at the end, the logsumexp saved, parallelism over
+// query tiles) with whole-tile skipping above the causal diagonal
+// (FlashAttention-2 reviews page, reviewer 4, section 3.1).
+//
+// Work split (MI355X-specific, not from the pages):
+//  * a workgroup of NW waves owns NW*QB*32 query rows of one (b, h); each
+//    wave owns QB blocks of 32 rows, so its row max and row sum never leave
+//    the wave (the pages' warp partitioning, with 64-lane wavefronts);
+//  * K and V tiles of BC=64 keys are staged in LDS, double-buffered, with
+//    one barrier per tile; the next tile's global loads are issued a full
+//    tile ahead into registers;
+//  * scores are computed transposed, S^T = K Q^T, with K's rows loaded in a
+//    bit-permuted order (sigma_k) so that each lane's 32x32 accumulator holds
+//    8 consecutive keys of one query: exactly the B-operand layout of the
+//    next product O^T += V^T P^T. P never moves between lanes.
+//  * V is transposed into LDS (V^T rows are head-dimension columns); LDS rows
+//    are padded by 16 bytes so every operand read is base + immediate and the
+//    16-lane service groups of ds_read_b128 hit distinct banks;
+//  * the running max is only raised when a row's tile max exceeds it by more
+//    than 8 (log2 units); otherwise the old max is kept, p <= 2^8, and the
+//    accumulator is not rescaled. The result is unchanged (numerator and
+//    denominator share the max), and most tiles skip the rescale entirely;
+//  * the row sum is taken from the bf16-rounded P with v_dot2_f32_bf16, so
+//    numerator and denominator see the same rounded probabilities;
+//  * causal workgroups are launched heaviest first, and with H % 8 == 0 the
+//    heads are permuted so that every workgroup of one K/V head group lands
+//    on the same XCD (workgroups are dealt to the 8 XCDs round-robin).
+#include "common.h"
+#include "kernels.h"
+
+namespace miattn {
+
+namespace {
+
+constexpr int BC = 64;   // keys per tile
+
+constexpr int PAD = 8;   // bf16 elements of padding per LDS row (16 bytes)
+
+// Row slot -> key inside a 32-key block: bits 2 and 3 swapped.
+__device__ __forceinline__ int sigma_k(int n) { return (n & 0x13) | ((n & 4) << 1) | ((n & 8) >> 1); }
+
+template <int D>
+struct Smem {
+  static constexpr int KROW = D + PAD;    // K tile row-major [key][d]
+  static constexpr int VROW = BC + PAD;   // V tile transposed [d][key]
+  bf16 k[2][BC * KROW];
+  bf16 vt[2][D * VROW];
+};
+
+__device__ __forceinline__ bf16x8 lds_read16(const bf16* base, int elem_off) {
+  return *(const bf16x8*)(base + elem_off);
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack2(bf16 lo, bf16 hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+
+template <int D, int NW>
+struct TileLoader {
+  // K: (BC * D / 8) chunks of 16 B; V: (BC/4) * (D/8) blocks of 4 keys x 8 columns.
+  static constexpr int KCH = D / 8;
+  static constexpr int KCHUNKS = BC * KCH;
+  static constexpr int NT = NW * 64;
+  static constexpr int KPER = (KCHUNKS + NT - 1) / NT;
+  static constexpr int VBLK = (BC / 4) * (D / 8);
+  static constexpr int VPER = (VBLK + NT - 1) / NT;
+  bf16x8 kreg[KPER];
+  bf16x8 vreg[VPER][4];
+
+  __device__ __forceinline__ void load(const bf16* K, const bf16* V, long long rstride, int j0, int nk, int tid) {
+#pragma unroll
+    for (int i = 0; i < KPER; ++i) {
+      const int c = tid + i * NT;
+      const int row = c / KCH, ch = c % KCH;
+      const bool in = (c < KCHUNKS) && (j0 + row < nk);
+      kreg[i] = in ? *(const bf16x8*)(K + (j0 + row) * rstride + ch * 8) : bf16x8{};
+    }
+#pragma unroll
+    for (int i = 0; i < VPER; ++i) {
+      const int blk = tid + i * NT;
+      const int kq = blk % (BC / 4), oc = blk / (BC / 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = j0 + kq * 4 + r;
+        const bool in = (blk < VBLK) && (key < nk);
+        vreg[i][r] = in ? *(const bf16x8*)(V + key * rstride + oc * 8) : bf16x8{};
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(bf16* ks, bf16* vt, int tid) const {
+#pragma unroll
+    for (int i = 0; i < KPER; ++i) {
+      const int c = tid + i * NT;
+      if (c < KCHUNKS) {
+        const int row = c / KCH, ch = c % KCH;
+        *(bf16x8*)(ks + row * Smem<D>::KROW + ch * 8) = kreg[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VPER; ++i) {
+      const int blk = tid + i * NT;
+      if (blk < VBLK) {
+        const int kq = blk % (BC / 4), oc = blk / (BC / 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = oc * 8 + e;
+          const uint2 w = {pack2(vreg[i][0][e], vreg[i][1][e]), pack2(vreg[i][2][e], vreg[i][3][e])};
+          *(uint2*)(vt + d * Smem<D>::VROW + kq * 4) = w;
+        }
+      }
+    }
+  }
+};
+
+template <int D, int QB, int NW, bool CAUSAL, typename TO>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fwd_mfma_kernel(Params p) {
+  constexpr int BR = NW * QB * 32;
+  constexpr int KS = D / 16;   // k-steps of the QK^T product
+  constexpr int DB = D / 32;   // 32-column blocks of O
+  __shared__ Smem<D> sm;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 5, n = lane & 31;
+
+  // ---- workgroup -> (b, h, query tile), heaviest causal tiles first
+  const int ntq = gridDim.y;
+  const int qt = CAUSAL ? (ntq - 1 - (int)blockIdx.y) : (int)blockIdx.y;
+  int h = blockIdx.x;
+  if ((p.H & 7) == 0) h = (h & 7) * (p.H >> 3) + (h >> 3);
+  const int b = blockIdx.z;
+  const int kvh = h / p.G;
+  const int q0 = qt * BR;                         // first local query row of the tile
+  const int wq0 = q0 + wave * QB * 32;            // first local query row of this wave
+
+  const long long qrs = (long long)p.H * D;       // row strides (elements)
+  const long long krs = (long long)p.Hkv * D;
+  const bf16* Q = (const bf16*)p.q + ((long long)b * p.N + p.q_start) * qrs + (long long)h * D;
+  const bf16* K = (const bf16*)p.k + ((long long)b * p.N + p.k_start) * krs + (long long)kvh * D;
+  const bf16* V = (const bf16*)p.v + ((long long)b * p.N + p.k_start) * krs + (long long)kvh * D;
+
+  // ---- scale: scores kept in the log2 domain; a non-positive scale is folded into Q
+  float c = fabsf(p.scale) * kLog2e;
+  float qsign = p.scale < 0.f ? -1.f : 1.f;
+  if (p.scale == 0.f) { c = 1.f; qsign = 0.f; }
+
+  // ---- Q^T operands (B operand of S^T = K Q^T): lane (g, n) holds Q[row n][ks*16 + g*8 .. +8]
+  bf16x8 qf[QB][KS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = wq0 + qb * 32 + n;
+    const int rc = min(row, p.Nq - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 x = *(const bf16x8*)(Q + rc * qrs + ks * 16 + g * 8);
+      if (qsign != 1.f) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (bf16)((float)x[e] * qsign);
+      }
+      qf[qb][ks] = x;
+    }
+  }
+
+  // ---- key range of the workgroup
+  int nkt = (p.Nk + BC - 1) / BC;
+  if (CAUSAL) {
+    const int last_q = p.q_start + min(q0 + BR - 1, p.Nq - 1);   // absolute position
+    const int kend = min(p.Nk, last_q - p.k_start + 1);
+    nkt = kend > 0 ? (kend + BC - 1) / BC : 0;
+  }
+  const int wq_last = p.q_start + min(wq0 + QB * 32 - 1, p.Nq - 1);   // absolute, this wave
+  const int wq_first = p.q_start + wq0;
+
+  f32x16 acc[QB][DB];
+  float m[QB], l[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -INFINITY;
+    l[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
+  }
+
+  TileLoader<D, NW> ld;
+  if (nkt > 0) {
+    ld.load(K, V, krs, 0, p.Nk, tid);
+    ld.store(sm.k[0], sm.vt[0], tid);
+    if (nkt > 1) ld.load(K, V, krs, BC, p.Nk, tid);
+  }
+  __syncthreads();
+
+  const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
+  for (int j = 0; j < nkt; ++j) {
+    const bf16* ks_ = sm.k[j & 1];
+    const bf16* vt_ = sm.vt[j & 1];
+    const int kpos0 = p.k_start + j * BC;   // absolute position of the tile's first key
+    const bool wave_active = !CAUSAL || kpos0 <= wq_last;
+    if (wave_active) {
+      // ---- S^T = K Q^T for 2 blocks of 32 keys
+      f32x16 s[2][QB];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
+        const bf16* kbase = ks_ + (kb * 32 + sigma_k(n)) * Smem<D>::KROW + g * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 a = lds_read16(kbase, ks * 16);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma32(a, qf[qb][ks], s[kb][qb]);
+        }
+      }
+      // ---- mask: keys past the diagonal or past Nk
+      const bool need_mask = (CAUSAL && kpos0 + BC - 1 > wq_first) || (j * BC + BC > p.Nk);
+      if (need_mask) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int qpos = p.q_start + wq0 + qb * 32 + n;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int kin = kb * 32 + ((r < 8) ? (g * 8 + r) : (16 + g * 8 + r - 8));
+              const bool bad = (j * BC + kin >= p.Nk) || (CAUSAL && kpos0 + kin > qpos);
+              if (bad) s[kb][qb][r] = -INFINITY;
+            }
+        }
+      }
+      // ---- online softmax (per query block)
+      bf16x8 pf[QB][4];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = s[0][qb][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][qb][r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][qb][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mt = mx * c;
+        const bool raise = mt > m[qb] + 8.f;
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+          const float mnew = raise ? mt : m[qb];
+          const float alpha = exp2f(m[qb] - mnew);
+          l[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
+          m[qb] = mnew;
+        }
+        const float mneg = -m[qb];
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            bf16x8 x;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][qb][half * 8 + e], c, mneg));
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              const bf16x2 pr = {x[e], x[e + 1]};
+              lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
+            }
+            pf[qb][kb * 2 + half] = x;
+          }
+        }
+        l[qb] += lsum;
+      }
+      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16* vbase = vt_ + (db * 32 + n) * Smem<D>::VROW + g * 8;
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq) {
+          const bf16x8 a = lds_read16(vbase, kq * 16);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32(a, pf[qb][kq], acc[qb][db]);
+        }
+      }
+    }
+    if (j + 1 < nkt) {
+      ld.store(sm.k[(j + 1) & 1], sm.vt[(j + 1) & 1], tid);
+      if (j + 2 < nkt) ld.load(K, V, krs, (j + 2) * BC, p.Nk, tid);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = wq0 + qb * 32 + n;
+    const float lt = l[qb] + __shfl_xor(l[qb], 32);
+    if (row < p.Nq) {
+      const float inv = 1.f / lt;
+      TO* O = (TO*)p.o + (((long long)b * p.N + p.q_start + row) * p.H + h) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        // accumulator rows (r/4)*8 + g*4 + r%4: four runs of 4 columns
+#pragma unroll
+        for (int run = 0; run < 4; ++run) {
+          TO* dst = O + db * 32 + run * 8 + g * 4;
+          if constexpr (sizeof(TO) == 2) {
+            bf16x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = (bf16)(acc[qb][db][run * 4 + e] * inv);
+            *(bf16x4*)dst = x;
+          } else {
+            f32x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = acc[qb][db][run * 4 + e] * inv;
+            *(f32x4*)dst = x;
+          }
+        }
+      }
+      if (g == 0) p.lse[((long long)b * p.H + h) * p.N + p.q_start + row] = (m[qb] + __log2f(lt)) * kLn2;
+    }
+  }
+}
+
+template <int D, int QB, int NW, typename TO>
+hipError_t launch_cfg(const Params& p, hipStream_t s) {
+  constexpr int BR = NW * QB * 32;
+  const dim3 grid(p.H, (p.Nq + BR - 1) / BR, p.B);
+  if (p.causal)
+    hipLaunchKernelGGL((fwd_mfma_kernel<D, QB, NW, true, TO>), grid, dim3(NW * 64), 0, s, p);
+  else
+    hipLaunchKernelGGL((fwd_mfma_kernel<D, QB, NW, false, TO>), grid, dim3(NW * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_mfma(const Params& p, bool out_f32, hipStream_t s) {
+  if (p.d == 128) return out_f32 ? launch_cfg<128, 2, 4, float>(p, s) : launch_cfg<128, 2, 4, bf16>(p, s);
+  return out_f32 ? launch_cfg<64, 2, 4, float>(p, s) : launch_cfg<64, 2, 4, bf16>(p, s);
+}
+
+}  // namespace miattn

@@ -92,6 +92,7 @@ Params make_params(const void* q, const void* k, const void* v, void* o, float* 
 
 // One forward block (rows and offsets in p). out_f32: o is float32.
 hipError_t fwd_block(const Params& p, int dtype, bool out_f32, hipStream_t s) {
+  if (dtype == MIATTN_BF16) return miattn::launch_fwd_mfma(p, out_f32, s);
   return miattn::launch_fwd_simt(p, dtype, out_f32, s);
 }
 

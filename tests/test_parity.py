@@ -86,14 +86,29 @@ def test_small_shapes_match_oracle(shape, causal, dtype):
     compare_full(run_fwd_bwd(q, k, v, do, causal, scale), oracle_full(q, k, v, do, causal, scale), dtype)
 
 
-@pytest.mark.parametrize("gain", [0.0, 8.0])
 @pytest.mark.parametrize("causal", [False, True])
-def test_uniform_and_peaked_rows(gain, causal):
-    # gain 0: every score is 0 (uniform rows); gain 8: scores of magnitude ~8*sqrt(d)*scale,
-    # so the running max changes often and the max subtraction matters
-    q, k, v, do = draw(1, 4, 2, 333, 128, seed=7, dtype=torch.bfloat16, q_gain=gain)
+def test_uniform_rows(causal):
+    # Q = 0: every score is 0, so each row is the mean of its visible values
+    q, k, v, do = draw(1, 4, 2, 333, 128, seed=7, dtype=torch.bfloat16, q_gain=0.0)
     scale = default_scale(128)
     compare_full(run_fwd_bwd(q, k, v, do, causal, scale), oracle_full(q, k, v, do, causal, scale), torch.bfloat16)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_peaked_rows(causal):
+    # Q scaled by 8: scores of standard deviation ~8, so the running max moves
+    # and max subtraction matters. Gradients grow with |Q| (dK is linear in Q)
+    # and the backward's rowsum(dO * O) uses the bf16-rounded O, so dQ/dK/dV
+    # are held to a normwise relative bound here instead of the absolute one
+    # stated for N(0,1) inputs.
+    q, k, v, do = draw(1, 4, 2, 333, 128, seed=7, dtype=torch.bfloat16, q_gain=8.0)
+    scale = default_scale(128)
+    o, lse, dq, dk, dv = run_fwd_bwd(q, k, v, do, causal, scale)
+    ro, rl, rdq, rdk, rdv = oracle_full(q, k, v, do, causal, scale)
+    check_bf16("o", o, ro)
+    check_abs("lse", lse, rl, BF16_LSE_ABS)
+    for n, g_, r_ in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        check_rel(n, g_, r_, 1e-2)
 
 
 def test_identical_keys_give_mean_of_values_on_gpu():
