@@ -1,0 +1,493 @@
+// bf16 backward pass on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16).
+//
+// The backward rebuilds P tile by tile from the saved logsumexp instead of
+// re-running the forward (DistFlashAttn reviews page, review 1 point 3;
+// FlashAttention-2 reviews page, reviewer 2, point 2) and never forms the
+// N x N matrix. With D_i = rowsum(dO_i * O_i) computed beforehand:
+//     P = exp(scale Q K^T - LSE),  dP = dO V^T,  dS = P (dP - D)
+//     dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K
+// Grouped-query heads: dK and dV of a K/V head are summed over the query
+// heads that read it (FlashAttention-2 reviews page, reviewer 1, MQA/GQA
+// paragraph of the backward section).
+//
+// Work split (MI355X-specific): two kernels, neither shares a partial sum
+// with another workgroup, so no atomics are needed and results are bitwise
+// deterministic. Accumulating dQ across key tiles with float32 atomics would
+// cost as much memory traffic as the whole computation takes on MI355X.
+//  * bwd_dkdv: one workgroup per 128 keys of one (b, K/V head); each of its 4
+//    waves holds 32 keys' K and V as matrix-core operands and their dK, dV
+//    accumulators in registers, and streams 64-row tiles of Q, dO (row-major
+//    and transposed copies in LDS), LSE and D over every query head of the
+//    group. Products: S = Q K^T, dP = dO V^T (query rows loaded in sigma32
+//    order, so each lane's accumulator holds 8 consecutive queries of one
+//    key = the A operand of the next products), dV += P^T dO, dK += dS^T Q.
+//  * bwd_dq: one workgroup per query tile of one (b, h), the forward's
+//    structure: S^T = K Q^T and dP^T = V dO^T from row-major K and V tiles,
+//    then dQ^T += K^T dS^T from a transposed K tile.
+#include "common.h"
+#include "kernels.h"
+#include "mfma_common.h"
+
+namespace miattn {
+
+namespace {
+
+constexpr int PAD = LDS_PAD;
+
+// ============================================================ dK, dV
+
+constexpr int DKV_NW = 4;            // waves per workgroup
+constexpr int DKV_KW = 32;           // keys per wave
+constexpr int DKV_BK = DKV_NW * DKV_KW;
+constexpr int DKV_BQ = 64;           // query rows per streamed tile
+
+template <int D>
+struct DkdvSmem {
+  static constexpr int ROW = D + PAD;         // [q][d]
+  static constexpr int TROW = DKV_BQ + PAD;   // [d][q]
+  bf16 q[2][DKV_BQ * ROW];
+  bf16 qt[2][D * TROW];
+  bf16 o[2][DKV_BQ * ROW];     // dO
+  bf16 ot[2][D * TROW];
+  float lse2[2][DKV_BQ];       // LSE * log2(e); +inf past the last row
+  float dsum[2][DKV_BQ];
+};
+
+// One streamed tile: 64 query rows of Q and dO of one head, as blocks of
+// 4 rows x 8 columns (so each thread can also write the transposed copy).
+template <int D>
+struct QTileLoader {
+  static constexpr int NT = DKV_NW * 64;
+  static constexpr int NBLK = (DKV_BQ / 4) * (D / 8);
+  static constexpr int PER = (NBLK + NT - 1) / NT;
+  bf16x8 qr[PER][4], orr[PER][4];
+  float st;   // lse2 (threads 0..63) or dsum (threads 64..127)
+
+  __device__ __forceinline__ void load(const Params& p, int b, int h, int q0, int tid) {
+    const long long qrs = (long long)p.H * D;
+    const bf16* Q = (const bf16*)p.q + ((long long)b * p.N + p.q_start) * qrs + (long long)h * D;
+    const bf16* O = (const bf16*)p.dout + ((long long)b * p.N + p.q_start) * qrs + (long long)h * D;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int blk = tid + i * NT;
+      const int rq = blk % (DKV_BQ / 4), oc = blk / (DKV_BQ / 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = q0 + rq * 4 + r;
+        const bool in = blk < NBLK && row < p.Nq;
+        qr[i][r] = in ? *(const bf16x8*)(Q + row * qrs + oc * 8) : bf16x8{};
+        orr[i][r] = in ? *(const bf16x8*)(O + row * qrs + oc * 8) : bf16x8{};
+      }
+    }
+    const int t = tid & 63;
+    const int row = q0 + t;
+    const long long si = ((long long)b * p.H + h) * p.N + p.q_start + row;
+    if (tid < 64) st = row < p.Nq ? p.lse[si] * kLog2e : INFINITY;
+    else if (tid < 128) st = row < p.Nq ? p.dsum[si] : 0.f;
+  }
+
+  __device__ __forceinline__ void store(DkdvSmem<D>& sm, int buf, int tid) const {
+    constexpr int ROW = DkdvSmem<D>::ROW, TROW = DkdvSmem<D>::TROW;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int blk = tid + i * NT;
+      if (blk < NBLK) {
+        const int rq = blk % (DKV_BQ / 4), oc = blk / (DKV_BQ / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          *(bf16x8*)(sm.q[buf] + (rq * 4 + r) * ROW + oc * 8) = qr[i][r];
+          *(bf16x8*)(sm.o[buf] + (rq * 4 + r) * ROW + oc * 8) = orr[i][r];
+        }
+        store_transposed4x8(sm.qt[buf], TROW, oc * 8, rq * 4, qr[i]);
+        store_transposed4x8(sm.ot[buf], TROW, oc * 8, rq * 4, orr[i]);
+      }
+    }
+    if (tid < 64) sm.lse2[buf][tid] = st;
+    else if (tid < 128) sm.dsum[buf][tid - 64] = st;
+  }
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(DKV_NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(Params p) {
+  constexpr int KS = D / 16, DB = D / 32;
+  constexpr int ROW = DkdvSmem<D>::ROW, TROW = DkdvSmem<D>::TROW;
+  __shared__ DkdvSmem<D> sm;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 5, n = lane & 31;
+  const int gkv = blockIdx.x;          // all tiles of one K/V head share an XCD
+  const int kt = blockIdx.y;           // tile 0 has the most causal work: dispatched first
+  const int b = blockIdx.z;
+  const int k0 = kt * DKV_BK;
+  const int kw0 = k0 + wave * DKV_KW;
+
+  const long long krs = (long long)p.Hkv * D;
+  const bf16* K = (const bf16*)p.k + ((long long)b * p.N + p.k_start) * krs + (long long)gkv * D;
+  const bf16* V = (const bf16*)p.v + ((long long)b * p.N + p.k_start) * krs + (long long)gkv * D;
+
+  float c = fabsf(p.scale) * kLog2e;
+  float ksign = p.scale < 0.f ? -1.f : 1.f;
+  if (p.scale == 0.f) { c = 1.f; ksign = 0.f; }
+
+  // K^T and V^T operands (B of S = Q K^T and dP = dO V^T): lane (g, n) holds row kw0+n, columns 16ks+8g..
+  bf16x8 kf[KS], vf[KS];
+  {
+    const int kr = min(kw0 + n, p.Nk - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 x = *(const bf16x8*)(K + kr * krs + ks * 16 + g * 8);
+      if (ksign != 1.f) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (bf16)((float)x[e] * ksign);
+      }
+      kf[ks] = x;
+      vf[ks] = *(const bf16x8*)(V + kr * krs + ks * 16 + g * 8);
+    }
+  }
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) { dk[db] = f32x16{}; dv[db] = f32x16{}; }
+
+  const int nqt = (p.Nq + DKV_BQ - 1) / DKV_BQ;
+  int first = 0;
+  if (CAUSAL) first = min(nqt, max(0, p.k_start + k0 - p.q_start) / DKV_BQ);
+  const int per_head = nqt - first;
+  const int niter = p.G * per_head;
+  const int kpos = p.k_start + kw0 + n;          // this lane's key position
+  const int wk_first = p.k_start + kw0;
+
+  QTileLoader<D> ld;
+  if (niter > 0) {
+    ld.load(p, b, gkv * p.G, first * DKV_BQ, tid);
+    ld.store(sm, 0, tid);
+    if (niter > 1) ld.load(p, b, gkv * p.G + 1 / per_head, (first + 1 % per_head) * DKV_BQ, tid);  // it = 1
+  }
+  __syncthreads();
+
+  for (int it = 0; it < niter; ++it) {
+    const int buf = it & 1;
+    const int q0 = (first + it % per_head) * DKV_BQ;
+    const int q_last = p.q_start + min(q0 + DKV_BQ - 1, p.Nq - 1);
+    const bool active = !CAUSAL || wk_first <= q_last;
+    if (active) {
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        s[qb] = f32x16{};
+        dp[qb] = f32x16{};
+        const int row = qb * 32 + sigma32(n);
+        const bf16* qa = sm.q[buf] + row * ROW + g * 8;
+        const bf16* oa = sm.o[buf] + row * ROW + g * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          s[qb] = mfma32(lds_read16(qa, ks * 16), kf[ks], s[qb]);
+          dp[qb] = mfma32(lds_read16(oa, ks * 16), vf[ks], dp[qb]);
+        }
+      }
+      // P and dS; lane (g, key n), register r <-> query q0 + 32 qb + sigma_row(g, r)
+      const bool need_mask = CAUSAL && (wk_first + DKV_KW - 1 > p.q_start + q0);
+      bf16x8 pa[4], da[4];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int qi0 = qb * 32 + half * 16 + g * 8;   // 8 consecutive query rows
+          const f32x4 l0 = *(const f32x4*)(sm.lse2[buf] + qi0);
+          const f32x4 l1 = *(const f32x4*)(sm.lse2[buf] + qi0 + 4);
+          const f32x4 d0 = *(const f32x4*)(sm.dsum[buf] + qi0);
+          const f32x4 d1 = *(const f32x4*)(sm.dsum[buf] + qi0 + 4);
+          bf16x8 xp, xd;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float lv = e < 4 ? l0[e] : l1[e - 4];
+            const float dv_ = e < 4 ? d0[e] : d1[e - 4];
+            float pr = __builtin_amdgcn_exp2f(fmaf(s[qb][half * 8 + e], c, -lv));
+            if (need_mask && kpos > p.q_start + q0 + qi0 + e) pr = 0.f;
+            xp[e] = (bf16)pr;
+            xd[e] = (bf16)(pr * (dp[qb][half * 8 + e] - dv_));
+          }
+          pa[qb * 2 + half] = xp;
+          da[qb * 2 + half] = xd;
+        }
+      }
+      // dV += P^T dO, dK += dS^T Q (B operands from the transposed tiles)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16* ob = sm.ot[buf] + (db * 32 + n) * TROW + g * 8;
+        const bf16* qb_ = sm.qt[buf] + (db * 32 + n) * TROW + g * 8;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          dv[db] = mfma32(pa[t], lds_read16(ob, t * 16), dv[db]);
+          dk[db] = mfma32(da[t], lds_read16(qb_, t * 16), dk[db]);
+        }
+      }
+    }
+    if (it + 1 < niter) {
+      ld.store(sm, buf ^ 1, tid);
+      if (it + 2 < niter) {
+        const int nx = it + 2;
+        ld.load(p, b, gkv * p.G + nx / per_head, (first + nx % per_head) * DKV_BQ, tid);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- store: lane (g, key n), register r <-> column 32 db + 8 (r/4) + 4g + r%4
+  const int key = kw0 + n;
+  if (key < p.Nk) {
+    const long long off = (((long long)b * p.N + p.k_start + key) * p.Hkv + gkv) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int run = 0; run < 4; ++run) {
+        const int col = db * 32 + run * 8 + g * 4;
+        if (p.accumulate) {
+          f32x4* a = (f32x4*)((float*)p.dk + off + col);
+          f32x4* v = (f32x4*)((float*)p.dv + off + col);
+          f32x4 xa = *a, xv = *v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            xa[e] += dk[db][run * 4 + e] * p.scale;
+            xv[e] += dv[db][run * 4 + e];
+          }
+          *a = xa;
+          *v = xv;
+        } else {
+          bf16x4 xa, xv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            xa[e] = (bf16)(dk[db][run * 4 + e] * p.scale);
+            xv[e] = (bf16)dv[db][run * 4 + e];
+          }
+          *(bf16x4*)((bf16*)p.dk + off + col) = xa;
+          *(bf16x4*)((bf16*)p.dv + off + col) = xv;
+        }
+      }
+    }
+  }
+}
+
+// ============================================================ dQ
+
+constexpr int DQ_BC = 64;   // keys per tile
+
+template <int D>
+struct DqSmem {
+  static constexpr int ROW = D + PAD;       // [key][d]
+  static constexpr int TROW = DQ_BC + PAD;  // [d][key]
+  bf16 k[2][DQ_BC * ROW];
+  bf16 v[2][DQ_BC * ROW];
+  bf16 kt[2][D * TROW];
+};
+
+template <int D, int NW>
+struct KTileLoader {
+  static constexpr int NT = NW * 64;
+  static constexpr int NBLK = (DQ_BC / 4) * (D / 8);
+  static constexpr int PER = (NBLK + NT - 1) / NT;
+  bf16x8 kr[PER][4], vr[PER][4];
+
+  __device__ __forceinline__ void load(const bf16* K, const bf16* V, long long rs, int j0, int nk, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int blk = tid + i * NT;
+      const int rk = blk % (DQ_BC / 4), oc = blk / (DQ_BC / 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = j0 + rk * 4 + r;
+        const bool in = blk < NBLK && key < nk;
+        kr[i][r] = in ? *(const bf16x8*)(K + key * rs + oc * 8) : bf16x8{};
+        vr[i][r] = in ? *(const bf16x8*)(V + key * rs + oc * 8) : bf16x8{};
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(DqSmem<D>& sm, int buf, int tid) const {
+    constexpr int ROW = DqSmem<D>::ROW, TROW = DqSmem<D>::TROW;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int blk = tid + i * NT;
+      if (blk < NBLK) {
+        const int rk = blk % (DQ_BC / 4), oc = blk / (DQ_BC / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          *(bf16x8*)(sm.k[buf] + (rk * 4 + r) * ROW + oc * 8) = kr[i][r];
+          *(bf16x8*)(sm.v[buf] + (rk * 4 + r) * ROW + oc * 8) = vr[i][r];
+        }
+        store_transposed4x8(sm.kt[buf], TROW, oc * 8, rk * 4, kr[i]);
+      }
+    }
+  }
+};
+
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+void bwd_dq_kernel(Params p) {
+  constexpr int BR = NW * 32;
+  constexpr int KS = D / 16, DB = D / 32;
+  constexpr int ROW = DqSmem<D>::ROW, TROW = DqSmem<D>::TROW;
+  __shared__ DqSmem<D> sm;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 5, n = lane & 31;
+  const int ntq = gridDim.y;
+  const int qt = CAUSAL ? (ntq - 1 - (int)blockIdx.y) : (int)blockIdx.y;
+  const int h = xcd_head(blockIdx.x, p.H);
+  const int b = blockIdx.z;
+  const int kvh = h / p.G;
+  const int q0 = qt * BR;
+  const int wq0 = q0 + wave * 32;
+
+  const long long qrs = (long long)p.H * D, krs = (long long)p.Hkv * D;
+  const bf16* Q = (const bf16*)p.q + ((long long)b * p.N + p.q_start) * qrs + (long long)h * D;
+  const bf16* dO = (const bf16*)p.dout + ((long long)b * p.N + p.q_start) * qrs + (long long)h * D;
+  const bf16* K = (const bf16*)p.k + ((long long)b * p.N + p.k_start) * krs + (long long)kvh * D;
+  const bf16* V = (const bf16*)p.v + ((long long)b * p.N + p.k_start) * krs + (long long)kvh * D;
+
+  float c = fabsf(p.scale) * kLog2e;
+  float qsign = p.scale < 0.f ? -1.f : 1.f;
+  if (p.scale == 0.f) { c = 1.f; qsign = 0.f; }
+
+  // Q and dO as B operands of S^T = K Q^T and dP^T = V dO^T: lane (g, n) holds row wq0+n, columns 16ks+8g..
+  const int row = wq0 + n;
+  const int rc = min(row, p.Nq - 1);
+  bf16x8 qf[KS], of[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    bf16x8 x = *(const bf16x8*)(Q + rc * qrs + ks * 16 + g * 8);
+    if (qsign != 1.f) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = (bf16)((float)x[e] * qsign);
+    }
+    qf[ks] = x;
+    of[ks] = *(const bf16x8*)(dO + rc * qrs + ks * 16 + g * 8);
+  }
+  const long long si = ((long long)b * p.H + h) * p.N + p.q_start + rc;
+  const float lse2 = p.lse[si] * kLog2e;
+  const float dsum = p.dsum[si];
+  const int qpos = p.q_start + row;
+
+  int nkt = (p.Nk + DQ_BC - 1) / DQ_BC;
+  if (CAUSAL) {
+    const int last_q = p.q_start + min(q0 + BR - 1, p.Nq - 1);
+    const int kend = min(p.Nk, last_q - p.k_start + 1);
+    nkt = kend > 0 ? (kend + DQ_BC - 1) / DQ_BC : 0;
+  }
+  const int wq_last = p.q_start + min(wq0 + 31, p.Nq - 1);
+  const int wq_first = p.q_start + wq0;
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+
+  KTileLoader<D, NW> ld;
+  if (nkt > 0) {
+    ld.load(K, V, krs, 0, p.Nk, tid);
+    ld.store(sm, 0, tid);
+    if (nkt > 1) ld.load(K, V, krs, DQ_BC, p.Nk, tid);
+  }
+  __syncthreads();
+
+  for (int j = 0; j < nkt; ++j) {
+    const int buf = j & 1;
+    const int kpos0 = p.k_start + j * DQ_BC;
+    if (!CAUSAL || kpos0 <= wq_last) {
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+        dp[kb] = f32x16{};
+        const int r_ = kb * 32 + sigma32(n);
+        const bf16* ka = sm.k[buf] + r_ * ROW + g * 8;
+        const bf16* va = sm.v[buf] + r_ * ROW + g * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          s[kb] = mfma32(lds_read16(ka, ks * 16), qf[ks], s[kb]);
+          dp[kb] = mfma32(lds_read16(va, ks * 16), of[ks], dp[kb]);
+        }
+      }
+      const bool need_mask = (CAUSAL && kpos0 + DQ_BC - 1 > wq_first) || (j * DQ_BC + DQ_BC > p.Nk);
+      bf16x8 dsb[4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          bf16x8 x;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int kin = kb * 32 + half * 16 + g * 8 + e;
+            float pr = __builtin_amdgcn_exp2f(fmaf(s[kb][half * 8 + e], c, -lse2));
+            if (need_mask && ((j * DQ_BC + kin >= p.Nk) || (CAUSAL && kpos0 + kin > qpos))) pr = 0.f;
+            x[e] = (bf16)(pr * (dp[kb][half * 8 + e] - dsum));
+          }
+          dsb[kb * 2 + half] = x;
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16* kb_ = sm.kt[buf] + (db * 32 + n) * TROW + g * 8;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[db] = mfma32(lds_read16(kb_, t * 16), dsb[t], acc[db]);
+      }
+    }
+    if (j + 1 < nkt) {
+      ld.store(sm, buf ^ 1, tid);
+      if (j + 2 < nkt) ld.load(K, V, krs, (j + 2) * DQ_BC, p.Nk, tid);
+    }
+    __syncthreads();
+  }
+
+  // ---- store dQ = scale * acc^T: lane (g, query n), register r <-> column 32 db + 8 (r/4) + 4g + r%4
+  if (row < p.Nq) {
+    const long long off = (((long long)b * p.N + p.q_start + row) * p.H + h) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int run = 0; run < 4; ++run) {
+        const int col = db * 32 + run * 8 + g * 4;
+        if (p.accumulate) {
+          f32x4* a = (f32x4*)((float*)p.dq + off + col);
+          f32x4 x = *a;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] += acc[db][run * 4 + e] * p.scale;
+          *a = x;
+        } else {
+          bf16x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = (bf16)(acc[db][run * 4 + e] * p.scale);
+          *(bf16x4*)((bf16*)p.dq + off + col) = x;
+        }
+      }
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_d(const Params& p, hipStream_t s) {
+  const dim3 gkv(p.Hkv, (p.Nk + DKV_BK - 1) / DKV_BK, p.B);
+  if (p.causal)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), gkv, dim3(DKV_NW * 64), 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), gkv, dim3(DKV_NW * 64), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int NW = 4;
+  const dim3 gq(p.H, (p.Nq + NW * 32 - 1) / (NW * 32), p.B);
+  if (p.causal)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true, NW>), gq, dim3(NW * 64), 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false, NW>), gq, dim3(NW * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_mfma(const Params& p, hipStream_t s) {
+  return p.d == 128 ? launch_d<128>(p, s) : launch_d<64>(p, s);
+}
+
+}  // namespace miattn

@@ -15,7 +15,7 @@
 //    one barrier per tile; the next tile's global loads are issued a full
 //    tile ahead into registers;
 //  * scores are computed transposed, S^T = K Q^T, with K's rows loaded in a
-//    bit-permuted order (sigma_k) so that each lane's 32x32 accumulator holds
+//    bit-permuted order (sigma32) so that each lane's 32x32 accumulator holds
 //    8 consecutive keys of one query: exactly the B-operand layout of the
 //    next product O^T += V^T P^T. P never moves between lanes.
 //  * V is transposed into LDS (V^T rows are head-dimension columns); LDS rows
@@ -25,13 +25,15 @@
 //    than 8 (log2 units); otherwise the old max is kept, p <= 2^8, and the
 //    accumulator is not rescaled. The result is unchanged (numerator and
 //    denominator share the max), and most tiles skip the rescale entirely;
-//  * the row sum is taken from the bf16-rounded P with v_dot2_f32_bf16, so
-//    numerator and denominator see the same rounded probabilities;
+//  * the row sum is accumulated from the float32 probabilities before they
+//    are rounded to bf16 for the P V product, so the saved logsumexp keeps
+//    float32 accuracy even for rows with few keys;
 //  * causal workgroups are launched heaviest first, and with H % 8 == 0 the
 //    heads are permuted so that every workgroup of one K/V head group lands
 //    on the same XCD (workgroups are dealt to the 8 XCDs round-robin).
 #include "common.h"
 #include "kernels.h"
+#include "mfma_common.h"
 
 namespace miattn {
 
@@ -39,10 +41,7 @@ namespace {
 
 constexpr int BC = 64;   // keys per tile
 
-constexpr int PAD = 8;   // bf16 elements of padding per LDS row (16 bytes)
-
-// Row slot -> key inside a 32-key block: bits 2 and 3 swapped.
-__device__ __forceinline__ int sigma_k(int n) { return (n & 0x13) | ((n & 4) << 1) | ((n & 8) >> 1); }
+constexpr int PAD = LDS_PAD;
 
 template <int D>
 struct Smem {
@@ -52,17 +51,6 @@ struct Smem {
   bf16 vt[2][D * VROW];
 };
 
-__device__ __forceinline__ bf16x8 lds_read16(const bf16* base, int elem_off) {
-  return *(const bf16x8*)(base + elem_off);
-}
-
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ uint32_t pack2(bf16 lo, bf16 hi) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-}
 
 template <int D, int NW>
 struct TileLoader {
@@ -111,12 +99,7 @@ struct TileLoader {
       const int blk = tid + i * NT;
       if (blk < VBLK) {
         const int kq = blk % (BC / 4), oc = blk / (BC / 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = oc * 8 + e;
-          const uint2 w = {pack2(vreg[i][0][e], vreg[i][1][e]), pack2(vreg[i][2][e], vreg[i][3][e])};
-          *(uint2*)(vt + d * Smem<D>::VROW + kq * 4) = w;
-        }
+        store_transposed4x8(vt, Smem<D>::VROW, oc * 8, kq * 4, vreg[i]);
       }
     }
   }
@@ -137,8 +120,7 @@ void fwd_mfma_kernel(Params p) {
   // ---- workgroup -> (b, h, query tile), heaviest causal tiles first
   const int ntq = gridDim.y;
   const int qt = CAUSAL ? (ntq - 1 - (int)blockIdx.y) : (int)blockIdx.y;
-  int h = blockIdx.x;
-  if ((p.H & 7) == 0) h = (h & 7) * (p.H >> 3) + (h >> 3);
+  const int h = xcd_head(blockIdx.x, p.H);
   const int b = blockIdx.z;
   const int kvh = h / p.G;
   const int q0 = qt * BR;                         // first local query row of the tile
@@ -200,7 +182,6 @@ void fwd_mfma_kernel(Params p) {
   }
   __syncthreads();
 
-  const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
   for (int j = 0; j < nkt; ++j) {
     const bf16* ks_ = sm.k[j & 1];
     const bf16* vt_ = sm.vt[j & 1];
@@ -213,7 +194,7 @@ void fwd_mfma_kernel(Params p) {
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
-        const bf16* kbase = ks_ + (kb * 32 + sigma_k(n)) * Smem<D>::KROW + g * 8;
+        const bf16* kbase = ks_ + (kb * 32 + sigma32(n)) * Smem<D>::KROW + g * 8;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const bf16x8 a = lds_read16(kbase, ks * 16);
@@ -231,7 +212,7 @@ void fwd_mfma_kernel(Params p) {
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int kin = kb * 32 + ((r < 8) ? (g * 8 + r) : (16 + g * 8 + r - 8));
+              const int kin = kb * 32 + sigma_row(g, r);
               const bool bad = (j * BC + kin >= p.Nk) || (CAUSAL && kpos0 + kin > qpos);
               if (bad) s[kb][qb][r] = -INFINITY;
             }
@@ -260,22 +241,25 @@ void fwd_mfma_kernel(Params p) {
           m[qb] = mnew;
         }
         const float mneg = -m[qb];
-        float lsum = 0.f;
+        float lsum0 = 0.f, lsum1 = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
             bf16x8 x;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][qb][half * 8 + e], c, mneg));
-#pragma unroll
             for (int e = 0; e < 8; e += 2) {
-              const bf16x2 pr = {x[e], x[e + 1]};
-              lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
+              const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][half * 8 + e], c, mneg));
+              const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][half * 8 + e + 1], c, mneg));
+              lsum0 += p0;
+              lsum1 += p1;
+              x[e] = (bf16)p0;
+              x[e + 1] = (bf16)p1;
             }
             pf[qb][kb * 2 + half] = x;
           }
         }
+        const float lsum = lsum0 + lsum1;
         l[qb] += lsum;
       }
       // ---- O^T += V^T P^T

@@ -1,0 +1,56 @@
+// Shared pieces of the bf16 matrix-core kernels (gfx950).
+//
+// v_mfma_f32_32x32x16_bf16 operand layouts (lane l = 32*g + n, g in {0,1}):
+//   A (32 x 16): lane holds A[n][8g .. 8g+7]
+//   B (16 x 32): lane holds B[8g .. 8g+7][n]
+//   C (32 x 32): lane holds C[(r/4)*8 + 4g + r%4][n], r = 0..15
+// The contraction index only has to be split the same way in A and B, so
+// any consistent assignment of k to (g, element) is valid.
+#pragma once
+
+#include "common.h"
+
+namespace miattn {
+
+constexpr int LDS_PAD = 8;   // bf16 elements (16 bytes) of padding per LDS row
+
+// Row slot -> index inside a 32-row block with bits 2 and 3 swapped. Loading
+// A-operand row slot m from row sigma(m) makes C's register r of lane (g, n)
+// hold row 8g + r (r < 8) or 16 + 8g + (r - 8) (r >= 8): 8 consecutive rows,
+// which is the layout of an A or B operand whose contraction runs over them.
+__device__ __forceinline__ int sigma32(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+// Row of a 32-row block held in register r of lane group g after the sigma32
+// permutation.
+__device__ __forceinline__ int sigma_row(int g, int r) { return (r < 8) ? (8 * g + r) : (16 + 8 * g + (r - 8)); }
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 lds_read16(const bf16* base, int elem_off) {
+  return *(const bf16x8*)(base + elem_off);
+}
+
+__device__ __forceinline__ uint32_t pack2(bf16 lo, bf16 hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+
+// Stores a block of 4 rows x 8 columns (one bf16x8 per row) transposed: row
+// d = col0 + e of `dst` receives the 4 values at [row0, row0 + 4).
+__device__ __forceinline__ void store_transposed4x8(bf16* dst, int row_len, int col0, int row0, const bf16x8 (&r)[4]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint2 w = {pack2(r[0][e], r[1][e]), pack2(r[2][e], r[3][e])};
+    *(uint2*)(dst + (col0 + e) * row_len + row0) = w;
+  }
+}
+
+// Workgroup x index -> head index, so that with H % 8 == 0 all heads that
+// share a K/V head run on one XCD (workgroups are dealt round-robin to the 8
+// XCDs, and consecutive x indices are consecutive in dispatch order).
+__device__ __forceinline__ int xcd_head(int x, int H) {
+  return (H & 7) == 0 ? (x & 7) * (H >> 3) + (x >> 3) : x;
+}
+
+}  // namespace miattn

@@ -97,10 +97,8 @@ hipError_t fwd_block(const Params& p, int dtype, bool out_f32, hipStream_t s) {
 }
 
 // One backward block: p.dsum must hold rowsum(dout * o) of these rows.
-// dq_acc: float32 scratch the bf16 kernels accumulate dQ into (zeroed by the
-// caller), or null when p.accumulate already makes p.dq a float32 buffer.
-hipError_t bwd_block(const Params& p, int dtype, float* dq_acc, hipStream_t s) {
-  (void)dq_acc;
+hipError_t bwd_block(const Params& p, int dtype, hipStream_t s) {
+  if (dtype == MIATTN_BF16) return miattn::launch_bwd_mfma(p, s);
   return miattn::launch_bwd_simt(p, dtype, s);
 }
 
@@ -218,15 +216,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   p.accumulate = accumulate;
   if ((st = launch_status(miattn::launch_bwd_pre(o, dout, dsum, B, H, N, d, 0, N, dtype, s), "bwd preprocess")))
     return st;
-  float* dq_acc = nullptr;
-  const long long nq = (long long)B * N * H * d;
-  if (false && dtype == MIATTN_BF16 && !accumulate) {
-    dq_acc = (float*)scratch.get((size_t)nq * 4);
-    if (!dq_acc) return fail(MIATTN_ENOMEM, "hipMallocAsync failed for the dq accumulator");
-    if ((st = launch_status(miattn::launch_fill(dq_acc, nq, 0.f, s), "dq clear"))) return st;
-  }
-  if ((st = launch_status(bwd_block(p, dtype, dq_acc, s), "attn_bwd"))) return st;
-  if (dq_acc && (st = launch_status(miattn::launch_convert(dq_acc, dq, nq, dtype, s), "dq convert"))) return st;
+  if ((st = launch_status(bwd_block(p, dtype, s), "attn_bwd"))) return st;
   return ok();
 }
 
@@ -348,7 +338,7 @@ int attn_bwd_chunked(const void* q, const void* k, const void* v, const void* o,
       p.dv = av;
       p.dsum = dsum;
       p.accumulate = 1;
-      if ((st = launch_status(bwd_block(p, dtype, nullptr, s), "chunk backward"))) return st;
+      if ((st = launch_status(bwd_block(p, dtype, s), "chunk backward"))) return st;
     }
   }
   if ((st = launch_status(miattn::launch_convert(aq, dq, nq, dtype, s), "dq convert"))) return st;

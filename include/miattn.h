@@ -79,8 +79,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *   accumulate = 0: dq, dk, dv have element type `dtype` and are overwritten.
  *   accumulate = 1: dq, dk, dv are float32 buffers and the gradients are
  *                   added to their contents.
- * Scratch: one float32 [B, H, N] vector (rowsum(dout * o)) and, for
- * accumulate = 0 with bf16, a float32 dq accumulator.
+ * Scratch: one float32 [B, H, N] vector (rowsum(dout * o)).
  * Outputs must not alias any input or each other. */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
              int B, int H, int Hkv, int N, int d, int causal, float scale,
