@@ -20,7 +20,8 @@
 //    and transposed copies in LDS), LSE and D over every query head of the
 //    group. Products: S = Q K^T, dP = dO V^T (query rows loaded in sigma32
 //    order, so each lane's accumulator holds 8 consecutive queries of one
-//    key = the A operand of the next products), dV += P^T dO, dK += dS^T Q.
+//    key = the B operand of the next products), dV^T += dO^T P and
+//    dK^T += Q^T dS (accumulators hold 16 columns of one key per lane).
 //  * bwd_dq: one workgroup per query tile of one (b, h), the forward's
 //    structure: S^T = K Q^T and dP^T = V dO^T from row-major K and V tiles,
 //    then dQ^T += K^T dS^T from a transposed K tile.
@@ -187,7 +188,7 @@ void bwd_dkdv_kernel(Params p) {
           dp[qb] = mfma32(lds_read16(oa, ks * 16), vf[ks], dp[qb]);
         }
       }
-      // P and dS; lane (g, key n), register r <-> query q0 + 32 qb + sigma_row(g, r)
+          // P and dS; lane (g, key n), register r <-> query q0 + 32 qb + sigma_row(g, r)
       const bool need_mask = CAUSAL && (wk_first + DKV_KW - 1 > p.q_start + q0);
       bf16x8 pa[4], da[4];
 #pragma unroll
@@ -213,15 +214,16 @@ void bwd_dkdv_kernel(Params p) {
           da[qb * 2 + half] = xd;
         }
       }
-      // dV += P^T dO, dK += dS^T Q (B operands from the transposed tiles)
+      // dV^T += dO^T P and dK^T += Q^T dS: A operands from the transposed
+      // tiles (lane = column of dO / Q), B = P / dS as they sit in registers
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const bf16* ob = sm.ot[buf] + (db * 32 + n) * TROW + g * 8;
         const bf16* qb_ = sm.qt[buf] + (db * 32 + n) * TROW + g * 8;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          dv[db] = mfma32(pa[t], lds_read16(ob, t * 16), dv[db]);
-          dk[db] = mfma32(da[t], lds_read16(qb_, t * 16), dk[db]);
+          dv[db] = mfma32(lds_read16(ob, t * 16), pa[t], dv[db]);
+          dk[db] = mfma32(lds_read16(qb_, t * 16), da[t], dk[db]);
         }
       }
     }
@@ -235,7 +237,7 @@ void bwd_dkdv_kernel(Params p) {
     __syncthreads();
   }
 
-  // ---- store: lane (g, key n), register r <-> column 32 db + 8 (r/4) + 4g + r%4
+  // ---- store dK^T, dV^T: lane (g, key n), register r <-> column 32 db + 8 (r/4) + 4g + r%4
   const int key = kw0 + n;
   if (key < p.Nk) {
     const long long off = (((long long)b * p.N + p.k_start + key) * p.Hkv + gkv) * D;
