@@ -30,10 +30,13 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline leg")
     ap.add_argument("--extra", action="store_true", help="also time the chunked workloads")
     ap.add_argument("--workload", default="llama16k")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="after timing, run 3 plain device copies of MIB MiB (a known-size "
+                         "reference for the HBM traffic counters)")
     return ap.parse_args()
 
 
-def cpu_baseline(workload, heads=1):
+def cpu_baseline(workload, heads=3):
     """The float64 oracle, untouched, on a bounded sample of the workload:
     `heads` query heads at the full sequence length, forward + backward."""
     import numpy as np
@@ -159,6 +162,14 @@ def main():
                 "tflops": round((a + bb) / ((f_ms + b_ms) * 1e-3) / 1e12, 2)}
             del tq, tk, tv, tdo, oo, ll
         out["extra"] = extra
+    if args.calib_copy:
+        nbytes = args.calib_copy << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device=q.device)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calib_copy_bytes"] = nbytes
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
