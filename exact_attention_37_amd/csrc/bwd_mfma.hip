@@ -62,29 +62,32 @@ struct QTileLoader {
   static constexpr int NBLK = (DKV_BQ / 4) * (D / 8);
   static constexpr int PER = (NBLK + NT - 1) / NT;
   bf16x8 qr[PER][4], orr[PER][4];
-  float st;   // lse2 (threads 0..63) or dsum (threads 64..127)
+  float st;        // LSE (threads 0..63) or D (threads 64..127) of row q0 + tid % 64
+  bool st_valid;
 
+  // Loads are unconditional, from clamped rows (a select between a pending
+  // load and a constant would force a wait for it here). Rows past Nq hold
+  // finite copies of row Nq-1; their LSE is replaced by +inf when stored, so
+  // their P and dS are exactly 0.
   __device__ __forceinline__ void load(const Params& p, int b, int h, int q0, int tid) {
     const long long qrs = (long long)p.H * D;
     const bf16* Q = (const bf16*)p.q + ((long long)b * p.N + p.q_start) * qrs + (long long)h * D;
     const bf16* O = (const bf16*)p.dout + ((long long)b * p.N + p.q_start) * qrs + (long long)h * D;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int blk = tid + i * NT;
+      const int blk = min(tid + i * NT, NBLK - 1);
       const int rq = blk % (DKV_BQ / 4), oc = blk / (DKV_BQ / 4);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = q0 + rq * 4 + r;
-        const bool in = blk < NBLK && row < p.Nq;
-        qr[i][r] = in ? *(const bf16x8*)(Q + row * qrs + oc * 8) : bf16x8{};
-        orr[i][r] = in ? *(const bf16x8*)(O + row * qrs + oc * 8) : bf16x8{};
+        const int row = min(q0 + rq * 4 + r, p.Nq - 1);
+        qr[i][r] = *(const bf16x8*)(Q + row * qrs + oc * 8);
+        orr[i][r] = *(const bf16x8*)(O + row * qrs + oc * 8);
       }
     }
-    const int t = tid & 63;
-    const int row = q0 + t;
-    const long long si = ((long long)b * p.H + h) * p.N + p.q_start + row;
-    if (tid < 64) st = row < p.Nq ? p.lse[si] * kLog2e : INFINITY;
-    else if (tid < 128) st = row < p.Nq ? p.dsum[si] : 0.f;
+    const int row = q0 + (tid & 63);
+    st_valid = row < p.Nq;
+    const long long si = ((long long)b * p.H + h) * p.N + p.q_start + min(row, p.Nq - 1);
+    st = (tid < 64 ? p.lse : p.dsum)[si];
   }
 
   __device__ __forceinline__ void store(DkdvSmem<D>& sm, int buf, int tid) const {
@@ -103,8 +106,8 @@ struct QTileLoader {
         store_transposed4x8(sm.ot[buf], TROW, oc * 8, rq * 4, orr[i]);
       }
     }
-    if (tid < 64) sm.lse2[buf][tid] = st;
-    else if (tid < 128) sm.dsum[buf][tid - 64] = st;
+    if (tid < 64) sm.lse2[buf][tid] = st_valid ? st * kLog2e : INFINITY;
+    else if (tid < 128) sm.dsum[buf][tid - 64] = st_valid ? st : 0.f;
   }
 };
 
@@ -147,6 +150,7 @@ void bwd_dkdv_kernel(Params p) {
       vf[ks] = *(const bf16x8*)(V + kr * krs + ks * 16 + g * 8);
     }
   }
+  wait_global_loads();
 
   f32x16 dk[DB], dv[DB];
 #pragma unroll
@@ -171,24 +175,28 @@ void bwd_dkdv_kernel(Params p) {
   for (int it = 0; it < niter; ++it) {
     const int buf = it & 1;
     const int q0 = (first + it % per_head) * DKV_BQ;
-    const int q_last = p.q_start + min(q0 + DKV_BQ - 1, p.Nq - 1);
-    const bool active = !CAUSAL || wk_first <= q_last;
-    if (active) {
+    // Every wave computes every tile: on the one diagonal tile where a wave's
+    // keys are all after the tile's queries, the mask zeroes P. A per-wave
+    // branch here makes the register allocator shuttle the accumulators
+    // between AGPRs and VGPRs on every iteration.
+    {
+      // S = Q K^T, dP = dO V^T; step i = (ks, qb, which): 4 chains interleaved
       f32x16 s[2], dp[2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        s[qb] = f32x16{};
-        dp[qb] = f32x16{};
-        const int row = qb * 32 + sigma32(n);
-        const bf16* qa = sm.q[buf] + row * ROW + g * 8;
-        const bf16* oa = sm.o[buf] + row * ROW + g * 8;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          s[qb] = mfma32(lds_read16(qa, ks * 16), kf[ks], s[qb]);
-          dp[qb] = mfma32(lds_read16(oa, ks * 16), vf[ks], dp[qb]);
-        }
-      }
-          // P and dS; lane (g, key n), register r <-> query q0 + 32 qb + sigma_row(g, r)
+      for (int qb = 0; qb < 2; ++qb) { s[qb] = f32x16{}; dp[qb] = f32x16{}; }
+      const bf16* qa0 = sm.q[buf] + sigma32(n) * ROW + g * 8;
+      const bf16* oa0 = sm.o[buf] + sigma32(n) * ROW + g * 8;
+      pipelined_products<4 * KS, 6>(
+          [&](int i) {
+            const int ks = i >> 2, qb = (i >> 1) & 1;
+            return lds_read16((i & 1) ? oa0 : qa0, qb * 32 * ROW + ks * 16);
+          },
+          [&](int i, bf16x8 a) {
+            const int ks = i >> 2, qb = (i >> 1) & 1;
+            if (i & 1) dp[qb] = mfma32(a, vf[ks], dp[qb]);
+            else s[qb] = mfma32(a, kf[ks], s[qb]);
+          });
+      // P and dS; lane (g, key n), register r <-> query q0 + 32 qb + sigma_row(g, r)
       const bool need_mask = CAUSAL && (wk_first + DKV_KW - 1 > p.q_start + q0);
       bf16x8 pa[4], da[4];
 #pragma unroll
@@ -215,17 +223,20 @@ void bwd_dkdv_kernel(Params p) {
         }
       }
       // dV^T += dO^T P and dK^T += Q^T dS: A operands from the transposed
-      // tiles (lane = column of dO / Q), B = P / dS as they sit in registers
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16* ob = sm.ot[buf] + (db * 32 + n) * TROW + g * 8;
-        const bf16* qb_ = sm.qt[buf] + (db * 32 + n) * TROW + g * 8;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          dv[db] = mfma32(lds_read16(ob, t * 16), pa[t], dv[db]);
-          dk[db] = mfma32(lds_read16(qb_, t * 16), da[t], dk[db]);
-        }
-      }
+      // tiles (lane = column of dO / Q), B = P / dS as they sit in registers;
+      // step i = (t, db, which): 2*DB chains interleaved
+      const bf16* ob0 = sm.ot[buf] + n * TROW + g * 8;
+      const bf16* qb0 = sm.qt[buf] + n * TROW + g * 8;
+      pipelined_products<8 * DB, 6>(
+          [&](int i) {
+            const int t = i / (2 * DB), db = (i >> 1) % DB;
+            return lds_read16((i & 1) ? qb0 : ob0, db * 32 * TROW + t * 16);
+          },
+          [&](int i, bf16x8 a) {
+            const int t = i / (2 * DB), db = (i >> 1) % DB;
+            if (i & 1) dk[db] = mfma32(a, da[t], dk[db]);
+            else dv[db] = mfma32(a, pa[t], dv[db]);
+          });
     }
     if (it + 1 < niter) {
       ld.store(sm, buf ^ 1, tid);
@@ -285,41 +296,70 @@ struct DqSmem {
   bf16 kt[2][D * TROW];
 };
 
+// One K/V tile as blocks of 4 rows x 8 columns. With at least two blocks'
+// worth of threads, a thread loads either a K block or a V block; otherwise
+// each thread loads both for its blocks.
 template <int D, int NW>
 struct KTileLoader {
   static constexpr int NT = NW * 64;
   static constexpr int NBLK = (DQ_BC / 4) * (D / 8);
-  static constexpr int PER = (NBLK + NT - 1) / NT;
-  bf16x8 kr[PER][4], vr[PER][4];
+  static constexpr bool SPLIT = NT >= 2 * NBLK;
+  static constexpr int PER = SPLIT ? 1 : (NBLK + NT - 1) / NT;
+  bf16x8 kr[PER][4], vr[SPLIT ? 1 : PER][4];
 
+  // Unconditional loads from clamped rows (see QTileLoader); rows past nk
+  // are masked to P = 0.
   __device__ __forceinline__ void load(const bf16* K, const bf16* V, long long rs, int j0, int nk, int tid) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int blk = tid + i * NT;
+    if constexpr (SPLIT) {
+      const bool is_v = tid >= NBLK;
+      const int blk = min(is_v ? tid - NBLK : tid, NBLK - 1);
       const int rk = blk % (DQ_BC / 4), oc = blk / (DQ_BC / 4);
+      const bf16* src = is_v ? V : K;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = j0 + rk * 4 + r;
-        const bool in = blk < NBLK && key < nk;
-        kr[i][r] = in ? *(const bf16x8*)(K + key * rs + oc * 8) : bf16x8{};
-        vr[i][r] = in ? *(const bf16x8*)(V + key * rs + oc * 8) : bf16x8{};
+        const int key = min(j0 + rk * 4 + r, nk - 1);
+        kr[0][r] = *(const bf16x8*)(src + key * rs + oc * 8);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int blk = min(tid + i * NT, NBLK - 1);
+        const int rk = blk % (DQ_BC / 4), oc = blk / (DQ_BC / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = min(j0 + rk * 4 + r, nk - 1);
+          kr[i][r] = *(const bf16x8*)(K + key * rs + oc * 8);
+          vr[i][r] = *(const bf16x8*)(V + key * rs + oc * 8);
+        }
       }
     }
   }
 
   __device__ __forceinline__ void store(DqSmem<D>& sm, int buf, int tid) const {
     constexpr int ROW = DqSmem<D>::ROW, TROW = DqSmem<D>::TROW;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int blk = tid + i * NT;
-      if (blk < NBLK) {
+    if constexpr (SPLIT) {
+      if (tid < 2 * NBLK) {
+        const bool is_v = tid >= NBLK;
+        const int blk = is_v ? tid - NBLK : tid;
         const int rk = blk % (DQ_BC / 4), oc = blk / (DQ_BC / 4);
+        bf16* dst = is_v ? sm.v[buf] : sm.k[buf];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          *(bf16x8*)(sm.k[buf] + (rk * 4 + r) * ROW + oc * 8) = kr[i][r];
-          *(bf16x8*)(sm.v[buf] + (rk * 4 + r) * ROW + oc * 8) = vr[i][r];
+        for (int r = 0; r < 4; ++r) *(bf16x8*)(dst + (rk * 4 + r) * ROW + oc * 8) = kr[0][r];
+        if (!is_v) store_transposed4x8(sm.kt[buf], TROW, oc * 8, rk * 4, kr[0]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int blk = tid + i * NT;
+        if (blk < NBLK) {
+          const int rk = blk % (DQ_BC / 4), oc = blk / (DQ_BC / 4);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            *(bf16x8*)(sm.k[buf] + (rk * 4 + r) * ROW + oc * 8) = kr[i][r];
+            *(bf16x8*)(sm.v[buf] + (rk * 4 + r) * ROW + oc * 8) = vr[i][r];
+          }
+          store_transposed4x8(sm.kt[buf], TROW, oc * 8, rk * 4, kr[i]);
         }
-        store_transposed4x8(sm.kt[buf], TROW, oc * 8, rk * 4, kr[i]);
       }
     }
   }
@@ -371,6 +411,7 @@ void bwd_dq_kernel(Params p) {
   const long long si = ((long long)b * p.H + h) * p.N + p.q_start + rc;
   const float lse2 = p.lse[si] * kLog2e;
   const float dsum = p.dsum[si];
+  wait_global_loads();
   const int qpos = p.q_start + row;
 
   int nkt = (p.Nk + DQ_BC - 1) / DQ_BC;
@@ -379,7 +420,6 @@ void bwd_dq_kernel(Params p) {
     const int kend = min(p.Nk, last_q - p.k_start + 1);
     nkt = kend > 0 ? (kend + DQ_BC - 1) / DQ_BC : 0;
   }
-  const int wq_last = p.q_start + min(wq0 + 31, p.Nq - 1);
   const int wq_first = p.q_start + wq0;
 
   f32x16 acc[DB];
@@ -397,21 +437,23 @@ void bwd_dq_kernel(Params p) {
   for (int j = 0; j < nkt; ++j) {
     const int buf = j & 1;
     const int kpos0 = p.k_start + j * DQ_BC;
-    if (!CAUSAL || kpos0 <= wq_last) {
+    {   // no per-wave skip (see bwd_dkdv); fully masked waves compute P = 0
+      // S^T = K Q^T, dP^T = V dO^T; step i = (ks, kb, which): 4 chains interleaved
       f32x16 s[2], dp[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        dp[kb] = f32x16{};
-        const int r_ = kb * 32 + sigma32(n);
-        const bf16* ka = sm.k[buf] + r_ * ROW + g * 8;
-        const bf16* va = sm.v[buf] + r_ * ROW + g * 8;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          s[kb] = mfma32(lds_read16(ka, ks * 16), qf[ks], s[kb]);
-          dp[kb] = mfma32(lds_read16(va, ks * 16), of[ks], dp[kb]);
-        }
-      }
+      for (int kb = 0; kb < 2; ++kb) { s[kb] = f32x16{}; dp[kb] = f32x16{}; }
+      const bf16* ka0 = sm.k[buf] + sigma32(n) * ROW + g * 8;
+      const bf16* va0 = sm.v[buf] + sigma32(n) * ROW + g * 8;
+      pipelined_products<4 * KS, 4>(
+          [&](int i) {
+            const int ks = i >> 2, kb = (i >> 1) & 1;
+            return lds_read16((i & 1) ? va0 : ka0, kb * 32 * ROW + ks * 16);
+          },
+          [&](int i, bf16x8 a) {
+            const int ks = i >> 2, kb = (i >> 1) & 1;
+            if (i & 1) dp[kb] = mfma32(a, of[ks], dp[kb]);
+            else s[kb] = mfma32(a, qf[ks], s[kb]);
+          });
       const bool need_mask = (CAUSAL && kpos0 + DQ_BC - 1 > wq_first) || (j * DQ_BC + DQ_BC > p.Nk);
       bf16x8 dsb[4];
 #pragma unroll
@@ -429,12 +471,11 @@ void bwd_dq_kernel(Params p) {
           dsb[kb * 2 + half] = x;
         }
       }
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16* kb_ = sm.kt[buf] + (db * 32 + n) * TROW + g * 8;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[db] = mfma32(lds_read16(kb_, t * 16), dsb[t], acc[db]);
-      }
+      // dQ^T += K^T dS^T; step i = (t, db): DB chains interleaved
+      const bf16* kt0 = sm.kt[buf] + n * TROW + g * 8;
+      pipelined_products<4 * DB, 4>(
+          [&](int i) { return lds_read16(kt0, (i % DB) * 32 * TROW + (i / DB) * 16); },
+          [&](int i, bf16x8 a) { acc[i % DB] = mfma32(a, dsb[i / DB], acc[i % DB]); });
     }
     if (j + 1 < nkt) {
       ld.store(sm, buf ^ 1, tid);
@@ -477,7 +518,7 @@ hipError_t launch_d(const Params& p, hipStream_t s) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), gkv, dim3(DKV_NW * 64), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int NW = 4;
+  constexpr int NW = 8;
   const dim3 gq(p.H, (p.Nq + NW * 32 - 1) / (NW * 32), p.B);
   if (p.causal)
     hipLaunchKernelGGL((bwd_dq_kernel<D, true, NW>), gq, dim3(NW * 64), 0, s, p);

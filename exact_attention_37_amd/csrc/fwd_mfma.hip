@@ -64,23 +64,25 @@ struct TileLoader {
   bf16x8 kreg[KPER];
   bf16x8 vreg[VPER][4];
 
+  // Loads are unconditional, from clamped rows: a select between a pending
+  // load and a constant would force a wait for the load right here. Rows past
+  // nk hold copies of row nk-1 (finite); their scores are masked to -inf, so
+  // they contribute nothing.
   __device__ __forceinline__ void load(const bf16* K, const bf16* V, long long rstride, int j0, int nk, int tid) {
 #pragma unroll
     for (int i = 0; i < KPER; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / KCH, ch = c % KCH;
-      const bool in = (c < KCHUNKS) && (j0 + row < nk);
-      kreg[i] = in ? *(const bf16x8*)(K + (j0 + row) * rstride + ch * 8) : bf16x8{};
+      const int c = min(tid + i * NT, KCHUNKS - 1);
+      const int row = min(j0 + c / KCH, nk - 1), ch = c % KCH;
+      kreg[i] = *(const bf16x8*)(K + row * rstride + ch * 8);
     }
 #pragma unroll
     for (int i = 0; i < VPER; ++i) {
-      const int blk = tid + i * NT;
+      const int blk = min(tid + i * NT, VBLK - 1);
       const int kq = blk % (BC / 4), oc = blk / (BC / 4);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = j0 + kq * 4 + r;
-        const bool in = (blk < VBLK) && (key < nk);
-        vreg[i][r] = in ? *(const bf16x8*)(V + key * rstride + oc * 8) : bf16x8{};
+        const int key = min(j0 + kq * 4 + r, nk - 1);
+        vreg[i][r] = *(const bf16x8*)(V + key * rstride + oc * 8);
       }
     }
   }
@@ -106,7 +108,7 @@ struct TileLoader {
 };
 
 template <int D, int QB, int NW, bool CAUSAL, typename TO>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void fwd_mfma_kernel(Params p) {
   constexpr int BR = NW * QB * 32;
   constexpr int KS = D / 16;   // k-steps of the QK^T product
@@ -153,6 +155,7 @@ void fwd_mfma_kernel(Params p) {
       qf[qb][ks] = x;
     }
   }
+  wait_global_loads();
 
   // ---- key range of the workgroup
   int nkt = (p.Nk + BC - 1) / BC;
@@ -161,7 +164,6 @@ void fwd_mfma_kernel(Params p) {
     const int kend = min(p.Nk, last_q - p.k_start + 1);
     nkt = kend > 0 ? (kend + BC - 1) / BC : 0;
   }
-  const int wq_last = p.q_start + min(wq0 + QB * 32 - 1, p.Nq - 1);   // absolute, this wave
   const int wq_first = p.q_start + wq0;
 
   f32x16 acc[QB][DB];
@@ -186,22 +188,22 @@ void fwd_mfma_kernel(Params p) {
     const bf16* ks_ = sm.k[j & 1];
     const bf16* vt_ = sm.vt[j & 1];
     const int kpos0 = p.k_start + j * BC;   // absolute position of the tile's first key
-    const bool wave_active = !CAUSAL || kpos0 <= wq_last;
-    if (wave_active) {
-      // ---- S^T = K Q^T for 2 blocks of 32 keys
+    {   // no per-wave skip: a per-wave branch makes the register allocator
+        // shuttle accumulators between AGPRs and VGPRs every iteration; fully
+        // masked waves (diagonal tiles only) compute P = 0 instead
+      // ---- S^T = K Q^T for 2 blocks of 32 keys; step i = (ks, kb), chains kb interleaved
       f32x16 s[2][QB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
-        const bf16* kbase = ks_ + (kb * 32 + sigma32(n)) * Smem<D>::KROW + g * 8;
+      const bf16* kbase0 = ks_ + sigma32(n) * Smem<D>::KROW + g * 8;
+      pipelined_products<2 * KS, 4>(
+          [&](int i) { return lds_read16(kbase0, (i & 1) * 32 * Smem<D>::KROW + (i >> 1) * 16); },
+          [&](int i, bf16x8 a) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a = lds_read16(kbase, ks * 16);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma32(a, qf[qb][ks], s[kb][qb]);
-        }
-      }
+            for (int qb = 0; qb < QB; ++qb) s[i & 1][qb] = mfma32(a, qf[qb][i >> 1], s[i & 1][qb]);
+          });
       // ---- mask: keys past the diagonal or past Nk
       const bool need_mask = (CAUSAL && kpos0 + BC - 1 > wq_first) || (j * BC + BC > p.Nk);
       if (need_mask) {
@@ -262,17 +264,14 @@ void fwd_mfma_kernel(Params p) {
         const float lsum = lsum0 + lsum1;
         l[qb] += lsum;
       }
-      // ---- O^T += V^T P^T
+      // ---- O^T += V^T P^T; step i = (kq, db), chains db interleaved
+      const bf16* vbase0 = vt_ + n * Smem<D>::VROW + g * 8;
+      pipelined_products<4 * DB, 4>(
+          [&](int i) { return lds_read16(vbase0, (i % DB) * 32 * Smem<D>::VROW + (i / DB) * 16); },
+          [&](int i, bf16x8 a) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16* vbase = vt_ + (db * 32 + n) * Smem<D>::VROW + g * 8;
-#pragma unroll
-        for (int kq = 0; kq < 4; ++kq) {
-          const bf16x8 a = lds_read16(vbase, kq * 16);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32(a, pf[qb][kq], acc[qb][db]);
-        }
-      }
+            for (int qb = 0; qb < QB; ++qb) acc[qb][i % DB] = mfma32(a, pf[qb][i / DB], acc[qb][i % DB]);
+          });
     }
     if (j + 1 < nkt) {
       ld.store(sm.k[(j + 1) & 1], sm.vt[(j + 1) & 1], tid);
@@ -327,8 +326,8 @@ hipError_t launch_cfg(const Params& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd_mfma(const Params& p, bool out_f32, hipStream_t s) {
-  if (p.d == 128) return out_f32 ? launch_cfg<128, 2, 4, float>(p, s) : launch_cfg<128, 2, 4, bf16>(p, s);
-  return out_f32 ? launch_cfg<64, 2, 4, float>(p, s) : launch_cfg<64, 2, 4, bf16>(p, s);
+  if (p.d == 128) return out_f32 ? launch_cfg<128, 1, 8, float>(p, s) : launch_cfg<128, 1, 8, bf16>(p, s);
+  return out_f32 ? launch_cfg<64, 1, 8, float>(p, s) : launch_cfg<64, 1, 8, bf16>(p, s);
 }
 
 }  // namespace miattn

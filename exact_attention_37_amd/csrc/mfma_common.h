@@ -46,6 +46,38 @@ __device__ __forceinline__ void store_transposed4x8(bf16* dst, int row_len, int 
   }
 }
 
+// Waits for every outstanding global load of this wave. Used after the
+// loads of loop-invariant matrix operands: without it the compiler cannot
+// prove them complete across the loop back-edge and inserts vmcnt waits
+// (on the next tile's prefetch) in front of the loop's first products.
+// (gfx9 s_waitcnt encoding: vmcnt = 0, expcnt = 7, lgkmcnt = 15, i.e. wait on
+// vector memory only.)
+__device__ __forceinline__ void wait_global_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// A chain of N matrix-core products whose A (or B) operands come from LDS:
+// rd(i) reads step i's operand, mm(i, x) issues step i's MPS MFMAs. Keeps R
+// LDS reads in flight ahead of the MFMAs, and pins that order for the
+// scheduler (R reads, then alternating MPS MFMAs / 1 read), so LDS latency
+// overlaps the matrix cores instead of stalling each product.
+template <int N, int R, class RD, class MM, int MPS = 1>
+__device__ __forceinline__ void pipelined_products(RD rd, MM mm) {
+  bf16x8 ring[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) ring[i] = rd(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const bf16x8 a = ring[i % R];
+    if (i + R < N) ring[i % R] = rd(i + R);
+    mm(i, a);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, R, 0);   // DS reads
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, MPS, 0); // MFMA
+    if (i + R < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
 // Workgroup x index -> head index, so that with H % 8 == 0 all heads that
 // share a K/V head run on one XCD (workgroups are dealt round-robin to the 8
 // XCDs, and consecutive x indices are consecutive in dispatch order).
