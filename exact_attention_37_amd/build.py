@@ -21,7 +21,7 @@ SOURCES = ["miattn.cpp", "simt.hip", "prep.hip", "fwd_mfma.hip", "bwd_mfma.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed fp32 VALU instructions are disabled for every device pass.
-FLAGS = ["-O3", "-fPIC", "-std=c++17", "--offload-arch=" + ARCH,
+FLAGS = ["-O3", "-fPIC", "-std=c++20", "--offload-arch=" + ARCH,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I" + os.path.join(ROOT, "include"), "-Wno-unused-result"]
 

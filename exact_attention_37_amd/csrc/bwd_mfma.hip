@@ -50,8 +50,7 @@ struct DkdvSmem {
   bf16 qt[2][D * TROW];
   bf16 o[2][DKV_BQ * ROW];     // dO
   bf16 ot[2][D * TROW];
-  float lse2[2][DKV_BQ];       // LSE * log2(e); +inf past the last row
-  float dsum[2][DKV_BQ];
+  float stat[2][4][DKV_BQ];    // [0]: LSE * log2(e) (+inf past the last row), [1]: D; [2..3] unused
 };
 
 // One streamed tile: 64 query rows of Q and dO of one head, as blocks of
@@ -60,54 +59,73 @@ template <int D>
 struct QTileLoader {
   static constexpr int NT = DKV_NW * 64;
   static constexpr int NBLK = (DKV_BQ / 4) * (D / 8);
-  static constexpr int PER = (NBLK + NT - 1) / NT;
-  bf16x8 qr[PER][4], orr[PER][4];
-  float st;        // LSE (threads 0..63) or D (threads 64..127) of row q0 + tid % 64
+  static_assert(NBLK <= NT, "one 4x8 block per thread");
+  bf16x8 qr[4], orr[4];
+  float st;        // LSE (tid % 256 in [0, 64)) or D ([64, 128)) of row q0 + tid % 64
   bool st_valid;
 
-  // Loads are unconditional, from clamped rows (a select between a pending
-  // load and a constant would force a wait for it here). Rows past Nq hold
-  // finite copies of row Nq-1; their LSE is replaced by +inf when stored, so
-  // their P and dS are exactly 0.
-  __device__ __forceinline__ void load(const Params& p, int b, int h, int q0, int tid) {
-    const long long qrs = (long long)p.H * D;
-    const bf16* Q = (const bf16*)p.q + ((long long)b * p.N + p.q_start) * qrs + (long long)h * D;
-    const bf16* O = (const bf16*)p.dout + ((long long)b * p.N + p.q_start) * qrs + (long long)h * D;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int blk = min(tid + i * NT, NBLK - 1);
-      const int rq = blk % (DKV_BQ / 4), oc = blk / (DKV_BQ / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = min(q0 + rq * 4 + r, p.Nq - 1);
-        qr[i][r] = *(const bf16x8*)(Q + row * qrs + oc * 8);
-        orr[i][r] = *(const bf16x8*)(O + row * qrs + oc * 8);
-      }
-    }
-    const int row = q0 + (tid & 63);
-    st_valid = row < p.Nq;
-    const long long si = ((long long)b * p.H + h) * p.N + p.q_start + min(row, p.Nq - 1);
-    st = (tid < 64 ? p.lse : p.dsum)[si];
+  // Everything here is branch-free so it can be interleaved with the
+  // products. Loads are unconditional, from clamped rows (a select between a
+  // pending load and a constant would force a wait for it right away). Rows
+  // past Nq hold finite copies of row Nq-1; their LSE is replaced by +inf when
+  // stored, so their P and dS are exactly 0. With fewer blocks than threads,
+  // two threads load (and later write) the same block.
+  __device__ __forceinline__ const bf16* qptr(const Params& p, int b, int h) const {
+    return (const bf16*)p.q + ((long long)b * p.N + p.q_start) * ((long long)p.H * D) + (long long)h * D;
   }
-
-  __device__ __forceinline__ void store(DkdvSmem<D>& sm, int buf, int tid) const {
-    constexpr int ROW = DkdvSmem<D>::ROW, TROW = DkdvSmem<D>::TROW;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int blk = tid + i * NT;
-      if (blk < NBLK) {
-        const int rq = blk % (DKV_BQ / 4), oc = blk / (DKV_BQ / 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          *(bf16x8*)(sm.q[buf] + (rq * 4 + r) * ROW + oc * 8) = qr[i][r];
-          *(bf16x8*)(sm.o[buf] + (rq * 4 + r) * ROW + oc * 8) = orr[i][r];
-        }
-        store_transposed4x8(sm.qt[buf], TROW, oc * 8, rq * 4, qr[i]);
-        store_transposed4x8(sm.ot[buf], TROW, oc * 8, rq * 4, orr[i]);
-      }
+  __device__ __forceinline__ const bf16* optr(const Params& p, int b, int h) const {
+    return (const bf16*)p.dout + ((long long)b * p.N + p.q_start) * ((long long)p.H * D) + (long long)h * D;
+  }
+  // piece 0..3: Q row r = piece; 4..7: dO row r = piece - 4; 8: LSE or D
+  __device__ __forceinline__ void load_piece(int piece, const Params& p, int b, int h, int q0, int tid) {
+    const long long qrs = (long long)p.H * D;
+    const int blk = tid % NBLK;
+    const int rq = blk % (DKV_BQ / 4), oc = blk / (DKV_BQ / 4);
+    if (piece < 8) {
+      const int r = piece & 3;
+      const int row = min(q0 + rq * 4 + r, p.Nq - 1);
+      const bf16* base = piece < 4 ? qptr(p, b, h) : optr(p, b, h);
+      const bf16x8 x = *(const bf16x8*)(base + row * qrs + oc * 8);
+      if (piece < 4) qr[r] = x; else orr[r] = x;
+    } else {
+      const int row = q0 + (tid & 63);
+      st_valid = row < p.Nq;
+      const long long si = ((long long)b * p.H + h) * p.N + p.q_start + min(row, p.Nq - 1);
+      st = ((tid & 64) ? p.dsum : p.lse)[si];
     }
-    if (tid < 64) sm.lse2[buf][tid] = st_valid ? st * kLog2e : INFINITY;
-    else if (tid < 128) sm.dsum[buf][tid - 64] = st_valid ? st : 0.f;
+  }
+  __device__ __forceinline__ void load(const Params& p, int b, int h, int q0, int tid) {
+#pragma unroll
+    for (int piece = 0; piece < 9; ++piece) load_piece(piece, p, b, h, q0, tid);
+  }
+  // piece 0..3: Q row-major row r; 4..7: dO row-major; 8..11: Q transposed
+  // (columns 2k, 2k+1 of the block); 12..15: dO transposed; 16: LSE / D
+  __device__ __forceinline__ void store_piece(int piece, DkdvSmem<D>& sm, int buf, int tid) const {
+    constexpr int ROW = DkdvSmem<D>::ROW, TROW = DkdvSmem<D>::TROW;
+    const int blk = tid % NBLK;
+    const int rq = blk % (DKV_BQ / 4), oc = blk / (DKV_BQ / 4);
+    if (piece < 8) {
+      const int r = piece & 3;
+      bf16* dst = (piece < 4 ? sm.q[buf] : sm.o[buf]) + (rq * 4 + r) * ROW + oc * 8;
+      *(bf16x8*)dst = piece < 4 ? qr[r] : orr[r];
+    } else if (piece < 16) {
+      const bf16x8 (&x)[4] = piece < 12 ? qr : orr;
+      bf16* dst = piece < 12 ? sm.qt[buf] : sm.ot[buf];
+      const int e0 = 2 * (piece & 3);
+#pragma unroll
+      for (int e = e0; e < e0 + 2; ++e) {
+        const uint2 w = {pack2(x[0][e], x[1][e]), pack2(x[2][e], x[3][e])};
+        *(uint2*)(dst + (oc * 8 + e) * TROW + rq * 4) = w;
+      }
+    } else {
+      const int slot = (tid >> 6) & 3;     // 0: LSE, 1: D, 2-3: unused
+      const float v = slot == 0 ? (st_valid ? st * kLog2e : INFINITY) : (st_valid ? st : 0.f);
+      sm.stat[buf][slot][tid & 63] = v;
+    }
+  }
+  __device__ __forceinline__ void store(DkdvSmem<D>& sm, int buf, int tid) const {
+#pragma unroll
+    for (int piece = 0; piece < 17; ++piece) store_piece(piece, sm, buf, tid);
   }
 };
 
@@ -116,7 +134,7 @@ __global__ __launch_bounds__(DKV_NW * 64) __attribute__((amdgpu_waves_per_eu(1, 
 void bwd_dkdv_kernel(Params p) {
   constexpr int KS = D / 16, DB = D / 32;
   constexpr int ROW = DkdvSmem<D>::ROW, TROW = DkdvSmem<D>::TROW;
-  __shared__ DkdvSmem<D> sm;
+  __shared__ __attribute__((aligned(16))) DkdvSmem<D> sm;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -164,87 +182,128 @@ void bwd_dkdv_kernel(Params p) {
   const int kpos = p.k_start + kw0 + n;          // this lane's key position
   const int wk_first = p.k_start + kw0;
 
+  // query tile of iteration `it`: (head, first row); iterations past the end
+  // repeat the last tile so that loads and stores need no branch
+  auto tile_of = [&](int it, int& h, int& q0) {
+    it = min(it, niter - 1);
+    h = gkv * p.G + it / per_head;
+    q0 = (first + it % per_head) * DKV_BQ;
+  };
+
   QTileLoader<D> ld;
   if (niter > 0) {
-    ld.load(p, b, gkv * p.G, first * DKV_BQ, tid);
+    int h, q0;
+    tile_of(0, h, q0);
+    ld.load(p, b, h, q0, tid);
     ld.store(sm, 0, tid);
-    if (niter > 1) ld.load(p, b, gkv * p.G + 1 / per_head, (first + 1 % per_head) * DKV_BQ, tid);  // it = 1
+    tile_of(1, h, q0);
+    ld.load(p, b, h, q0, tid);
   }
   __syncthreads();
 
   for (int it = 0; it < niter; ++it) {
     const int buf = it & 1;
-    const int q0 = (first + it % per_head) * DKV_BQ;
+    int h_cur, q0;
+    tile_of(it, h_cur, q0);
+    int h_nx, q0_nx;
+    tile_of(it + 2, h_nx, q0_nx);
+    const bool need_mask = CAUSAL && (wk_first + DKV_KW - 1 > p.q_start + q0);
+    const bf16* qa0 = sm.q[buf] + sigma32(n) * ROW + g * 8;
+    const bf16* oa0 = sm.o[buf] + sigma32(n) * ROW + g * 8;
+    const bf16* ob0 = sm.ot[buf] + n * TROW + g * 8;
+    const bf16* qt0 = sm.qt[buf] + n * TROW + g * 8;
+    const float* lse2 = sm.stat[buf][0];
+    const float* dsm = sm.stat[buf][1];
+
     // Every wave computes every tile: on the one diagonal tile where a wave's
-    // keys are all after the tile's queries, the mask zeroes P. A per-wave
-    // branch here makes the register allocator shuttle the accumulators
-    // between AGPRs and VGPRs on every iteration.
-    {
-      // S = Q K^T, dP = dO V^T; step i = (ks, qb, which): 4 chains interleaved
-      f32x16 s[2], dp[2];
+    // keys are all after the tile's queries, the mask zeroes P (a per-wave
+    // branch would make the allocator shuttle accumulators through AGPRs).
+    //
+    // 4 phases of PL = D/8 lock steps, one MFMA each; the tile's 64 queries
+    // are two halves qb:
+    //   phase 0: S, dP of half 0          + store of the next tile to LDS
+    //   phase 1: S, dP of half 1          + softmax of half 0
+    //   phase 2: dV^T, dK^T over half 0   + softmax of half 1
+    //   phase 3: dV^T, dK^T over half 1   + global loads of the tile after next
+    // Each phase's extra work (17 store pieces, 16 softmax sub-steps, 9 load
+    // pieces) is spread evenly over its PL steps.
+    constexpr int PL = D / 8;
+    f32x16 s[2], dp[2];
+    s[0] = f32x16{}; dp[0] = f32x16{}; s[1] = f32x16{}; dp[1] = f32x16{};
+    bf16x8 pa[4], da[4];
+    float pr[16];
+    f32x4 lq[4], dq4[4];   // LSE and D of the 16 query rows of the half being softmaxed
+
+    // softmax sub-step w (0..15) of half qb: lane (g, key n), register r <->
+    // query q0 + 32 qb + sigma_row(g, r); sub-step w covers elements 2k, 2k+1
+    // (k = (w % 8) / 2) of register group h2 = w / 8; even sub-steps form P,
+    // odd ones dS.
+    auto softmax_sub = [&](auto qbc, auto wc) {
+      constexpr int qb = decltype(qbc)::value, w = decltype(wc)::value;
+      constexpr int h2 = w >> 3, k = (w & 7) >> 1;
+      const int qi0 = qb * 32 + h2 * 16 + g * 8;    // 8 consecutive query rows
+      if constexpr ((w & 7) == 0) {
+        lq[2 * h2] = *(const f32x4*)(lse2 + qi0);
+        lq[2 * h2 + 1] = *(const f32x4*)(lse2 + qi0 + 4);
+        dq4[2 * h2] = *(const f32x4*)(dsm + qi0);
+        dq4[2 * h2 + 1] = *(const f32x4*)(dsm + qi0 + 4);
+      }
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) { s[qb] = f32x16{}; dp[qb] = f32x16{}; }
-      const bf16* qa0 = sm.q[buf] + sigma32(n) * ROW + g * 8;
-      const bf16* oa0 = sm.o[buf] + sigma32(n) * ROW + g * 8;
-      pipelined_products<4 * KS, 6>(
-          [&](int i) {
-            const int ks = i >> 2, qb = (i >> 1) & 1;
-            return lds_read16((i & 1) ? oa0 : qa0, qb * 32 * ROW + ks * 16);
-          },
-          [&](int i, bf16x8 a) {
-            const int ks = i >> 2, qb = (i >> 1) & 1;
-            if (i & 1) dp[qb] = mfma32(a, vf[ks], dp[qb]);
-            else s[qb] = mfma32(a, kf[ks], s[qb]);
-          });
-      // P and dS; lane (g, key n), register r <-> query q0 + 32 qb + sigma_row(g, r)
-      const bool need_mask = CAUSAL && (wk_first + DKV_KW - 1 > p.q_start + q0);
-      bf16x8 pa[4], da[4];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int qi0 = qb * 32 + half * 16 + g * 8;   // 8 consecutive query rows
-          const f32x4 l0 = *(const f32x4*)(sm.lse2[buf] + qi0);
-          const f32x4 l1 = *(const f32x4*)(sm.lse2[buf] + qi0 + 4);
-          const f32x4 d0 = *(const f32x4*)(sm.dsum[buf] + qi0);
-          const f32x4 d1 = *(const f32x4*)(sm.dsum[buf] + qi0 + 4);
-          bf16x8 xp, xd;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float lv = e < 4 ? l0[e] : l1[e - 4];
-            const float dv_ = e < 4 ? d0[e] : d1[e - 4];
-            float pr = __builtin_amdgcn_exp2f(fmaf(s[qb][half * 8 + e], c, -lv));
-            if (need_mask && kpos > p.q_start + q0 + qi0 + e) pr = 0.f;
-            xp[e] = (bf16)pr;
-            xd[e] = (bf16)(pr * (dp[qb][half * 8 + e] - dv_));
-          }
-          pa[qb * 2 + half] = xp;
-          da[qb * 2 + half] = xd;
+      for (int u = 0; u < 2; ++u) {
+        const int e = 2 * k + u;
+        const int r = h2 * 8 + e;
+        if constexpr ((w & 1) == 0) {
+          const float lv = lq[2 * h2 + (e >> 2)][e & 3];
+          const float x = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, -lv));
+          pr[r] = (need_mask && kpos > p.q_start + q0 + qi0 + e) ? 0.f : x;
+          pa[qb * 2 + h2][e] = (bf16)pr[r];
+        } else {
+          const float dv_ = dq4[2 * h2 + (e >> 2)][e & 3];
+          da[qb * 2 + h2][e] = (bf16)(pr[r] * (dp[qb][r] - dv_));
         }
       }
-      // dV^T += dO^T P and dK^T += Q^T dS: A operands from the transposed
-      // tiles (lane = column of dO / Q), B = P / dS as they sit in registers;
-      // step i = (t, db, which): 2*DB chains interleaved
-      const bf16* ob0 = sm.ot[buf] + n * TROW + g * 8;
-      const bf16* qb0 = sm.qt[buf] + n * TROW + g * 8;
-      pipelined_products<8 * DB, 6>(
-          [&](int i) {
-            const int t = i / (2 * DB), db = (i >> 1) % DB;
-            return lds_read16((i & 1) ? qb0 : ob0, db * 32 * TROW + t * 16);
-          },
-          [&](int i, bf16x8 a) {
-            const int t = i / (2 * DB), db = (i >> 1) % DB;
-            if (i & 1) dk[db] = mfma32(a, da[t], dk[db]);
+    };
+
+    lockstep_products<4 * PL, 4>(
+        [&](auto ic) {
+          constexpr int i = decltype(ic)::value, ph = i / PL, j = i % PL;
+          if constexpr (ph < 2) {   // S / dP: step j = (ks, which), half ph
+            return lds_read16((j & 1) ? oa0 : qa0, ph * 32 * ROW + (j >> 1) * 16);
+          } else {                  // dV / dK: step j = (t, db, which)
+            constexpr int t = 2 * (ph - 2) + j / (2 * DB), db = (j >> 1) % DB;
+            return lds_read16((j & 1) ? qt0 : ob0, db * 32 * TROW + t * 16);
+          }
+        },
+        [&](auto ic, bf16x8 a) {
+          constexpr int i = decltype(ic)::value, ph = i / PL, j = i % PL;
+          if constexpr (ph < 2) {
+            if constexpr (j & 1) dp[ph] = mfma32(a, vf[j >> 1], dp[ph]);
+            else s[ph] = mfma32(a, kf[j >> 1], s[ph]);
+          } else {
+            constexpr int t = 2 * (ph - 2) + j / (2 * DB), db = (j >> 1) % DB;
+            if constexpr (j & 1) dk[db] = mfma32(a, da[t], dk[db]);
             else dv[db] = mfma32(a, pa[t], dv[db]);
-          });
-    }
-    if (it + 1 < niter) {
-      ld.store(sm, buf ^ 1, tid);
-      if (it + 2 < niter) {
-        const int nx = it + 2;
-        ld.load(p, b, gkv * p.G + nx / per_head, (first + nx % per_head) * DKV_BQ, tid);
-      }
-    }
+          }
+        },
+        [&](auto ic) {
+          constexpr int i = decltype(ic)::value, ph = i / PL, j = i % PL;
+          if constexpr (ph == 0) {
+            constexpr int lo = j * 17 / PL, hi = (j + 1) * 17 / PL;
+            [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
+              (ld.store_piece(lo + Ws, sm, buf ^ 1, tid), ...);
+            }(std::make_integer_sequence<int, hi - lo>{});
+          } else if constexpr (ph == 3) {
+            constexpr int lo = j * 9 / PL, hi = (j + 1) * 9 / PL;
+            [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
+              (ld.load_piece(lo + Ws, p, b, h_nx, q0_nx, tid), ...);
+            }(std::make_integer_sequence<int, hi - lo>{});
+          } else {
+            constexpr int lo = j * 16 / PL, hi = (j + 1) * 16 / PL;
+            [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
+              (softmax_sub(std::integral_constant<int, ph - 1>{}, std::integral_constant<int, lo + Ws>{}), ...);
+            }(std::make_integer_sequence<int, hi - lo>{});
+          }
+        });
     __syncthreads();
   }
 
@@ -371,7 +430,7 @@ void bwd_dq_kernel(Params p) {
   constexpr int BR = NW * 32;
   constexpr int KS = D / 16, DB = D / 32;
   constexpr int ROW = DqSmem<D>::ROW, TROW = DqSmem<D>::TROW;
-  __shared__ DqSmem<D> sm;
+  __shared__ __attribute__((aligned(16))) DqSmem<D> sm;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;

@@ -113,7 +113,7 @@ void fwd_mfma_kernel(Params p) {
   constexpr int BR = NW * QB * 32;
   constexpr int KS = D / 16;   // k-steps of the QK^T product
   constexpr int DB = D / 32;   // 32-column blocks of O
-  __shared__ Smem<D> sm;
+  __shared__ __attribute__((aligned(16))) Smem<D> sm;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;

@@ -8,6 +8,9 @@
 // any consistent assignment of k to (g, element) is valid.
 #pragma once
 
+#include <type_traits>
+#include <utility>
+
 #include "common.h"
 
 namespace miattn {
@@ -76,6 +79,66 @@ __device__ __forceinline__ void pipelined_products(RD rd, MM mm) {
     __builtin_amdgcn_sched_group_barrier(0x008, MPS, 0); // MFMA
     if (i + R < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
+}
+
+// The same pipeline split in two, so that other work can sit between the
+// issue and the scheduling pattern: sched_group_barrier groups are filled
+// from instructions that precede them in the block. issue_products() emits
+// the reads and MFMAs; products_pattern<N, R, V>() then pins R reads and
+// N x {MPS MFMAs, 1 read, V VALU}, pulling independent vector work written
+// between the two calls (same basic block: no branches) in between the
+// matrix-core products.
+template <int N, int R, class RD, class MM>
+__device__ __forceinline__ void issue_products(RD rd, MM mm) {
+  bf16x8 ring[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) ring[i] = rd(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const bf16x8 a = ring[i % R];
+    if (i + R < N) ring[i % R] = rd(i + R);
+    mm(i, a);
+  }
+}
+
+template <int N, int R, int V, int MPS = 1>
+__device__ __forceinline__ void products_pattern() {
+  __builtin_amdgcn_sched_group_barrier(0x100, R, 0);     // DS reads
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, MPS, 0); // MFMA
+    if (i + R < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (V > 0) __builtin_amdgcn_sched_group_barrier(0x002, V, 0);   // VALU
+  }
+}
+
+// A chain of N matrix-core products executed in lock step with other work:
+// step i issues the LDS read for step i + R, the MFMA(s) of step i and the
+// work ex(i), and nothing moves across step boundaries (sched_barrier). Work
+// that does not depend on the products in flight (softmax of an earlier
+// block, tile stores and loads) thereby runs on the vector units while the
+// matrix cores are busy, also with a single wave per SIMD. The steps are
+// expanded at compile time: rd, mm and ex receive std::integral_constant
+// step indices, so every per-step decision is resolved by `if constexpr`.
+template <int I, int N, int R, class RD, class MM, class EX>
+__device__ __forceinline__ void lockstep_step(bf16x8 (&ring)[R], RD& rd, MM& mm, EX& ex) {
+  if constexpr (I < N) {
+    const bf16x8 a = ring[I % R];
+    if constexpr (I + R < N) ring[I % R] = rd(std::integral_constant<int, I + R>{});
+    mm(std::integral_constant<int, I>{}, a);
+    ex(std::integral_constant<int, I>{});
+    __builtin_amdgcn_sched_barrier(0);
+    lockstep_step<I + 1, N, R>(ring, rd, mm, ex);
+  }
+}
+
+template <int N, int R, class RD, class MM, class EX>
+__device__ __forceinline__ void lockstep_products(RD rd, MM mm, EX ex) {
+  bf16x8 ring[R];
+  [&]<int... Is>(std::integer_sequence<int, Is...>) {
+    ((ring[Is] = rd(std::integral_constant<int, Is>{})), ...);
+  }(std::make_integer_sequence<int, R>{});
+  lockstep_step<0, N, R>(ring, rd, mm, ex);
 }
 
 // Workgroup x index -> head index, so that with H % 8 == 0 all heads that
