@@ -137,7 +137,8 @@ void bwd_dkdv_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) DkdvSmem<D> sm;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+  const int lane = tid & 63;
   const int g = lane >> 5, n = lane & 31;
   const int gkv = blockIdx.x;          // all tiles of one K/V head share an XCD
   const int kt = blockIdx.y;           // tile 0 has the most causal work: dispatched first
@@ -227,83 +228,85 @@ void bwd_dkdv_kernel(Params p) {
     //   phase 3: dV^T, dK^T over half 1   + global loads of the tile after next
     // Each phase's extra work (17 store pieces, 16 softmax sub-steps, 9 load
     // pieces) is spread evenly over its PL steps.
-    constexpr int PL = D / 8;
-    f32x16 s[2], dp[2];
-    s[0] = f32x16{}; dp[0] = f32x16{}; s[1] = f32x16{}; dp[1] = f32x16{};
-    bf16x8 pa[4], da[4];
-    float pr[16];
-    f32x4 lq[4], dq4[4];   // LSE and D of the 16 query rows of the half being softmaxed
+    // One body for every tile: a second copy specialised for tiles that need
+    // no causal mask doubles the code the register allocator must fit into
+    // one register budget, and it then spills. The mask test is a compare and
+    // a select per element against a per-lane threshold (never true on tiles
+    // below the diagonal).
+    const int mthr = need_mask ? kpos - (p.q_start + q0) : -0x40000000;
+    {
+      constexpr int PL = D / 8;
+      f32x16 s[2], dp[2];
+      s[0] = f32x16{}; dp[0] = f32x16{}; s[1] = f32x16{}; dp[1] = f32x16{};
+      bf16x8 pa[4], da[4];
+      f32x4 lq[2], dq4[2];   // LSE and D of the 8 query rows being softmaxed
 
-    // softmax sub-step w (0..15) of half qb: lane (g, key n), register r <->
-    // query q0 + 32 qb + sigma_row(g, r); sub-step w covers elements 2k, 2k+1
-    // (k = (w % 8) / 2) of register group h2 = w / 8; even sub-steps form P,
-    // odd ones dS.
-    auto softmax_sub = [&](auto qbc, auto wc) {
-      constexpr int qb = decltype(qbc)::value, w = decltype(wc)::value;
-      constexpr int h2 = w >> 3, k = (w & 7) >> 1;
-      const int qi0 = qb * 32 + h2 * 16 + g * 8;    // 8 consecutive query rows
-      if constexpr ((w & 7) == 0) {
-        lq[2 * h2] = *(const f32x4*)(lse2 + qi0);
-        lq[2 * h2 + 1] = *(const f32x4*)(lse2 + qi0 + 4);
-        dq4[2 * h2] = *(const f32x4*)(dsm + qi0);
-        dq4[2 * h2 + 1] = *(const f32x4*)(dsm + qi0 + 4);
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int e = 2 * k + u;
-        const int r = h2 * 8 + e;
-        if constexpr ((w & 1) == 0) {
-          const float lv = lq[2 * h2 + (e >> 2)][e & 3];
-          const float x = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, -lv));
-          pr[r] = (need_mask && kpos > p.q_start + q0 + qi0 + e) ? 0.f : x;
-          pa[qb * 2 + h2][e] = (bf16)pr[r];
-        } else {
-          const float dv_ = dq4[2 * h2 + (e >> 2)][e & 3];
-          da[qb * 2 + h2][e] = (bf16)(pr[r] * (dp[qb][r] - dv_));
+      // softmax sub-step w (0..7) of half qb: lane (g, key n), register r <->
+      // query q0 + 32 qb + sigma_row(g, r); sub-step w forms P and dS for
+      // elements 2k, 2k+1 (k = w % 4) of register group h2 = w / 4, whose 8
+      // query rows' LSE and D are read at the group's first sub-step.
+      auto softmax_sub = [&](auto qbc, auto wc) {
+        constexpr int qb = decltype(qbc)::value, w = decltype(wc)::value;
+        constexpr int h2 = w >> 2, k = w & 3;
+        const int qi0 = qb * 32 + h2 * 16 + g * 8;    // 8 consecutive query rows
+        if constexpr (k == 0) {
+          lq[0] = *(const f32x4*)(lse2 + qi0);
+          lq[1] = *(const f32x4*)(lse2 + qi0 + 4);
+          dq4[0] = *(const f32x4*)(dsm + qi0);
+          dq4[1] = *(const f32x4*)(dsm + qi0 + 4);
         }
-      }
-    };
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int e = 2 * k + u;
+          const int r = h2 * 8 + e;
+          const float x = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, -lq[e >> 2][e & 3]));
+          const float pv = (qi0 + e < mthr) ? 0.f : x;
+          pa[qb * 2 + h2][e] = (bf16)pv;
+          da[qb * 2 + h2][e] = (bf16)(pv * (dp[qb][r] - dq4[e >> 2][e & 3]));
+        }
+      };
 
-    lockstep_products<4 * PL, 4>(
-        [&](auto ic) {
-          constexpr int i = decltype(ic)::value, ph = i / PL, j = i % PL;
-          if constexpr (ph < 2) {   // S / dP: step j = (ks, which), half ph
-            return lds_read16((j & 1) ? oa0 : qa0, ph * 32 * ROW + (j >> 1) * 16);
-          } else {                  // dV / dK: step j = (t, db, which)
-            constexpr int t = 2 * (ph - 2) + j / (2 * DB), db = (j >> 1) % DB;
-            return lds_read16((j & 1) ? qt0 : ob0, db * 32 * TROW + t * 16);
-          }
-        },
-        [&](auto ic, bf16x8 a) {
-          constexpr int i = decltype(ic)::value, ph = i / PL, j = i % PL;
-          if constexpr (ph < 2) {
-            if constexpr (j & 1) dp[ph] = mfma32(a, vf[j >> 1], dp[ph]);
-            else s[ph] = mfma32(a, kf[j >> 1], s[ph]);
-          } else {
-            constexpr int t = 2 * (ph - 2) + j / (2 * DB), db = (j >> 1) % DB;
-            if constexpr (j & 1) dk[db] = mfma32(a, da[t], dk[db]);
-            else dv[db] = mfma32(a, pa[t], dv[db]);
-          }
-        },
-        [&](auto ic) {
-          constexpr int i = decltype(ic)::value, ph = i / PL, j = i % PL;
-          if constexpr (ph == 0) {
-            constexpr int lo = j * 17 / PL, hi = (j + 1) * 17 / PL;
-            [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
-              (ld.store_piece(lo + Ws, sm, buf ^ 1, tid), ...);
-            }(std::make_integer_sequence<int, hi - lo>{});
-          } else if constexpr (ph == 3) {
-            constexpr int lo = j * 9 / PL, hi = (j + 1) * 9 / PL;
-            [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
-              (ld.load_piece(lo + Ws, p, b, h_nx, q0_nx, tid), ...);
-            }(std::make_integer_sequence<int, hi - lo>{});
-          } else {
-            constexpr int lo = j * 16 / PL, hi = (j + 1) * 16 / PL;
-            [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
-              (softmax_sub(std::integral_constant<int, ph - 1>{}, std::integral_constant<int, lo + Ws>{}), ...);
-            }(std::make_integer_sequence<int, hi - lo>{});
-          }
-        });
+      lockstep_products<4 * PL, 4>(
+          [&](auto ic) {
+            constexpr int i = decltype(ic)::value, ph = i / PL, j = i % PL;
+            if constexpr (ph < 2) {   // S / dP: step j = (ks, which), half ph
+              return lds_read16((j & 1) ? oa0 : qa0, ph * 32 * ROW + (j >> 1) * 16);
+            } else {                  // dV / dK: step j = (t, db, which)
+              constexpr int t = 2 * (ph - 2) + j / (2 * DB), db = (j >> 1) % DB;
+              return lds_read16((j & 1) ? qt0 : ob0, db * 32 * TROW + t * 16);
+            }
+          },
+          [&](auto ic, bf16x8 a) {
+            constexpr int i = decltype(ic)::value, ph = i / PL, j = i % PL;
+            if constexpr (ph < 2) {
+              if constexpr (j & 1) dp[ph] = mfma32(a, vf[j >> 1], dp[ph]);
+              else s[ph] = mfma32(a, kf[j >> 1], s[ph]);
+            } else {
+              constexpr int t = 2 * (ph - 2) + j / (2 * DB), db = (j >> 1) % DB;
+              if constexpr (j & 1) dk[db] = mfma32(a, da[t], dk[db]);
+              else dv[db] = mfma32(a, pa[t], dv[db]);
+            }
+          },
+          [&](auto ic) {
+            constexpr int i = decltype(ic)::value, ph = i / PL, j = i % PL;
+            if constexpr (ph == 0) {
+              constexpr int lo = j * 17 / PL, hi = (j + 1) * 17 / PL;
+              [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
+                (ld.store_piece(lo + Ws, sm, buf ^ 1, tid), ...);
+              }(std::make_integer_sequence<int, hi - lo>{});
+            } else if constexpr (ph == 3) {
+              constexpr int lo = j * 9 / PL, hi = (j + 1) * 9 / PL;
+              [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
+                (ld.load_piece(lo + Ws, p, b, h_nx, q0_nx, tid), ...);
+              }(std::make_integer_sequence<int, hi - lo>{});
+            } else {
+              constexpr int lo = j * 8 / PL, hi = (j + 1) * 8 / PL;
+              [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
+                (softmax_sub(std::integral_constant<int, ph - 1>{}, std::integral_constant<int, lo + Ws>{}), ...);
+              }(std::make_integer_sequence<int, hi - lo>{});
+            }
+          });
+    }
     __syncthreads();
   }
 
@@ -433,7 +436,8 @@ void bwd_dq_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) DqSmem<D> sm;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+  const int lane = tid & 63;
   const int g = lane >> 5, n = lane & 31;
   const int ntq = gridDim.y;
   const int qt = CAUSAL ? (ntq - 1 - (int)blockIdx.y) : (int)blockIdx.y;

@@ -116,7 +116,8 @@ void fwd_mfma_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) Smem<D> sm;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+  const int lane = tid & 63;
   const int g = lane >> 5, n = lane & 31;
 
   // ---- workgroup -> (b, h, query tile), heaviest causal tiles first
