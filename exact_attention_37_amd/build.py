@@ -26,6 +26,12 @@ FLAGS = ["-O3", "-fPIC", "-std=c++20", "--offload-arch=" + ARCH,
          "-I" + os.path.join(ROOT, "include"), "-Wno-unused-result"]
 
 
+# Per-source extra flags. The backward kernels keep their softmax inputs in
+# VGPRs when MFMA results are allocated in VGPR form (otherwise every tile's
+# S and dP are copied out of AGPRs before the vector work).
+EXTRA = {"bwd_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -43,7 +49,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        cmd = [HIPCC] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC] + FLAGS + EXTRA.get(src, []) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
         _run(cmd, verbose)
         return obj
 

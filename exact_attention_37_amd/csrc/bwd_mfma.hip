@@ -16,12 +16,13 @@
 // cost as much memory traffic as the whole computation takes on MI355X.
 //  * bwd_dkdv: one workgroup per 128 keys of one (b, K/V head); each of its 4
 //    waves holds 32 keys' K and V as matrix-core operands and their dK, dV
-//    accumulators in registers, and streams 64-row tiles of Q, dO (row-major
-//    and transposed copies in LDS), LSE and D over every query head of the
-//    group. Products: S = Q K^T, dP = dO V^T (query rows loaded in sigma32
-//    order, so each lane's accumulator holds 8 consecutive queries of one
-//    key = the B operand of the next products), dV^T += dO^T P and
-//    dK^T += Q^T dS (accumulators hold 16 columns of one key per lane).
+//    accumulators in registers, and streams 64-row tiles of Q and dO
+//    (loaded straight from global memory into LDS), LSE and D over every
+//    query head of the group. Products: S = Q K^T, dP = dO V^T (query rows
+//    read in sigma32 order, so each lane's accumulator holds 8 consecutive
+//    queries of one key = the B operand of the next products), then
+//    dV^T += dO^T P and dK^T += Q^T dS with dO^T / Q^T read by transposing
+//    LDS reads (accumulators hold 16 columns of one key per lane).
 //  * bwd_dq: one workgroup per query tile of one (b, h), the forward's
 //    structure: S^T = K Q^T and dP^T = V dO^T from row-major K and V tiles,
 //    then dQ^T += K^T dS^T from a transposed K tile.
@@ -42,98 +43,33 @@ constexpr int DKV_KW = 32;           // keys per wave
 constexpr int DKV_BK = DKV_NW * DKV_KW;
 constexpr int DKV_BQ = 64;           // query rows per streamed tile
 
+// LDS tile of 64 query rows (Q or dO), row-major. Rows are padded to D + 32
+// elements and the 16-byte chunk index is XORed with (row / 4) % 4: then the
+// sigma32-ordered ds_read_b128 row reads of S = Q K^T, dP = dO V^T and the
+// 4-row transposing reads of dV^T = dO^T P, dK^T = Q^T dS are both free of
+// bank conflicts, and the tile is written by direct global -> LDS loads.
 template <int D>
 struct DkdvSmem {
-  static constexpr int ROW = D + PAD;         // [q][d]
-  static constexpr int TROW = DKV_BQ + PAD;   // [d][q]
-  bf16 q[2][DKV_BQ * ROW];
-  bf16 qt[2][D * TROW];
-  bf16 o[2][DKV_BQ * ROW];     // dO
-  bf16 ot[2][D * TROW];
-  float stat[2][4][DKV_BQ];    // [0]: LSE * log2(e) (+inf past the last row), [1]: D; [2..3] unused
+  static constexpr int ROW = D + 32;
+  static constexpr int TILE = DKV_BQ * ROW;    // elements per tile
+  bf16 q[2][TILE];
+  bf16 o[2][TILE];                             // dO
+  float stat[2][2][DKV_BQ];    // [0]: LSE * log2(e) (+inf past the last row), [1]: D
 };
 
-// One streamed tile: 64 query rows of Q and dO of one head, as blocks of
-// 4 rows x 8 columns (so each thread can also write the transposed copy).
 template <int D>
-struct QTileLoader {
-  static constexpr int NT = DKV_NW * 64;
-  static constexpr int NBLK = (DKV_BQ / 4) * (D / 8);
-  static_assert(NBLK <= NT, "one 4x8 block per thread");
-  bf16x8 qr[4], orr[4];
-  float st;        // LSE (tid % 256 in [0, 64)) or D ([64, 128)) of row q0 + tid % 64
-  bool st_valid;
-
-  // Everything here is branch-free so it can be interleaved with the
-  // products. Loads are unconditional, from clamped rows (a select between a
-  // pending load and a constant would force a wait for it right away). Rows
-  // past Nq hold finite copies of row Nq-1; their LSE is replaced by +inf when
-  // stored, so their P and dS are exactly 0. With fewer blocks than threads,
-  // two threads load (and later write) the same block.
-  __device__ __forceinline__ const bf16* qptr(const Params& p, int b, int h) const {
-    return (const bf16*)p.q + ((long long)b * p.N + p.q_start) * ((long long)p.H * D) + (long long)h * D;
-  }
-  __device__ __forceinline__ const bf16* optr(const Params& p, int b, int h) const {
-    return (const bf16*)p.dout + ((long long)b * p.N + p.q_start) * ((long long)p.H * D) + (long long)h * D;
-  }
-  // piece 0..3: Q row r = piece; 4..7: dO row r = piece - 4; 8: LSE or D
-  __device__ __forceinline__ void load_piece(int piece, const Params& p, int b, int h, int q0, int tid) {
-    const long long qrs = (long long)p.H * D;
-    const int blk = tid % NBLK;
-    const int rq = blk % (DKV_BQ / 4), oc = blk / (DKV_BQ / 4);
-    if (piece < 8) {
-      const int r = piece & 3;
-      const int row = min(q0 + rq * 4 + r, p.Nq - 1);
-      const bf16* base = piece < 4 ? qptr(p, b, h) : optr(p, b, h);
-      const bf16x8 x = *(const bf16x8*)(base + row * qrs + oc * 8);
-      if (piece < 4) qr[r] = x; else orr[r] = x;
-    } else {
-      const int row = q0 + (tid & 63);
-      st_valid = row < p.Nq;
-      const long long si = ((long long)b * p.H + h) * p.N + p.q_start + min(row, p.Nq - 1);
-      st = ((tid & 64) ? p.dsum : p.lse)[si];
-    }
-  }
-  __device__ __forceinline__ void load(const Params& p, int b, int h, int q0, int tid) {
-#pragma unroll
-    for (int piece = 0; piece < 9; ++piece) load_piece(piece, p, b, h, q0, tid);
-  }
-  // piece 0..3: Q row-major row r; 4..7: dO row-major; 8..11: Q transposed
-  // (columns 2k, 2k+1 of the block); 12..15: dO transposed; 16: LSE / D
-  __device__ __forceinline__ void store_piece(int piece, DkdvSmem<D>& sm, int buf, int tid) const {
-    constexpr int ROW = DkdvSmem<D>::ROW, TROW = DkdvSmem<D>::TROW;
-    const int blk = tid % NBLK;
-    const int rq = blk % (DKV_BQ / 4), oc = blk / (DKV_BQ / 4);
-    if (piece < 8) {
-      const int r = piece & 3;
-      bf16* dst = (piece < 4 ? sm.q[buf] : sm.o[buf]) + (rq * 4 + r) * ROW + oc * 8;
-      *(bf16x8*)dst = piece < 4 ? qr[r] : orr[r];
-    } else if (piece < 16) {
-      const bf16x8 (&x)[4] = piece < 12 ? qr : orr;
-      bf16* dst = piece < 12 ? sm.qt[buf] : sm.ot[buf];
-      const int e0 = 2 * (piece & 3);
-#pragma unroll
-      for (int e = e0; e < e0 + 2; ++e) {
-        const uint2 w = {pack2(x[0][e], x[1][e]), pack2(x[2][e], x[3][e])};
-        *(uint2*)(dst + (oc * 8 + e) * TROW + rq * 4) = w;
-      }
-    } else {
-      const int slot = (tid >> 6) & 3;     // 0: LSE, 1: D, 2-3: unused
-      const float v = slot == 0 ? (st_valid ? st * kLog2e : INFINITY) : (st_valid ? st : 0.f);
-      sm.stat[buf][slot][tid & 63] = v;
-    }
-  }
-  __device__ __forceinline__ void store(DkdvSmem<D>& sm, int buf, int tid) const {
-#pragma unroll
-    for (int piece = 0; piece < 17; ++piece) store_piece(piece, sm, buf, tid);
-  }
-};
+__device__ __forceinline__ int dkdv_swz(int row, int chunk) {
+  return row * DkdvSmem<D>::ROW + ((chunk ^ ((row >> 2) & 3)) << 3);
+}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(DKV_NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(Params p) {
   constexpr int KS = D / 16, DB = D / 32;
-  constexpr int ROW = DkdvSmem<D>::ROW, TROW = DkdvSmem<D>::TROW;
+  constexpr int ROW = DkdvSmem<D>::ROW, TILE = DkdvSmem<D>::TILE;
+  constexpr int TILE_KB = TILE * 2 / 1024;          // 1 KB direct loads per tile
+  static_assert(TILE_KB % DKV_NW == 0, "tile loads split evenly over the waves");
+  constexpr int NL = TILE_KB / DKV_NW;             // per wave, per tensor
   __shared__ __attribute__((aligned(16))) DkdvSmem<D> sm;
 
   const int tid = threadIdx.x;
@@ -146,9 +82,11 @@ void bwd_dkdv_kernel(Params p) {
   const int k0 = kt * DKV_BK;
   const int kw0 = k0 + wave * DKV_KW;
 
-  const long long krs = (long long)p.Hkv * D;
+  const long long krs = (long long)p.Hkv * D, qrs = (long long)p.H * D;
   const bf16* K = (const bf16*)p.k + ((long long)b * p.N + p.k_start) * krs + (long long)gkv * D;
   const bf16* V = (const bf16*)p.v + ((long long)b * p.N + p.k_start) * krs + (long long)gkv * D;
+  const bf16* Qb = (const bf16*)p.q + ((long long)b * p.N + p.q_start) * qrs;
+  const bf16* Ob = (const bf16*)p.dout + ((long long)b * p.N + p.q_start) * qrs;
 
   float c = fabsf(p.scale) * kLog2e;
   float ksign = p.scale < 0.f ? -1.f : 1.f;
@@ -184,21 +122,74 @@ void bwd_dkdv_kernel(Params p) {
   const int wk_first = p.k_start + kw0;
 
   // query tile of iteration `it`: (head, first row); iterations past the end
-  // repeat the last tile so that loads and stores need no branch
+  // repeat the last tile so that loads need no branch
   auto tile_of = [&](int it, int& h, int& q0) {
     it = min(it, niter - 1);
     h = gkv * p.G + it / per_head;
     q0 = (first + it % per_head) * DKV_BQ;
   };
 
-  QTileLoader<D> ld;
+  // Direct loads: this wave's i-th 1 KB piece of a tile covers LDS bytes
+  // [(wave*NL + i) KB, +1 KB); lane l fills 16 bytes at offset 16 l: tile row
+  // lrow[i], logical chunk lch[i] (padding bytes are filled from chunk 0).
+  int lrow[NL], lcol[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int off = (wave * NL + i) * 1024 + 16 * lane;      // bytes into the tile
+    const int row = off / (ROW * 2), pch = (off % (ROW * 2)) / 16;
+    lrow[i] = row;
+    lcol[i] = pch < D / 8 ? ((pch ^ ((row >> 2) & 3)) << 3) : 0;
+  }
+  auto load_piece = [&](int piece, int buf, int h, int q0) {   // piece < 2 NL: Q then dO
+    const int i = piece % NL;
+    const bool is_o = piece >= NL;
+    const int row = min(q0 + lrow[i], p.Nq - 1);
+    const bf16* src = (is_o ? Ob : Qb) + row * qrs + (long long)h * D + lcol[i];
+    global_load_lds16(src, (is_o ? sm.o[buf] : sm.q[buf]) + (wave * NL + i) * 512);
+  };
+  float st;          // LSE (tid < 64) or D (64 <= tid < 128) of row q0 + tid % 64
+  bool st_valid;
+  auto stat_load = [&](int h, int q0) {
+    const int row = q0 + (tid & 63);
+    st_valid = row < p.Nq;
+    const long long si = ((long long)b * p.H + h) * p.N + p.q_start + min(row, p.Nq - 1);
+    st = ((tid & 64) ? p.dsum : p.lse)[si];
+  };
+  auto stat_store = [&](int buf) {
+    if (tid < 128) {
+      const float v = (tid < 64) ? (st_valid ? st * kLog2e : INFINITY) : (st_valid ? st : 0.f);
+      sm.stat[buf][tid >> 6][tid & 63] = v;
+    }
+  };
+
+  // per-lane LDS read bases (elements). S/dP A operands: row sigma32(n) (+32 qb),
+  // logical chunk 2 ks + g = 4 (ks/2) + 2 (ks%2) + g -> base for ks parity e.
+  const int srow = sigma32(n), sf = (srow >> 2) & 3;
+  int rd_s[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) rd_s[e] = srow * ROW + (((2 * e + g) ^ sf) << 3);
+  // transposing reads for dO^T / Q^T (k-step t, column block db): lane j of
+  // 16-lane group G4 = (g, hf) addresses row 16t + 8g + 4rd + j/4,
+  // columns 32db + 16hf + 4(j%4).
+  int rd_t[2];
+  {
+    const int G4 = lane >> 4, j = lane & 15, hf = G4 & 1;
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int row = 8 * g + 4 * rd + (j >> 2);
+      const int chunk = (2 * hf + ((j & 3) >> 1)) ^ ((2 * g + rd) & 3);
+      rd_t[rd] = row * ROW + (chunk << 3) + 4 * (j & 1);
+    }
+  }
+
   if (niter > 0) {
     int h, q0;
     tile_of(0, h, q0);
-    ld.load(p, b, h, q0, tid);
-    ld.store(sm, 0, tid);
-    tile_of(1, h, q0);
-    ld.load(p, b, h, q0, tid);
+#pragma unroll
+    for (int piece = 0; piece < 2 * NL; ++piece) load_piece(piece, 0, h, q0);
+    stat_load(h, q0);
+    wait_global_loads();
+    stat_store(0);
   }
   __syncthreads();
 
@@ -207,12 +198,10 @@ void bwd_dkdv_kernel(Params p) {
     int h_cur, q0;
     tile_of(it, h_cur, q0);
     int h_nx, q0_nx;
-    tile_of(it + 2, h_nx, q0_nx);
+    tile_of(it + 1, h_nx, q0_nx);
     const bool need_mask = CAUSAL && (wk_first + DKV_KW - 1 > p.q_start + q0);
-    const bf16* qa0 = sm.q[buf] + sigma32(n) * ROW + g * 8;
-    const bf16* oa0 = sm.o[buf] + sigma32(n) * ROW + g * 8;
-    const bf16* ob0 = sm.ot[buf] + n * TROW + g * 8;
-    const bf16* qt0 = sm.qt[buf] + n * TROW + g * 8;
+    const bf16* qt = sm.q[buf];
+    const bf16* ot = sm.o[buf];
     const float* lse2 = sm.stat[buf][0];
     const float* dsm = sm.stat[buf][1];
 
@@ -222,91 +211,88 @@ void bwd_dkdv_kernel(Params p) {
     //
     // 4 phases of PL = D/8 lock steps, one MFMA each; the tile's 64 queries
     // are two halves qb:
-    //   phase 0: S, dP of half 0          + store of the next tile to LDS
+    //   phase 0: S, dP of half 0          + direct loads of the next tile
     //   phase 1: S, dP of half 1          + softmax of half 0
     //   phase 2: dV^T, dK^T over half 0   + softmax of half 1
-    //   phase 3: dV^T, dK^T over half 1   + global loads of the tile after next
-    // Each phase's extra work (17 store pieces, 16 softmax sub-steps, 9 load
-    // pieces) is spread evenly over its PL steps.
-    // One body for every tile: a second copy specialised for tiles that need
-    // no causal mask doubles the code the register allocator must fit into
-    // one register budget, and it then spills. The mask test is a compare and
-    // a select per element against a per-lane threshold (never true on tiles
-    // below the diagonal).
+    //   phase 3: dV^T, dK^T over half 1   + the next tile's LSE / D to LDS
+    // One body serves every tile: the mask test is a compare and a select per
+    // element against a per-lane threshold (never true below the diagonal).
+    constexpr int PL = D / 8;
     const int mthr = need_mask ? kpos - (p.q_start + q0) : -0x40000000;
-    {
-      constexpr int PL = D / 8;
-      f32x16 s[2], dp[2];
-      s[0] = f32x16{}; dp[0] = f32x16{}; s[1] = f32x16{}; dp[1] = f32x16{};
-      bf16x8 pa[4], da[4];
-      f32x4 lq[2], dq4[2];   // LSE and D of the 8 query rows being softmaxed
+    f32x16 s[2], dp[2];
+    s[0] = f32x16{}; dp[0] = f32x16{}; s[1] = f32x16{}; dp[1] = f32x16{};
+    bf16x8 pa[4], da[4];
+    f32x4 lq[2], dq4[2];   // LSE and D of the 8 query rows being softmaxed
 
-      // softmax sub-step w (0..7) of half qb: lane (g, key n), register r <->
-      // query q0 + 32 qb + sigma_row(g, r); sub-step w forms P and dS for
-      // elements 2k, 2k+1 (k = w % 4) of register group h2 = w / 4, whose 8
-      // query rows' LSE and D are read at the group's first sub-step.
-      auto softmax_sub = [&](auto qbc, auto wc) {
-        constexpr int qb = decltype(qbc)::value, w = decltype(wc)::value;
-        constexpr int h2 = w >> 2, k = w & 3;
-        const int qi0 = qb * 32 + h2 * 16 + g * 8;    // 8 consecutive query rows
-        if constexpr (k == 0) {
-          lq[0] = *(const f32x4*)(lse2 + qi0);
-          lq[1] = *(const f32x4*)(lse2 + qi0 + 4);
-          dq4[0] = *(const f32x4*)(dsm + qi0);
-          dq4[1] = *(const f32x4*)(dsm + qi0 + 4);
-        }
+    // softmax sub-step w (0..7) of half qb: lane (g, key n), register r <->
+    // query q0 + 32 qb + sigma_row(g, r); sub-step w forms P and dS for
+    // elements 2k, 2k+1 (k = w % 4) of register group h2 = w / 4, whose 8
+    // query rows' LSE and D are read at the group's first sub-step.
+    auto softmax_sub = [&](auto qbc, auto wc) {
+      constexpr int qb = decltype(qbc)::value, w = decltype(wc)::value;
+      constexpr int h2 = w >> 2, k = w & 3;
+      const int qi0 = qb * 32 + h2 * 16 + g * 8;    // 8 consecutive query rows
+      if constexpr (k == 0) {
+        lq[0] = *(const f32x4*)(lse2 + qi0);
+        lq[1] = *(const f32x4*)(lse2 + qi0 + 4);
+        dq4[0] = *(const f32x4*)(dsm + qi0);
+        dq4[1] = *(const f32x4*)(dsm + qi0 + 4);
+      }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int e = 2 * k + u;
-          const int r = h2 * 8 + e;
-          const float x = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, -lq[e >> 2][e & 3]));
-          const float pv = (qi0 + e < mthr) ? 0.f : x;
-          pa[qb * 2 + h2][e] = (bf16)pv;
-          da[qb * 2 + h2][e] = (bf16)(pv * (dp[qb][r] - dq4[e >> 2][e & 3]));
-        }
-      };
+      for (int u = 0; u < 2; ++u) {
+        const int e = 2 * k + u;
+        const int r = h2 * 8 + e;
+        const float x = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, -lq[e >> 2][e & 3]));
+        const float pv = (qi0 + e < mthr) ? 0.f : x;
+        pa[qb * 2 + h2][e] = (bf16)pv;
+        da[qb * 2 + h2][e] = (bf16)(pv * (dp[qb][r] - dq4[e >> 2][e & 3]));
+      }
+    };
 
-      lockstep_products<4 * PL, 4>(
-          [&](auto ic) {
-            constexpr int i = decltype(ic)::value, ph = i / PL, j = i % PL;
-            if constexpr (ph < 2) {   // S / dP: step j = (ks, which), half ph
-              return lds_read16((j & 1) ? oa0 : qa0, ph * 32 * ROW + (j >> 1) * 16);
-            } else {                  // dV / dK: step j = (t, db, which)
-              constexpr int t = 2 * (ph - 2) + j / (2 * DB), db = (j >> 1) % DB;
-              return lds_read16((j & 1) ? qt0 : ob0, db * 32 * TROW + t * 16);
-            }
-          },
-          [&](auto ic, bf16x8 a) {
-            constexpr int i = decltype(ic)::value, ph = i / PL, j = i % PL;
-            if constexpr (ph < 2) {
-              if constexpr (j & 1) dp[ph] = mfma32(a, vf[j >> 1], dp[ph]);
-              else s[ph] = mfma32(a, kf[j >> 1], s[ph]);
-            } else {
-              constexpr int t = 2 * (ph - 2) + j / (2 * DB), db = (j >> 1) % DB;
-              if constexpr (j & 1) dk[db] = mfma32(a, da[t], dk[db]);
-              else dv[db] = mfma32(a, pa[t], dv[db]);
-            }
-          },
-          [&](auto ic) {
-            constexpr int i = decltype(ic)::value, ph = i / PL, j = i % PL;
-            if constexpr (ph == 0) {
-              constexpr int lo = j * 17 / PL, hi = (j + 1) * 17 / PL;
-              [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
-                (ld.store_piece(lo + Ws, sm, buf ^ 1, tid), ...);
-              }(std::make_integer_sequence<int, hi - lo>{});
-            } else if constexpr (ph == 3) {
-              constexpr int lo = j * 9 / PL, hi = (j + 1) * 9 / PL;
-              [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
-                (ld.load_piece(lo + Ws, p, b, h_nx, q0_nx, tid), ...);
-              }(std::make_integer_sequence<int, hi - lo>{});
-            } else {
-              constexpr int lo = j * 8 / PL, hi = (j + 1) * 8 / PL;
-              [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
-                (softmax_sub(std::integral_constant<int, ph - 1>{}, std::integral_constant<int, lo + Ws>{}), ...);
-              }(std::make_integer_sequence<int, hi - lo>{});
-            }
-          });
-    }
+    lockstep_products<4 * PL, 4>(
+        [&](auto ic) {
+          constexpr int i = decltype(ic)::value, ph = i / PL, j = i % PL;
+          if constexpr (ph < 2) {   // S / dP: step j = (ks, which), half ph
+            constexpr int ks = j >> 1;
+            const bf16* t = (j & 1) ? ot : qt;
+            return lds_read16(t + rd_s[ks & 1], ph * 32 * ROW + (ks >> 1) * 32);
+          } else {                  // dV / dK: step j = (t, db, which), two transposing reads
+            constexpr int t = 2 * (ph - 2) + j / (2 * DB), db = (j >> 1) % DB;
+            const bf16* src = (j & 1) ? qt : ot;
+            const bf16x4 r0 = lds_read_tr4(src + rd_t[0] + 16 * t * ROW + 32 * db);
+            const bf16x4 r1 = lds_read_tr4(src + rd_t[1] + 16 * t * ROW + 32 * db);
+            return bf16x8{r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+          }
+        },
+        [&](auto ic, bf16x8 a) {
+          constexpr int i = decltype(ic)::value, ph = i / PL, j = i % PL;
+          if constexpr (ph < 2) {
+            if constexpr (j & 1) dp[ph] = mfma32(a, vf[j >> 1], dp[ph]);
+            else s[ph] = mfma32(a, kf[j >> 1], s[ph]);
+          } else {
+            constexpr int t = 2 * (ph - 2) + j / (2 * DB), db = (j >> 1) % DB;
+            if constexpr (j & 1) dk[db] = mfma32(a, da[t], dk[db]);
+            else dv[db] = mfma32(a, pa[t], dv[db]);
+          }
+        },
+        [&](auto ic) {
+          constexpr int i = decltype(ic)::value, ph = i / PL, j = i % PL;
+          if constexpr (ph == 0) {
+            constexpr int lo = j * (2 * NL) / PL, hi = (j + 1) * (2 * NL) / PL;
+            [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
+              (load_piece(lo + Ws, buf ^ 1, h_nx, q0_nx), ...);
+            }(std::make_integer_sequence<int, hi - lo>{});
+            if constexpr (j == PL - 1) stat_load(h_nx, q0_nx);
+          } else if constexpr (ph == 3) {
+            if constexpr (j == PL - 1) stat_store(buf ^ 1);
+          } else {
+            constexpr int lo = j * 8 / PL, hi = (j + 1) * 8 / PL;
+            [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
+              (softmax_sub(std::integral_constant<int, ph - 1>{}, std::integral_constant<int, lo + Ws>{}), ...);
+            }(std::make_integer_sequence<int, hi - lo>{});
+          }
+        });
+    wait_global_loads();
     __syncthreads();
   }
 

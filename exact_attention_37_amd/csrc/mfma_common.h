@@ -49,6 +49,24 @@ __device__ __forceinline__ void store_transposed4x8(bf16* dst, int row_len, int 
   }
 }
 
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// lane i receives in slot s element (i % 4) of the 8-byte chunk addressed by
+// lane 4s + i / 4 of its group. So if lane j of a group addresses row
+// r0 + j / 4, columns c0 + 4 (j % 4) .. +3 of a row-major tile, lane i gets
+// column c0 + i of rows r0 .. r0 + 3: a transposed operand fragment.
+__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+}
+
+// Direct global -> LDS load of 16 bytes per lane: the wave writes 1 KB of
+// LDS contiguously, lane l at lds_base + 16 l; lds_base must be the same in
+// every lane. Completion is tracked by vmcnt like any global load.
+__device__ __forceinline__ void global_load_lds16(const void* g, bf16* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
 // Waits for every outstanding global load of this wave. Used after the
 // loads of loop-invariant matrix operands: without it the compiler cannot
 // prove them complete across the loop back-edge and inserts vmcnt waits
