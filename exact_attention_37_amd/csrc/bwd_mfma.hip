@@ -25,7 +25,8 @@
 //    LDS reads (accumulators hold 16 columns of one key per lane).
 //  * bwd_dq: one workgroup per query tile of one (b, h), the forward's
 //    structure: S^T = K Q^T and dP^T = V dO^T from row-major K and V tiles,
-//    then dQ^T += K^T dS^T from a transposed K tile.
+//    then dQ^T += K^T dS^T with K^T read from the same K tile by
+//    transposing LDS reads.
 #include "common.h"
 #include "kernels.h"
 #include "mfma_common.h"
@@ -335,82 +336,16 @@ void bwd_dkdv_kernel(Params p) {
 
 constexpr int DQ_BC = 64;   // keys per tile
 
+// K and V tiles (64 keys), row-major in the padded, chunk-swizzled layout of
+// DkdvSmem: the sigma32-ordered row reads of S^T = K Q^T and dP^T = V dO^T
+// and the transposing reads of K^T for dQ^T = K^T dS^T are conflict-free,
+// and both tiles are written by direct global -> LDS loads.
 template <int D>
 struct DqSmem {
-  static constexpr int ROW = D + PAD;       // [key][d]
-  static constexpr int TROW = DQ_BC + PAD;  // [d][key]
-  bf16 k[2][DQ_BC * ROW];
-  bf16 v[2][DQ_BC * ROW];
-  bf16 kt[2][D * TROW];
-};
-
-// One K/V tile as blocks of 4 rows x 8 columns. With at least two blocks'
-// worth of threads, a thread loads either a K block or a V block; otherwise
-// each thread loads both for its blocks.
-template <int D, int NW>
-struct KTileLoader {
-  static constexpr int NT = NW * 64;
-  static constexpr int NBLK = (DQ_BC / 4) * (D / 8);
-  static constexpr bool SPLIT = NT >= 2 * NBLK;
-  static constexpr int PER = SPLIT ? 1 : (NBLK + NT - 1) / NT;
-  bf16x8 kr[PER][4], vr[SPLIT ? 1 : PER][4];
-
-  // Unconditional loads from clamped rows (see QTileLoader); rows past nk
-  // are masked to P = 0.
-  __device__ __forceinline__ void load(const bf16* K, const bf16* V, long long rs, int j0, int nk, int tid) {
-    if constexpr (SPLIT) {
-      const bool is_v = tid >= NBLK;
-      const int blk = min(is_v ? tid - NBLK : tid, NBLK - 1);
-      const int rk = blk % (DQ_BC / 4), oc = blk / (DQ_BC / 4);
-      const bf16* src = is_v ? V : K;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = min(j0 + rk * 4 + r, nk - 1);
-        kr[0][r] = *(const bf16x8*)(src + key * rs + oc * 8);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int blk = min(tid + i * NT, NBLK - 1);
-        const int rk = blk % (DQ_BC / 4), oc = blk / (DQ_BC / 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = min(j0 + rk * 4 + r, nk - 1);
-          kr[i][r] = *(const bf16x8*)(K + key * rs + oc * 8);
-          vr[i][r] = *(const bf16x8*)(V + key * rs + oc * 8);
-        }
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(DqSmem<D>& sm, int buf, int tid) const {
-    constexpr int ROW = DqSmem<D>::ROW, TROW = DqSmem<D>::TROW;
-    if constexpr (SPLIT) {
-      if (tid < 2 * NBLK) {
-        const bool is_v = tid >= NBLK;
-        const int blk = is_v ? tid - NBLK : tid;
-        const int rk = blk % (DQ_BC / 4), oc = blk / (DQ_BC / 4);
-        bf16* dst = is_v ? sm.v[buf] : sm.k[buf];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) *(bf16x8*)(dst + (rk * 4 + r) * ROW + oc * 8) = kr[0][r];
-        if (!is_v) store_transposed4x8(sm.kt[buf], TROW, oc * 8, rk * 4, kr[0]);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int blk = tid + i * NT;
-        if (blk < NBLK) {
-          const int rk = blk % (DQ_BC / 4), oc = blk / (DQ_BC / 4);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            *(bf16x8*)(sm.k[buf] + (rk * 4 + r) * ROW + oc * 8) = kr[i][r];
-            *(bf16x8*)(sm.v[buf] + (rk * 4 + r) * ROW + oc * 8) = vr[i][r];
-          }
-          store_transposed4x8(sm.kt[buf], TROW, oc * 8, rk * 4, kr[i]);
-        }
-      }
-    }
-  }
+  static constexpr int ROW = D + 32;
+  static constexpr int TILE = DQ_BC * ROW;
+  bf16 k[2][TILE];
+  bf16 v[2][TILE];
 };
 
 template <int D, bool CAUSAL, int NW>
@@ -418,7 +353,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 void bwd_dq_kernel(Params p) {
   constexpr int BR = NW * 32;
   constexpr int KS = D / 16, DB = D / 32;
-  constexpr int ROW = DqSmem<D>::ROW, TROW = DqSmem<D>::TROW;
+  constexpr int ROW = DqSmem<D>::ROW, TILE = DqSmem<D>::TILE;
+  constexpr int TILES_KB = 2 * TILE * 2 / 1024;     // K and V, in 1 KB direct loads
+  static_assert(TILES_KB % NW == 0, "tile loads split evenly over the waves");
+  constexpr int NL = TILES_KB / NW;                // per wave
+  constexpr int TILE_KB = TILES_KB / 2;
   __shared__ __attribute__((aligned(16))) DqSmem<D> sm;
 
   const int tid = threadIdx.x;
@@ -471,65 +410,133 @@ void bwd_dq_kernel(Params p) {
   }
   const int wq_first = p.q_start + wq0;
 
+  // Direct loads: 1 KB piece s = wave*NL + i of the two tiles (K: s < TILE_KB,
+  // then V) covers tile bytes [(s % TILE_KB) KB, +1 KB); lane l fills 16 bytes
+  // at 16 l: tile row lrow[i], logical chunk lcol[i] (padding from chunk 0).
+  int lrow[NL], lcol[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int off = ((wave * NL + i) % TILE_KB) * 1024 + 16 * lane;
+    const int r_ = off / (ROW * 2), pch = (off % (ROW * 2)) / 16;
+    lrow[i] = r_;
+    lcol[i] = pch < D / 8 ? ((pch ^ ((r_ >> 2) & 3)) << 3) : 0;
+  }
+  auto load_piece = [&](int i, int buf, int j0) {
+    const int sl = wave * NL + i;                  // wave-uniform
+    const bool is_v = sl >= TILE_KB;
+    const int key = min(j0 + lrow[i], p.Nk - 1);
+    const bf16* src = (is_v ? V : K) + key * krs + lcol[i];
+    global_load_lds16(src, (is_v ? sm.v[buf] : sm.k[buf]) + (sl % TILE_KB) * 512);
+  };
+
+  // per-lane LDS read bases (elements): K / V rows sigma32(n) (+32 kb), logical
+  // chunk 2 ks + g -> base for ks parity e; K^T transposing reads: lane j of
+  // 16-lane group (g, hf) addresses key row 16t + 8g + 4rd + j/4, columns
+  // 32db + 16hf + 4(j%4).
+  const int srow = sigma32(n), sf = (srow >> 2) & 3;
+  int rd_s[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) rd_s[e] = srow * ROW + (((2 * e + g) ^ sf) << 3);
+  int rd_t[2];
+  {
+    const int G4 = lane >> 4, j = lane & 15, hf = G4 & 1;
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int r_ = 8 * g + 4 * rd + (j >> 2);
+      const int chunk = (2 * hf + ((j & 3) >> 1)) ^ ((2 * g + rd) & 3);
+      rd_t[rd] = r_ * ROW + (chunk << 3) + 4 * (j & 1);
+    }
+  }
+
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
-  KTileLoader<D, NW> ld;
   if (nkt > 0) {
-    ld.load(K, V, krs, 0, p.Nk, tid);
-    ld.store(sm, 0, tid);
-    if (nkt > 1) ld.load(K, V, krs, DQ_BC, p.Nk, tid);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) load_piece(i, 0, 0);
+    wait_global_loads();
   }
   __syncthreads();
 
+  // Lock steps per key tile (PS = 2 KS products per key block, PD = 2 DB per 16 keys):
+  //   phase 0 (PS steps): S^T, dP^T of keys 0-31    + direct loads of the next tile
+  //   phase 1 (PS steps): S^T, dP^T of keys 32-63   + dS of keys 0-31
+  //   phase 2 (PD steps): dQ^T over keys 0-31       + dS of keys 32-63
+  //   phase 3 (PD steps): dQ^T over keys 32-63
+  constexpr int PS = 2 * KS, PD = 2 * DB;
   for (int j = 0; j < nkt; ++j) {
     const int buf = j & 1;
     const int kpos0 = p.k_start + j * DQ_BC;
-    {   // no per-wave skip (see bwd_dkdv); fully masked waves compute P = 0
-      // S^T = K Q^T, dP^T = V dO^T; step i = (ks, kb, which): 4 chains interleaved
-      f32x16 s[2], dp[2];
+    const int jn = min(j + 1, nkt - 1) * DQ_BC;      // next tile (the last tile repeats itself)
+    // masked iff key index inside the tile > thr (causal and the ragged end)
+    int thr = p.Nk - 1 - j * DQ_BC;
+    if (CAUSAL && kpos0 + DQ_BC - 1 > wq_first) thr = min(thr, qpos - kpos0);
+    const bf16* kt = sm.k[buf];
+    const bf16* vt = sm.v[buf];
+    f32x16 s[2], dp[2];
+    s[0] = f32x16{}; dp[0] = f32x16{}; s[1] = f32x16{}; dp[1] = f32x16{};
+    bf16x8 dsb[4];
+
+    // dS for elements 2w, 2w+1 (w = 0..7) of key block kb: lane (g, query n),
+    // register r <-> key 32 kb + sigma_row(g, r)
+    auto ds_sub = [&](auto kbc, auto wc) {
+      constexpr int kb = decltype(kbc)::value, w = decltype(wc)::value;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) { s[kb] = f32x16{}; dp[kb] = f32x16{}; }
-      const bf16* ka0 = sm.k[buf] + sigma32(n) * ROW + g * 8;
-      const bf16* va0 = sm.v[buf] + sigma32(n) * ROW + g * 8;
-      pipelined_products<4 * KS, 4>(
-          [&](int i) {
-            const int ks = i >> 2, kb = (i >> 1) & 1;
-            return lds_read16((i & 1) ? va0 : ka0, kb * 32 * ROW + ks * 16);
-          },
-          [&](int i, bf16x8 a) {
-            const int ks = i >> 2, kb = (i >> 1) & 1;
-            if (i & 1) dp[kb] = mfma32(a, of[ks], dp[kb]);
-            else s[kb] = mfma32(a, qf[ks], s[kb]);
-          });
-      const bool need_mask = (CAUSAL && kpos0 + DQ_BC - 1 > wq_first) || (j * DQ_BC + DQ_BC > p.Nk);
-      bf16x8 dsb[4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          bf16x8 x;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int kin = kb * 32 + half * 16 + g * 8 + e;
-            float pr = __builtin_amdgcn_exp2f(fmaf(s[kb][half * 8 + e], c, -lse2));
-            if (need_mask && ((j * DQ_BC + kin >= p.Nk) || (CAUSAL && kpos0 + kin > qpos))) pr = 0.f;
-            x[e] = (bf16)(pr * (dp[kb][half * 8 + e] - dsum));
-          }
-          dsb[kb * 2 + half] = x;
-        }
+      for (int u = 0; u < 2; ++u) {
+        const int r = 2 * w + u;
+        const int kin = kb * 32 + ((r < 8) ? (g * 8 + r) : (16 + g * 8 + r - 8));
+        const float x = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -lse2));
+        const float pv = kin > thr ? 0.f : x;
+        dsb[kb * 2 + (r >> 3)][r & 7] = (bf16)(pv * (dp[kb][r] - dsum));
       }
-      // dQ^T += K^T dS^T; step i = (t, db): DB chains interleaved
-      const bf16* kt0 = sm.kt[buf] + n * TROW + g * 8;
-      pipelined_products<4 * DB, 4>(
-          [&](int i) { return lds_read16(kt0, (i % DB) * 32 * TROW + (i / DB) * 16); },
-          [&](int i, bf16x8 a) { acc[i % DB] = mfma32(a, dsb[i / DB], acc[i % DB]); });
-    }
-    if (j + 1 < nkt) {
-      ld.store(sm, buf ^ 1, tid);
-      if (j + 2 < nkt) ld.load(K, V, krs, (j + 2) * DQ_BC, p.Nk, tid);
-    }
+    };
+
+    lockstep_products<2 * PS + 2 * PD, 4>(
+        [&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          if constexpr (i < 2 * PS) {            // S^T / dP^T: (kb, ks, which)
+            constexpr int kb = i / PS, jj = i % PS, ks = jj >> 1;
+            const bf16* t = (jj & 1) ? vt : kt;
+            return lds_read16(t + rd_s[ks & 1], kb * 32 * ROW + (ks >> 1) * 32);
+          } else {                                // dQ^T: (t, db) with t = key block of 16
+            constexpr int ii = i - 2 * PS, t = ii / DB, db = ii % DB;
+            const bf16x4 r0 = lds_read_tr4(kt + rd_t[0] + 16 * t * ROW + 32 * db);
+            const bf16x4 r1 = lds_read_tr4(kt + rd_t[1] + 16 * t * ROW + 32 * db);
+            return bf16x8{r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+          }
+        },
+        [&](auto ic, bf16x8 a) {
+          constexpr int i = decltype(ic)::value;
+          if constexpr (i < 2 * PS) {
+            constexpr int kb = i / PS, jj = i % PS, ks = jj >> 1;
+            if constexpr (jj & 1) dp[kb] = mfma32(a, of[ks], dp[kb]);
+            else s[kb] = mfma32(a, qf[ks], s[kb]);
+          } else {
+            constexpr int ii = i - 2 * PS, t = ii / DB, db = ii % DB;
+            acc[db] = mfma32(a, dsb[t], acc[db]);
+          }
+        },
+        [&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          if constexpr (i < PS) {                 // phase 0: next tile's direct loads
+            constexpr int lo = i * NL / PS, hi = (i + 1) * NL / PS;
+            [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
+              (load_piece(lo + Ws, buf ^ 1, jn), ...);
+            }(std::make_integer_sequence<int, hi - lo>{});
+          } else if constexpr (i < 2 * PS) {      // phase 1: dS of key block 0
+            constexpr int ii = i - PS, lo = ii * 8 / PS, hi = (ii + 1) * 8 / PS;
+            [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
+              (ds_sub(std::integral_constant<int, 0>{}, std::integral_constant<int, lo + Ws>{}), ...);
+            }(std::make_integer_sequence<int, hi - lo>{});
+          } else if constexpr (i < 2 * PS + PD) { // phase 2: dS of key block 1
+            constexpr int ii = i - 2 * PS, lo = ii * 8 / PD, hi = (ii + 1) * 8 / PD;
+            [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
+              (ds_sub(std::integral_constant<int, 1>{}, std::integral_constant<int, lo + Ws>{}), ...);
+            }(std::make_integer_sequence<int, hi - lo>{});
+          }
+        });
+    wait_global_loads();
     __syncthreads();
   }
 
