@@ -110,9 +110,14 @@ void bwd_dkdv_kernel(Params p) {
   }
   wait_global_loads();
 
+  // dK^T, dV^T accumulators, in AGPRs (mfma32_agpr)
   f32x16 dk[DB], dv[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) { dk[db] = f32x16{}; dv[db] = f32x16{}; }
+  for (int db = 0; db < DB; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+    agpr_settle(dk[db], dv[db]);
+  }
 
   const int nqt = (p.Nq + DKV_BQ - 1) / DKV_BQ;
   int first = 0;
@@ -132,21 +137,24 @@ void bwd_dkdv_kernel(Params p) {
 
   // Direct loads: this wave's i-th 1 KB piece of a tile covers LDS bytes
   // [(wave*NL + i) KB, +1 KB); lane l fills 16 bytes at offset 16 l: tile row
-  // lrow[i], logical chunk lch[i] (padding bytes are filled from chunk 0).
-  int lrow[NL], lcol[NL];
+  // r, logical chunk ch (padding bytes are filled from chunk 0), read from
+  // byte loff[i] = 2 (r * row stride + 8 ch) past the tile's first row. Rows
+  // past the last query read as zeros (buffer range check).
+  uint32_t loff[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int off = (wave * NL + i) * 1024 + 16 * lane;      // bytes into the tile
     const int row = off / (ROW * 2), pch = (off % (ROW * 2)) / 16;
-    lrow[i] = row;
-    lcol[i] = pch < D / 8 ? ((pch ^ ((row >> 2) & 3)) << 3) : 0;
+    const int col = pch < D / 8 ? ((pch ^ ((row >> 2) & 3)) << 3) : 0;
+    loff[i] = (uint32_t)(row * qrs + col) * 2u;
   }
+  const uint32_t qbytes = (uint32_t)(p.Nq * qrs * 2);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qb, qbytes), ro = make_rsrc(Ob, qbytes);
   auto load_piece = [&](int piece, int buf, int h, int q0) {   // piece < 2 NL: Q then dO
     const int i = piece % NL;
     const bool is_o = piece >= NL;
-    const int row = min(q0 + lrow[i], p.Nq - 1);
-    const bf16* src = (is_o ? Ob : Qb) + row * qrs + (long long)h * D + lcol[i];
-    global_load_lds16(src, (is_o ? sm.o[buf] : sm.q[buf]) + (wave * NL + i) * 512);
+    const uint32_t soff = (uint32_t)(q0 * qrs + h * D) * 2u;
+    buffer_load_lds16(is_o ? ro : rq, loff[i], soff, (is_o ? sm.o[buf] : sm.q[buf]) + (wave * NL + i) * 512);
   };
   float st;          // LSE (tid < 64) or D (64 <= tid < 128) of row q0 + tid % 64
   bool st_valid;
@@ -233,6 +241,7 @@ void bwd_dkdv_kernel(Params p) {
       constexpr int qb = decltype(qbc)::value, w = decltype(wc)::value;
       constexpr int h2 = w >> 2, k = w & 3;
       const int qi0 = qb * 32 + h2 * 16 + g * 8;    // 8 consecutive query rows
+      const int tq = mthr - qi0;                     // element e masked iff e < tq
       if constexpr (k == 0) {
         lq[0] = *(const f32x4*)(lse2 + qi0);
         lq[1] = *(const f32x4*)(lse2 + qi0 + 4);
@@ -244,7 +253,7 @@ void bwd_dkdv_kernel(Params p) {
         const int e = 2 * k + u;
         const int r = h2 * 8 + e;
         const float x = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, -lq[e >> 2][e & 3]));
-        const float pv = (qi0 + e < mthr) ? 0.f : x;
+        const float pv = (e < tq) ? 0.f : x;
         pa[qb * 2 + h2][e] = (bf16)pv;
         da[qb * 2 + h2][e] = (bf16)(pv * (dp[qb][r] - dq4[e >> 2][e & 3]));
       }
@@ -272,8 +281,8 @@ void bwd_dkdv_kernel(Params p) {
             else s[ph] = mfma32(a, kf[j >> 1], s[ph]);
           } else {
             constexpr int t = 2 * (ph - 2) + j / (2 * DB), db = (j >> 1) % DB;
-            if constexpr (j & 1) dk[db] = mfma32(a, da[t], dk[db]);
-            else dv[db] = mfma32(a, pa[t], dv[db]);
+            if constexpr (j & 1) mfma32_agpr(dk[db], a, da[t]);
+            else mfma32_agpr(dv[db], a, pa[t]);
           }
         },
         [&](auto ic) {
@@ -298,6 +307,8 @@ void bwd_dkdv_kernel(Params p) {
   }
 
   // ---- store dK^T, dV^T: lane (g, key n), register r <-> column 32 db + 8 (r/4) + 4g + r%4
+#pragma unroll
+  for (int db = 0; db < DB; ++db) agpr_settle(dk[db], dv[db]);
   const int key = kw0 + n;
   if (key < p.Nk) {
     const long long off = (((long long)b * p.N + p.k_start + key) * p.Hkv + gkv) * D;
@@ -412,21 +423,24 @@ void bwd_dq_kernel(Params p) {
 
   // Direct loads: 1 KB piece s = wave*NL + i of the two tiles (K: s < TILE_KB,
   // then V) covers tile bytes [(s % TILE_KB) KB, +1 KB); lane l fills 16 bytes
-  // at 16 l: tile row lrow[i], logical chunk lcol[i] (padding from chunk 0).
-  int lrow[NL], lcol[NL];
+  // at 16 l: tile row r, logical chunk ch (padding from chunk 0), read from
+  // byte loff[i] = 2 (r * row stride + 8 ch) past the tile's first key.
+  uint32_t loff[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int off = ((wave * NL + i) % TILE_KB) * 1024 + 16 * lane;
     const int r_ = off / (ROW * 2), pch = (off % (ROW * 2)) / 16;
-    lrow[i] = r_;
-    lcol[i] = pch < D / 8 ? ((pch ^ ((r_ >> 2) & 3)) << 3) : 0;
+    const int col = pch < D / 8 ? ((pch ^ ((r_ >> 2) & 3)) << 3) : 0;
+    loff[i] = (uint32_t)(r_ * krs + col) * 2u;
   }
+  // keys past the last one read as zeros (buffer range check); the mask drops them
+  const uint32_t kbytes = (uint32_t)(((p.Nk - 1) * krs + D) * 2);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K, kbytes), rv = make_rsrc(V, kbytes);
   auto load_piece = [&](int i, int buf, int j0) {
     const int sl = wave * NL + i;                  // wave-uniform
     const bool is_v = sl >= TILE_KB;
-    const int key = min(j0 + lrow[i], p.Nk - 1);
-    const bf16* src = (is_v ? V : K) + key * krs + lcol[i];
-    global_load_lds16(src, (is_v ? sm.v[buf] : sm.k[buf]) + (sl % TILE_KB) * 512);
+    buffer_load_lds16(is_v ? rv : rk, loff[i], (uint32_t)(j0 * krs) * 2u,
+                      (is_v ? sm.v[buf] : sm.k[buf]) + (sl % TILE_KB) * 512);
   };
 
   // per-lane LDS read bases (elements): K / V rows sigma32(n) (+32 kb), logical

@@ -117,23 +117,26 @@ void fwd_mfma_kernel(Params p) {
   }
   const int wq_first = p.q_start + wq0;
 
-  // ---- direct loads: 1 KB piece s = wave*NL + i of the K and V tiles (K:
-  // s < TILE_KB, then V); lane l fills 16 bytes at 16 l: tile row lrow[i],
-  // logical chunk lcol[i] (the padding is filled from chunk 0)
-  int lrow[NL], lcol[NL];
+  // Direct loads: 1 KB piece s = wave*NL + i of the two tiles (K: s < TILE_KB,
+  // then V) covers tile bytes [(s % TILE_KB) KB, +1 KB); lane l fills 16 bytes
+  // at 16 l: tile row r, logical chunk ch (padding from chunk 0), read from
+  // byte loff[i] = 2 (r * row stride + 8 ch) past the tile's first key.
+  uint32_t loff[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int off = ((wave * NL + i) % TILE_KB) * 1024 + 16 * lane;
     const int r_ = off / (ROW * 2), pch = (off % (ROW * 2)) / 16;
-    lrow[i] = r_;
-    lcol[i] = pch < D / 8 ? ((pch ^ ((r_ >> 2) & 3)) << 3) : 0;
+    const int col = pch < D / 8 ? ((pch ^ ((r_ >> 2) & 3)) << 3) : 0;
+    loff[i] = (uint32_t)(r_ * krs + col) * 2u;
   }
+  // keys past the last one read as zeros (buffer range check); the mask drops them
+  const uint32_t kbytes = (uint32_t)(((p.Nk - 1) * krs + D) * 2);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K, kbytes), rv = make_rsrc(V, kbytes);
   auto load_piece = [&](int i, int buf, int j0) {
     const int sl = wave * NL + i;                  // wave-uniform
     const bool is_v = sl >= TILE_KB;
-    const int key = min(j0 + lrow[i], p.Nk - 1);   // rows past Nk: finite copies, masked below
-    const bf16* src = (is_v ? V : K) + key * krs + lcol[i];
-    global_load_lds16(src, (is_v ? sm.v[buf] : sm.k[buf]) + (sl % TILE_KB) * 512);
+    buffer_load_lds16(is_v ? rv : rk, loff[i], (uint32_t)(j0 * krs) * 2u,
+                      (is_v ? sm.v[buf] : sm.k[buf]) + (sl % TILE_KB) * 512);
   };
 
   // ---- per-lane LDS read bases (elements): K rows sigma32(n) (+32 kb), logical

@@ -67,6 +67,41 @@ __device__ __forceinline__ void global_load_lds16(const void* g, bf16* lds_base)
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
+// Buffer descriptor for raw loads from the `bytes` bytes at `base`. The
+// hardware checks every dword against the range: one at or past `bytes`
+// (vector plus scalar offset) reads as zero and touches no memory, so tiles
+// that run past the last row need no clamping. Word 3 (0x00020000) selects
+// the 32-bit data format that gfx9-family raw loads need for the check.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Direct buffer -> LDS load of 16 bytes per lane from byte offset voff + soff
+// (voff per lane, soff wave-uniform): the wave writes 1 KB of LDS
+// contiguously, lane l at lds_base + 16 l (lds_base the same in every lane).
+// Completion is tracked by vmcnt like any global load.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                                  bf16* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voff, soff,
+                                           0, 0);
+}
+
+// acc += A B with the accumulator held in AGPRs (the matrix cores' own
+// accumulation registers), for accumulators that live through a whole loop
+// and are read only after it: they then take no VGPRs. The compiler does not
+// see this product's latency, so agpr_settle() must separate it from any
+// other access to the accumulator (see below).
+__device__ __forceinline__ void mfma32_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// 24 wait states tied to two accumulators: covers both the write of their
+// initial values before the first mfma32_agpr and the last product's result
+// latency before they are read (both below 20 wait states on gfx950).
+__device__ __forceinline__ void agpr_settle(f32x16& x, f32x16& y) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(x), "+a"(y));
+}
+
 // Waits for every outstanding global load of this wave. Used after the
 // loads of loop-invariant matrix operands: without it the compiler cannot
 // prove them complete across the loop back-edge and inserts vmcnt waits

@@ -46,8 +46,10 @@ int check_common(int B, int H, int Hkv, int N, int d, int dtype) {
   if (d != 64 && d != 128) return fail(MIATTN_EUNSUPPORTED, "head dimension d must be 64 or 128");
   if (dtype != MIATTN_F32 && dtype != MIATTN_BF16) return fail(MIATTN_EUNSUPPORTED, "dtype must be MIATTN_F32 or MIATTN_BF16");
   if (B > 65535 || H > 65535) return fail(MIATTN_EUNSUPPORTED, "B and H must be <= 65535");
-  // [B, H, N] statistics and row positions are indexed with 32-bit ints
-  if ((long long)B * H * N >= (1LL << 31) || (long long)N * H * d >= (1LL << 31))
+  // [B, H, N] statistics and row positions are indexed with 32-bit ints; the
+  // matrix-core kernels address one sequence of a tensor (plus one tile past
+  // its end) with 32-bit byte offsets
+  if ((long long)B * H * N >= (1LL << 31) || (long long)(N + 64) * H * d >= (1LL << 31))
     return fail(MIATTN_EUNSUPPORTED, "problem too large for 32-bit row indexing");
   return MIATTN_OK;
 }

@@ -29,8 +29,9 @@
  *                       0/1, non-finite scale, pointer not 16-byte aligned,
  *                       nchunks not a positive divisor of N (chunked calls),
  *                       outputs aliasing inputs where forbidden.
- *   MIATTN_EUNSUPPORTED d not 64 or 128, unknown dtype, or a size whose
- *                       element count does not fit the 32-bit row indexing.
+ *   MIATTN_EUNSUPPORTED d not 64 or 128, unknown dtype, or a size that does
+ *                       not fit 32-bit indexing: B*H*N >= 2^31 or
+ *                       (N + 64)*H*d >= 2^31.
  *   MIATTN_ELAUNCH      the HIP runtime reported an error at launch.
  *   MIATTN_ENOMEM       a stream-ordered scratch allocation failed.
  *
