@@ -127,14 +127,6 @@ void bwd_dkdv_kernel(Params p) {
   const int kpos = p.k_start + kw0 + n;          // this lane's key position
   const int wk_first = p.k_start + kw0;
 
-  // query tile of iteration `it`: (head, first row); iterations past the end
-  // repeat the last tile so that loads need no branch
-  auto tile_of = [&](int it, int& h, int& q0) {
-    it = min(it, niter - 1);
-    h = gkv * p.G + it / per_head;
-    q0 = (first + it % per_head) * DKV_BQ;
-  };
-
   // Direct loads: this wave's i-th 1 KB piece of a tile covers LDS bytes
   // [(wave*NL + i) KB, +1 KB); lane l fills 16 bytes at offset 16 l: tile row
   // r, logical chunk ch (padding bytes are filled from chunk 0), read from
@@ -191,9 +183,8 @@ void bwd_dkdv_kernel(Params p) {
     }
   }
 
-  if (niter > 0) {
-    int h, q0;
-    tile_of(0, h, q0);
+  if (niter > 0) {   // first tile: head gkv * G, rows from first * 64
+    const int h = gkv * p.G, q0 = first * DKV_BQ;
 #pragma unroll
     for (int piece = 0; piece < 2 * NL; ++piece) load_piece(piece, 0, h, q0);
     stat_load(h, q0);
@@ -202,13 +193,13 @@ void bwd_dkdv_kernel(Params p) {
   }
   __syncthreads();
 
-  for (int it = 0; it < niter; ++it) {
+  // One query tile: `it` counts tiles (buffer parity), (h_nx, q0_nx) is the
+  // tile to prefetch. Only tiles that cross the causal diagonal of the
+  // workgroup's keys run the body with the mask test.
+  auto tile = [&](auto mc, int it, int q0, int h_nx, int q0_nx) {
+    constexpr bool MASKED = decltype(mc)::value;
     const int buf = it & 1;
-    int h_cur, q0;
-    tile_of(it, h_cur, q0);
-    int h_nx, q0_nx;
-    tile_of(it + 1, h_nx, q0_nx);
-    const bool need_mask = CAUSAL && (wk_first + DKV_KW - 1 > p.q_start + q0);
+    const bool need_mask = MASKED && (wk_first + DKV_KW - 1 > p.q_start + q0);
     const bf16* qt = sm.q[buf];
     const bf16* ot = sm.o[buf];
     const float* lse2 = sm.stat[buf][0];
@@ -253,7 +244,7 @@ void bwd_dkdv_kernel(Params p) {
         const int e = 2 * k + u;
         const int r = h2 * 8 + e;
         const float x = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, -lq[e >> 2][e & 3]));
-        const float pv = (e < tq) ? 0.f : x;
+        const float pv = (MASKED && e < tq) ? 0.f : x;
         pa[qb * 2 + h2][e] = (bf16)pv;
         da[qb * 2 + h2][e] = (bf16)(pv * (dp[qb][r] - dq4[e >> 2][e & 3]));
       }
@@ -304,6 +295,36 @@ void bwd_dkdv_kernel(Params p) {
         });
     wait_global_loads();
     __syncthreads();
+  };
+  // tiles of query tile rows first + t, t < ndiag, cross the diagonal
+  int ndiag = 0;
+  if (CAUSAL) {
+    const int x = p.k_start + k0 + DKV_BK - 1 - p.q_start;   // last key, relative to the query rows
+    ndiag = x > 0 ? min(per_head, max(0, (x + DKV_BQ - 1) / DKV_BQ - first)) : 0;
+  }
+  int it = 0;
+  for (int hh = 0; hh < p.G; ++hh) {
+    const int h = gkv * p.G + hh;
+    // prefetch target after tile t of this head (the very last tile repeats itself)
+    auto next = [&](int t, int& hn, int& qn) {
+      hn = h;
+      qn = (first + t + 1) * DKV_BQ;
+      if (t + 1 == per_head) {
+        if (hh + 1 < p.G) { hn = h + 1; qn = first * DKV_BQ; }
+        else qn = (first + t) * DKV_BQ;
+      }
+    };
+    int t = 0;
+    for (; t < ndiag; ++t, ++it) {
+      int hn, qn;
+      next(t, hn, qn);
+      tile(std::true_type{}, it, (first + t) * DKV_BQ, hn, qn);
+    }
+    for (; t < per_head; ++t, ++it) {
+      int hn, qn;
+      next(t, hn, qn);
+      tile(std::false_type{}, it, (first + t) * DKV_BQ, hn, qn);
+    }
   }
 
   // ---- store dK^T, dV^T: lane (g, key n), register r <-> column 32 db + 8 (r/4) + 4g + r%4
@@ -478,8 +499,14 @@ void bwd_dq_kernel(Params p) {
   //   phase 1 (PS steps): S^T, dP^T of keys 32-63   + dS of keys 0-31
   //   phase 2 (PD steps): dQ^T over keys 0-31       + dS of keys 32-63
   //   phase 3 (PD steps): dQ^T over keys 32-63
+  // Key tiles before nplain lie entirely below the causal diagonal of every
+  // row of the workgroup and before the ragged end: they run a body without
+  // the mask test; the rest (at most 5 tiles) run the masked body.
   constexpr int PS = 2 * KS, PD = 2 * DB;
-  for (int j = 0; j < nkt; ++j) {
+  int nplain = min(nkt, p.Nk / DQ_BC);
+  if (CAUSAL) nplain = min(nplain, max(0, p.q_start + q0 - p.k_start + 1) / DQ_BC);
+  auto tile = [&](auto mc, int j) {
+    constexpr bool MASKED = decltype(mc)::value;
     const int buf = j & 1;
     const int kpos0 = p.k_start + j * DQ_BC;
     const int jn = min(j + 1, nkt - 1) * DQ_BC;      // next tile (the last tile repeats itself)
@@ -499,9 +526,12 @@ void bwd_dq_kernel(Params p) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int r = 2 * w + u;
-        const int kin = kb * 32 + ((r < 8) ? (g * 8 + r) : (16 + g * 8 + r - 8));
         const float x = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -lse2));
-        const float pv = kin > thr ? 0.f : x;
+        float pv = x;
+        if constexpr (MASKED) {
+          const int kin = kb * 32 + ((r < 8) ? (g * 8 + r) : (16 + g * 8 + r - 8));
+          pv = kin > thr ? 0.f : x;
+        }
         dsb[kb * 2 + (r >> 3)][r & 7] = (bf16)(pv * (dp[kb][r] - dsum));
       }
     };
@@ -552,7 +582,9 @@ void bwd_dq_kernel(Params p) {
         });
     wait_global_loads();
     __syncthreads();
-  }
+  };
+  for (int j = 0; j < nplain; ++j) tile(std::false_type{}, j);
+  for (int j = nplain; j < nkt; ++j) tile(std::true_type{}, j);
 
   // ---- store dQ = scale * acc^T: lane (g, query n), register r <-> column 32 db + 8 (r/4) + 4g + r%4
   if (row < p.Nq) {
