@@ -49,19 +49,19 @@ constexpr int DKV_BQ = 64;           // query rows per streamed tile
 // sigma32-ordered ds_read_b128 row reads of S = Q K^T, dP = dO V^T and the
 // 4-row transposing reads of dV^T = dO^T P, dK^T = Q^T dS are both free of
 // bank conflicts, and the tile is written by direct global -> LDS loads.
+// Three buffers (previous, current and next tile); within a buffer dO
+// follows Q, so both are reached from one base address.
 template <int D>
 struct DkdvSmem {
   static constexpr int ROW = D + 32;
   static constexpr int TILE = DKV_BQ * ROW;    // elements per tile
-  bf16 q[2][TILE];
-  bf16 o[2][TILE];                             // dO
-  float stat[2][2][DKV_BQ];    // [0]: LSE * log2(e) (+inf past the last row), [1]: D
+  struct Buf {
+    bf16 q[TILE];
+    bf16 o[TILE];              // dO
+  };
+  float stat[3][2][DKV_BQ];    // [0]: LSE * log2(e) (+inf past the last row), [1]: D
+  Buf buf[3];
 };
-
-template <int D>
-__device__ __forceinline__ int dkdv_swz(int row, int chunk) {
-  return row * DkdvSmem<D>::ROW + ((chunk ^ ((row >> 2) & 3)) << 3);
-}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(DKV_NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -109,6 +109,10 @@ void bwd_dkdv_kernel(Params p) {
     }
   }
   wait_global_loads();
+  // K and V operands live in AGPRs (matrix-core operands may be read from
+  // there directly), leaving the VGPRs to the per-tile values
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+a"(kf[ks]), "+a"(vf[ks]));
 
   // dK^T, dV^T accumulators, in AGPRs (mfma32_agpr)
   f32x16 dk[DB], dv[DB];
@@ -141,12 +145,13 @@ void bwd_dkdv_kernel(Params p) {
     loff[i] = (uint32_t)(row * qrs + col) * 2u;
   }
   const uint32_t qbytes = (uint32_t)(p.Nq * qrs * 2);
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qb, qbytes), ro = make_rsrc(Ob, qbytes);
+  const u32x4 rq = rsrc_words(Qb, qbytes), ro = rsrc_words(Ob, qbytes);
   auto load_piece = [&](int piece, int buf, int h, int q0) {   // piece < 2 NL: Q then dO
     const int i = piece % NL;
     const bool is_o = piece >= NL;
     const uint32_t soff = (uint32_t)(q0 * qrs + h * D) * 2u;
-    buffer_load_lds16(is_o ? ro : rq, loff[i], soff, (is_o ? sm.o[buf] : sm.q[buf]) + (wave * NL + i) * 512);
+    buffer_load_lds16_async(is_o ? ro : rq, loff[i], soff,
+                            lds_addr((is_o ? sm.buf[buf].o : sm.buf[buf].q) + (wave * NL + i) * 512));
   };
   float st;          // LSE (tid < 64) or D (64 <= tid < 128) of row q0 + tid % 64
   bool st_valid;
@@ -183,8 +188,34 @@ void bwd_dkdv_kernel(Params p) {
     }
   }
 
-  if (niter > 0) {   // first tile: head gkv * G, rows from first * 64
-    const int h = gkv * p.G, q0 = first * DKV_BQ;
+  // Tiles are taken in the order (query head of the group, query tile);
+  // tile k sits in LDS buffer k % 3. The work of one tile is spread over two
+  // iterations (software pipeline), so that every phase of matrix-core
+  // products carries a quarter of the softmax work:
+  //   phase 0: S, dP of half 0 of tile k       + softmax group 1 of half 1 of tile k-1
+  //            (+ direct loads of tile k+1)
+  //   phase 1: dV^T, dK^T over half 1 of k-1   + softmax group 0 of half 0 of tile k
+  //   phase 2: S, dP of half 1 of tile k       + softmax group 1 of half 0 of tile k
+  //   phase 3: dV^T, dK^T over half 0 of k     + softmax group 0 of half 1 of tile k
+  // (half = 32 query rows, group = 16 of them). Tile -1 is an all-zero buffer
+  // with LSE = +inf (P = 0), and one empty tile past the last query row
+  // (zero rows, LSE = +inf) drains the pipeline. Each phase prefetches the
+  // LSE / D values the next phase's softmax group needs.
+  constexpr int PL = D / 8;          // lock steps per phase
+  const int ntiles = niter + 1;      // plus the draining tile
+  const int empty_q0 = nqt * DKV_BQ; // rows past the end: zeros, LSE = +inf
+
+  // buffer 2 = tile -1: zero Q / dO, LSE = +inf, D = 0
+  {
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    for (int i = tid; i < TILE / 8; i += DKV_NW * 64) {
+      *(f32x4*)(sm.buf[2].q + 8 * i) = z;
+      *(f32x4*)(sm.buf[2].o + 8 * i) = z;
+    }
+    if (tid < 128) sm.stat[2][tid >> 6][tid & 63] = (tid < 64) ? INFINITY : 0.f;
+  }
+  {  // tile 0 (the empty tile if this workgroup has none)
+    const int h = gkv * p.G, q0 = niter > 0 ? first * DKV_BQ : empty_q0;
 #pragma unroll
     for (int piece = 0; piece < 2 * NL; ++piece) load_piece(piece, 0, h, q0);
     stat_load(h, q0);
@@ -193,138 +224,139 @@ void bwd_dkdv_kernel(Params p) {
   }
   __syncthreads();
 
-  // One query tile: `it` counts tiles (buffer parity), (h_nx, q0_nx) is the
-  // tile to prefetch. Only tiles that cross the causal diagonal of the
-  // workgroup's keys run the body with the mask test.
-  auto tile = [&](auto mc, int it, int q0, int h_nx, int q0_nx) {
-    constexpr bool MASKED = decltype(mc)::value;
-    const int buf = it & 1;
-    const bool need_mask = MASKED && (wk_first + DKV_KW - 1 > p.q_start + q0);
-    const bf16* qt = sm.q[buf];
-    const bf16* ot = sm.o[buf];
-    const float* lse2 = sm.stat[buf][0];
-    const float* dsm = sm.stat[buf][1];
-
-    // Every wave computes every tile: on the one diagonal tile where a wave's
-    // keys are all after the tile's queries, the mask zeroes P (a per-wave
-    // branch would make the allocator shuttle accumulators through AGPRs).
-    //
-    // 4 phases of PL = D/8 lock steps, one MFMA each; the tile's 64 queries
-    // are two halves qb:
-    //   phase 0: S, dP of half 0          + direct loads of the next tile
-    //   phase 1: S, dP of half 1          + softmax of half 0
-    //   phase 2: dV^T, dK^T over half 0   + softmax of half 1
-    //   phase 3: dV^T, dK^T over half 1   + the next tile's LSE / D to LDS
-    // One body serves every tile: the mask test is a compare and a select per
-    // element against a per-lane threshold (never true below the diagonal).
-    constexpr int PL = D / 8;
-    const int mthr = need_mask ? kpos - (p.q_start + q0) : -0x40000000;
-    f32x16 s[2], dp[2];
-    s[0] = f32x16{}; dp[0] = f32x16{}; s[1] = f32x16{}; dp[1] = f32x16{};
-    bf16x8 pa[4], da[4];
-    f32x4 lq[2], dq4[2];   // LSE and D of the 8 query rows being softmaxed
-
-    // softmax sub-step w (0..7) of half qb: lane (g, key n), register r <->
-    // query q0 + 32 qb + sigma_row(g, r); sub-step w forms P and dS for
-    // elements 2k, 2k+1 (k = w % 4) of register group h2 = w / 4, whose 8
-    // query rows' LSE and D are read at the group's first sub-step.
-    auto softmax_sub = [&](auto qbc, auto wc) {
-      constexpr int qb = decltype(qbc)::value, w = decltype(wc)::value;
-      constexpr int h2 = w >> 2, k = w & 3;
-      const int qi0 = qb * 32 + h2 * 16 + g * 8;    // 8 consecutive query rows
-      const int tq = mthr - qi0;                     // element e masked iff e < tq
-      if constexpr (k == 0) {
-        lq[0] = *(const f32x4*)(lse2 + qi0);
-        lq[1] = *(const f32x4*)(lse2 + qi0 + 4);
-        dq4[0] = *(const f32x4*)(dsm + qi0);
-        dq4[1] = *(const f32x4*)(dsm + qi0 + 4);
-      }
+  // S, dP of the two halves of a tile: lane (g, key n), register r <-> query
+  // 32 half + sigma_row(g, r). s1 / dp1 stay live into the next iteration.
+  f32x16 s0, dp0, s1 = f32x16{}, dp1 = f32x16{};
+  bf16x8 pa[4], da[4];               // P, dS of the 16-query blocks t = 0..3
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int e = 2 * k + u;
-        const int r = h2 * 8 + e;
-        const float x = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, -lq[e >> 2][e & 3]));
-        const float pv = (MASKED && e < tq) ? 0.f : x;
-        pa[qb * 2 + h2][e] = (bf16)pv;
-        da[qb * 2 + h2][e] = (bf16)(pv * (dp[qb][r] - dq4[e >> 2][e & 3]));
-      }
-    };
+  for (int t = 0; t < 4; ++t) {
+    pa[t] = bf16x8{};
+    da[t] = bf16x8{};
+  }
+  // LSE (log2 units) and D of the 8 query rows of the group being softmaxed,
+  // double-buffered: slot (phase & 1) is consumed, the other one prefetched
+  f32x4 st_l[2][2], st_d[2][2];
+  const uint32_t stat_lane = lds_addr(&sm.stat[0][0][0]) + 32 * g;   // + rows 8g..8g+7
+  // stb: LDS address of this lane's rows in the stats of one buffer
+  auto stat_read = [&](int slot, uint32_t stb, int qb, int g2) {
+    const int off = (qb * 32 + g2 * 16) * 4;
+    st_l[slot][0] = lds_read_f32x4_at(stb + off);
+    st_l[slot][1] = lds_read_f32x4_at(stb + off + 16);
+    st_d[slot][0] = lds_read_f32x4_at(stb + DKV_BQ * 4 + off);
+    st_d[slot][1] = lds_read_f32x4_at(stb + DKV_BQ * 4 + off + 16);
+  };
+  stat_read(0, stat_lane + 2 * (2 * DKV_BQ * 4), 1, 1);   // tile -1, half 1, group 1
+
+  // softmax sub-step k (0..3) of group g2 of half qb: P and dS of elements
+  // e = 2k, 2k+1 of the group (register r = 8 g2 + e), stats from `slot`
+  auto softmax_sub = [&](auto qbc, auto g2c, auto kc, auto slotc) {
+    constexpr int qb = decltype(qbc)::value, g2 = decltype(g2c)::value;
+    constexpr int k = decltype(kc)::value, slot = decltype(slotc)::value;
+    const f32x16& sv = qb ? s1 : s0;
+    const f32x16& dv_ = qb ? dp1 : dp0;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = 2 * k + u, r = g2 * 8 + e;
+      const float x = __builtin_amdgcn_exp2f(fmaf(sv[r], c, -st_l[slot][e >> 2][e & 3]));
+      pa[qb * 2 + g2][e] = (bf16)x;
+      da[qb * 2 + g2][e] = (bf16)(x * (dv_[r] - st_d[slot][e >> 2][e & 3]));
+    }
+  };
+  // causal mask on the scores of one half of a diagonal tile: query
+  // 32 qb + sigma_row(g, r) before this lane's key -> -inf (P = 0)
+  auto mask_half = [&](f32x16& sv, int mthr_h) {
+    const int tq = mthr_h - 8 * g;    // register r masked iff r' < tq, r' = r (r < 8) or r + 8
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rr = r < 8 ? r : r + 8;
+      if (rr < tq) sv[r] = -INFINITY;
+    }
+  };
+
+  int h_cur = gkv * p.G, t_cur = 0;   // (query head, tile index within the head) of tile k
+  for (int kt_ = 0; kt_ < ntiles; ++kt_) {
+    const int cb = kt_ % 3, pb = (kt_ + 2) % 3, nb = (kt_ + 1) % 3;
+    const bool real = kt_ < niter;
+    const int q0 = real ? (first + t_cur) * DKV_BQ : empty_q0;
+    // the tile after this one
+    int h_nx = h_cur, t_nx = t_cur + 1;
+    if (t_nx == per_head) { h_nx = h_cur + 1; t_nx = 0; }
+    const bool nx_real = kt_ + 1 < niter;
+    const int q0_nx = nx_real ? (first + t_nx) * DKV_BQ : empty_q0;
+    const int h_ld = nx_real ? h_nx : gkv * p.G;   // a valid head also for the empty tile
+    const bool need_mask = CAUSAL && real && (wk_first + DKV_KW - 1 > p.q_start + q0);
+    const int mthr = kpos - (p.q_start + q0);     // query index inside the tile < mthr -> masked
+    // LDS read bases of this iteration (byte addresses; dO at +TILE from Q)
+    const uint32_t cq = lds_addr(sm.buf[0].q) + cb * (uint32_t)sizeof(typename DkdvSmem<D>::Buf);
+    const uint32_t pq = lds_addr(sm.buf[0].q) + pb * (uint32_t)sizeof(typename DkdvSmem<D>::Buf);
+    const uint32_t bs[2] = {lds_opaque(cq + 2 * rd_s[0]), lds_opaque(cq + 2 * rd_s[1])};
+    const uint32_t bt[2] = {lds_opaque(cq + 2 * rd_t[0]), lds_opaque(cq + 2 * rd_t[1])};
+    const uint32_t btp[2] = {lds_opaque(pq + 2 * rd_t[0]), lds_opaque(pq + 2 * rd_t[1])};
+    const uint32_t stb = lds_opaque(stat_lane + cb * (2 * DKV_BQ * 4));
 
     lockstep_products<4 * PL, 4>(
         [&](auto ic) {
           constexpr int i = decltype(ic)::value, ph = i / PL, j = i % PL;
-          if constexpr (ph < 2) {   // S / dP: step j = (ks, which), half ph
+          if constexpr (ph == 0 || ph == 2) {   // S / dP of half ph/2: step j = (ks, which)
             constexpr int ks = j >> 1;
-            const bf16* t = (j & 1) ? ot : qt;
-            return lds_read16(t + rd_s[ks & 1], ph * 32 * ROW + (ks >> 1) * 32);
-          } else {                  // dV / dK: step j = (t, db, which), two transposing reads
-            constexpr int t = 2 * (ph - 2) + j / (2 * DB), db = (j >> 1) % DB;
-            const bf16* src = (j & 1) ? qt : ot;
-            const bf16x4 r0 = lds_read_tr4(src + rd_t[0] + 16 * t * ROW + 32 * db);
-            const bf16x4 r1 = lds_read_tr4(src + rd_t[1] + 16 * t * ROW + 32 * db);
+            return lds_read16_at(bs[ks & 1] + 2 * ((j & 1) * TILE + (ph / 2) * 32 * ROW + (ks >> 1) * 32));
+          } else {                              // dV / dK: step j = (t, db, which), two transposing reads
+            constexpr int t = (ph == 1 ? 2 : 0) + j / (2 * DB), db = (j >> 1) % DB;
+            constexpr int off = ((j & 1) ? 0 : TILE) + 16 * t * ROW + 32 * db;   // Q^T for dK, dO^T for dV
+            const bf16x4 r0 = lds_read_tr4_at((ph == 1 ? btp[0] : bt[0]) + 2 * off);
+            const bf16x4 r1 = lds_read_tr4_at((ph == 1 ? btp[1] : bt[1]) + 2 * off);
             return bf16x8{r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
           }
         },
         [&](auto ic, bf16x8 a) {
           constexpr int i = decltype(ic)::value, ph = i / PL, j = i % PL;
-          if constexpr (ph < 2) {
-            if constexpr (j & 1) dp[ph] = mfma32(a, vf[j >> 1], dp[ph]);
-            else s[ph] = mfma32(a, kf[j >> 1], s[ph]);
+          if constexpr (ph == 0 || ph == 2) {
+            constexpr int ks = j >> 1;
+            f32x16& acc = (j & 1) ? (ph == 0 ? dp0 : dp1) : (ph == 0 ? s0 : s1);
+            const bf16x8& bop = (j & 1) ? vf[ks] : kf[ks];
+            acc = mfma32(a, bop, ks == 0 ? f32x16{} : acc);
           } else {
-            constexpr int t = 2 * (ph - 2) + j / (2 * DB), db = (j >> 1) % DB;
+            constexpr int t = (ph == 1 ? 2 : 0) + j / (2 * DB), db = (j >> 1) % DB;
             if constexpr (j & 1) mfma32_agpr(dk[db], a, da[t]);
             else mfma32_agpr(dv[db], a, pa[t]);
           }
         },
         [&](auto ic) {
           constexpr int i = decltype(ic)::value, ph = i / PL, j = i % PL;
-          if constexpr (ph == 0) {
+          // stats for the next phase's group, into slot (ph + 1) & 1
+          if constexpr (j == 0) {
+            if constexpr (ph == 0) stat_read(1, stb, 0, 0);
+            else if constexpr (ph == 1) stat_read(0, stb, 0, 1);
+            else if constexpr (ph == 2) stat_read(1, stb, 1, 0);
+            else stat_read(0, stb, 1, 1);
+          }
+          // softmax sub-steps at steps (2k + 1) PL / 8
+          if constexpr ((j * 8) % PL == 0 && ((j * 8) / PL) % 2 == 1) {
+            constexpr int k = ((j * 8) / PL) / 2;
+            using KC = std::integral_constant<int, k>;
+            using SL = std::integral_constant<int, ph & 1>;
+            if constexpr (ph == 0) softmax_sub(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, KC{}, SL{});
+            else if constexpr (ph == 1) softmax_sub(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, KC{}, SL{});
+            else if constexpr (ph == 2) softmax_sub(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, KC{}, SL{});
+            else softmax_sub(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}, KC{}, SL{});
+          }
+          if constexpr (ph == 0) {            // next tile: direct loads, then its LSE / D
             constexpr int lo = j * (2 * NL) / PL, hi = (j + 1) * (2 * NL) / PL;
             [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
-              (load_piece(lo + Ws, buf ^ 1, h_nx, q0_nx), ...);
+              (load_piece(lo + Ws, nb, h_ld, q0_nx), ...);
             }(std::make_integer_sequence<int, hi - lo>{});
-            if constexpr (j == PL - 1) stat_load(h_nx, q0_nx);
-          } else if constexpr (ph == 3) {
-            if constexpr (j == PL - 1) stat_store(buf ^ 1);
-          } else {
-            constexpr int lo = j * 8 / PL, hi = (j + 1) * 8 / PL;
-            [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
-              (softmax_sub(std::integral_constant<int, ph - 1>{}, std::integral_constant<int, lo + Ws>{}), ...);
-            }(std::make_integer_sequence<int, hi - lo>{});
+            if constexpr (j == PL - 1) stat_load(h_ld, q0_nx);
+          }
+          if constexpr (ph == 3 && j == PL - 1) stat_store(nb);
+          // diagonal tiles: mask each half's scores once its products are done
+          if constexpr ((ph == 0 || ph == 2) && j == PL - 1) {
+            if (need_mask) mask_half(ph == 0 ? s0 : s1, mthr - (ph / 2) * 32);
           }
         });
     wait_global_loads();
     __syncthreads();
-  };
-  // tiles of query tile rows first + t, t < ndiag, cross the diagonal
-  int ndiag = 0;
-  if (CAUSAL) {
-    const int x = p.k_start + k0 + DKV_BK - 1 - p.q_start;   // last key, relative to the query rows
-    ndiag = x > 0 ? min(per_head, max(0, (x + DKV_BQ - 1) / DKV_BQ - first)) : 0;
-  }
-  int it = 0;
-  for (int hh = 0; hh < p.G; ++hh) {
-    const int h = gkv * p.G + hh;
-    // prefetch target after tile t of this head (the very last tile repeats itself)
-    auto next = [&](int t, int& hn, int& qn) {
-      hn = h;
-      qn = (first + t + 1) * DKV_BQ;
-      if (t + 1 == per_head) {
-        if (hh + 1 < p.G) { hn = h + 1; qn = first * DKV_BQ; }
-        else qn = (first + t) * DKV_BQ;
-      }
-    };
-    int t = 0;
-    for (; t < ndiag; ++t, ++it) {
-      int hn, qn;
-      next(t, hn, qn);
-      tile(std::true_type{}, it, (first + t) * DKV_BQ, hn, qn);
-    }
-    for (; t < per_head; ++t, ++it) {
-      int hn, qn;
-      next(t, hn, qn);
-      tile(std::false_type{}, it, (first + t) * DKV_BQ, hn, qn);
-    }
+    h_cur = h_nx;
+    t_cur = t_nx;
   }
 
   // ---- store dK^T, dV^T: lane (g, key n), register r <-> column 32 db + 8 (r/4) + 4g + r%4
@@ -456,12 +488,12 @@ void bwd_dq_kernel(Params p) {
   }
   // keys past the last one read as zeros (buffer range check); the mask drops them
   const uint32_t kbytes = (uint32_t)(((p.Nk - 1) * krs + D) * 2);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K, kbytes), rv = make_rsrc(V, kbytes);
+  const u32x4 rk = rsrc_words(K, kbytes), rv = rsrc_words(V, kbytes);
   auto load_piece = [&](int i, int buf, int j0) {
     const int sl = wave * NL + i;                  // wave-uniform
     const bool is_v = sl >= TILE_KB;
-    buffer_load_lds16(is_v ? rv : rk, loff[i], (uint32_t)(j0 * krs) * 2u,
-                      (is_v ? sm.v[buf] : sm.k[buf]) + (sl % TILE_KB) * 512);
+    buffer_load_lds16_async(is_v ? rv : rk, loff[i], (uint32_t)(j0 * krs) * 2u,
+                            lds_addr((is_v ? sm.v[buf] : sm.k[buf]) + (sl % TILE_KB) * 512));
   };
 
   // per-lane LDS read bases (elements): K / V rows sigma32(n) (+32 kb), logical

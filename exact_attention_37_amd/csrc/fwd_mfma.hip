@@ -131,12 +131,12 @@ void fwd_mfma_kernel(Params p) {
   }
   // keys past the last one read as zeros (buffer range check); the mask drops them
   const uint32_t kbytes = (uint32_t)(((p.Nk - 1) * krs + D) * 2);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K, kbytes), rv = make_rsrc(V, kbytes);
+  const u32x4 rk = rsrc_words(K, kbytes), rv = rsrc_words(V, kbytes);
   auto load_piece = [&](int i, int buf, int j0) {
     const int sl = wave * NL + i;                  // wave-uniform
     const bool is_v = sl >= TILE_KB;
-    buffer_load_lds16(is_v ? rv : rk, loff[i], (uint32_t)(j0 * krs) * 2u,
-                      (is_v ? sm.v[buf] : sm.k[buf]) + (sl % TILE_KB) * 512);
+    buffer_load_lds16_async(is_v ? rv : rk, loff[i], (uint32_t)(j0 * krs) * 2u,
+                            lds_addr((is_v ? sm.v[buf] : sm.k[buf]) + (sl % TILE_KB) * 512));
   };
 
   // ---- per-lane LDS read bases (elements): K rows sigma32(n) (+32 kb), logical

@@ -60,6 +60,27 @@ __device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
 }
 
+// LDS reads through 32-bit LDS byte addresses. lds_addr() gives the address
+// of a shared-memory object; lds_opaque() hides an address from the
+// optimizer, so that reads at constant offsets from it are encoded with the
+// instruction's offset field instead of recomputing addresses per read.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ uint32_t lds_opaque(uint32_t a) {
+  asm("" : "+v"(a));
+  return a;
+}
+__device__ __forceinline__ bf16x8 lds_read16_at(uint32_t a) {
+  return *(const __attribute__((address_space(3))) bf16x8*)a;
+}
+__device__ __forceinline__ f32x4 lds_read_f32x4_at(uint32_t a) {
+  return *(const __attribute__((address_space(3))) f32x4*)a;
+}
+__device__ __forceinline__ bf16x4 lds_read_tr4_at(uint32_t a) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a);
+}
+
 // Direct global -> LDS load of 16 bytes per lane: the wave writes 1 KB of
 // LDS contiguously, lane l at lds_base + 16 l; lds_base must be the same in
 // every lane. Completion is tracked by vmcnt like any global load.
@@ -84,6 +105,28 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, uint
                                                   bf16* lds_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voff, soff,
                                            0, 0);
+}
+
+// Buffer descriptor as four dwords (for inline assembly): base address,
+// stride 0, `bytes` records, and the same range-checked raw format as
+// make_rsrc().
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
+}
+
+// buffer_load_lds16 issued through inline assembly. The compiler then does
+// not know that the load writes LDS; otherwise it makes every later LDS read
+// it cannot prove disjoint from the destination (transposing reads, reads
+// through computed addresses) wait for all outstanding tile loads. The tile
+// being loaded is never read before the caller's wait_global_loads() and
+// barrier, so no such wait is needed. lds_base: LDS byte address.
+__device__ __forceinline__ void buffer_load_lds16_async(u32x4 rsrc, uint32_t voff, uint32_t soff,
+                                                        uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff)
+               : "m0");
 }
 
 // acc += A B with the accumulator held in AGPRs (the matrix cores' own
