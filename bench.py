@@ -21,6 +21,23 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 
+# HBM traffic of one bwd_dkdv_kernel launch on the 16K workload, from two
+# rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; calibrated against a plain
+# 1 GiB device copy in the same process), valid only for the kernel sources
+# whose SHA-1 is recorded with it (profiles/llama16k_causal_bf16_traffic.md).
+DKDV_TRAFFIC = {"sources_sha1": "d0dc0ac248101195f6a827495d4eb0fa049a31b2", "bytes": 2849158352}   # fetch 2.581 GB + write 0.268 GB
+DKDV_SOURCES = ("exact_attention_37_amd/csrc/bwd_mfma.hip", "exact_attention_37_amd/csrc/mfma_common.h",
+                "exact_attention_37_amd/csrc/common.h")
+
+
+def sources_sha1():
+    import hashlib
+    h = hashlib.sha1()
+    for rel in DKDV_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -82,36 +99,48 @@ def main():
     torch.cuda.synchronize()
 
     def step(ev=None):
+        # events (all on torch's current stream, which is the stream the
+        # library launches on): before fwd | after fwd | after the rowsum
+        # kernel | after the dK/dV kernel | after the dQ kernel
         if ev is not None:
             ev[0].record()
         mi.fwd(q, k, v, causal, scale, out=o, out_lse=lse)
         if ev is not None:
             ev[1].record()
-        mi.bwd(q, k, v, o, lse, do, causal, scale, dq=dq, dk=dk, dv=dv)
+        mi.bwd(q, k, v, o, lse, do, causal, scale, dq=dq, dk=dk, dv=dv,
+               marks=None if ev is None else (ev[2], ev[3]))
         if ev is not None:
-            ev[2].record()
+            ev[4].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    def avg(a, b):
+        return sum(e[a].elapsed_time(e[b]) for e in evs) / args.steps
+    fwd_ms, bwd_ms = avg(0, 1), avg(1, 4)
+    pre_ms, dkdv_ms, dq_ms = avg(1, 2), avg(2, 3), avg(3, 4)
     ms = wall * 1e3 / args.steps
 
     ff, fb = flops(w.B, w.H, w.N, w.d, causal)
     value = (ff + fb) / (ms * 1e-3) / 1e12
     fwd_tf = ff / (fwd_ms * 1e-3) / 1e12
     bwd_tf = fb / (bwd_ms * 1e-3) / 1e12
-    # dominant kernel: the one with the larger share of the step
-    dom = "bwd" if bwd_ms >= fwd_ms else "fwd"
-    ach = bwd_tf if dom == "bwd" else fwd_tf
+    # Dominant kernel: bwd_dkdv_kernel (the largest share of the step). Its
+    # algorithmic work is 4 of the backward's 5 counted products (S, dP,
+    # dV^T, dK^T: 8 d FLOPs per visible (query, key) pair) = 2 x the forward
+    # count; the dQ kernel's recomputed S and dP are not algorithmic.
+    dkdv_flops = 2.0 * ff
+    dkdv_tf = dkdv_flops / (dkdv_ms * 1e-3) / 1e12
+    traffic = None
+    if DKDV_TRAFFIC is not None and args.workload == "llama16k" and DKDV_TRAFFIC["sources_sha1"] == sources_sha1():
+        traffic = DKDV_TRAFFIC["bytes"]
     out = {
         "metric": "causal bf16 attention fwd+bwd TFLOP/s on 1 GPU and % of bf16 MFMA peak",
         "value": round(value, 2),
@@ -130,9 +159,11 @@ def main():
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
         "fwd_tflops": round(fwd_tf, 2), "bwd_tflops": round(bwd_tf, 2),
-        "roofline": {"bound": "mfma", "kernel": "attn_%s call" % dom, "achieved": round(ach, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+        "kernel_ms": {"fwd_mfma": round(fwd_ms, 4), "bwd_pre": round(pre_ms, 4),
+                      "bwd_dkdv": round(dkdv_ms, 4), "bwd_dq": round(dq_ms, 4)},
+        "roofline": {"bound": "mfma", "kernel": "bwd_dkdv_kernel", "achieved": round(dkdv_tf, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dkdv_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
     }
     if args.extra:
         extra = {}

@@ -47,10 +47,11 @@ def lib():
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i]
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, vp, vp, vp, i, i]
+    L.attn_bwd_timed.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, vp, vp, vp, i, i, vp]
     L.attn_merge.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     L.attn_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, i, i]
     L.attn_bwd_chunked.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, vp, vp, vp, i, i]
-    for fn in ("attn_fwd", "attn_bwd", "attn_merge", "attn_fwd_chunked", "attn_bwd_chunked"):
+    for fn in ("attn_fwd", "attn_bwd", "attn_bwd_timed", "attn_merge", "attn_fwd_chunked", "attn_bwd_chunked"):
         getattr(L, fn).restype = i
     L.attn_last_error.restype = ctypes.c_char_p
     L.attn_last_error.argtypes = []
@@ -125,11 +126,14 @@ def fwd(q, k, v, causal=False, scale=None, out=None, out_lse=None):
     return o, lse
 
 
-def bwd(q, k, v, o, lse, dout, causal=False, scale=None, accumulate=False, dq=None, dk=None, dv=None):
+def bwd(q, k, v, o, lse, dout, causal=False, scale=None, accumulate=False, dq=None, dk=None, dv=None,
+        marks=None):
     """Exact attention backward from the forward's o and lse. Returns (dq, dk, dv).
 
     accumulate=True: dq/dk/dv are float32 tensors (given or zero-initialised)
     that the gradients are added to; otherwise they have q's dtype.
+    marks: optional pair of torch.cuda.Event, recorded on the stream after the
+    rowsum kernel and after the dK/dV kernel (attn_bwd_timed).
     """
     B, N, H, Hkv, d = _dims(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -145,9 +149,16 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, accumulate=False, dq=No
     _need(dq, "dq", gdt, q.shape, q.device)
     _need(dk, "dk", gdt, k.shape, q.device)
     _need(dv, "dv", gdt, v.shape, q.device)
-    _check(lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
-                          int(bool(causal)), scale, _stream(q), _ptr(dout), _ptr(dq), _ptr(dk),
-                          _ptr(dv), _dtype_code(q), int(bool(accumulate))))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d, int(bool(causal)), scale,
+            _stream(q), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _dtype_code(q), int(bool(accumulate)))
+    if marks is None:
+        _check(lib().attn_bwd(*args))
+    else:
+        for m in marks:           # torch creates the HIP event at its first record
+            if not m.cuda_event:
+                m.record()
+        ev = (ctypes.c_void_p * 2)(*[ctypes.c_void_p(m.cuda_event) for m in marks])
+        _check(lib().attn_bwd_timed(*args, ev))
     return dq, dk, dv
 
 

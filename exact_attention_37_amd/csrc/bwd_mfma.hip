@@ -644,14 +644,17 @@ void bwd_dq_kernel(Params p) {
 }
 
 template <int D>
-hipError_t launch_d(const Params& p, hipStream_t s) {
+hipError_t launch_dkdv_d(const Params& p, hipStream_t s) {
   const dim3 gkv(p.Hkv, (p.Nk + DKV_BK - 1) / DKV_BK, p.B);
   if (p.causal)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), gkv, dim3(DKV_NW * 64), 0, s, p);
   else
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), gkv, dim3(DKV_NW * 64), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dq_d(const Params& p, hipStream_t s) {
   constexpr int NW = 8;
   const dim3 gq(p.H, (p.Nq + NW * 32 - 1) / (NW * 32), p.B);
   if (p.causal)
@@ -663,8 +666,18 @@ hipError_t launch_d(const Params& p, hipStream_t s) {
 
 }  // namespace
 
+hipError_t launch_bwd_dkdv_mfma(const Params& p, hipStream_t s) {
+  return p.d == 128 ? launch_dkdv_d<128>(p, s) : launch_dkdv_d<64>(p, s);
+}
+
+hipError_t launch_bwd_dq_mfma(const Params& p, hipStream_t s) {
+  return p.d == 128 ? launch_dq_d<128>(p, s) : launch_dq_d<64>(p, s);
+}
+
 hipError_t launch_bwd_mfma(const Params& p, hipStream_t s) {
-  return p.d == 128 ? launch_d<128>(p, s) : launch_d<64>(p, s);
+  const hipError_t e = launch_bwd_dkdv_mfma(p, s);
+  if (e != hipSuccess) return e;
+  return launch_bwd_dq_mfma(p, s);
 }
 
 }  // namespace miattn

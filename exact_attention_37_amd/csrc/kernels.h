@@ -12,7 +12,9 @@ hipError_t launch_bwd_simt(const Params& p, int dtype, hipStream_t s);
 
 // bf16 matrix-core kernels (gfx950 MFMA).
 hipError_t launch_fwd_mfma(const Params& p, bool out_f32, hipStream_t s);
-hipError_t launch_bwd_mfma(const Params& p, hipStream_t s);
+hipError_t launch_bwd_mfma(const Params& p, hipStream_t s);          // dK/dV kernel, then dQ kernel
+hipError_t launch_bwd_dkdv_mfma(const Params& p, hipStream_t s);
+hipError_t launch_bwd_dq_mfma(const Params& p, hipStream_t s);
 
 // rowsum(dout * o) for query rows [row0, row0 + nrows) of every (b, h).
 hipError_t launch_bwd_pre(const void* o, const void* dout, float* dsum, int B, int H, int N,

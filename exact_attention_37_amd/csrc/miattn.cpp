@@ -185,9 +185,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   return ok();
 }
 
-int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
-             int Hkv, int N, int d, int causal, float scale, void* stream, const void* dout, void* dq, void* dk,
-             void* dv, int dtype, int accumulate) {
+int attn_bwd_timed(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
+                   int Hkv, int N, int d, int causal, float scale, void* stream, const void* dout, void* dq,
+                   void* dk, void* dv, int dtype, int accumulate, void* const* marks) {
   int st = check_common(B, H, Hkv, N, d, dtype);
   if (st) return st;
   if ((st = check_ptrs({q, k, v, o, lse, dout, dq, dk, dv}))) return st;
@@ -218,8 +218,23 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   p.accumulate = accumulate;
   if ((st = launch_status(miattn::launch_bwd_pre(o, dout, dsum, B, H, N, d, 0, N, dtype, s), "bwd preprocess")))
     return st;
-  if ((st = launch_status(bwd_block(p, dtype, s), "attn_bwd"))) return st;
+  if (marks && (st = launch_status(hipEventRecord((hipEvent_t)marks[0], s), "timing mark 0"))) return st;
+  if (dtype == MIATTN_BF16) {
+    if ((st = launch_status(miattn::launch_bwd_dkdv_mfma(p, s), "attn_bwd dK/dV"))) return st;
+    if (marks && (st = launch_status(hipEventRecord((hipEvent_t)marks[1], s), "timing mark 1"))) return st;
+    if ((st = launch_status(miattn::launch_bwd_dq_mfma(p, s), "attn_bwd dQ"))) return st;
+  } else {
+    if ((st = launch_status(bwd_block(p, dtype, s), "attn_bwd"))) return st;
+    if (marks && (st = launch_status(hipEventRecord((hipEvent_t)marks[1], s), "timing mark 1"))) return st;
+  }
   return ok();
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
+             int Hkv, int N, int d, int causal, float scale, void* stream, const void* dout, void* dq, void* dk,
+             void* dv, int dtype, int accumulate) {
+  return attn_bwd_timed(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, stream, dout, dq, dk, dv, dtype,
+                        accumulate, nullptr);
 }
 
 int attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* o, float* lse, int B,

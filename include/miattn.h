@@ -87,6 +87,22 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              void* stream, const void* dout, void* dq, void* dk, void* dv,
              int dtype, int accumulate);
 
+/* attn_bwd with per-kernel timing marks, for measurement tools: the same
+ * arguments, results and errors as attn_bwd, and additionally
+ *   marks[0] is recorded on `stream` after the rowsum(dout * o) kernel,
+ *   marks[1] after the dK/dV kernel (the dQ kernel follows),
+ * where marks[0], marks[1] are hipEvent_t handles (passed as void*) that the
+ * caller created and owns. marks == NULL records nothing. For dtype
+ * MIATTN_BF16 the two intervals between an event the caller records before
+ * the call, marks[0], marks[1] and one recorded after it are the durations
+ * of the three kernels of the backward; for MIATTN_F32 marks[1] follows the
+ * single float32 backward block and the last interval is empty.
+ * MIATTN_ELAUNCH also covers a failed hipEventRecord. */
+int attn_bwd_timed(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   int B, int H, int Hkv, int N, int d, int causal, float scale,
+                   void* stream, const void* dout, void* dq, void* dk, void* dv,
+                   int dtype, int accumulate, void* const* marks);
+
 /* Merge of two partial results of the same query rows over disjoint key
  * sets a and b into the result over a u b (DistFlashAttn reviews page,
  * reviews 1 and 4: partial chunk results are combined; BurstAttention

@@ -278,3 +278,25 @@ def test_backward_accumulate_adds_float32_gradients():
         assert g.dtype == torch.float32
         # two identical float32 accumulations: half of the sum is one call's gradient
         check_abs(n + " (sum of 2 calls) / 2", f64(g) / 2, r, 2e-2)
+
+
+# ---------------------------------------------------------------- timed backward
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_bwd_timed_matches_bwd_and_records_marks(dtype):
+    """attn_bwd_timed gives bitwise the same gradients as attn_bwd (the
+    backward has no atomics) and records its two marks in stream order."""
+    B, H, Hkv, N, d = 1, 4, 2, 300, 64
+    q, k, v, do = draw(B, H, Hkv, N, d, seed=41, dtype=dtype)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    o, lse = mi.fwd(qd, kd, vd, True, default_scale(d))
+    ref = mi.bwd(qd, kd, vd, o, lse, dod, True, default_scale(d))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record()
+    got = mi.bwd(qd, kd, vd, o, lse, dod, True, default_scale(d), marks=(ev[1], ev[2]))
+    ev[3].record()
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        assert torch.equal(a, b), name
+    for i in range(3):
+        assert ev[i].elapsed_time(ev[i + 1]) >= 0.0
