@@ -5,7 +5,9 @@ One step = one forward (attn_fwd) and one backward (attn_bwd) of causal
 exact attention over the Llama-7B-shaped 16K workload (B=1, H=Hkv=32,
 N=16384, d=128, bf16, iid N(0,1) synthetic inputs resident in HBM). Prints
 one JSON line. FLOPs: forward 4*B*H*N^2*d halved for the causal mask,
-backward 2.5x the forward.
+backward 2.5x the forward. The line also carries "kvcache": the key/value-
+cache forward (attn_fwd_kvcache) on a decode and a chunked-prefill workload,
+each against its own roofline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--extra]
 """
@@ -77,6 +79,49 @@ def cpu_baseline(workload, heads=3):
             "kind": "oracle", "seconds": round(dt, 2),
             "sample": "%d query heads (B=1, N=%d, d=%d, causal) fwd+bwd in float64; "
                       "FLOPs counted as for the GPU" % (heads, w.N, w.d)}
+
+
+def bench_cache(mi, torch, name, reps=20):
+    """Key/value-cache forward (attn_fwd_kvcache) on one cache workload:
+    event-timed average over `reps` calls, against the HBM roofline.
+    Algorithmic bytes: the valid K and V cache rows once, Q and O once, LSE."""
+    from workloads import CACHE_WORKLOADS, draw_cache_workload
+    w = CACHE_WORKLOADS[name]
+    q, k, v, lens = [t.to("cuda:0") for t in draw_cache_workload(w)]
+    scale = w.d ** -0.5
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=q.device)
+    for _ in range(3):
+        mi.fwd_kvcache(q, k, v, lens, True, scale, 0, out=o, out_lse=lse)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        mi.fwd_kvcache(q, k, v, lens, True, scale, 0, out=o, out_lse=lse)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    L = [int(x) for x in lens.tolist()]
+    kv_bytes = 2.0 * sum(L) * w.Hkv * w.d * 2
+    qo_bytes = 2.0 * w.B * w.Nq * w.H * w.d * 2 + w.B * w.H * w.Nq * 4
+    nbytes = kv_bytes + qo_bytes
+    # visible (query, key) pairs: row i sees L - Nq + i + 1 keys
+    pairs = sum(sum(max(0, Lb - w.Nq + i + 1) for i in range(w.Nq)) for Lb in L) * w.H
+    nflops = 4.0 * w.d * pairs
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tfs = nflops / (ms * 1e-3) / 1e12
+    del q, k, v, lens, o, lse
+    # the bound follows from the arithmetic intensity against the ridge point
+    if nflops / nbytes < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tfs, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tfs / PEAK_BF16_TFLOPS, 4)}
+    return {"workload": "%s: B=%d H=%d Hkv=%d Nq=%d cache=%d d=%d causal, lens %d..%d" % (
+                w.name, w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d, min(L), max(L)),
+            "ms": round(ms, 4), "bytes": int(nbytes), "flops": nflops, "GB_per_s": round(gbs, 1),
+            "tflops": round(tfs, 2), "roofline": roof}
 
 
 def main():
@@ -165,6 +210,7 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dkdv_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
     }
+    out["kvcache"] = {name: bench_cache(mi, torch, name) for name in ("decode16k", "prefill16k")}
     if args.extra:
         extra = {}
         for name in ("llama16k", "gqa64k"):

@@ -49,9 +49,11 @@ def lib():
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, vp, vp, vp, i, i]
     L.attn_bwd_timed.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, vp, vp, vp, i, i, vp]
     L.attn_merge.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+    L.attn_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, i]
     L.attn_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, i, i]
     L.attn_bwd_chunked.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, vp, vp, vp, i, i]
-    for fn in ("attn_fwd", "attn_bwd", "attn_bwd_timed", "attn_merge", "attn_fwd_chunked", "attn_bwd_chunked"):
+    for fn in ("attn_fwd", "attn_bwd", "attn_bwd_timed", "attn_merge", "attn_fwd_chunked", "attn_bwd_chunked",
+               "attn_fwd_kvcache"):
         getattr(L, fn).restype = i
     L.attn_last_error.restype = ctypes.c_char_p
     L.attn_last_error.argtypes = []
@@ -203,6 +205,36 @@ def bwd_chunked(q, k, v, o, lse, dout, nchunks, scale=None):
                                   scale, _stream(q), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
                                   _dtype_code(q), int(nchunks)))
     return dq, dk, dv
+
+
+def fwd_kvcache(q, k_cache, v_cache, k_lens=None, causal=True, scale=None, nsplit=0, out=None, out_lse=None):
+    """Nq new query rows against a key/value cache (attn_fwd_kvcache, bf16).
+
+    q: [B, Nq, H, d]; k_cache, v_cache: [B, Nk, Hkv, d]; k_lens: int32 tensor
+    [B] of valid cache rows on the same device, or None for Nk. Under causal,
+    query row i of batch b sits at position k_lens[b] - Nq + i. nsplit = 0
+    lets the library choose the number of key chunks. Returns (o, lse) with
+    lse [B, H, Nq] float32.
+    """
+    _need(q, "q", torch.bfloat16)
+    if q.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q and the caches must be 4-D [B, rows, heads, d]")
+    B, Nq, H, d = q.shape
+    Nk, Hkv = k_cache.shape[1], k_cache.shape[2]
+    _need(k_cache, "k_cache", torch.bfloat16, (B, Nk, Hkv, d), q.device)
+    _need(v_cache, "v_cache", torch.bfloat16, (B, Nk, Hkv, d), q.device)
+    if k_lens is not None:
+        _need(k_lens, "k_lens", torch.int32, (B,), q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if out_lse is None else out_lse
+    _need(o, "out", q.dtype, q.shape, q.device)
+    _need(lse, "out_lse", torch.float32, (B, H, Nq), q.device)
+    _check(lib().attn_fwd_kvcache(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                  None if k_lens is None else _ptr(k_lens), _ptr(o), _ptr(lse),
+                                  B, H, Hkv, Nq, Nk, d, int(bool(causal)), scale, int(nsplit),
+                                  _stream(q), _dtype_code(q)))
+    return o, lse
 
 
 def balanced_rounds(P):

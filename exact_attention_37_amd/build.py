@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmiattn.so")
 BUILD = os.path.join(PKG, "_build")
 
-SOURCES = ["miattn.cpp", "simt.hip", "prep.hip", "fwd_mfma.hip", "bwd_mfma.hip"]
+SOURCES = ["miattn.cpp", "simt.hip", "prep.hip", "fwd_mfma.hip", "bwd_mfma.hip", "decode.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

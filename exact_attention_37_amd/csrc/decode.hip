@@ -1,0 +1,331 @@
+// Attention of a few new query rows against a key/value cache (decode and
+// chunked prefill), split over key ranges and combined by the logsumexp
+// merge.
+//
+// The operation is the forward pass of exact attention (FlashAttention
+// abstract page) applied at inference time (FlashAttention-2 reviews page,
+// reviewer 2, strengths: the method serves training and inference alike;
+// reviewer 3, point 3), with the key range cut into chunks whose partial
+// results are combined (DistFlashAttn reviews page, reviews 1 and 4;
+// BurstAttention rebuttal page: partial softmax results are merged).
+//
+// Work split (MI355X-specific): with one or a few query rows per head the
+// work is a stream over the cache, bound by HBM bandwidth, and one
+// (batch, K/V head) offers far too little parallelism for 256 CUs. So:
+//  * one single-wave workgroup per (key split, K/V head, block of 32 query
+//    rows, batch); the 32 rows are the (query, head) pairs of one grouped-
+//    query group, so the group's K/V are read from HBM once per split;
+//  * the wave streams 32-key tiles of K and V straight from global memory
+//    into double-buffered LDS (buffer loads with a hardware range check) and
+//    runs the forward's tile step on them: S^T = K Q^T with K rows in sigma32
+//    order so P stays in registers, online softmax with a lazily raised max,
+//    O^T += V^T P^T with V^T from transposing LDS reads;
+//  * it writes its normalised partial output (float32) and logsumexp; a
+//    second kernel merges the splits of every row.
+#include "common.h"
+#include "kernels.h"
+#include "mfma_common.h"
+
+namespace miattn {
+
+namespace {
+
+constexpr int DBC = 32;   // keys per tile
+constexpr int NBUF = 2;   // tiles in LDS: the one being used and the next one in flight
+
+// K and V tiles of 32 keys, row-major; rows padded to D + 32 elements with
+// the 16-byte chunk index XORed by (row / 4) % 4 (the forward's layout).
+// NBUF buffers: the stream keeps NBUF - 1 tiles in flight per wave. (Four
+// buffers, three tiles in flight, measured no faster on the decode workload
+// and slower on chunked prefill, which then fits fewer waves per CU.)
+template <int D>
+struct DecSmem {
+  static constexpr int ROW = D + 32;
+  static constexpr int TILE = DBC * ROW;
+  bf16 k[NBUF][TILE];
+  bf16 v[NBUF][TILE];
+};
+
+// s_waitcnt immediate for "at most n vector-memory loads outstanding"
+// (gfx9 encoding: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt not waited on)
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64) void fwd_split_kernel(SplitParams p) {
+  constexpr int KS = D / 16;   // k-steps of the QK^T product
+  constexpr int DB = D / 32;   // 32-column blocks of O
+  constexpr int ROW = DecSmem<D>::ROW, TILE = DecSmem<D>::TILE;
+  constexpr int TILE_KB = TILE * 2 / 1024;          // 1 KB direct loads per tensor tile
+  static_assert(TILE * 2 % 1024 == 0, "whole 1 KB pieces");
+  constexpr int PIECES = 2 * TILE_KB;               // load instructions per tile (K, V)
+  static_assert(PIECES % NW == 0, "tile loads split evenly over the waves");
+  constexpr int NL = PIECES / NW;                   // per wave
+  __shared__ __attribute__((aligned(16))) DecSmem<D> sm;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+  const int lane = tid & 63;
+  const int g = lane >> 5, n = lane & 31;
+  const int split = blockIdx.x;
+  const int gkv = (int)blockIdx.y % p.Hkv;
+  const int rb = ((int)blockIdx.y / p.Hkv) * NW + wave;   // this wave's block of 32 rows
+  const int b = blockIdx.z;
+
+  // ---- the wave's 32 columns: row r = 32 rb + n of the group = (query i, head h)
+  const int M = p.Nq * p.G;
+  const int r = 32 * rb + n;
+  const bool valid = r < M;
+  const int rc = valid ? r : M - 1;
+  const int i = rc / p.G, h = gkv * p.G + rc % p.G;
+  const int L = p.k_lens ? min(max(p.k_lens[b], 0), p.Nk) : p.Nk;   // valid cache rows
+  const int qpos = L - p.Nq + i;                  // position of query i in the sequence
+
+  const long long qrs = (long long)p.H * D, krs = (long long)p.Hkv * D;
+  const bf16* Q = (const bf16*)p.q + ((long long)b * p.Nq) * qrs;
+  const bf16* K = (const bf16*)p.k + ((long long)b * p.Nk) * krs + (long long)gkv * D;
+  const bf16* V = (const bf16*)p.v + ((long long)b * p.Nk) * krs + (long long)gkv * D;
+
+  float c = fabsf(p.scale) * kLog2e;
+  float qsign = p.scale < 0.f ? -1.f : 1.f;
+  if (p.scale == 0.f) { c = 1.f; qsign = 0.f; }
+
+  // Q^T operand (B of S^T = K Q^T): lane (g, n) holds Q[i][h][16 ks + 8 g .. +8]
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    bf16x8 x = *(const bf16x8*)(Q + (long long)i * qrs + (long long)h * D + ks * 16 + g * 8);
+    if (qsign != 1.f) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = (bf16)((float)x[e] * qsign);
+    }
+    qf[ks] = x;
+  }
+  wait_global_loads();
+
+  // ---- this split's keys [k_lo, k_hi)
+  const int k_lo = split * p.chunk;
+  const int k_hi = min(L, k_lo + p.chunk);
+  const int ntile = k_hi > k_lo ? (k_hi - k_lo + DBC - 1) / DBC : 0;
+
+  // Direct loads: piece s = wave * NL + j of a tile (K: s < TILE_KB, then V)
+  // covers tensor tile bytes [(s % TILE_KB) KB, +1 KB); lane l fills 16 bytes
+  // at 16 l: tile row rr, logical chunk ch (padding from chunk 0), read from
+  // byte loff[j] = 2 (rr * row stride + 8 ch) past the tile's first key. Keys
+  // past the cache's last row read as zeros (buffer range check); keys past
+  // k_hi are masked.
+  uint32_t loff[NL];
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    const int off = ((wave * NL + j) % TILE_KB) * 1024 + 16 * lane;
+    const int rr = off / (ROW * 2), pch = (off % (ROW * 2)) / 16;
+    const int col = pch < D / 8 ? ((pch ^ ((rr >> 2) & 3)) << 3) : 0;
+    loff[j] = (uint32_t)(rr * krs + col) * 2u;
+  }
+  const uint32_t kbytes = (uint32_t)(((p.Nk - 1) * krs + D) * 2);
+  const u32x4 rk = rsrc_words(K, kbytes), rv = rsrc_words(V, kbytes);
+  auto load_tile = [&](int buf, int key0) {
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int s_ = wave * NL + j;                // wave-uniform
+      const bool is_v = s_ >= TILE_KB;
+      buffer_load_lds16_async(is_v ? rv : rk, loff[j], (uint32_t)(key0 * krs) * 2u,
+                              lds_addr((is_v ? sm.v[buf] : sm.k[buf]) + (s_ % TILE_KB) * 512));
+    }
+  };
+
+  // per-lane LDS read offsets (elements), as in the forward kernel
+  const int srow = sigma32(n), sf = (srow >> 2) & 3;
+  int rd_s[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) rd_s[e] = srow * ROW + (((2 * e + g) ^ sf) << 3);
+  int rd_t[2];
+  {
+    const int G4 = lane >> 4, j = lane & 15, hf = G4 & 1;
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int r_ = 8 * g + 4 * rd + (j >> 2);
+      const int chunk = (2 * hf + ((j & 3) >> 1)) ^ ((2 * g + rd) & 3);
+      rd_t[rd] = r_ * ROW + (chunk << 3) + 4 * (j & 1);
+    }
+  }
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+
+  static_assert(NBUF <= 4 && (NBUF - 2) * NL < 64, "vmcnt range");
+  for (int t = 0; t < NBUF - 1 && t < ntile; ++t) load_tile(t, k_lo + t * DBC);
+  for (int t = 0; t < ntile; ++t) {
+    const int buf = t % NBUF;
+    const int key0 = k_lo + t * DBC;
+    // wait for tile t; the (at most NBUF - 2) tiles issued after it may stay in flight
+    const int later = min(NBUF - 2, ntile - 1 - t);
+    if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NL));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NL));
+    else wait_global_loads();
+    // every wave's pieces of tile t are in LDS, and every wave is done with
+    // the buffer that the next loads overwrite
+    __syncthreads();
+    if (t + NBUF - 1 < ntile) load_tile((t + NBUF - 1) % NBUF, key0 + (NBUF - 1) * DBC);
+    const bf16* kt = sm.k[buf];
+    const bf16* vt = sm.v[buf];
+
+    // ---- S^T = K Q^T: register r of lane (g, n) <-> key key0 + sigma_row(g, r)
+    f32x16 s = f32x16{};
+    pipelined_products<KS, 4>(
+        [&](int ks) { return lds_read16(kt + rd_s[ks & 1], (ks >> 1) * 32); },
+        [&](int ks, bf16x8 a) { s = mfma32(a, qf[ks], s); });
+
+    // ---- mask: keys past k_hi, and (causal) keys after the query's position
+    int thr = k_hi - 1 - key0;
+    if (CAUSAL) thr = min(thr, qpos - key0);
+    if (__builtin_amdgcn_ballot_w64(thr < DBC - 1) != 0) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr)
+        if (sigma_row(g, rr) > thr) s[rr] = -INFINITY;
+    }
+
+    // ---- online softmax; rows that have seen no key yet keep m = -inf and p = 0
+    float mx = s[0];
+#pragma unroll
+    for (int rr = 1; rr < 16; ++rr) mx = fmaxf(mx, s[rr]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mt = mx * c;
+    const bool raise = mt > m + 8.f;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      const float mnew = raise ? mt : m;
+      const float alpha = exp2f(m - mnew);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) acc[db][rr] *= alpha;
+      m = mnew;
+    }
+    const float mneg = m == -INFINITY ? 0.f : -m;
+    bf16x8 pf[2];
+    float lsum = 0.f;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      bf16x8 x;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(s[half * 8 + e], c, mneg));
+        lsum += pv;
+        x[e] = (bf16)pv;
+      }
+      pf[half] = x;
+    }
+    l += lsum;
+
+    // ---- O^T += V^T P^T: step i = (kq, db)
+    pipelined_products<2 * DB, 4>(
+        [&](int st) {
+          const int kq = st / DB, db = st % DB;
+          const bf16x4 r0 = lds_read_tr4(vt + rd_t[0] + 16 * kq * ROW + 32 * db);
+          const bf16x4 r1 = lds_read_tr4(vt + rd_t[1] + 16 * kq * ROW + 32 * db);
+          return bf16x8{r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+        },
+        [&](int st, bf16x8 a) { acc[st % DB] = mfma32(a, pf[st / DB], acc[st % DB]); });
+  }
+
+  // ---- partial result of this split: normalised O (float32) and logsumexp;
+  // a row without visible keys here gives (0, -inf), the merge's identity
+  const float lt = l + __shfl_xor(l, 32);
+  if (valid) {
+    const long long row = ((long long)split * p.B + b) * p.Nq + i;   // [split][b][i]
+    float* O = p.o_part + (row * p.H + h) * D;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int run = 0; run < 4; ++run) {
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = acc[db][run * 4 + e] * inv;
+        *(f32x4*)(O + db * 32 + run * 8 + g * 4) = x;
+      }
+    if (g == 0)
+      p.lse_part[(((long long)split * p.B + b) * p.H + h) * p.Nq + i] =
+          lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+  }
+}
+
+// Merge of the splits of every (b, query, head) row: with M the largest
+// partial logsumexp, lse = M + ln sum_s e^(lse_s - M) and
+// o = sum_s e^(lse_s - lse) o_s; a row with no visible key gives o = 0,
+// lse = -inf. One wave per row: lane s < nsplit reads split s's logsumexp
+// (64 splits per pass), the wave reduces them, and lane t then accumulates
+// columns t, t + 64, ... over the splits with the weights broadcast from
+// the lane that holds them.
+template <int D>
+__global__ __launch_bounds__(64) void split_merge_kernel(SplitParams p) {
+  const int lane = threadIdx.x;
+  const int row = blockIdx.x;                     // (b, i, h), h fastest
+  const int h = row % p.H, i = (row / p.H) % p.Nq, b = row / (p.H * p.Nq);
+  const long long ps = (long long)p.B * p.Nq * p.H;   // rows per split
+  auto lse_at = [&](int s) { return p.lse_part[(((long long)s * p.B + b) * p.H + h) * p.Nq + i]; };
+  float mx = -INFINITY;
+  for (int s = lane; s < p.nsplit; s += 64) mx = fmaxf(mx, lse_at(s));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  float tot = 0.f;
+  if (mx != -INFINITY)
+    for (int s = lane; s < p.nsplit; s += 64) tot += expf(lse_at(s) - mx);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
+  const float lse = mx == -INFINITY ? -INFINITY : mx + logf(tot);
+  constexpr int CPL = D / 64;                     // columns per lane
+  float acc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+  if (mx != -INFINITY) {
+    for (int s0 = 0; s0 < p.nsplit; s0 += 64) {
+      const int sl = s0 + lane;
+      const float w_l = sl < p.nsplit ? expf(lse_at(sl) - lse) : 0.f;
+      const int n = min(64, p.nsplit - s0);
+      for (int t = 0; t < n; ++t) {
+        const float w = __shfl(w_l, t);
+        const float* src = p.o_part + ((s0 + t) * ps + row) * D + lane;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[c] += w * src[64 * c];
+      }
+    }
+  }
+  bf16* O = (bf16*)p.o + (((long long)b * p.Nq + i) * p.H + h) * D + lane;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) O[64 * c] = (bf16)acc[c];
+  if (lane == 0) p.lse[((long long)b * p.H + h) * p.Nq + i] = lse;
+}
+
+template <int D, int NW>
+void launch_split_nw(const SplitParams& p, hipStream_t s) {
+  const int rbs = (p.Nq * p.G + 31) / 32;
+  const dim3 grid(p.nsplit, p.Hkv * ((rbs + NW - 1) / NW), p.B);
+  if (p.causal)
+    hipLaunchKernelGGL((fwd_split_kernel<D, true, NW>), grid, dim3(NW * 64), 0, s, p);
+  else
+    hipLaunchKernelGGL((fwd_split_kernel<D, false, NW>), grid, dim3(NW * 64), 0, s, p);
+}
+
+template <int D>
+hipError_t launch_split_d(const SplitParams& p, hipStream_t s) {
+  // waves per workgroup = blocks of 32 rows sharing each K/V tile
+  const int rbs = (p.Nq * p.G + 31) / 32;
+  if (rbs >= 4) launch_split_nw<D, 4>(p, s);
+  else if (rbs >= 2) launch_split_nw<D, 2>(p, s);
+  else launch_split_nw<D, 1>(p, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((split_merge_kernel<D>), dim3(p.B * p.Nq * p.H), dim3(64), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_split(const SplitParams& p, hipStream_t s) {
+  return p.d == 128 ? launch_split_d<128>(p, s) : launch_split_d<64>(p, s);
+}
+
+}  // namespace miattn

@@ -26,6 +26,28 @@ hipError_t launch_merge(const void* o_a, const float* lse_a, const void* o_b, co
                         void* o, float* lse, int B, int H, int N, int d, int row0, int nrows,
                         int ta, int tb, int to, hipStream_t s);
 
+// Query rows against a key/value cache, split over key ranges (bf16).
+// q, o: [B, Nq, H, d]; k, v: [B, Nk, Hkv, d]; lse: [B, H, Nq]; k_lens: [B]
+// valid cache rows per batch entry, or null for Nk. Causal: query i of batch
+// b sits at position k_lens[b] - Nq + i. Split s covers keys
+// [s * chunk, (s + 1) * chunk); its partial output and logsumexp go to
+// o_part [nsplit, B, Nq, H, d] and lse_part [nsplit, B, H, Nq] (float32)
+// before the merge writes o and lse.
+struct SplitParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int* k_lens;
+  void* o;
+  float* lse;
+  float* o_part;
+  float* lse_part;
+  int B, H, Hkv, G, Nq, Nk, d, causal;
+  float scale;
+  int nsplit, chunk;
+};
+hipError_t launch_fwd_split(const SplitParams& p, hipStream_t s);
+
 // dst[i] = (bf16 or float) src[i] for n float32 elements.
 hipError_t launch_convert(const float* src, void* dst, long long n, int dtype, hipStream_t s);
 

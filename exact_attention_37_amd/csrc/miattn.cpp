@@ -2,6 +2,7 @@
 // management and the chunk-pair driver. No entry point synchronises the host.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -182,6 +183,70 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (overlap(ro, rl)) return fail(MIATTN_EINVAL, "o and lse must not overlap");
   Params p = make_params(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale);
   if ((st = launch_status(fwd_block(p, dtype, dtype == MIATTN_F32, (hipStream_t)stream), "attn_fwd"))) return st;
+  return ok();
+}
+
+int attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, const int* k_lens, void* o,
+                     float* lse, int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale, int nsplit,
+                     void* stream, int dtype) {
+  int st = check_common(B, H, Hkv, Nk, d, dtype);
+  if (st) return st;
+  if (Nq < 1) return fail(MIATTN_EINVAL, "Nq must be >= 1");
+  if ((long long)B * H * Nq >= (1LL << 31) || (long long)(Nq + 64) * H * d >= (1LL << 31))
+    return fail(MIATTN_EUNSUPPORTED, "problem too large for 32-bit row indexing");
+  if (dtype != MIATTN_BF16) return fail(MIATTN_EUNSUPPORTED, "attn_fwd_kvcache supports MIATTN_BF16 only");
+  if ((st = check_ptrs({q, k_cache, v_cache, o, lse}))) return st;
+  if (k_lens && (reinterpret_cast<uintptr_t>(k_lens) & 3u)) return fail(MIATTN_EINVAL, "k_lens not 4-byte aligned");
+  if (causal != 0 && causal != 1) return fail(MIATTN_EINVAL, "causal must be 0 or 1");
+  if (!std::isfinite(scale)) return fail(MIATTN_EINVAL, "scale must be finite");
+  if (nsplit < 0 || nsplit > 1024) return fail(MIATTN_EINVAL, "nsplit must be in [0, 1024]");
+  const long long qb = (long long)B * Nq * H * d * 2, kb = (long long)B * Nk * Hkv * d * 2;
+  const Range ro = span(o, qb), rl = span(lse, (long long)B * H * Nq * 4);
+  for (Range r : {span(q, qb), span(k_cache, kb), span(v_cache, kb)})
+    if (overlap(ro, r) || overlap(rl, r)) return fail(MIATTN_EINVAL, "o/lse must not alias q, k_cache or v_cache");
+  if (overlap(ro, rl)) return fail(MIATTN_EINVAL, "o and lse must not overlap");
+
+  // Splits: enough single-wave workgroups to keep every CU streaming (about
+  // 8 per CU), each split at least 256 keys; keys per split a multiple of the
+  // 32-key tile.
+  const int G = H / Hkv;
+  const long long groups = (long long)B * Hkv * ((Nq * G + 31) / 32);
+  if (nsplit == 0) {
+    const long long want = (2048 + groups - 1) / groups;
+    const long long most = (Nk + 255) / 256;
+    nsplit = (int)std::max(1LL, std::min(want, most));
+  }
+  int chunk = (Nk + nsplit - 1) / nsplit;
+  chunk = (chunk + 31) / 32 * 32;
+  nsplit = (Nk + chunk - 1) / chunk;     // no empty trailing split
+
+  hipStream_t s = (hipStream_t)stream;
+  Scratch scratch(s);
+  const long long rows = (long long)B * Nq * H;
+  float* o_part = (float*)scratch.get((size_t)nsplit * rows * d * 4);
+  float* lse_part = (float*)scratch.get((size_t)nsplit * rows * 4);
+  if (!o_part || !lse_part) return fail(MIATTN_ENOMEM, "hipMallocAsync failed for the split partials");
+  miattn::SplitParams p{};
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.k_lens = k_lens;
+  p.o = o;
+  p.lse = lse;
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.B = B;
+  p.H = H;
+  p.Hkv = Hkv;
+  p.G = G;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.d = d;
+  p.causal = causal;
+  p.scale = scale;
+  p.nsplit = nsplit;
+  p.chunk = chunk;
+  if ((st = launch_status(miattn::launch_fwd_split(p, s), "attn_fwd_kvcache"))) return st;
   return ok();
 }
 

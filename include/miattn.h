@@ -71,6 +71,36 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int Hkv, int N, int d, int causal, float scale,
              void* stream, int dtype);
 
+/* Forward pass of Nq new query rows against a key/value cache: decoding
+ * (Nq = 1) and chunked prefill (Nq > 1) at inference time, which the
+ * FlashAttention-2 reviews page names as a use of the method (reviewer 2,
+ * strengths; reviewer 3, point 3). The cache's key range is cut into nsplit
+ * chunks processed in parallel, and their partial results are combined with
+ * the logsumexp merge of attn_merge (DistFlashAttn reviews page, reviews 1
+ * and 4: partial results over key chunks are combined). Writes o and lse.
+ *   q, o          : [B, Nq, H, d] bf16 (o is overwritten)
+ *   k_cache, v_cache: [B, Nk, Hkv, d] bf16, Nk = cache capacity in rows
+ *   k_lens        : device int32 [B], the number of valid cache rows of each
+ *                   batch entry (values are clamped to [0, Nk]), or NULL for
+ *                   Nk everywhere. Rows at or past k_lens[b] are never read
+ *                   into the result.
+ *   lse           : [B, H, Nq] float32
+ *   causal        : 0 = every query row sees all valid cache rows; 1 = query
+ *                   row i of batch b sits at position k_lens[b] - Nq + i and
+ *                   sees cache rows j <= that position (the new rows are the
+ *                   last Nq positions of the sequence). A row that sees no
+ *                   key gets o = 0 and lse = -inf.
+ *   nsplit        : number of key chunks, 1..1024, or 0 to let the library
+ *                   choose (about 2048 single-wave workgroups in all, each
+ *                   chunk at least 256 keys). Chunks are rounded up to a
+ *                   multiple of 32 keys, which can lower the count.
+ *   dtype         : MIATTN_BF16 only (MIATTN_EUNSUPPORTED otherwise).
+ * Scratch: float32 partials, nsplit * B * Nq * H * (d + 1) * 4 bytes.
+ * o and lse must not alias q, k_cache or v_cache. */
+int attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, const int* k_lens,
+                     void* o, float* lse, int B, int H, int Hkv, int Nq, int Nk, int d, int causal,
+                     float scale, int nsplit, void* stream, int dtype);
+
 /* Backward pass: from q, k, v, the forward's o and lse, and dout = dL/dO,
  * produces dq, dk, dv without forming the N x N matrix. The forward is not
  * re-run: P is rebuilt tile by tile from the saved lse (DistFlashAttn

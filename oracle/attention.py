@@ -42,6 +42,7 @@ import numpy as np
 __all__ = [
     "scores", "forward", "backward", "merge", "tiled_forward",
     "forward_rows", "backward_dq_rows", "backward_dkdv_rows", "probs",
+    "forward_kvcache",
 ]
 
 
@@ -135,6 +136,36 @@ def forward(q, k, v, causal, scale, q_offset=0, k_offset=0, row_block=512):
                 p, l = _softmax_rows(s)
                 o[b, r0:r1, h] = p @ v[b, :, g]
                 lse[b, h, r0:r1] = l
+    return o, lse
+
+
+def forward_kvcache(q, k, v, k_lens, causal, scale):
+    """O and LSE of Nq new query rows against a key/value cache.
+
+    Inference use of the method (FlashAttention-2 reviews page, reviewer 2,
+    strengths; reviewer 3, point 3). q: [B, Nq, H, d]; k, v: [B, Nk, Hkv, d];
+    k_lens: the number of valid cache rows of each batch entry (None: Nk),
+    clamped to [0, Nk]. Batch entry b attends to cache rows [0, L_b) only.
+    Reading where the pages are silent: the new rows are the last Nq
+    positions of the sequence, so under the causal mask query row i sits at
+    position L_b - Nq + i and sees cache rows j <= that position. A row that
+    sees no key gets o = 0 and lse = -inf. Returns o [B, Nq, H, d] and
+    lse [B, H, Nq], float64.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    B, Nq, H, d = q.shape
+    Nk = k.shape[1]
+    o = np.zeros((B, Nq, H, d))
+    lse = np.full((B, H, Nq), -np.inf)
+    for b in range(B):
+        L = Nk if k_lens is None else int(min(max(int(k_lens[b]), 0), Nk))
+        if L == 0:
+            continue
+        ob, lb = forward(q[b:b + 1], k[b:b + 1, :L], v[b:b + 1, :L], causal, scale, q_offset=L - Nq)
+        o[b] = ob[0]
+        lse[b] = lb[0]
     return o, lse
 
 

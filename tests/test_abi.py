@@ -122,3 +122,33 @@ def test_chunk_schedule_rejects_bad_counts():
     assert L.attn_chunk_schedule(3, arr, arr, arr, 64) == -1
     assert L.attn_chunk_schedule(0, arr, arr, arr, 64) == -1
     assert L.attn_chunk_schedule(8, arr, arr, arr, 10) == -1
+
+
+def kv_call(**kw):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, lens=0, o=FAKE * 4, lse=FAKE * 5, B=2, H=8, Hkv=2, Nq=1, Nk=100,
+             d=128, causal=1, scale=0.1, nsplit=0, dtype=1)
+    a.update(kw)
+    L = mi.lib()
+    return L.attn_fwd_kvcache(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["lens"]) if a["lens"] else None,
+                              vp(a["o"]), vp(a["lse"]), a["B"], a["H"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
+                              a["causal"], a["scale"], a["nsplit"], None, a["dtype"])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(q=0), 1, "null"),
+    (dict(v=FAKE * 3 + 8), 1, "aligned"),
+    (dict(lens=FAKE * 6 + 2), 1, "k_lens"),
+    (dict(Nq=0), 1, "Nq"),
+    (dict(Nk=0), 1, ">= 1"),
+    (dict(H=6, Hkv=4), 1, "multiple"),
+    (dict(d=96), 2, "64 or 128"),
+    (dict(dtype=0), 2, "BF16"),
+    (dict(causal=3), 1, "causal"),
+    (dict(nsplit=-1), 1, "nsplit"),
+    (dict(nsplit=5000), 1, "nsplit"),
+    (dict(scale=float("nan")), 1, "finite"),
+    (dict(o=FAKE * 2), 1, "alias"),
+])
+def test_kvcache_rejects_bad_arguments(kw, code, msg):
+    assert kv_call(**kw) == code
+    assert msg in mi.lib().attn_last_error().decode()

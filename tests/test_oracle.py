@@ -344,3 +344,100 @@ def test_workload_draws_are_seeded_and_rounded():
     # the oracle consumes the rounded values exactly
     q = as_f64(a[0])
     assert np.array_equal(q, a[0].float().double().numpy())
+
+
+# ---------------------------------------------------------------- key/value cache (decode, chunked prefill)
+
+def _kvcache_by_loops(q, k, v, k_lens, causal, scale):
+    """The cache case written out element by element with math.exp: batch b
+    uses cache rows [0, L_b); query row i sits at position L_b - Nq + i."""
+    B, Nq, H, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    G = H // Hkv
+    o = np.zeros((B, Nq, H, d))
+    lse = np.full((B, H, Nq), -np.inf)
+    for b in range(B):
+        L = Nk if k_lens is None else min(max(int(k_lens[b]), 0), Nk)
+        for i in range(Nq):
+            pos = L - Nq + i
+            for h in range(H):
+                g = h // G
+                keys = [j for j in range(L) if not causal or j <= pos]
+                if not keys:
+                    continue
+                sc = [scale * sum(float(q[b, i, h, c]) * float(k[b, j, g, c]) for c in range(d)) for j in keys]
+                mx = max(sc)
+                w = [math.exp(x - mx) for x in sc]
+                tot = sum(w)
+                lse[b, h, i] = mx + math.log(tot)
+                for c in range(d):
+                    o[b, i, h, c] = sum(wj * float(v[b, j, g, c]) for wj, j in zip(w, keys)) / tot
+    return o, lse
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_kvcache_matches_elementwise_loops(causal):
+    q, k, v, _ = draw(2, 4, 2, 7, 3, seed=71, dtype=torch.float64)
+    q = q[:, :3]                                   # Nq = 3 new rows, Nk = 7 cache rows
+    lens = [7, 4]
+    o, lse = oracle.forward_kvcache(q.numpy(), k.numpy(), v.numpy(), lens, causal, 0.7)
+    ro, rl = _kvcache_by_loops(q.numpy(), k.numpy(), v.numpy(), lens, causal, 0.7)
+    assert np.max(np.abs(o - ro)) < 1e-12
+    assert np.max(np.abs(lse - rl)) < 1e-12
+
+
+def test_kvcache_square_case_is_causal_attention():
+    q, k, v, _ = draw(1, 2, 1, 9, 4, seed=72, dtype=torch.float64)
+    o, lse = oracle.forward_kvcache(q.numpy(), k.numpy(), v.numpy(), None, True, 0.5)
+    ro, rl = oracle.forward(q.numpy(), k.numpy(), v.numpy(), True, 0.5)
+    assert np.max(np.abs(o - ro)) < 1e-13 and np.max(np.abs(lse - rl)) < 1e-13
+
+
+def test_kvcache_single_new_row_sees_the_whole_cache():
+    # the last position sees every valid cache row, so causal = non-causal
+    q, k, v, _ = draw(3, 4, 2, 11, 8, seed=73, dtype=torch.float64)
+    q = q[:, :1]
+    lens = [11, 6, 1]
+    a = oracle.forward_kvcache(q.numpy(), k.numpy(), v.numpy(), lens, True, 0.3)
+    b = oracle.forward_kvcache(q.numpy(), k.numpy(), v.numpy(), lens, False, 0.3)
+    assert np.max(np.abs(a[0] - b[0])) < 1e-14 and np.max(np.abs(a[1] - b[1])) < 1e-14
+    # a single valid key returns its value exactly, with lse = its score
+    assert np.max(np.abs(a[0][2, 0] - np.repeat(v.numpy()[2, 0], 2, axis=0))) < 1e-14
+    s0 = 0.3 * np.einsum("hd,hd->h", q.numpy()[2, 0], np.repeat(k.numpy()[2, 0], 2, axis=0))
+    assert np.max(np.abs(a[1][2, :, 0] - s0)) < 1e-13
+
+
+def test_kvcache_ignores_rows_past_the_valid_length():
+    q, k, v, _ = draw(2, 2, 2, 10, 4, seed=74, dtype=torch.float64)
+    q = q[:, :2]
+    lens = [6, 3]
+    a = oracle.forward_kvcache(q.numpy(), k.numpy(), v.numpy(), lens, True, 0.5)
+    k2, v2 = k.numpy().copy(), v.numpy().copy()
+    k2[0, 6:] = 100.0
+    v2[1, 3:] = -50.0
+    b = oracle.forward_kvcache(q.numpy(), k2, v2, lens, True, 0.5)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_kvcache_rows_without_keys_are_the_merge_identity():
+    # L = 2 cache rows and Nq = 4 new rows: rows 0 and 1 sit at positions -2, -1
+    q, k, v, _ = draw(1, 2, 2, 4, 4, seed=75, dtype=torch.float64)
+    o, lse = oracle.forward_kvcache(q.numpy(), k.numpy(), v.numpy(), [2], True, 0.5)
+    assert np.all(o[0, :2] == 0.0) and np.all(np.isneginf(lse[0, :, :2]))
+    assert np.all(np.isfinite(lse[0, :, 2:]))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_kvcache_key_splits_merge_to_the_whole(causal):
+    # the split-KV scheme: partials over [0, s) and [s, L) merged by LSE
+    q, k, v, _ = draw(1, 4, 2, 13, 8, seed=76, dtype=torch.float64)
+    q = q[:, :2]
+    L, cut = 13, 5
+    full = oracle.forward_kvcache(q.numpy(), k.numpy(), v.numpy(), [L], causal, 0.4)
+    qpos = L - 2 + np.arange(2)
+    parts = []
+    for lo, hi in ((0, cut), (cut, L)):
+        parts.append(oracle.forward(q.numpy(), k.numpy()[:, lo:hi], v.numpy()[:, lo:hi], causal, 0.4,
+                                    q_offset=int(qpos[0]), k_offset=lo))
+    o, lse = oracle.merge(parts[0][0], parts[0][1], parts[1][0], parts[1][1])
+    assert np.max(np.abs(o - full[0])) < 1e-13 and np.max(np.abs(lse - full[1])) < 1e-13

@@ -20,6 +20,8 @@ def _pins():
     yield lambda: T.test_backward_identities(True)
     yield lambda: T.test_merge_of_two_key_chunks_equals_full(True)
     yield lambda: T.test_tiled_online_softmax_equals_naive(True, 13, 7)
+    yield lambda: T.test_kvcache_matches_elementwise_loops(True)
+    yield lambda: T.test_kvcache_ignores_rows_past_the_valid_length()
 
 
 def _caught():
@@ -61,7 +63,26 @@ def _merge_swapped_weights(o_a, lse_a, o_b, lse_b):
     return _orig_merge(o_b, lse_a, o_a, lse_b)
 
 
+def _kvcache_top_left(q, k, v, k_lens, causal, scale):
+    # new rows aligned to the start of the cache instead of its end
+    q = np.asarray(q, np.float64)
+    B, Nq = q.shape[:2]
+    o = np.zeros(q.shape)
+    lse = np.full((B, q.shape[2], Nq), -np.inf)
+    for b in range(B):
+        L = k.shape[1] if k_lens is None else int(k_lens[b])
+        ob, lb = A.forward(q[b:b + 1], k[b:b + 1, :L], v[b:b + 1, :L], causal, scale, q_offset=0)
+        o[b], lse[b] = ob[0], lb[0]
+    return o, lse
+
+
+def _kvcache_whole_cache(q, k, v, k_lens, causal, scale):
+    # valid lengths ignored: every cache row attended to
+    return _orig_kvcache(q, k, v, None, causal, scale)
+
+
 _orig_scores = A.scores
+_orig_kvcache = A.forward_kvcache
 _orig_softmax = A._softmax_rows
 _orig_merge = A.merge
 
@@ -71,6 +92,8 @@ MUTATIONS = {
     "lse_missing_max": ("_softmax_rows", _lse_without_max),
     "no_max_subtraction": ("_softmax_rows", _softmax_no_max_subtraction),
     "merge_weights_swapped": ("merge", _merge_swapped_weights),
+    "kvcache_top_left_alignment": ("forward_kvcache", _kvcache_top_left),
+    "kvcache_lengths_ignored": ("forward_kvcache", _kvcache_whole_cache),
 }
 
 
@@ -78,9 +101,9 @@ MUTATIONS = {
 def test_pins_catch_planted_mistake(name, monkeypatch):
     attr, fn = MUTATIONS[name]
     monkeypatch.setattr(A, attr, fn)
-    if attr == "merge":
+    if attr in ("merge", "forward_kvcache"):   # re-exported by the package
         import oracle
-        monkeypatch.setattr(oracle, "merge", fn)
+        monkeypatch.setattr(oracle, attr, fn)
     assert _caught(), "planted mistake %r passed every pin" % name
 
 

@@ -21,6 +21,14 @@ in for real activations -- the pages' datasets and weights are not used):
 Draw order (fixed): ``torch.Generator('cpu').manual_seed(seed)``, then
 ``randn`` in float32 for Q, K, V, dO at their [B, N, heads, d] shapes, then a
 round-to-nearest-even cast to the compute dtype.
+
+Key/value-cache workloads (decode and chunked prefill, inference use of the
+method): ``decode16k`` -- 16 sequences, 32 query heads over 8 K/V heads
+(Llama-style GQA), d=128, one new row per sequence against a 16K-row cache
+whose valid lengths are drawn uniformly from [8K, 16K]; ``prefill16k`` -- 4
+sequences appending 128 rows each to the same kind of cache. Draw order:
+Q [B, Nq, H, d], K cache, V cache [B, Nk, Hkv, d] as above, then the lengths
+with ``torch.randint`` from the same generator.
 """
 from __future__ import annotations
 
@@ -82,6 +90,44 @@ def draw_workload(w: Workload, seed: int | None = None, N: int | None = None):
     """Inputs for workload ``w`` (optionally at a shorter sequence length)."""
     return draw(w.B, w.H, w.Hkv, w.N if N is None else N, w.d,
                 w.seed if seed is None else seed, w.torch_dtype)
+
+
+@dataclass(frozen=True)
+class CacheWorkload:
+    name: str
+    B: int
+    H: int
+    Hkv: int
+    Nq: int                    # new query rows per sequence
+    Nk: int                    # cache capacity (rows)
+    d: int
+    min_len: int               # valid cache lengths drawn from [min_len, Nk]
+    seed: int = 1
+
+
+CACHE_WORKLOADS = {
+    "decode16k": CacheWorkload("decode16k", 16, 32, 8, 1, 16384, 128, 8192, seed=6),
+    "prefill16k": CacheWorkload("prefill16k", 4, 32, 8, 128, 16384, 128, 8192, seed=7),
+}
+
+
+def draw_cache(B: int, H: int, Hkv: int, Nq: int, Nk: int, d: int, seed: int,
+               min_len: int | None = None, dtype: torch.dtype = torch.bfloat16):
+    """Return (q [B, Nq, H, d], k_cache, v_cache [B, Nk, Hkv, d], lens [B] int32)
+    as CPU tensors; lens uniform in [min_len, Nk] (all Nk if min_len is None)."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    q = torch.randn((B, Nq, H, d), generator=g, dtype=torch.float32).to(dtype)
+    k = torch.randn((B, Nk, Hkv, d), generator=g, dtype=torch.float32).to(dtype)
+    v = torch.randn((B, Nk, Hkv, d), generator=g, dtype=torch.float32).to(dtype)
+    if min_len is None:
+        lens = torch.full((B,), Nk, dtype=torch.int32)
+    else:
+        lens = torch.randint(min_len, Nk + 1, (B,), generator=g, dtype=torch.int64).to(torch.int32)
+    return q, k, v, lens
+
+
+def draw_cache_workload(w: CacheWorkload):
+    return draw_cache(w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d, w.seed, w.min_len)
 
 
 def as_f64(t: torch.Tensor) -> np.ndarray:
