@@ -27,7 +27,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 # rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; calibrated against a plain
 # 1 GiB device copy in the same process), valid only for the kernel sources
 # whose SHA-1 is recorded with it (profiles/llama16k_causal_bf16_traffic.md).
-DKDV_TRAFFIC = {"sources_sha1": "d0dc0ac248101195f6a827495d4eb0fa049a31b2", "bytes": 2849158352}   # fetch 2.581 GB + write 0.268 GB
+DKDV_TRAFFIC = {"sources_sha1": "fe856ed0aa36b4a988d13916c04d4c778d3f54f1", "bytes": 2849749894}   # fetch 2.581 GB + write 0.269 GB
 DKDV_SOURCES = ("exact_attention_37_amd/csrc/bwd_mfma.hip", "exact_attention_37_amd/csrc/mfma_common.h",
                 "exact_attention_37_amd/csrc/common.h")
 
@@ -124,6 +124,36 @@ def bench_cache(mi, torch, name, reps=20):
             "tflops": round(tfs, 2), "roofline": roof}
 
 
+def bench_window(mi, torch, q, k, v, do, w, window, reps=10):
+    """Causal sliding-window fwd+bwd (attn_fwd_window / attn_bwd_window) on
+    the main workload's tensors. FLOPs count the visible pairs only: row i
+    sees min(i + 1, window) keys; backward 2.5x forward."""
+    scale = w.d ** -0.5
+    for _ in range(2):
+        o, lse = mi.fwd(q, k, v, True, scale, window=window)
+        mi.bwd(q, k, v, o, lse, do, True, scale, window=window)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    f_ms = b_ms = 0.0
+    for _ in range(reps):
+        e[0].record()
+        o, lse = mi.fwd(q, k, v, True, scale, window=window)
+        e[1].record()
+        mi.bwd(q, k, v, o, lse, do, True, scale, window=window)
+        e[2].record()
+        torch.cuda.synchronize()
+        f_ms += e[0].elapsed_time(e[1]) / reps
+        b_ms += e[1].elapsed_time(e[2]) / reps
+    W, N = window, w.N
+    pairs = (W * (W + 1) // 2 + (N - W) * W) if N > W else N * (N + 1) // 2
+    ff = 4.0 * w.B * w.H * w.d * pairs
+    fb = 2.5 * ff
+    tf = (ff + fb) / ((f_ms + b_ms) * 1e-3) / 1e12
+    return {"workload": "%s with a causal sliding window of %d keys" % (w.name, W),
+            "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4), "tflops": round(tf, 2),
+            "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -210,6 +240,7 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dkdv_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
     }
+    out["window"] = bench_window(mi, torch, q, k, v, do, w, 4096)
     out["kvcache"] = {name: bench_cache(mi, torch, name) for name in ("decode16k", "prefill16k")}
     if args.extra:
         extra = {}

@@ -48,12 +48,14 @@ def lib():
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i]
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, vp, vp, vp, i, i]
     L.attn_bwd_timed.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, vp, vp, vp, i, i, vp]
+    L.attn_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i]
+    L.attn_bwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, vp, vp, vp, i, i]
     L.attn_merge.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     L.attn_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, i]
     L.attn_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, i, i]
     L.attn_bwd_chunked.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, vp, vp, vp, i, i]
     for fn in ("attn_fwd", "attn_bwd", "attn_bwd_timed", "attn_merge", "attn_fwd_chunked", "attn_bwd_chunked",
-               "attn_fwd_kvcache"):
+               "attn_fwd_kvcache", "attn_fwd_window", "attn_bwd_window"):
         getattr(L, fn).restype = i
     L.attn_last_error.restype = ctypes.c_char_p
     L.attn_last_error.argtypes = []
@@ -115,27 +117,36 @@ def _dims(q, k, v):
     return B, N, H, Hkv, d
 
 
-def fwd(q, k, v, causal=False, scale=None, out=None, out_lse=None):
-    """Exact attention forward. Returns (o, lse)."""
+def fwd(q, k, v, causal=False, scale=None, out=None, out_lse=None, window=0):
+    """Exact attention forward. Returns (o, lse).
+
+    window > 0: causal sliding-window attention (attn_fwd_window): query row
+    i sees key rows i - window < j <= i; causal is implied.
+    """
     B, N, H, Hkv, d = _dims(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if out_lse is None else out_lse
     _need(o, "out", q.dtype, q.shape, q.device)
     _need(lse, "out_lse", torch.float32, (B, H, N), q.device)
-    _check(lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
-                          int(bool(causal)), scale, _stream(q), _dtype_code(q)))
+    if window:
+        _check(lib().attn_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
+                                     int(window), scale, _stream(q), _dtype_code(q)))
+    else:
+        _check(lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
+                              int(bool(causal)), scale, _stream(q), _dtype_code(q)))
     return o, lse
 
 
 def bwd(q, k, v, o, lse, dout, causal=False, scale=None, accumulate=False, dq=None, dk=None, dv=None,
-        marks=None):
+        marks=None, window=0):
     """Exact attention backward from the forward's o and lse. Returns (dq, dk, dv).
 
     accumulate=True: dq/dk/dv are float32 tensors (given or zero-initialised)
     that the gradients are added to; otherwise they have q's dtype.
     marks: optional pair of torch.cuda.Event, recorded on the stream after the
     rowsum kernel and after the dK/dV kernel (attn_bwd_timed).
+    window > 0: backward of causal sliding-window attention (attn_bwd_window).
     """
     B, N, H, Hkv, d = _dims(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -153,7 +164,12 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, accumulate=False, dq=No
     _need(dv, "dv", gdt, v.shape, q.device)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d, int(bool(causal)), scale,
             _stream(q), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _dtype_code(q), int(bool(accumulate)))
-    if marks is None:
+    if window:
+        if marks is not None:
+            raise ValueError("marks are not supported with a window")
+        wargs = args[:10] + (int(window),) + args[11:]
+        _check(lib().attn_bwd_window(*wargs))
+    elif marks is None:
         _check(lib().attn_bwd(*args))
     else:
         for m in marks:           # torch creates the HIP event at its first record

@@ -63,7 +63,7 @@ struct DkdvSmem {
   Buf buf[3];
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WIN = false>
 __global__ __launch_bounds__(DKV_NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(Params p) {
   constexpr int KS = D / 16, DB = D / 32;
@@ -126,7 +126,12 @@ void bwd_dkdv_kernel(Params p) {
   const int nqt = (p.Nq + DKV_BQ - 1) / DKV_BQ;
   int first = 0;
   if (CAUSAL) first = min(nqt, max(0, p.k_start + k0 - p.q_start) / DKV_BQ);
-  const int per_head = nqt - first;
+  int nqt_end = nqt;   // sliding window: query tiles past the window of the last key see none
+  if constexpr (WIN) {
+    const int q_hi = p.k_start + k0 + DKV_BK - 1 + p.window - 1 - p.q_start;
+    nqt_end = min(nqt, max(0, q_hi / DKV_BQ + 1));
+  }
+  const int per_head = max(0, nqt_end - first);
   const int niter = p.G * per_head;
   const int kpos = p.k_start + kw0 + n;          // this lane's key position
   const int wk_first = p.k_start + kw0;
@@ -263,13 +268,14 @@ void bwd_dkdv_kernel(Params p) {
     }
   };
   // causal mask on the scores of one half of a diagonal tile: query
-  // 32 qb + sigma_row(g, r) before this lane's key -> -inf (P = 0)
+  // 32 qb + sigma_row(g, r) before this lane's key -> -inf (P = 0); under a
+  // sliding window also the queries at or past this key + window
   auto mask_half = [&](f32x16& sv, int mthr_h) {
     const int tq = mthr_h - 8 * g;    // register r masked iff r' < tq, r' = r (r < 8) or r + 8
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int rr = r < 8 ? r : r + 8;
-      if (rr < tq) sv[r] = -INFINITY;
+      if (rr < tq || (WIN && rr >= tq + p.window)) sv[r] = -INFINITY;
     }
   };
 
@@ -284,7 +290,9 @@ void bwd_dkdv_kernel(Params p) {
     const bool nx_real = kt_ + 1 < niter;
     const int q0_nx = nx_real ? (first + t_nx) * DKV_BQ : empty_q0;
     const int h_ld = nx_real ? h_nx : gkv * p.G;   // a valid head also for the empty tile
-    const bool need_mask = CAUSAL && real && (wk_first + DKV_KW - 1 > p.q_start + q0);
+    const bool need_mask = CAUSAL && real &&
+                           (wk_first + DKV_KW - 1 > p.q_start + q0 ||
+                            (WIN && p.q_start + q0 + DKV_BQ - 1 - wk_first >= p.window));
     const int mthr = kpos - (p.q_start + q0);     // query index inside the tile < mthr -> masked
     // LDS read bases of this iteration (byte addresses; dO at +TILE from Q)
     const uint32_t cq = lds_addr(sm.buf[0].q) + cb * (uint32_t)sizeof(typename DkdvSmem<D>::Buf);
@@ -412,7 +420,7 @@ struct DqSmem {
   bf16 v[2][TILE];
 };
 
-template <int D, bool CAUSAL, int NW>
+template <int D, bool CAUSAL, int NW, bool WIN = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void bwd_dq_kernel(Params p) {
   constexpr int BR = NW * 32;
@@ -519,9 +527,13 @@ void bwd_dq_kernel(Params p) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
-  if (nkt > 0) {
+  // sliding window (causal): key tiles wholly before the window of the
+  // workgroup's first row are skipped too
+  int jt0 = 0;
+  if constexpr (WIN) jt0 = max(0, p.q_start + q0 - (p.window - 1) - p.k_start) / DQ_BC;
+  if (nkt > jt0) {
 #pragma unroll
-    for (int i = 0; i < NL; ++i) load_piece(i, 0, 0);
+    for (int i = 0; i < NL; ++i) load_piece(i, jt0 & 1, jt0 * DQ_BC);
     wait_global_loads();
   }
   __syncthreads();
@@ -545,6 +557,8 @@ void bwd_dq_kernel(Params p) {
     // masked iff key index inside the tile > thr (causal and the ragged end)
     int thr = p.Nk - 1 - j * DQ_BC;
     if (CAUSAL && kpos0 + DQ_BC - 1 > wq_first) thr = min(thr, qpos - kpos0);
+    int lo = 0;   // sliding window: key index inside the tile < lo is before the row's window
+    if constexpr (WIN) lo = qpos - (p.window - 1) - kpos0;
     const bf16* kt = sm.k[buf];
     const bf16* vt = sm.v[buf];
     f32x16 s[2], dp[2];
@@ -562,7 +576,7 @@ void bwd_dq_kernel(Params p) {
         float pv = x;
         if constexpr (MASKED) {
           const int kin = kb * 32 + ((r < 8) ? (g * 8 + r) : (16 + g * 8 + r - 8));
-          pv = kin > thr ? 0.f : x;
+          pv = (kin > thr || (WIN && kin < lo)) ? 0.f : x;
         }
         dsb[kb * 2 + (r >> 3)][r & 7] = (bf16)(pv * (dp[kb][r] - dsum));
       }
@@ -615,8 +629,19 @@ void bwd_dq_kernel(Params p) {
     wait_global_loads();
     __syncthreads();
   };
-  for (int j = 0; j < nplain; ++j) tile(std::false_type{}, j);
-  for (int j = nplain; j < nkt; ++j) tile(std::true_type{}, j);
+  if constexpr (WIN) {
+    // tiles before jlow hold keys before the window of some row of the
+    // workgroup: masked prefix [jt0, a), plain [a, b), masked [b, nkt)
+    const int jlow = max(0, (p.q_start + q0 + BR - p.window - p.k_start + DQ_BC - 1) / DQ_BC);
+    const int a = min(max(jlow, jt0), nkt);
+    const int b = max(a, min(nplain, nkt));
+    for (int j = jt0; j < a; ++j) tile(std::true_type{}, j);
+    for (int j = a; j < b; ++j) tile(std::false_type{}, j);
+    for (int j = b; j < nkt; ++j) tile(std::true_type{}, j);
+  } else {
+    for (int j = 0; j < nplain; ++j) tile(std::false_type{}, j);
+    for (int j = nplain; j < nkt; ++j) tile(std::true_type{}, j);
+  }
 
   // ---- store dQ = scale * acc^T: lane (g, query n), register r <-> column 32 db + 8 (r/4) + 4g + r%4
   if (row < p.Nq) {
@@ -646,7 +671,9 @@ void bwd_dq_kernel(Params p) {
 template <int D>
 hipError_t launch_dkdv_d(const Params& p, hipStream_t s) {
   const dim3 gkv(p.Hkv, (p.Nk + DKV_BK - 1) / DKV_BK, p.B);
-  if (p.causal)
+  if (p.causal && p.window > 0)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, true>), gkv, dim3(DKV_NW * 64), 0, s, p);
+  else if (p.causal)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), gkv, dim3(DKV_NW * 64), 0, s, p);
   else
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), gkv, dim3(DKV_NW * 64), 0, s, p);
@@ -657,7 +684,9 @@ template <int D>
 hipError_t launch_dq_d(const Params& p, hipStream_t s) {
   constexpr int NW = 8;
   const dim3 gq(p.H, (p.Nq + NW * 32 - 1) / (NW * 32), p.B);
-  if (p.causal)
+  if (p.causal && p.window > 0)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true, NW, true>), gq, dim3(NW * 64), 0, s, p);
+  else if (p.causal)
     hipLaunchKernelGGL((bwd_dq_kernel<D, true, NW>), gq, dim3(NW * 64), 0, s, p);
   else
     hipLaunchKernelGGL((bwd_dq_kernel<D, false, NW>), gq, dim3(NW * 64), 0, s, p);

@@ -42,6 +42,7 @@ struct Params {
   int causal;        // mask keys whose absolute position exceeds the query's
   float scale;
   int accumulate;        // backward: add into float32 dq/dk/dv
+  int window;            // > 0 (causal only): key visible iff query position - window < key position
 };
 
 __device__ __forceinline__ float to_f(float x) { return x; }

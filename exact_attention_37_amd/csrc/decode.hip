@@ -195,7 +195,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_split_kernel(SplitParams p) {
     const bool raise = mt > m + 8.f;
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
       const float mnew = raise ? mt : m;
-      const float alpha = exp2f(m - mnew);
+      // rows that keep their max keep alpha = 1: a row that has seen no key
+      // yet has m = -inf, and -inf - -inf has no value
+      const float alpha = raise ? exp2f(m - mnew) : 1.f;
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)

@@ -52,7 +52,7 @@ struct FwdSmem {
   bf16 v[2][TILE];
 };
 
-template <int D, int NW, bool CAUSAL, typename TO>
+template <int D, int NW, bool CAUSAL, typename TO, bool WIN = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void fwd_mfma_kernel(Params p) {
   constexpr int BR = NW * 32;  // query rows per workgroup, 32 per wave
@@ -116,6 +116,10 @@ void fwd_mfma_kernel(Params p) {
     nkt = kend > 0 ? (kend + BC - 1) / BC : 0;
   }
   const int wq_first = p.q_start + wq0;
+  // sliding window (causal): key tiles wholly before the window of the
+  // workgroup's first row are skipped too
+  int jt0 = 0;
+  if constexpr (WIN) jt0 = max(0, p.q_start + q0 - (p.window - 1) - p.k_start) / BC;
 
   // Direct loads: 1 KB piece s = wave*NL + i of the two tiles (K: s < TILE_KB,
   // then V) covers tile bytes [(s % TILE_KB) KB, +1 KB); lane l fills 16 bytes
@@ -163,15 +167,15 @@ void fwd_mfma_kernel(Params p) {
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
   float m = -INFINITY, l = 0.f;
 
-  if (nkt > 0) {
+  if (nkt > jt0) {
 #pragma unroll
-    for (int i = 0; i < NL; ++i) load_piece(i, 0, 0);
+    for (int i = 0; i < NL; ++i) load_piece(i, 0, jt0 * BC);
     wait_global_loads();
   }
   __syncthreads();
 
-  for (int j = 0; j < nkt; ++j) {
-    const int buf = j & 1;
+  for (int j = jt0; j < nkt; ++j) {
+    const int buf = (j - jt0) & 1;
     const bf16* kt = sm.k[buf];
     const bf16* vt = sm.v[buf];
     const int kpos0 = p.k_start + j * BC;          // absolute position of the tile's first key
@@ -203,14 +207,19 @@ void fwd_mfma_kernel(Params p) {
         });
 
     // ---- mask: key index inside the tile > thr (causal diagonal, ragged end)
+    // or, under a sliding window, < lo (before the row's window)
     int thr = p.Nk - 1 - j * BC;
     if (CAUSAL && kpos0 + BC - 1 > wq_first) thr = min(thr, qpos - kpos0);
-    if (__builtin_amdgcn_ballot_w64(thr < BC - 1) != 0) {
+    int lo = 0;
+    if constexpr (WIN) lo = qpos - (p.window - 1) - kpos0;
+    if (__builtin_amdgcn_ballot_w64(thr < BC - 1 || (WIN && lo > 0)) != 0) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kb * 32 + sigma_row(g, r) > thr) s[kb][r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          const int kin = kb * 32 + sigma_row(g, r);
+          if (kin > thr || (WIN && kin < lo)) s[kb][r] = -INFINITY;
+        }
     }
 
     // ---- online softmax: lane (g, query n), register r of block kb <-> key 32 kb + sigma_row(g, r)
@@ -224,7 +233,9 @@ void fwd_mfma_kernel(Params p) {
     const bool raise = mt > m + 8.f;
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
       const float mnew = raise ? mt : m;
-      const float alpha = exp2f(m - mnew);
+      // rows that keep their max keep alpha = 1 (with a window a row's max
+      // can still be -inf here, and -inf - -inf has no value)
+      const float alpha = (WIN && !raise) ? 1.f : exp2f(m - mnew);
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -232,7 +243,8 @@ void fwd_mfma_kernel(Params p) {
         for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
       m = mnew;
     }
-    const float mneg = -m;
+    // (a row whose window has not begun yet keeps m = -inf and p = 0)
+    const float mneg = (WIN && m == -INFINITY) ? 0.f : -m;
     bf16x8 pf[4];
     float lsum0 = 0.f, lsum1 = 0.f;
 #pragma unroll
@@ -299,7 +311,9 @@ template <int D, int NW, typename TO>
 hipError_t launch_cfg(const Params& p, hipStream_t s) {
   constexpr int BR = NW * 32;
   const dim3 grid(p.H, (p.Nq + BR - 1) / BR, p.B);
-  if (p.causal)
+  if (p.causal && p.window > 0)
+    hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, true, TO, true>), grid, dim3(NW * 64), 0, s, p);
+  else if (p.causal)
     hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, true, TO>), grid, dim3(NW * 64), 0, s, p);
   else
     hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, false, TO>), grid, dim3(NW * 64), 0, s, p);

@@ -168,8 +168,12 @@ int attn_chunk_schedule(int nchunks, int* round_of, int* q_chunk, int* k_chunk, 
   return n;
 }
 
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
-             int d, int causal, float scale, void* stream, int dtype) {
+}  // extern "C"
+
+namespace {
+
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N, int d,
+             int causal, float scale, void* stream, int dtype, int window) {
   int st = check_common(B, H, Hkv, N, d, dtype);
   if (st) return st;
   if ((st = check_ptrs({q, k, v, o, lse}))) return st;
@@ -182,8 +186,24 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     if (overlap(ro, r) || overlap(rl, r)) return fail(MIATTN_EINVAL, "o/lse must not alias q, k or v");
   if (overlap(ro, rl)) return fail(MIATTN_EINVAL, "o and lse must not overlap");
   Params p = make_params(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale);
+  p.window = window;
   if ((st = launch_status(fwd_block(p, dtype, dtype == MIATTN_F32, (hipStream_t)stream), "attn_fwd"))) return st;
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
+             int d, int causal, float scale, void* stream, int dtype) {
+  return fwd_impl(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, stream, dtype, 0);
+}
+
+int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
+                    int N, int d, int window, float scale, void* stream, int dtype) {
+  if (window < 1) return fail(MIATTN_EINVAL, "window must be >= 1");
+  return fwd_impl(q, k, v, o, lse, B, H, Hkv, N, d, 1, scale, stream, dtype, window);
 }
 
 int attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, const int* k_lens, void* o,
@@ -250,9 +270,13 @@ int attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, co
   return ok();
 }
 
-int attn_bwd_timed(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
-                   int Hkv, int N, int d, int causal, float scale, void* stream, const void* dout, void* dq,
-                   void* dk, void* dv, int dtype, int accumulate, void* const* marks) {
+}  // extern "C"
+
+namespace {
+
+int bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H, int Hkv,
+             int N, int d, int causal, float scale, void* stream, const void* dout, void* dq, void* dk, void* dv,
+             int dtype, int accumulate, void* const* marks, int window) {
   int st = check_common(B, H, Hkv, N, d, dtype);
   if (st) return st;
   if ((st = check_ptrs({q, k, v, o, lse, dout, dq, dk, dv}))) return st;
@@ -281,6 +305,7 @@ int attn_bwd_timed(const void* q, const void* k, const void* v, const void* o, c
   p.dv = dv;
   p.dsum = dsum;
   p.accumulate = accumulate;
+  p.window = window;
   if ((st = launch_status(miattn::launch_bwd_pre(o, dout, dsum, B, H, N, d, 0, N, dtype, s), "bwd preprocess")))
     return st;
   if (marks && (st = launch_status(hipEventRecord((hipEvent_t)marks[0], s), "timing mark 0"))) return st;
@@ -295,11 +320,30 @@ int attn_bwd_timed(const void* q, const void* k, const void* v, const void* o, c
   return ok();
 }
 
+}  // namespace
+
+extern "C" {
+
+int attn_bwd_timed(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
+                   int Hkv, int N, int d, int causal, float scale, void* stream, const void* dout, void* dq,
+                   void* dk, void* dv, int dtype, int accumulate, void* const* marks) {
+  return bwd_impl(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, stream, dout, dq, dk, dv, dtype, accumulate,
+                  marks, 0);
+}
+
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
              int Hkv, int N, int d, int causal, float scale, void* stream, const void* dout, void* dq, void* dk,
              void* dv, int dtype, int accumulate) {
-  return attn_bwd_timed(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, stream, dout, dq, dk, dv, dtype,
-                        accumulate, nullptr);
+  return bwd_impl(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, stream, dout, dq, dk, dv, dtype, accumulate,
+                  nullptr, 0);
+}
+
+int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
+                    int Hkv, int N, int d, int window, float scale, void* stream, const void* dout, void* dq,
+                    void* dk, void* dv, int dtype, int accumulate) {
+  if (window < 1) return fail(MIATTN_EINVAL, "window must be >= 1");
+  return bwd_impl(q, k, v, o, lse, B, H, Hkv, N, d, 1, scale, stream, dout, dq, dk, dv, dtype, accumulate,
+                  nullptr, window);
 }
 
 int attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* o, float* lse, int B,

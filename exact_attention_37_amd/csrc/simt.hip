@@ -54,7 +54,9 @@ __global__ __launch_bounds__(kRows) void fwd_simt(Params p) {
     kend = max(0, min(p.Nk, last_q - p.k_start + 1));
   }
   const int qpos = p.q_start + i;
-  for (int j0 = 0; j0 < kend; j0 += kTile) {
+  // sliding window: keys before the window of the block's first row are skipped
+  const int jbeg = p.window > 0 ? max(0, p.q_start + i0 - (p.window - 1) - p.k_start) / kTile * kTile : 0;
+  for (int j0 = jbeg; j0 < kend; j0 += kTile) {
     for (int e = tid; e < kTile * D; e += kRows) {
       const int r = e / D, col = e % D;
       const bool in = j0 + r < p.Nk;
@@ -65,6 +67,7 @@ __global__ __launch_bounds__(kRows) void fwd_simt(Params p) {
     const int jn = min(kTile, kend - j0);
     for (int jj = 0; jj < jn; ++jj) {
       if (p.causal && p.k_start + j0 + jj > qpos) break;
+      if (p.window > 0 && p.k_start + j0 + jj <= qpos - p.window) continue;
       float s = 0.f;
 #pragma unroll
       for (int t = 0; t < D; ++t) s = fmaf(q[t], Ks[jj][t], s);
@@ -125,6 +128,9 @@ __global__ __launch_bounds__(kRows) void bwd_dkdv_simt(Params p) {
   // first query row that can see any key of this block
   int ibeg = 0;
   if (p.causal) ibeg = max(0, p.k_start + j0 - p.q_start);
+  // sliding window: query rows past the window of the block's last key see none of it
+  int iend = p.Nq;
+  if (p.window > 0) iend = min(p.Nq, max(0, p.k_start + j0 + kRows - 1 + p.window - p.q_start));
   __syncthreads();
 
   for (int h = g * p.G; h < (g + 1) * p.G; ++h) {
@@ -132,7 +138,7 @@ __global__ __launch_bounds__(kRows) void bwd_dkdv_simt(Params p) {
     const T* dO = (const T*)p.dout + (qrow(p, b, p.q_start) + h) * D;
     const float* L = p.lse + ((long long)b * p.H + h) * p.N + p.q_start;
     const float* Dv = p.dsum + ((long long)b * p.H + h) * p.N + p.q_start;
-    for (int i0 = ibeg; i0 < p.Nq; i0 += kTile) {
+    for (int i0 = ibeg; i0 < iend; i0 += kTile) {
       for (int e = tid; e < kTile * D; e += kRows) {
         const int r = e / D, col = e % D;
         const bool in = i0 + r < p.Nq;
@@ -148,6 +154,7 @@ __global__ __launch_bounds__(kRows) void bwd_dkdv_simt(Params p) {
       const int in_n = min(kTile, p.Nq - i0);
       for (int ii = 0; ii < in_n; ++ii) {
         if (p.causal && kpos > p.q_start + i0 + ii) continue;
+        if (p.window > 0 && p.q_start + i0 + ii >= kpos + p.window) continue;
         float s = 0.f, dp = 0.f;
 #pragma unroll
         for (int t = 0; t < D; ++t) {
@@ -212,7 +219,8 @@ __global__ __launch_bounds__(kRows) void bwd_dq_simt(Params p) {
     kend = max(0, min(p.Nk, last_q - p.k_start + 1));
   }
   const int qpos = p.q_start + i;
-  for (int j0 = 0; j0 < kend; j0 += kTile) {
+  const int jbeg = p.window > 0 ? max(0, p.q_start + i0 - (p.window - 1) - p.k_start) / kTile * kTile : 0;
+  for (int j0 = jbeg; j0 < kend; j0 += kTile) {
     for (int e = tid; e < kTile * D; e += kRows) {
       const int r = e / D, col = e % D;
       const bool in = j0 + r < p.Nk;
@@ -223,6 +231,7 @@ __global__ __launch_bounds__(kRows) void bwd_dq_simt(Params p) {
     const int jn = min(kTile, kend - j0);
     for (int jj = 0; jj < jn; ++jj) {
       if (p.causal && p.k_start + j0 + jj > qpos) break;
+      if (p.window > 0 && p.k_start + j0 + jj <= qpos - p.window) continue;
       float s = 0.f, dp = 0.f;
 #pragma unroll
       for (int t = 0; t < D; ++t) {

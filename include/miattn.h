@@ -101,6 +101,19 @@ int attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, co
                      void* o, float* lse, int B, int H, int Hkv, int Nq, int Nk, int d, int causal,
                      float scale, int nsplit, void* stream, int dtype);
 
+/* Causal sliding-window (local) attention, forward: the same operation as
+ * attn_fwd with causal = 1 and a banded mask -- query row i sees key rows j
+ * with i - window < j <= i (window keys including its own). FlashAttention-2
+ * reviews page, the authors' general response: the method with local
+ * (sliding-window) attention trained Mistral-7B; BurstAttention rebuttal
+ * page: sparse attention only changes the attention mask. Key tiles wholly
+ * outside every row's window are skipped. window >= 1 (MIATTN_EINVAL
+ * otherwise); window >= N gives plain causal attention. All other arguments,
+ * layouts and errors as attn_fwd. */
+int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int Hkv, int N, int d, int window, float scale,
+                    void* stream, int dtype);
+
 /* Backward pass: from q, k, v, the forward's o and lse, and dout = dL/dO,
  * produces dq, dk, dv without forming the N x N matrix. The forward is not
  * re-run: P is rebuilt tile by tile from the saved lse (DistFlashAttn
@@ -116,6 +129,15 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              int B, int H, int Hkv, int N, int d, int causal, float scale,
              void* stream, const void* dout, void* dq, void* dk, void* dv,
              int dtype, int accumulate);
+
+/* Backward of attn_fwd_window: dq, dk, dv of causal sliding-window attention
+ * (query row i sees key rows j with i - window < j <= i), from that forward's
+ * o and lse. window >= 1; all other arguments, layouts, scratch and errors as
+ * attn_bwd. */
+int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    int B, int H, int Hkv, int N, int d, int window, float scale,
+                    void* stream, const void* dout, void* dq, void* dk, void* dv,
+                    int dtype, int accumulate);
 
 /* attn_bwd with per-kernel timing marks, for measurement tools: the same
  * arguments, results and errors as attn_bwd, and additionally

@@ -21,7 +21,11 @@ readings taken are listed next to each function):
   backward-pass section); DistFlashAttn reviews page, review 3 (GQA setting);
 * partial results over key chunks are combined -- DistFlashAttn reviews page,
   reviews 1 and 4 (chunks of the attention computation spread over workers);
-  BurstAttention rebuttal page (RingAttention vs. online softmax).
+  BurstAttention rebuttal page (RingAttention vs. online softmax);
+* local (sliding-window) attention is the same method with a banded mask --
+  FlashAttention-2 reviews page, the authors' general response (local
+  attention used to train Mistral-7B); BurstAttention rebuttal page (sparse
+  attention only changes the attention mask).
 
 Readings where the pages are silent (each also listed in the design notes):
 scores are scale * Q K^T with a caller-given scale; causal keeps key position
@@ -50,11 +54,13 @@ __all__ = [
 # the definition, one (batch, query head) at a time
 # ---------------------------------------------------------------------------
 
-def scores(q_h, k_g, scale, causal, q_pos=None, k_pos=None):
+def scores(q_h, k_g, scale, causal, q_pos=None, k_pos=None, window=0):
     """S[i, j] = scale * q_i . k_j, and -inf where a causal mask forbids j.
 
     q_h: [Nq, d], k_g: [Nk, d] float64. Positions default to 0..N-1; key j is
-    allowed for query i iff k_pos[j] <= q_pos[i] under the causal mask.
+    allowed for query i iff k_pos[j] <= q_pos[i] under the causal mask, and,
+    with a sliding window of ``window`` > 0 keys (local attention, causal
+    only), also iff k_pos[j] > q_pos[i] - window.
     """
     s = scale * (q_h @ k_g.T)
     if causal:
@@ -62,7 +68,10 @@ def scores(q_h, k_g, scale, causal, q_pos=None, k_pos=None):
             q_pos = np.arange(q_h.shape[0])
         if k_pos is None:
             k_pos = np.arange(k_g.shape[0])
-        s = np.where(k_pos[None, :] <= q_pos[:, None], s, -np.inf)
+        allowed = k_pos[None, :] <= q_pos[:, None]
+        if window > 0:
+            allowed &= k_pos[None, :] > q_pos[:, None] - window
+        s = np.where(allowed, s, -np.inf)
     return s
 
 
@@ -108,8 +117,9 @@ def _row_blocks(n, blk):
 # forward
 # ---------------------------------------------------------------------------
 
-def forward(q, k, v, causal, scale, q_offset=0, k_offset=0, row_block=512):
-    """O and LSE of exact attention.
+def forward(q, k, v, causal, scale, q_offset=0, k_offset=0, row_block=512, window=0):
+    """O and LSE of exact attention (``window`` > 0: causal sliding window of
+    that many keys, see ``scores``).
 
     q: [B, Nq, H, d]; k, v: [B, Nk, Hkv, d] (any float dtype, used as float64).
     Returns o [B, Nq, H, d] float64 and lse [B, H, Nq] float64.
@@ -132,7 +142,7 @@ def forward(q, k, v, causal, scale, q_offset=0, k_offset=0, row_block=512):
             g = h // G
             for r0, r1 in _row_blocks(Nq, row_block):
                 q_pos = q_offset + np.arange(r0, r1)
-                s = scores(q[b, r0:r1, h], k[b, :, g], scale, causal, q_pos, k_pos)
+                s = scores(q[b, r0:r1, h], k[b, :, g], scale, causal, q_pos, k_pos, window)
                 p, l = _softmax_rows(s)
                 o[b, r0:r1, h] = p @ v[b, :, g]
                 lse[b, h, r0:r1] = l
@@ -195,8 +205,9 @@ def forward_rows(q, k, v, causal, scale, b, h, rows):
 # backward
 # ---------------------------------------------------------------------------
 
-def backward(q, k, v, do, causal, scale, row_block=512):
-    """dQ, dK, dV: gradients of sum(dO * O) through exact attention.
+def backward(q, k, v, do, causal, scale, row_block=512, window=0):
+    """dQ, dK, dV: gradients of sum(dO * O) through exact attention
+    (``window`` > 0: causal sliding window of that many keys).
 
     With P the softmax of the masked scaled scores (recomputed exactly here):
       dV_j  = sum_i P_ij dO_i
@@ -221,7 +232,7 @@ def backward(q, k, v, do, causal, scale, row_block=512):
             g = h // G
             for r0, r1 in _row_blocks(N, row_block):
                 s = scores(q[b, r0:r1, h], k[b, :, g], scale, causal,
-                           np.arange(r0, r1), np.arange(Nk))
+                           np.arange(r0, r1), np.arange(Nk), window)
                 p, _ = _softmax_rows(s)
                 dob = do[b, r0:r1, h]
                 dv[b, :, g] += p.T @ dob

@@ -152,3 +152,13 @@ def kv_call(**kw):
 def test_kvcache_rejects_bad_arguments(kw, code, msg):
     assert kv_call(**kw) == code
     assert msg in mi.lib().attn_last_error().decode()
+
+
+def test_window_entry_points_reject_bad_windows():
+    L = mi.lib()
+    q = [vp(FAKE * i) for i in range(1, 6)]
+    assert L.attn_fwd_window(*q, 1, 2, 2, 16, 64, 0, 0.1, None, 1) == 1
+    assert b"window" in L.attn_last_error()
+    assert L.attn_fwd_window(*q, 1, 2, 2, 16, 96, 4, 0.1, None, 1) == 2
+    assert L.attn_bwd_window(*q, 1, 2, 2, 16, 64, -3, 0.1, None, vp(FAKE * 6), vp(FAKE * 7), vp(FAKE * 8),
+                             vp(FAKE * 9), 1, 0) == 1

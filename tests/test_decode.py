@@ -38,6 +38,7 @@ CASES = [
     (1, 4, 2, 17, 129, 128, [129], True, 0),           # chunked prefill, 34 rows per group
     (2, 4, 2, 1, 64, 64, [0, 64], True, 0),            # an empty cache: o = 0, lse = -inf
     (1, 8, 8, 2, 5000, 128, [4999], False, 40),        # many small splits
+    (1, 4, 4, 3, 600, 64, [546], True, 19),            # last split (keys 544, 545) unseen by row 0
 ]
 
 

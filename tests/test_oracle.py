@@ -441,3 +441,77 @@ def test_kvcache_key_splits_merge_to_the_whole(causal):
                                     q_offset=int(qpos[0]), k_offset=lo))
     o, lse = oracle.merge(parts[0][0], parts[0][1], parts[1][0], parts[1][1])
     assert np.max(np.abs(o - full[0])) < 1e-13 and np.max(np.abs(lse - full[1])) < 1e-13
+
+
+# ---------------------------------------------------------------- sliding window (local attention)
+
+def _window_by_loops(q, k, v, scale, window):
+    """Causal sliding-window attention element by element with math.exp:
+    query i sees keys j with i - window < j <= i."""
+    B, N, H, d = q.shape
+    G = H // k.shape[2]
+    o = np.zeros(q.shape)
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            g = h // G
+            for i in range(N):
+                keys = range(max(0, i - window + 1), i + 1)
+                sc = [scale * sum(float(q[b, i, h, c]) * float(k[b, j, g, c]) for c in range(d)) for j in keys]
+                mx = max(sc)
+                w = [math.exp(x - mx) for x in sc]
+                tot = sum(w)
+                lse[b, h, i] = mx + math.log(tot)
+                for c in range(d):
+                    o[b, i, h, c] = sum(wj * float(v[b, j, g, c]) for wj, j in zip(w, keys)) / tot
+    return o, lse
+
+
+@pytest.mark.parametrize("window", [1, 3, 6])
+def test_window_matches_elementwise_loops(window):
+    q, k, v, _ = draw(1, 4, 2, 9, 3, seed=81, dtype=torch.float64)
+    o, lse = oracle.forward(q.numpy(), k.numpy(), v.numpy(), True, 0.6, window=window)
+    ro, rl = _window_by_loops(q.numpy(), k.numpy(), v.numpy(), 0.6, window)
+    assert np.max(np.abs(o - ro)) < 1e-12 and np.max(np.abs(lse - rl)) < 1e-12
+
+
+def test_window_covering_the_sequence_is_causal():
+    q, k, v, do = draw(1, 2, 1, 12, 4, seed=82, dtype=torch.float64)
+    a = oracle.forward(q.numpy(), k.numpy(), v.numpy(), True, 0.5, window=12)
+    b = oracle.forward(q.numpy(), k.numpy(), v.numpy(), True, 0.5)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    ga = oracle.backward(q.numpy(), k.numpy(), v.numpy(), do.numpy(), True, 0.5, window=40)
+    gb = oracle.backward(q.numpy(), k.numpy(), v.numpy(), do.numpy(), True, 0.5)
+    assert all(np.array_equal(x, y) for x, y in zip(ga, gb))
+
+
+def test_window_of_one_key_is_the_identity_map():
+    # each query sees only its own key: O = V, LSE = its score, dQ = dK = 0, dV = dO summed per group
+    q, k, v, do = draw(2, 4, 2, 10, 8, seed=83, dtype=torch.float64)
+    o, lse = oracle.forward(q.numpy(), k.numpy(), v.numpy(), True, 0.3, window=1)
+    vr = np.repeat(v.numpy(), 2, axis=2)
+    assert np.max(np.abs(o - vr)) < 1e-14
+    s = 0.3 * np.einsum("bnhd,bnhd->bhn", q.numpy(), np.repeat(k.numpy(), 2, axis=2))
+    assert np.max(np.abs(lse - s)) < 1e-13
+    dq, dk, dv = oracle.backward(q.numpy(), k.numpy(), v.numpy(), do.numpy(), True, 0.3, window=1)
+    assert np.max(np.abs(dq)) < 1e-13 and np.max(np.abs(dk)) < 1e-13
+    dvr = do.numpy().reshape(2, 10, 2, 2, 8).sum(axis=3)
+    assert np.max(np.abs(dv - dvr)) < 1e-13
+
+
+def test_window_backward_matches_finite_differences():
+    q, k, v, do = draw(1, 2, 1, 7, 3, seed=84, dtype=torch.float64)
+    q, k, v, do = (t.numpy() for t in (q, k, v, do))
+    W, sc, eps = 3, 0.8, 1e-6
+    f = lambda qq, kk, vv: float(np.sum(do * oracle.forward(qq, kk, vv, True, sc, window=W)[0]))
+    dq, dk, dv = oracle.backward(q, k, v, do, True, sc, window=W)
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = [xp if y is x else y for y in (q, k, v)]
+            args_m = [xm if y is x else y for y in (q, k, v)]
+            num[idx] = (f(*args_p) - f(*args_m)) / (2 * eps)
+        assert np.max(np.abs(num - g)) < 1e-7

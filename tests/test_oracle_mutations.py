@@ -22,6 +22,7 @@ def _pins():
     yield lambda: T.test_tiled_online_softmax_equals_naive(True, 13, 7)
     yield lambda: T.test_kvcache_matches_elementwise_loops(True)
     yield lambda: T.test_kvcache_ignores_rows_past_the_valid_length()
+    yield lambda: T.test_window_matches_elementwise_loops(3)
 
 
 def _caught():
@@ -34,17 +35,21 @@ def _caught():
     return False
 
 
-def _no_scale(q_h, k_g, scale, causal, q_pos=None, k_pos=None):
-    return _orig_scores(q_h, k_g, 1.0, causal, q_pos, k_pos)
+def _no_scale(q_h, k_g, scale, causal, q_pos=None, k_pos=None, window=0):
+    return _orig_scores(q_h, k_g, 1.0, causal, q_pos, k_pos, window)
 
 
-def _flipped_causal(q_h, k_g, scale, causal, q_pos=None, k_pos=None):
+def _flipped_causal(q_h, k_g, scale, causal, q_pos=None, k_pos=None, window=0):
     s = scale * (q_h @ k_g.T)
     if causal:
         q_pos = np.arange(q_h.shape[0]) if q_pos is None else q_pos
         k_pos = np.arange(k_g.shape[0]) if k_pos is None else k_pos
         s = np.where(k_pos[None, :] >= q_pos[:, None], s, -np.inf)
     return s
+
+
+def _window_off_by_one(q_h, k_g, scale, causal, q_pos=None, k_pos=None, window=0):
+    return _orig_scores(q_h, k_g, scale, causal, q_pos, k_pos, window + 1 if window > 0 else 0)
 
 
 def _lse_without_max(s):
@@ -93,6 +98,7 @@ MUTATIONS = {
     "no_max_subtraction": ("_softmax_rows", _softmax_no_max_subtraction),
     "merge_weights_swapped": ("merge", _merge_swapped_weights),
     "kvcache_top_left_alignment": ("forward_kvcache", _kvcache_top_left),
+    "window_off_by_one": ("scores", _window_off_by_one),
     "kvcache_lengths_ignored": ("forward_kvcache", _kvcache_whole_cache),
 }
 
