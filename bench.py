@@ -154,6 +154,40 @@ def bench_window(mi, torch, q, k, v, do, w, window, reps=10):
             "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2)}
 
 
+def bench_varlen(mi, torch, reps=10):
+    """Causal fwd+bwd over the packed variable-length workload
+    (attn_fwd_varlen / attn_bwd_varlen). FLOPs count the visible pairs of
+    each sequence, L (L + 1) / 2; backward 2.5x forward."""
+    from workloads import VARLEN_WORKLOADS, draw_varlen_workload
+    w = VARLEN_WORKLOADS["packed16k"]
+    q, k, v, do, cu = draw_varlen_workload(w)
+    lengths = (cu[1:] - cu[:-1]).tolist()
+    q, k, v, do, cu = (t.to("cuda:0") for t in (q, k, v, do, cu))
+    scale, L = w.d ** -0.5, max(lengths)
+    for _ in range(2):
+        o, lse = mi.fwd_varlen(q, k, v, cu, L, True, scale)
+        mi.bwd_varlen(q, k, v, o, lse, do, cu, L, True, scale)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    f_ms = b_ms = 0.0
+    for _ in range(reps):
+        e[0].record()
+        o, lse = mi.fwd_varlen(q, k, v, cu, L, True, scale)
+        e[1].record()
+        mi.bwd_varlen(q, k, v, o, lse, do, cu, L, True, scale)
+        e[2].record()
+        torch.cuda.synchronize()
+        f_ms += e[0].elapsed_time(e[1]) / reps
+        b_ms += e[1].elapsed_time(e[2]) / reps
+    pairs = sum(n * (n + 1) // 2 for n in lengths)
+    ff = 4.0 * w.H * w.d * pairs
+    tf = 3.5 * ff / ((f_ms + b_ms) * 1e-3) / 1e12
+    return {"workload": "%s: %d tokens packed as sequences of %s, %d heads, d=%d, causal"
+                        % (w.name, w.total, lengths, w.H, w.d),
+            "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4), "tflops": round(tf, 2),
+            "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -241,6 +275,7 @@ def main():
                      "traffic": traffic},
     }
     out["window"] = bench_window(mi, torch, q, k, v, do, w, 4096)
+    out["varlen"] = bench_varlen(mi, torch)
     out["kvcache"] = {name: bench_cache(mi, torch, name) for name in ("decode16k", "prefill16k")}
     if args.extra:
         extra = {}

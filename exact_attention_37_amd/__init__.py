@@ -16,7 +16,8 @@ import os
 
 import torch
 
-__all__ = ["fwd", "bwd", "merge", "fwd_chunked", "bwd_chunked", "lib", "MiattnError",
+__all__ = ["fwd", "bwd", "merge", "fwd_chunked", "bwd_chunked", "fwd_kvcache", "fwd_varlen", "bwd_varlen",
+           "lib", "MiattnError",
            "library_path", "balanced_rounds"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -52,10 +53,12 @@ def lib():
     L.attn_bwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, vp, vp, vp, i, i]
     L.attn_merge.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     L.attn_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, i]
+    L.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp, i]
+    L.attn_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp, vp, vp, vp, vp, i, i]
     L.attn_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, i, i]
     L.attn_bwd_chunked.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, vp, vp, vp, i, i]
     for fn in ("attn_fwd", "attn_bwd", "attn_bwd_timed", "attn_merge", "attn_fwd_chunked", "attn_bwd_chunked",
-               "attn_fwd_kvcache", "attn_fwd_window", "attn_bwd_window"):
+               "attn_fwd_kvcache", "attn_fwd_window", "attn_bwd_window", "attn_fwd_varlen", "attn_bwd_varlen"):
         getattr(L, fn).restype = i
     L.attn_last_error.restype = ctypes.c_char_p
     L.attn_last_error.argtypes = []
@@ -251,6 +254,65 @@ def fwd_kvcache(q, k_cache, v_cache, k_lens=None, causal=True, scale=None, nspli
                                   B, H, Hkv, Nq, Nk, d, int(bool(causal)), scale, int(nsplit),
                                   _stream(q), _dtype_code(q)))
     return o, lse
+
+
+def _varlen_dims(q, k, v, cu_seqlens, max_len):
+    _need(q, "q")
+    dt = q.dtype
+    _dtype_code(q)
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("packed q, k, v must be 3-D [total, heads, d]")
+    total, H, d = q.shape
+    Hkv = k.shape[1]
+    _need(k, "k", dt, (total, Hkv, d), q.device)
+    _need(v, "v", dt, (total, Hkv, d), q.device)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, None, q.device)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be 1-D with nseq + 1 >= 2 entries")
+    return cu_seqlens.numel() - 1, int(max_len), total, H, Hkv, d
+
+
+def fwd_varlen(q, k, v, cu_seqlens, max_len, causal=False, scale=None, window=0, out=None, out_lse=None):
+    """Forward over a packed batch of sequences of different lengths (attn_fwd_varlen).
+
+    q: [total, H, d]; k, v: [total, Hkv, d]; cu_seqlens: int32 device tensor
+    [nseq + 1] of row offsets (0, ..., total); max_len: the longest sequence.
+    Each sequence attends only within itself. Returns (o, lse), lse [H, total].
+    """
+    nseq, max_len, total, H, Hkv, d = _varlen_dims(q, k, v, cu_seqlens, max_len)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((H, total), dtype=torch.float32, device=q.device) if out_lse is None else out_lse
+    _need(o, "out", q.dtype, q.shape, q.device)
+    _need(lse, "out_lse", torch.float32, (H, total), q.device)
+    _check(lib().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens), nseq,
+                                 max_len, total, H, Hkv, d, int(bool(causal)), int(window), scale,
+                                 _stream(q), _dtype_code(q)))
+    return o, lse
+
+
+def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_len, causal=False, scale=None, window=0,
+               accumulate=False, dq=None, dk=None, dv=None):
+    """Backward of fwd_varlen from its o and lse (attn_bwd_varlen). Returns (dq, dk, dv)."""
+    nseq, max_len, total, H, Hkv, d = _varlen_dims(q, k, v, cu_seqlens, max_len)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _need(o, "o", q.dtype, q.shape, q.device)
+    _need(dout, "dout", q.dtype, q.shape, q.device)
+    _need(lse, "lse", torch.float32, (H, total), q.device)
+    gdt = torch.float32 if accumulate else q.dtype
+    mk = (lambda t: torch.zeros(t.shape, dtype=gdt, device=q.device)) if accumulate else \
+         (lambda t: torch.empty(t.shape, dtype=gdt, device=q.device))
+    dq = mk(q) if dq is None else dq
+    dk = mk(k) if dk is None else dk
+    dv = mk(v) if dv is None else dv
+    _need(dq, "dq", gdt, q.shape, q.device)
+    _need(dk, "dk", gdt, k.shape, q.device)
+    _need(dv, "dv", gdt, v.shape, q.device)
+    _check(lib().attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens), nseq,
+                                 max_len, total, H, Hkv, d, int(bool(causal)), int(window), scale,
+                                 _stream(q), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _dtype_code(q),
+                                 int(bool(accumulate))))
+    return dq, dk, dv
 
 
 def balanced_rounds(P):

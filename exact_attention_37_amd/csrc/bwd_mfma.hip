@@ -79,8 +79,12 @@ void bwd_dkdv_kernel(Params p) {
   const int g = lane >> 5, n = lane & 31;
   const int gkv = blockIdx.x;          // all tiles of one K/V head share an XCD
   const int kt = blockIdx.y;           // tile 0 has the most causal work: dispatched first
-  const int b = blockIdx.z;
+  int b = blockIdx.z;
   const int k0 = kt * DKV_BK;
+  if (p.cu_seqlens) {                  // packed batch: z is the sequence
+    if (!narrow_to_sequence(p, b, k0)) return;
+    b = 0;
+  }
   const int kw0 = k0 + wave * DKV_KW;
 
   const long long krs = (long long)p.Hkv * D, qrs = (long long)p.H * D;
@@ -439,9 +443,13 @@ void bwd_dq_kernel(Params p) {
   const int ntq = gridDim.y;
   const int qt = CAUSAL ? (ntq - 1 - (int)blockIdx.y) : (int)blockIdx.y;
   const int h = xcd_head(blockIdx.x, p.H);
-  const int b = blockIdx.z;
+  int b = blockIdx.z;
   const int kvh = h / p.G;
   const int q0 = qt * BR;
+  if (p.cu_seqlens) {                  // packed batch: z is the sequence
+    if (!narrow_to_sequence(p, b, q0)) return;
+    b = 0;
+  }
   const int wq0 = q0 + wave * 32;
 
   const long long qrs = (long long)p.H * D, krs = (long long)p.Hkv * D;

@@ -43,7 +43,24 @@ struct Params {
   float scale;
   int accumulate;        // backward: add into float32 dq/dk/dv
   int window;            // > 0 (causal only): key visible iff query position - window < key position
+  // Packed variable-length batch: sequence z of the grid owns rows
+  // [cu_seqlens[z], cu_seqlens[z + 1]) of a B = 1 layout of N rows; null otherwise.
+  const int* cu_seqlens;
 };
+
+// For a packed variable-length batch, narrows p to sequence s (rows
+// [cu_seqlens[s], cu_seqlens[s + 1]) of the single B = 1 layout; the offsets
+// are clamped to [0, N] so malformed ones cannot move any access out of the
+// tensors) and returns false when the workgroup's first row `row0` lies past
+// the sequence. A no-op returning true for ordinary batches.
+__device__ __forceinline__ bool narrow_to_sequence(Params& p, int s, int row0) {
+  if (!p.cu_seqlens) return true;
+  const int e = min(max(p.cu_seqlens[s + 1], 0), p.N);
+  const int a = min(max(p.cu_seqlens[s], 0), e);
+  p.q_start = p.k_start = a;
+  p.Nq = p.Nk = e - a;
+  return row0 < p.Nq;
+}
 
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }

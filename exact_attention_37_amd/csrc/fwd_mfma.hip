@@ -74,9 +74,13 @@ void fwd_mfma_kernel(Params p) {
   const int ntq = gridDim.y;
   const int qt = CAUSAL ? (ntq - 1 - (int)blockIdx.y) : (int)blockIdx.y;
   const int h = xcd_head(blockIdx.x, p.H);
-  const int b = blockIdx.z;
+  int b = blockIdx.z;
   const int kvh = h / p.G;
   const int q0 = qt * BR;                         // first local query row of the tile
+  if (p.cu_seqlens) {                             // packed batch: z is the sequence
+    if (!narrow_to_sequence(p, b, q0)) return;
+    b = 0;
+  }
   const int wq0 = q0 + wave * 32;                 // first local query row of this wave
 
   const long long qrs = (long long)p.H * D;       // row strides (elements)

@@ -206,6 +206,86 @@ int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float*
   return fwd_impl(q, k, v, o, lse, B, H, Hkv, N, d, 1, scale, stream, dtype, window);
 }
 
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens,
+                    int nseq, int max_len, int total, int H, int Hkv, int d, int causal, int window, float scale,
+                    void* stream, int dtype) {
+  int st = check_common(1, H, Hkv, total, d, dtype);
+  if (st) return st;
+  if (nseq < 1 || nseq > 65535) return fail(MIATTN_EINVAL, "nseq must be in [1, 65535]");
+  if (max_len < 1 || max_len > total) return fail(MIATTN_EINVAL, "max_len must be in [1, total]");
+  if ((st = check_ptrs({q, k, v, o, lse}))) return st;
+  if (!cu_seqlens || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
+    return fail(MIATTN_EINVAL, "cu_seqlens must be a non-null, 4-byte aligned device pointer");
+  if (causal != 0 && causal != 1) return fail(MIATTN_EINVAL, "causal must be 0 or 1");
+  if (window < 0 || (window > 0 && !causal)) return fail(MIATTN_EINVAL, "window must be 0, or >= 1 with causal");
+  if (!std::isfinite(scale)) return fail(MIATTN_EINVAL, "scale must be finite");
+  const long long qb = (long long)total * H * d * esize(dtype), kb = (long long)total * Hkv * d * esize(dtype);
+  const Range ro = span(o, qb), rl = span(lse, (long long)H * total * 4);
+  for (Range r : {span(q, qb), span(k, kb), span(v, kb)})
+    if (overlap(ro, r) || overlap(rl, r)) return fail(MIATTN_EINVAL, "o/lse must not alias q, k or v");
+  if (overlap(ro, rl)) return fail(MIATTN_EINVAL, "o and lse must not overlap");
+  const Range rcu = span(cu_seqlens, (long long)(nseq + 1) * 4);
+  if (overlap(ro, rcu) || overlap(rl, rcu)) return fail(MIATTN_EINVAL, "o/lse must not alias cu_seqlens");
+  Params p = make_params(q, k, v, o, lse, nseq, H, Hkv, total, d, causal, scale);
+  p.Nq = p.Nk = max_len;       // grid extent; each workgroup narrows to its sequence
+  p.window = window;
+  p.cu_seqlens = cu_seqlens;
+  if ((st = launch_status(fwd_block(p, dtype, dtype == MIATTN_F32, (hipStream_t)stream), "attn_fwd_varlen")))
+    return st;
+  return ok();
+}
+
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const int* cu_seqlens, int nseq, int max_len, int total, int H, int Hkv, int d, int causal,
+                    int window, float scale, void* stream, const void* dout, void* dq, void* dk, void* dv,
+                    int dtype, int accumulate) {
+  int st = check_common(1, H, Hkv, total, d, dtype);
+  if (st) return st;
+  if (nseq < 1 || nseq > 65535) return fail(MIATTN_EINVAL, "nseq must be in [1, 65535]");
+  if (max_len < 1 || max_len > total) return fail(MIATTN_EINVAL, "max_len must be in [1, total]");
+  if ((st = check_ptrs({q, k, v, o, lse, dout, dq, dk, dv}))) return st;
+  if (!cu_seqlens || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
+    return fail(MIATTN_EINVAL, "cu_seqlens must be a non-null, 4-byte aligned device pointer");
+  if (causal != 0 && causal != 1) return fail(MIATTN_EINVAL, "causal must be 0 or 1");
+  if (window < 0 || (window > 0 && !causal)) return fail(MIATTN_EINVAL, "window must be 0, or >= 1 with causal");
+  if (accumulate != 0 && accumulate != 1) return fail(MIATTN_EINVAL, "accumulate must be 0 or 1");
+  if (!std::isfinite(scale)) return fail(MIATTN_EINVAL, "scale must be finite");
+  const size_t ge = accumulate ? 4 : esize(dtype);
+  const long long qb = (long long)total * H * d * esize(dtype), kb = (long long)total * Hkv * d * esize(dtype);
+  const Range rdq = span(dq, (long long)total * H * d * ge), rdk = span(dk, (long long)total * Hkv * d * ge),
+              rdv = span(dv, (long long)total * Hkv * d * ge);
+  for (Range out : {rdq, rdk, rdv})
+    for (Range in : {span(q, qb), span(k, kb), span(v, kb), span(o, qb), span(dout, qb),
+                     span(lse, (long long)H * total * 4)})
+      if (overlap(out, in)) return fail(MIATTN_EINVAL, "dq/dk/dv must not alias an input");
+  if (overlap(rdq, rdk) || overlap(rdq, rdv) || overlap(rdk, rdv))
+    return fail(MIATTN_EINVAL, "dq, dk and dv must not overlap");
+  const Range rcu = span(cu_seqlens, (long long)(nseq + 1) * 4);
+  if (overlap(rdq, rcu) || overlap(rdk, rcu) || overlap(rdv, rcu))
+    return fail(MIATTN_EINVAL, "dq/dk/dv must not alias cu_seqlens");
+  hipStream_t s = (hipStream_t)stream;
+  Scratch scratch(s);
+  float* dsum = (float*)scratch.get((size_t)H * total * 4);
+  if (!dsum) return fail(MIATTN_ENOMEM, "hipMallocAsync failed for the rowsum vector");
+  Params p = make_params(q, k, v, const_cast<void*>(o), const_cast<float*>(lse), nseq, H, Hkv, total, d, causal,
+                         scale);
+  p.Nq = p.Nk = max_len;
+  p.window = window;
+  p.cu_seqlens = cu_seqlens;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.dsum = dsum;
+  p.accumulate = accumulate;
+  // rowsum(dout * o) is per token: the packed rows as one sequence
+  if ((st = launch_status(miattn::launch_bwd_pre(o, dout, dsum, 1, H, total, d, 0, total, dtype, s),
+                          "bwd preprocess")))
+    return st;
+  if ((st = launch_status(bwd_block(p, dtype, s), "attn_bwd_varlen"))) return st;
+  return ok();
+}
+
 int attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, const int* k_lens, void* o,
                      float* lse, int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale, int nsplit,
                      void* stream, int dtype) {

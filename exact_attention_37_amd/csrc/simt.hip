@@ -28,10 +28,15 @@ __device__ __forceinline__ long long krow(const Params& p, int b, int row) {
 
 template <typename T, typename TO, int D>
 __global__ __launch_bounds__(kRows) void fwd_simt(Params p) {
-  const int b = blockIdx.z, h = blockIdx.y;
+  int b = blockIdx.z;
+  const int h = blockIdx.y;
   const int g = h / p.G;
   const int tid = threadIdx.x;
   const int i0 = blockIdx.x * kRows;
+  if (p.cu_seqlens) {                 // packed batch: z is the sequence
+    if (!narrow_to_sequence(p, b, i0)) return;
+    b = 0;
+  }
   const int i = i0 + tid;
   const int ic = min(i, p.Nq - 1);
   const T* Q = (const T*)p.q + (qrow(p, b, p.q_start + ic) + h) * D;
@@ -97,9 +102,14 @@ __global__ __launch_bounds__(kRows) void fwd_simt(Params p) {
 // dK, dV of one key row per thread, summed over the query heads of its group.
 template <typename T, int D>
 __global__ __launch_bounds__(kRows) void bwd_dkdv_simt(Params p) {
-  const int b = blockIdx.z, g = blockIdx.y;
+  int b = blockIdx.z;
+  const int g = blockIdx.y;
   const int tid = threadIdx.x;
   const int j0 = blockIdx.x * kRows;
+  if (p.cu_seqlens) {                 // packed batch: z is the sequence
+    if (!narrow_to_sequence(p, b, j0)) return;
+    b = 0;
+  }
   const int j = j0 + tid;
   const int jc = min(j, p.Nk - 1);
   const long long kstride = (long long)p.Hkv * D;
@@ -191,10 +201,15 @@ __global__ __launch_bounds__(kRows) void bwd_dkdv_simt(Params p) {
 // dQ of one query row per thread.
 template <typename T, int D>
 __global__ __launch_bounds__(kRows) void bwd_dq_simt(Params p) {
-  const int b = blockIdx.z, h = blockIdx.y;
+  int b = blockIdx.z;
+  const int h = blockIdx.y;
   const int g = h / p.G;
   const int tid = threadIdx.x;
   const int i0 = blockIdx.x * kRows;
+  if (p.cu_seqlens) {                 // packed batch: z is the sequence
+    if (!narrow_to_sequence(p, b, i0)) return;
+    b = 0;
+  }
   const int i = i0 + tid;
   const int ic = min(i, p.Nq - 1);
   const long long kstride = (long long)p.Hkv * D;

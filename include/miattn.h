@@ -114,6 +114,36 @@ int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float*
                     int B, int H, int Hkv, int N, int d, int window, float scale,
                     void* stream, int dtype);
 
+/* Packed variable-length batch, forward: nseq sequences of different
+ * lengths stored back to back (FlashAttention-2 reviews page, reviewer 2's
+ * questions: batches whose tokens carry no explicit sequence dimension; here
+ * the boundaries are given as offsets). Sequence s owns rows
+ * [cu_seqlens[s], cu_seqlens[s + 1]) of q, k, v, o and attends only within
+ * itself, with the causal mask (and, if window > 0, the sliding window of
+ * attn_fwd_window) applied at positions relative to its first row.
+ *   q, o      : [total, H, d];  k, v: [total, Hkv, d];  lse: [H, total]
+ *   cu_seqlens: device int32 [nseq + 1], 0 = cu_seqlens[0] <= ... <=
+ *               cu_seqlens[nseq] = total, each length <= max_len. The host
+ *               cannot read them; a kernel clamps every offset to [0, total],
+ *               so malformed offsets give wrong rows but no access outside
+ *               the tensors.
+ *   max_len   : the longest sequence (sizes the grid), 1 <= max_len <= total.
+ *   window    : 0, or >= 1 with causal = 1.
+ * Errors as attn_fwd, plus MIATTN_EINVAL for nseq outside [1, 65535],
+ * max_len outside [1, total], or a null or misaligned cu_seqlens. */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* cu_seqlens, int nseq, int max_len, int total, int H, int Hkv, int d,
+                    int causal, int window, float scale, void* stream, int dtype);
+
+/* Backward of attn_fwd_varlen: dq [total, H, d], dk, dv [total, Hkv, d]
+ * (dtype, or float32 added into under accumulate = 1) from that forward's o
+ * and lse. Scratch: float32 [H, total]. Arguments and errors as
+ * attn_fwd_varlen and attn_bwd. */
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const int* cu_seqlens, int nseq, int max_len, int total, int H, int Hkv, int d,
+                    int causal, int window, float scale, void* stream, const void* dout, void* dq,
+                    void* dk, void* dv, int dtype, int accumulate);
+
 /* Backward pass: from q, k, v, the forward's o and lse, and dout = dL/dO,
  * produces dq, dk, dv without forming the N x N matrix. The forward is not
  * re-run: P is rebuilt tile by tile from the saved lse (DistFlashAttn

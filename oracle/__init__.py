@@ -6,4 +6,5 @@ baseline leg; never by the GPU library.
 from .attention import (  # noqa: F401
     scores, forward, backward, merge, tiled_forward, forward_rows,
     backward_dq_rows, backward_dkdv_rows, probs, forward_kvcache,
+    forward_varlen, backward_varlen,
 )

@@ -25,7 +25,10 @@ readings taken are listed next to each function):
 * local (sliding-window) attention is the same method with a banded mask --
   FlashAttention-2 reviews page, the authors' general response (local
   attention used to train Mistral-7B); BurstAttention rebuttal page (sparse
-  attention only changes the attention mask).
+  attention only changes the attention mask);
+* a batch may pack sequences of different lengths back to back --
+  FlashAttention-2 reviews page, reviewer 2's questions (training batches
+  whose tokens carry no explicit sequence dimension).
 
 Readings where the pages are silent (each also listed in the design notes):
 scores are scale * Q K^T with a caller-given scale; causal keeps key position
@@ -46,7 +49,7 @@ import numpy as np
 __all__ = [
     "scores", "forward", "backward", "merge", "tiled_forward",
     "forward_rows", "backward_dq_rows", "backward_dkdv_rows", "probs",
-    "forward_kvcache",
+    "forward_kvcache", "forward_varlen", "backward_varlen",
 ]
 
 
@@ -177,6 +180,61 @@ def forward_kvcache(q, k, v, k_lens, causal, scale):
         o[b] = ob[0]
         lse[b] = lb[0]
     return o, lse
+
+
+def _sequences(cu_seqlens, total):
+    """(start, end) row ranges of a packed batch, each clamped to [0, total]."""
+    cu = [int(x) for x in cu_seqlens]
+    out = []
+    for s in range(len(cu) - 1):
+        e = min(max(cu[s + 1], 0), total)
+        a = min(max(cu[s], 0), e)
+        out.append((a, e))
+    return out
+
+
+def forward_varlen(q, k, v, cu_seqlens, causal, scale, window=0):
+    """O and LSE of a packed batch of sequences of different lengths.
+
+    q: [total, H, d]; k, v: [total, Hkv, d]; sequence s owns rows
+    [cu_seqlens[s], cu_seqlens[s + 1]). Reading where the pages are silent
+    (the reviewer asks what happens without sequence boundaries): the
+    boundaries are given, and each sequence is its own attention problem --
+    its queries see only its own keys, the causal mask and the window use
+    positions counted from its first row. Rows outside every sequence are
+    left at o = 0, lse = -inf. Returns o [total, H, d] and lse [H, total],
+    float64.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    total, H, d = q.shape
+    o = np.zeros((total, H, d))
+    lse = np.full((H, total), -np.inf)
+    for a, e in _sequences(cu_seqlens, total):
+        if e == a:
+            continue
+        ob, lb = forward(q[None, a:e], k[None, a:e], v[None, a:e], causal, scale, window=window)
+        o[a:e] = ob[0]
+        lse[:, a:e] = lb[0]
+    return o, lse
+
+
+def backward_varlen(q, k, v, do, cu_seqlens, causal, scale, window=0):
+    """dQ, dK, dV of ``forward_varlen``: each sequence's gradients are those of
+    its own attention problem (``backward``); rows outside every sequence get
+    zero. Returns float64 arrays shaped like q, k, v."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    do = np.asarray(do, np.float64)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for a, e in _sequences(cu_seqlens, q.shape[0]):
+        if e == a:
+            continue
+        g = backward(q[None, a:e], k[None, a:e], v[None, a:e], do[None, a:e], causal, scale, window=window)
+        dq[a:e], dk[a:e], dv[a:e] = g[0][0], g[1][0], g[2][0]
+    return dq, dk, dv
 
 
 def forward_rows(q, k, v, causal, scale, b, h, rows):

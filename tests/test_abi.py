@@ -162,3 +162,48 @@ def test_window_entry_points_reject_bad_windows():
     assert L.attn_fwd_window(*q, 1, 2, 2, 16, 96, 4, 0.1, None, 1) == 2
     assert L.attn_bwd_window(*q, 1, 2, 2, 16, 64, -3, 0.1, None, vp(FAKE * 6), vp(FAKE * 7), vp(FAKE * 8),
                              vp(FAKE * 9), 1, 0) == 1
+
+
+def varlen_call(bwd=False, **kw):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, o=FAKE * 4, lse=FAKE * 5, cu=FAKE * 6, nseq=3, max_len=40,
+             total=100, H=4, Hkv=2, d=128, causal=1, window=0, scale=0.1, dtype=1, dout=FAKE * 7,
+             dq=FAKE * 8, dk=FAKE * 9, dv=FAKE * 10, accumulate=0)
+    a.update(kw)
+    L = mi.lib()
+    head = (vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["o"]), vp(a["lse"]), vp(a["cu"]), a["nseq"],
+            a["max_len"], a["total"], a["H"], a["Hkv"], a["d"], a["causal"], a["window"], a["scale"], None)
+    if not bwd:
+        return L.attn_fwd_varlen(*head, a["dtype"])
+    return L.attn_bwd_varlen(*head, vp(a["dout"]), vp(a["dq"]), vp(a["dk"]), vp(a["dv"]), a["dtype"],
+                             a["accumulate"])
+
+
+@pytest.mark.parametrize("bwd", [False, True])
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(q=0), 1, "null"),
+    (dict(cu=0), 1, "cu_seqlens"),
+    (dict(cu=FAKE * 6 + 2), 1, "cu_seqlens"),
+    (dict(nseq=0), 1, "nseq"),
+    (dict(nseq=70000), 1, "nseq"),
+    (dict(max_len=0), 1, "max_len"),
+    (dict(max_len=101), 1, "max_len"),
+    (dict(total=0), 1, ">= 1"),
+    (dict(H=6, Hkv=4), 1, "multiple"),
+    (dict(d=96), 2, "64 or 128"),
+    (dict(dtype=5), 2, "dtype"),
+    (dict(causal=2), 1, "causal"),
+    (dict(window=4, causal=0), 1, "window"),
+    (dict(window=-1), 1, "window"),
+    (dict(scale=float("inf")), 1, "finite"),
+])
+def test_varlen_rejects_bad_arguments(bwd, kw, code, msg):
+    assert varlen_call(bwd, **kw) == code
+    assert msg in mi.lib().attn_last_error().decode()
+
+
+def test_varlen_rejects_outputs_aliasing_inputs():
+    assert varlen_call(False, o=FAKE * 2) == 1 and b"alias" in mi.lib().attn_last_error()
+    assert varlen_call(False, lse=FAKE * 6) == 1 and b"cu_seqlens" in mi.lib().attn_last_error()
+    assert varlen_call(True, dk=FAKE * 6) == 1 and b"cu_seqlens" in mi.lib().attn_last_error()
+    assert varlen_call(True, dq=FAKE) == 1 and b"alias" in mi.lib().attn_last_error()
+    assert varlen_call(True, accumulate=2) == 1 and b"accumulate" in mi.lib().attn_last_error()

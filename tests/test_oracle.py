@@ -515,3 +515,103 @@ def test_window_backward_matches_finite_differences():
             args_m = [xm if y is x else y for y in (q, k, v)]
             num[idx] = (f(*args_p) - f(*args_m)) / (2 * eps)
         assert np.max(np.abs(num - g)) < 1e-7
+
+
+# ---------------------------------------------------------------- packed variable-length batches
+
+def _varlen_by_loops(q, k, v, cu, causal, scale, window=0):
+    """Packed-batch attention element by element with math.exp: token i of
+    sequence s sees the tokens j of the same sequence (j <= i under causal,
+    and i - window < j with a window)."""
+    total, H, d = q.shape
+    G = H // k.shape[1]
+    seq_of = [None] * total
+    for s in range(len(cu) - 1):
+        for t in range(int(cu[s]), int(cu[s + 1])):
+            seq_of[t] = s
+    o = np.zeros(q.shape)
+    lse = np.full((H, total), -np.inf)
+    for h in range(H):
+        g = h // G
+        for i in range(total):
+            keys = [j for j in range(total) if seq_of[j] == seq_of[i] and (not causal or j <= i)
+                    and (window == 0 or i - j < window)]
+            sc = [scale * sum(float(q[i, h, c]) * float(k[j, g, c]) for c in range(d)) for j in keys]
+            mx = max(sc)
+            w = [math.exp(x - mx) for x in sc]
+            tot = sum(w)
+            lse[h, i] = mx + math.log(tot)
+            for c in range(d):
+                o[i, h, c] = sum(wj * float(v[j, g, c]) for wj, j in zip(w, keys)) / tot
+    return o, lse
+
+
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 2)])
+def test_varlen_matches_elementwise_loops(causal, window):
+    from workloads import draw_varlen
+    q, k, v, _, cu = draw_varlen([3, 0, 5, 1, 4], 4, 2, 3, seed=91, dtype=torch.float64)
+    o, lse = oracle.forward_varlen(q.numpy(), k.numpy(), v.numpy(), cu.numpy(), causal, 0.7, window)
+    ro, rl = _varlen_by_loops(q.numpy(), k.numpy(), v.numpy(), cu.numpy(), causal, 0.7, window)
+    assert np.max(np.abs(o - ro)) < 1e-12 and np.max(np.abs(lse - rl)) < 1e-12
+
+
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 3)])
+def test_varlen_matches_torch_block_diagonal_attention(causal, window):
+    # the packed batch as one sequence under a block-diagonal mask, through
+    # torch's float64 attention and autograd
+    from workloads import draw_varlen
+    lengths = [6, 1, 9, 4]
+    q, k, v, do, cu = draw_varlen(lengths, 4, 2, 8, seed=92, dtype=torch.float64)
+    scale = 0.35
+    o, lse = oracle.forward_varlen(q.numpy(), k.numpy(), v.numpy(), cu.numpy(), causal, scale, window)
+    dq, dk, dv = oracle.backward_varlen(q.numpy(), k.numpy(), v.numpy(), do.numpy(), cu.numpy(), causal,
+                                        scale, window)
+    seq = torch.repeat_interleave(torch.arange(len(lengths)), torch.tensor(lengths))
+    pos = torch.arange(seq.numel())
+    allow = seq[:, None] == seq[None, :]
+    if causal:
+        allow &= pos[None, :] <= pos[:, None]
+    if window:
+        allow &= pos[:, None] - pos[None, :] < window
+    tq = q.permute(1, 0, 2).clone().requires_grad_(True)
+    tk = k.permute(1, 0, 2).clone().requires_grad_(True)
+    tv = v.permute(1, 0, 2).clone().requires_grad_(True)
+    to = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk.repeat_interleave(2, dim=0), tv.repeat_interleave(2, dim=0), attn_mask=allow, scale=scale)
+    to.backward(do.permute(1, 0, 2))
+    np.testing.assert_allclose(o, to.detach().permute(1, 0, 2).numpy(), atol=1e-12)
+    np.testing.assert_allclose(dq, tq.grad.permute(1, 0, 2).numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.permute(1, 0, 2).numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.permute(1, 0, 2).numpy(), atol=1e-12)
+    s = torch.matmul(q.permute(1, 0, 2), k.permute(1, 2, 0).repeat_interleave(2, dim=0)) * scale
+    ref_lse = torch.logsumexp(s.masked_fill(~allow, float("-inf")), dim=-1)
+    np.testing.assert_allclose(lse, ref_lse.numpy(), atol=1e-12)
+
+
+def test_varlen_equal_lengths_is_batched_attention():
+    from workloads import draw_varlen
+    q, k, v, do, cu = draw_varlen([7, 7, 7], 2, 1, 4, seed=93, dtype=torch.float64)
+    o, lse = oracle.forward_varlen(q.numpy(), k.numpy(), v.numpy(), cu.numpy(), True, 0.5)
+    bo, bl = oracle.forward(q.numpy().reshape(3, 7, 2, 4), k.numpy().reshape(3, 7, 1, 4),
+                            v.numpy().reshape(3, 7, 1, 4), True, 0.5)
+    assert np.array_equal(o, bo.reshape(21, 2, 4))
+    assert np.array_equal(lse, bl.transpose(1, 0, 2).reshape(2, 21))
+    g = oracle.backward_varlen(q.numpy(), k.numpy(), v.numpy(), do.numpy(), cu.numpy(), True, 0.5)
+    bg = oracle.backward(*(t.numpy().reshape(3, 7, t.shape[1], 4) for t in (q, k, v, do)), True, 0.5)
+    assert all(np.array_equal(x, y.reshape(x.shape)) for x, y in zip(g, bg))
+
+
+def test_varlen_sequences_do_not_see_each_other():
+    from workloads import draw_varlen
+    q, k, v, do, cu = draw_varlen([5, 8, 3], 2, 2, 4, seed=94, dtype=torch.float64)
+    base = oracle.forward_varlen(q.numpy(), k.numpy(), v.numpy(), cu.numpy(), False, 0.5)
+    gb = oracle.backward_varlen(q.numpy(), k.numpy(), v.numpy(), do.numpy(), cu.numpy(), False, 0.5)
+    k2, v2 = k.numpy().copy(), v.numpy().copy()
+    k2[5:13] += 3.0
+    v2[5:13] -= 2.0
+    pert = oracle.forward_varlen(q.numpy(), k2, v2, cu.numpy(), False, 0.5)
+    gp = oracle.backward_varlen(q.numpy(), k2, v2, do.numpy(), cu.numpy(), False, 0.5)
+    keep = np.r_[0:5, 13:16]
+    assert np.array_equal(base[0][keep], pert[0][keep]) and np.array_equal(base[1][:, keep], pert[1][:, keep])
+    assert all(np.array_equal(x[keep], y[keep]) for x, y in zip(gb, gp))
+    assert not np.allclose(base[0][5:13], pert[0][5:13])

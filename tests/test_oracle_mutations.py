@@ -23,6 +23,8 @@ def _pins():
     yield lambda: T.test_kvcache_matches_elementwise_loops(True)
     yield lambda: T.test_kvcache_ignores_rows_past_the_valid_length()
     yield lambda: T.test_window_matches_elementwise_loops(3)
+    yield lambda: T.test_varlen_matches_elementwise_loops(True, 0)
+    yield lambda: T.test_varlen_matches_torch_block_diagonal_attention(True, 0)
 
 
 def _caught():
@@ -86,7 +88,25 @@ def _kvcache_whole_cache(q, k, v, k_lens, causal, scale):
     return _orig_kvcache(q, k, v, None, causal, scale)
 
 
+def _varlen_one_sequence(q, k, v, cu_seqlens, causal, scale, window=0):
+    # sequence boundaries ignored: the pack attended to as one sequence
+    return _orig_varlen(q, k, v, [0, np.asarray(q).shape[0]], causal, scale, window)
+
+
+def _varlen_backward_one_sequence(q, k, v, do, cu_seqlens, causal, scale, window=0):
+    return _orig_varlen_bwd(q, k, v, do, [0, np.asarray(q).shape[0]], causal, scale, window)
+
+
+def _varlen_offset_by_one(q, k, v, cu_seqlens, causal, scale, window=0):
+    # each boundary taken one row late
+    cu = [min(int(c) + 1, np.asarray(q).shape[0]) for c in cu_seqlens]
+    cu[0] = 0
+    return _orig_varlen(q, k, v, cu, causal, scale, window)
+
+
 _orig_scores = A.scores
+_orig_varlen = A.forward_varlen
+_orig_varlen_bwd = A.backward_varlen
 _orig_kvcache = A.forward_kvcache
 _orig_softmax = A._softmax_rows
 _orig_merge = A.merge
@@ -100,6 +120,9 @@ MUTATIONS = {
     "kvcache_top_left_alignment": ("forward_kvcache", _kvcache_top_left),
     "window_off_by_one": ("scores", _window_off_by_one),
     "kvcache_lengths_ignored": ("forward_kvcache", _kvcache_whole_cache),
+    "varlen_boundaries_ignored": ("forward_varlen", _varlen_one_sequence),
+    "varlen_backward_boundaries_ignored": ("backward_varlen", _varlen_backward_one_sequence),
+    "varlen_boundaries_off_by_one": ("forward_varlen", _varlen_offset_by_one),
 }
 
 
@@ -107,7 +130,7 @@ MUTATIONS = {
 def test_pins_catch_planted_mistake(name, monkeypatch):
     attr, fn = MUTATIONS[name]
     monkeypatch.setattr(A, attr, fn)
-    if attr in ("merge", "forward_kvcache"):   # re-exported by the package
+    if attr in ("merge", "forward_kvcache", "forward_varlen", "backward_varlen"):   # re-exported by the package
         import oracle
         monkeypatch.setattr(oracle, attr, fn)
     assert _caught(), "planted mistake %r passed every pin" % name

@@ -29,6 +29,13 @@ whose valid lengths are drawn uniformly from [8K, 16K]; ``prefill16k`` -- 4
 sequences appending 128 rows each to the same kind of cache. Draw order:
 Q [B, Nq, H, d], K cache, V cache [B, Nk, Hkv, d] as above, then the lengths
 with ``torch.randint`` from the same generator.
+
+Packed variable-length workload (a training batch of documents of different
+lengths stored back to back): ``packed16k`` -- Llama-7B heads, bf16, causal,
+16384 tokens split into sequences whose lengths are drawn uniformly from
+[256, 4096] until the tokens run out (the last one takes the remainder).
+Draw order: the lengths with ``torch.randint`` one at a time, then Q, K, V,
+dO at [total, heads, d] from the same generator.
 """
 from __future__ import annotations
 
@@ -128,6 +135,52 @@ def draw_cache(B: int, H: int, Hkv: int, Nq: int, Nk: int, d: int, seed: int,
 
 def draw_cache_workload(w: CacheWorkload):
     return draw_cache(w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d, w.seed, w.min_len)
+
+
+@dataclass(frozen=True)
+class VarlenWorkload:
+    name: str
+    total: int                 # packed tokens
+    H: int
+    Hkv: int
+    d: int
+    min_len: int               # sequence lengths drawn from [min_len, max_draw]
+    max_draw: int
+    seed: int = 1
+
+
+VARLEN_WORKLOADS = {
+    "packed16k": VarlenWorkload("packed16k", 16384, 32, 32, 128, 256, 4096, seed=8),
+}
+
+
+def draw_varlen(lengths, H: int, Hkv: int, d: int, seed: int, dtype: torch.dtype = torch.bfloat16,
+                gen: torch.Generator | None = None):
+    """Return (q, k, v, do [total, heads, d], cu_seqlens int32 [nseq + 1]) as CPU
+    tensors for sequences of the given lengths (zero-length ones allowed)."""
+    g = torch.Generator("cpu").manual_seed(int(seed)) if gen is None else gen
+    lengths = [int(x) for x in lengths]
+    total = sum(lengths)
+    q = torch.randn((total, H, d), generator=g, dtype=torch.float32).to(dtype)
+    k = torch.randn((total, Hkv, d), generator=g, dtype=torch.float32).to(dtype)
+    v = torch.randn((total, Hkv, d), generator=g, dtype=torch.float32).to(dtype)
+    do = torch.randn((total, H, d), generator=g, dtype=torch.float32).to(dtype)
+    cu = torch.tensor([0] + list(np.cumsum(lengths)), dtype=torch.int32) if lengths else \
+        torch.zeros(1, dtype=torch.int32)
+    return q, k, v, do, cu
+
+
+def draw_varlen_workload(w: VarlenWorkload, total: int | None = None):
+    """Inputs of ``w`` (optionally with fewer packed tokens): the lengths are
+    drawn first, then the tensors, from one generator."""
+    total = w.total if total is None else int(total)
+    g = torch.Generator("cpu").manual_seed(int(w.seed))
+    lengths, left = [], total
+    while left > 0:
+        n = int(torch.randint(w.min_len, w.max_draw + 1, (1,), generator=g).item())
+        lengths.append(min(n, left))
+        left -= lengths[-1]
+    return draw_varlen(lengths, w.H, w.Hkv, w.d, w.seed, gen=g)
 
 
 def as_f64(t: torch.Tensor) -> np.ndarray:
