@@ -28,7 +28,12 @@ readings taken are listed next to each function):
   attention only changes the attention mask);
 * a batch may pack sequences of different lengths back to back --
   FlashAttention-2 reviews page, reviewer 2's questions (training batches
-  whose tokens carry no explicit sequence dimension).
+  whose tokens carry no explicit sequence dimension);
+* block-sparse attention computes only the blocks a block mask keeps --
+  FlashAttention abstract page (the extension to block-sparse attention, an
+  approximation of dense attention); FlashAttention-2 reviews page, reviewer
+  3's question on sparse block masks; BurstAttention rebuttal page (sparsity
+  is a change of the attention mask).
 
 Readings where the pages are silent (each also listed in the design notes):
 scores are scale * Q K^T with a caller-given scale; causal keeps key position
@@ -50,6 +55,8 @@ __all__ = [
     "scores", "forward", "backward", "merge", "tiled_forward",
     "forward_rows", "backward_dq_rows", "backward_dkdv_rows", "probs",
     "forward_kvcache", "forward_varlen", "backward_varlen",
+    "block_allowed", "forward_blocksparse", "backward_blocksparse",
+    "blocksparse_rows", "blocksparse_dkdv_cols",
 ]
 
 
@@ -235,6 +242,122 @@ def backward_varlen(q, k, v, do, cu_seqlens, causal, scale, window=0):
         g = backward(q[None, a:e], k[None, a:e], v[None, a:e], do[None, a:e], causal, scale, window=window)
         dq[a:e], dk[a:e], dv[a:e] = g[0][0], g[1][0], g[2][0]
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# block-sparse attention
+# ---------------------------------------------------------------------------
+#
+# Reading where the pages are silent: the block mask has one entry per block
+# of bq query rows x bk keys (the library fixes bq = 256, bk = 128); a zero
+# entry removes every (query, key) pair of its block, on top of the causal
+# mask. The result is exact attention under that mask (and an approximation
+# of dense attention, which is the pages' point). A query row left with no
+# key gets o = 0 and lse = -inf (the merge identity) and zero gradients.
+
+def block_allowed(block_mask, Nq, Nk, bq=256, bk=128):
+    """allowed[i, j] = block_mask[i // bq, j // bk] != 0, for i < Nq, j < Nk."""
+    bm = np.asarray(block_mask) != 0
+    return bm[np.arange(Nq)[:, None] // bq, np.arange(Nk)[None, :] // bk]
+
+
+def _masked_scores(q_h, k_g, scale, causal, allowed):
+    return np.where(allowed, scores(q_h, k_g, scale, causal), -np.inf)
+
+
+def forward_blocksparse(q, k, v, block_mask, causal, scale, bq=256, bk=128):
+    """O [B, N, H, d] and LSE [B, H, N] (float64) of attention under a block
+    mask (see above), one (batch, head) at a time."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    B, N, H, Hkv, d, Nk = _check(q, k, v)
+    G = H // Hkv
+    allowed = block_allowed(block_mask, N, Nk, bq, bk)
+    o = np.zeros((B, N, H, d))
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            p, l = _softmax_rows(_masked_scores(q[b, :, h], k[b, :, h // G], scale, causal, allowed))
+            o[b, :, h] = p @ v[b, :, h // G]
+            lse[b, h] = l
+    return o, lse
+
+
+def backward_blocksparse(q, k, v, do, block_mask, causal, scale, bq=256, bk=128):
+    """dQ, dK, dV of ``forward_blocksparse``: the gradient formulas of
+    ``backward`` with P taken under the block mask (float64)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    do = np.asarray(do, np.float64)
+    B, N, H, Hkv, d, Nk = _check(q, k, v)
+    G = H // Hkv
+    allowed = block_allowed(block_mask, N, Nk, bq, bk)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            g = h // G
+            p, _ = _softmax_rows(_masked_scores(q[b, :, h], k[b, :, g], scale, causal, allowed))
+            dv[b, :, g] += p.T @ do[b, :, h]
+            dp = do[b, :, h] @ v[b, :, g].T
+            ds = p * (dp - np.sum(p * dp, axis=1)[:, None])
+            dq[b, :, h] = scale * (ds @ k[b, :, g])
+            dk[b, :, g] += scale * (ds.T @ q[b, :, h])
+    return dq, dk, dv
+
+
+def blocksparse_rows(q, k, v, do, block_mask, causal, scale, b, h, rows, bq=256, bk=128):
+    """O, LSE and dQ of selected query rows of one (batch, head) under a block
+    mask; every quantity of a query row depends on that row alone, so long
+    sequences can be checked by sampling."""
+    G = q.shape[2] // k.shape[2]
+    kg = np.asarray(k[b, :, h // G], np.float64)
+    vg = np.asarray(v[b, :, h // G], np.float64)
+    rows = np.asarray(rows)
+    qh = np.asarray(q[b, rows, h], np.float64)
+    doh = np.asarray(do[b, rows, h], np.float64)
+    bm = np.asarray(block_mask) != 0
+    allowed = bm[rows[:, None] // bq, np.arange(kg.shape[0])[None, :] // bk]
+    s = scale * (qh @ kg.T)
+    if causal:
+        allowed = allowed & (np.arange(kg.shape[0])[None, :] <= rows[:, None])
+    p, lse = _softmax_rows(np.where(allowed, s, -np.inf))
+    dp = doh @ vg.T
+    ds = p * (dp - np.sum(p * dp, axis=1)[:, None])
+    return p @ vg, lse, scale * (ds @ kg)
+
+
+def blocksparse_dkdv_cols(q, k, v, do, block_mask, causal, scale, b, g, cols, bq=256, bk=128, row_block=512):
+    """dK and dV of selected key rows of K/V head g under a block mask, summed
+    over the query heads of the group. Each query row's LSE is computed over
+    all its keys (row blocks at a time); P and dS are then taken for the
+    selected keys only."""
+    H, Hkv = q.shape[2], k.shape[2]
+    G = H // Hkv
+    kg = np.asarray(k[b, :, g], np.float64)
+    vg = np.asarray(v[b, :, g], np.float64)
+    cols = np.asarray(cols)
+    N, Nk = q.shape[1], kg.shape[0]
+    bm = np.asarray(block_mask) != 0
+    dk = np.zeros((len(cols), kg.shape[1]))
+    dv = np.zeros((len(cols), kg.shape[1]))
+    for h in range(g * G, (g + 1) * G):
+        for r0, r1 in _row_blocks(N, row_block):
+            ri = np.arange(r0, r1)
+            qh = np.asarray(q[b, r0:r1, h], np.float64)
+            doh = np.asarray(do[b, r0:r1, h], np.float64)
+            allowed = bm[ri[:, None] // bq, np.arange(Nk)[None, :] // bk]
+            if causal:
+                allowed = allowed & (np.arange(Nk)[None, :] <= ri[:, None])
+            p, _ = _softmax_rows(np.where(allowed, scale * (qh @ kg.T), -np.inf))
+            dp = doh @ vg.T
+            rowdot = np.sum(p * dp, axis=1)
+            pc = p[:, cols]
+            dsc = pc * (dp[:, cols] - rowdot[:, None])
+            dv += pc.T @ doh
+            dk += scale * (dsc.T @ qh)
+    return dk, dv
 
 
 def forward_rows(q, k, v, causal, scale, b, h, rows):

@@ -615,3 +615,154 @@ def test_varlen_sequences_do_not_see_each_other():
     assert np.array_equal(base[0][keep], pert[0][keep]) and np.array_equal(base[1][:, keep], pert[1][:, keep])
     assert all(np.array_equal(x[keep], y[keep]) for x, y in zip(gb, gp))
     assert not np.allclose(base[0][5:13], pert[0][5:13])
+
+
+# ---------------------------------------------------------------- block-sparse attention
+
+def _bs_mask(nbr, nbc, seed, density=0.5):
+    return (np.random.default_rng(seed).random((nbr, nbc)) < density).astype(np.uint8)
+
+
+def _blocksparse_by_loops(q, k, v, mask, causal, scale, bq, bk):
+    """Block-sparse attention element by element with math.exp: query i sees
+    key j iff mask[i // bq][j // bk] != 0 (and j <= i under causal); a row
+    with no key gets o = 0, lse = -inf."""
+    B, N, H, d = q.shape
+    G = H // k.shape[2]
+    o = np.zeros(q.shape)
+    lse = np.full((B, H, N), -np.inf)
+    for b in range(B):
+        for h in range(H):
+            g = h // G
+            for i in range(N):
+                keys = [j for j in range(N) if mask[i // bq][j // bk] and (not causal or j <= i)]
+                if not keys:
+                    continue
+                sc = [scale * sum(float(q[b, i, h, c]) * float(k[b, j, g, c]) for c in range(d)) for j in keys]
+                mx = max(sc)
+                w = [math.exp(x - mx) for x in sc]
+                tot = sum(w)
+                lse[b, h, i] = mx + math.log(tot)
+                for c in range(d):
+                    o[b, i, h, c] = sum(wj * float(v[b, j, g, c]) for wj, j in zip(w, keys)) / tot
+    return o, lse
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_blocksparse_matches_elementwise_loops(causal):
+    q, k, v, _ = draw(1, 4, 2, 11, 3, seed=101, dtype=torch.float64)
+    mask = np.array([[0, 1, 1, 1], [0, 1, 0, 1], [1, 1, 0, 0]], np.uint8)   # 4-row x 3-key blocks
+    o, lse = oracle.forward_blocksparse(q.numpy(), k.numpy(), v.numpy(), mask, causal, 0.6, bq=4, bk=3)
+    ro, rl = _blocksparse_by_loops(q.numpy(), k.numpy(), v.numpy(), mask, causal, 0.6, 4, 3)
+    assert np.array_equal(np.isfinite(lse), np.isfinite(rl))
+    fin = np.isfinite(rl)
+    assert np.max(np.abs(o - ro)) < 1e-12 and np.max(np.abs(lse[fin] - rl[fin])) < 1e-12
+    if causal:   # rows 0-2 see only key block 0, masked out for row block 0: empty
+        assert np.all(lse[:, :, :3] == -np.inf) and np.all(o[:, :3] == 0.0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_blocksparse_matches_torch_masked_attention(causal):
+    # the expanded element mask through torch's float64 attention and autograd
+    # (the mask keeps the diagonal blocks, so no row is empty)
+    B, H, Hkv, N, d, bq, bk = 2, 4, 2, 20, 8, 4, 2
+    q, k, v, do = rnd(B, H, Hkv, N, d, 102)
+    mask = _bs_mask(5, 10, 7)
+    for r in range(5):
+        mask[r, 2 * r:2 * r + 2] = 1
+    scale = 0.4
+    o, lse = oracle.forward_blocksparse(q, k, v, mask, causal, scale, bq, bk)
+    dq, dk, dv = oracle.backward_blocksparse(q, k, v, do, mask, causal, scale, bq, bk)
+    allow = torch.tensor(mask[np.arange(N)[:, None] // bq, np.arange(N)[None, :] // bk] != 0)
+    if causal:
+        allow &= torch.ones(N, N, dtype=torch.bool).tril()
+    tq = torch.tensor(q).permute(0, 2, 1, 3).requires_grad_(True)
+    tk = torch.tensor(k).permute(0, 2, 1, 3).requires_grad_(True)
+    tv = torch.tensor(v).permute(0, 2, 1, 3).requires_grad_(True)
+    to = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk.repeat_interleave(2, dim=1), tv.repeat_interleave(2, dim=1), attn_mask=allow, scale=scale)
+    to.backward(torch.tensor(do).permute(0, 2, 1, 3))
+    np.testing.assert_allclose(o, to.detach().permute(0, 2, 1, 3).numpy(), atol=1e-12)
+    np.testing.assert_allclose(dq, tq.grad.permute(0, 2, 1, 3).numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.permute(0, 2, 1, 3).numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.permute(0, 2, 1, 3).numpy(), atol=1e-12)
+    s = torch.matmul(tq.detach(), tk.detach().repeat_interleave(2, dim=1).transpose(-1, -2)) * scale
+    np.testing.assert_allclose(lse, torch.logsumexp(s.masked_fill(~allow, float("-inf")), -1).numpy(),
+                               atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_blocksparse_with_every_block_kept_is_dense_attention(causal):
+    q, k, v, do = rnd(1, 2, 1, 13, 4, 103)
+    ones = np.ones((4, 7), np.uint8)
+    a = oracle.forward_blocksparse(q, k, v, ones, causal, 0.5, 4, 2)
+    b = oracle.forward(q, k, v, causal, 0.5)
+    assert np.max(np.abs(a[0] - b[0])) < 1e-14 and np.max(np.abs(a[1] - b[1])) < 1e-14
+    ga = oracle.backward_blocksparse(q, k, v, do, ones, causal, 0.5, 4, 2)
+    gb = oracle.backward(q, k, v, do, causal, 0.5)
+    assert all(np.max(np.abs(x - y)) < 1e-14 for x, y in zip(ga, gb))
+
+
+def test_blocksparse_equals_attention_over_the_kept_keys():
+    # non-causal: each row block attends to exactly the keys of its kept
+    # blocks, so deleting the other keys gives the same rows
+    q, k, v, _ = rnd(1, 2, 2, 24, 4, 104)
+    mask = np.array([[1, 0, 0, 1], [0, 1, 1, 0], [1, 1, 1, 0]], np.uint8)   # 8-row x 6-key blocks
+    o, lse = oracle.forward_blocksparse(q, k, v, mask, False, 0.7, 8, 6)
+    for r in range(3):
+        keys = np.concatenate([np.arange(6 * c, 6 * c + 6) for c in range(4) if mask[r, c]])
+        ro, rl = oracle.forward(q[:, 8 * r:8 * r + 8], k[:, keys], v[:, keys], False, 0.7)
+        assert np.max(np.abs(o[:, 8 * r:8 * r + 8] - ro)) < 1e-13
+        assert np.max(np.abs(lse[:, :, 8 * r:8 * r + 8] - rl)) < 1e-13
+
+
+def test_blocksparse_empty_rows_have_no_gradient_path():
+    q, k, v, do = rnd(1, 2, 2, 12, 4, 105)
+    mask = np.array([[0, 1], [1, 1], [0, 0]], np.uint8)                    # 4-row x 6-key blocks
+    o, lse = oracle.forward_blocksparse(q, k, v, mask, True, 0.5, 4, 6)
+    assert np.all(lse[:, :, 0:4] == -np.inf) and np.all(lse[:, :, 8:12] == -np.inf)
+    assert np.all(o[:, 0:4] == 0.0) and np.all(o[:, 8:12] == 0.0)
+    dq, dk, dv = oracle.backward_blocksparse(q, k, v, do, mask, True, 0.5, 4, 6)
+    assert np.all(dq[:, 0:4] == 0.0) and np.all(dq[:, 8:12] == 0.0)
+    do2 = do.copy()
+    do2[:, 0:4] += 5.0
+    do2[:, 8:12] -= 3.0
+    g2 = oracle.backward_blocksparse(q, k, v, do2, mask, True, 0.5, 4, 6)
+    assert np.array_equal(g2[1], dk) and np.array_equal(g2[2], dv)
+
+
+def test_blocksparse_backward_matches_finite_differences():
+    q, k, v, do = rnd(1, 2, 1, 9, 3, 106)
+    mask = np.array([[1, 0, 1], [1, 1, 0], [0, 1, 1]], np.uint8)          # 3-row x 3-key blocks
+    f = lambda qq, kk, vv: float(np.sum(do * oracle.forward_blocksparse(qq, kk, vv, mask, False, 0.8, 3, 3)[0]))
+    grads = oracle.backward_blocksparse(q, k, v, do, mask, False, 0.8, 3, 3)
+    eps = 1e-6
+    for x, g in zip((q, k, v), grads):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            old = x[idx]
+            x[idx] = old + eps
+            fp = f(q, k, v)
+            x[idx] = old - eps
+            fm = f(q, k, v)
+            x[idx] = old
+            num[idx] = (fp - fm) / (2 * eps)
+        assert np.max(np.abs(num - g)) < 2e-8
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_blocksparse_row_and_column_helpers_match_full(causal):
+    q, k, v, do = rnd(1, 4, 2, 40, 4, 107)
+    mask = _bs_mask(5, 10, 8)
+    o, lse = oracle.forward_blocksparse(q, k, v, mask, causal, 0.3, 8, 4)
+    dq, dk, dv = oracle.backward_blocksparse(q, k, v, do, mask, causal, 0.3, 8, 4)
+    rows = [0, 3, 9, 17, 31, 39]
+    for h in range(4):
+        ro, rl, rq = oracle.blocksparse_rows(q, k, v, do, mask, causal, 0.3, 0, h, rows, 8, 4)
+        fin = np.isfinite(rl)
+        assert np.array_equal(fin, np.isfinite(lse[0, h, rows]))
+        assert np.max(np.abs(ro - o[0, rows, h])) < 1e-13 and np.max(np.abs(rl[fin] - lse[0, h, rows][fin])) < 1e-13
+        assert np.max(np.abs(rq - dq[0, rows, h])) < 1e-13
+    for g in range(2):
+        rk, rv = oracle.blocksparse_dkdv_cols(q, k, v, do, mask, causal, 0.3, 0, g, rows, 8, 4, row_block=16)
+        assert np.max(np.abs(rk - dk[0, rows, g])) < 1e-13 and np.max(np.abs(rv - dv[0, rows, g])) < 1e-13

@@ -25,6 +25,9 @@ def _pins():
     yield lambda: T.test_window_matches_elementwise_loops(3)
     yield lambda: T.test_varlen_matches_elementwise_loops(True, 0)
     yield lambda: T.test_varlen_matches_torch_block_diagonal_attention(True, 0)
+    yield lambda: T.test_blocksparse_matches_elementwise_loops(True)
+    yield lambda: T.test_blocksparse_matches_torch_masked_attention(False)
+    yield lambda: T.test_blocksparse_equals_attention_over_the_kept_keys()
 
 
 def _caught():
@@ -104,6 +107,21 @@ def _varlen_offset_by_one(q, k, v, cu_seqlens, causal, scale, window=0):
     return _orig_varlen(q, k, v, cu, causal, scale, window)
 
 
+def _block_allowed_transposed(block_mask, Nq, Nk, bq=256, bk=128):
+    # block mask indexed [key block, query block]
+    bm = np.asarray(block_mask) != 0
+    r = np.minimum(np.arange(Nq)[:, None] // bq, bm.shape[1] - 1)
+    c = np.minimum(np.arange(Nk)[None, :] // bk, bm.shape[0] - 1)
+    return bm[c, r]
+
+
+def _block_allowed_sizes_swapped(block_mask, Nq, Nk, bq=256, bk=128):
+    bm = np.asarray(block_mask) != 0
+    r = np.minimum(np.arange(Nq)[:, None] // bk, bm.shape[0] - 1)
+    c = np.minimum(np.arange(Nk)[None, :] // bq, bm.shape[1] - 1)
+    return bm[r, c]
+
+
 _orig_scores = A.scores
 _orig_varlen = A.forward_varlen
 _orig_varlen_bwd = A.backward_varlen
@@ -123,6 +141,8 @@ MUTATIONS = {
     "varlen_boundaries_ignored": ("forward_varlen", _varlen_one_sequence),
     "varlen_backward_boundaries_ignored": ("backward_varlen", _varlen_backward_one_sequence),
     "varlen_boundaries_off_by_one": ("forward_varlen", _varlen_offset_by_one),
+    "block_mask_transposed": ("block_allowed", _block_allowed_transposed),
+    "block_sizes_swapped": ("block_allowed", _block_allowed_sizes_swapped),
 }
 
 
@@ -130,7 +150,8 @@ MUTATIONS = {
 def test_pins_catch_planted_mistake(name, monkeypatch):
     attr, fn = MUTATIONS[name]
     monkeypatch.setattr(A, attr, fn)
-    if attr in ("merge", "forward_kvcache", "forward_varlen", "backward_varlen"):   # re-exported by the package
+    if attr in ("merge", "forward_kvcache", "forward_varlen", "backward_varlen", "block_allowed"):
+        # re-exported by the package
         import oracle
         monkeypatch.setattr(oracle, attr, fn)
     assert _caught(), "planted mistake %r passed every pin" % name
