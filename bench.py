@@ -27,7 +27,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 # rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; calibrated against a plain
 # 1 GiB device copy in the same process), valid only for the kernel sources
 # whose SHA-1 is recorded with it (profiles/llama16k_causal_bf16_traffic.md).
-DKDV_TRAFFIC = {"sources_sha1": "fe856ed0aa36b4a988d13916c04d4c778d3f54f1", "bytes": 2849749894}   # fetch 2.581 GB + write 0.269 GB
+DKDV_TRAFFIC = {"sources_sha1": "01adacfcb764657bfaf668e1bbc89d6c0ff902bd", "bytes": 2849911549}   # fetch 2.581 GB + write 0.268 GB
 DKDV_SOURCES = ("exact_attention_37_amd/csrc/bwd_mfma.hip", "exact_attention_37_amd/csrc/mfma_common.h",
                 "exact_attention_37_amd/csrc/common.h")
 
@@ -188,6 +188,52 @@ def bench_varlen(mi, torch, reps=10):
             "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2)}
 
 
+def visible_pairs_blocksparse(mask, N, causal, rows=256, cols=128):
+    """(query, key) pairs a block mask keeps (and the causal mask allows)."""
+    import numpy as np
+    total = 0
+    i = np.arange(N)
+    for r, c in zip(*np.nonzero(mask)):
+        ii = i[r * rows:min(N, (r + 1) * rows)]
+        c0, c1 = c * cols, min(N, (c + 1) * cols)
+        total += int(np.sum(np.clip(np.minimum(ii, c1 - 1) - c0 + 1, 0, c1 - c0))) if causal else len(ii) * (c1 - c0)
+    return total
+
+
+def bench_blocksparse(mi, torch, q, k, v, do, w, density=0.25, reps=10):
+    """Causal block-sparse fwd+bwd (attn_fwd_blocksparse / attn_bwd_blocksparse)
+    on the main workload's tensors with a quarter of the 256 x 128 blocks kept
+    plus the diagonal. FLOPs count the kept, visible pairs; backward 2.5x."""
+    from workloads import draw_block_mask
+    mask = draw_block_mask(w.N, density, seed=9)
+    md = mask.to("cuda:0")
+    scale = w.d ** -0.5
+    for _ in range(2):
+        o, lse = mi.fwd_blocksparse(q, k, v, md, True, scale)
+        mi.bwd_blocksparse(q, k, v, o, lse, do, md, True, scale)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    f_ms = b_ms = 0.0
+    for _ in range(reps):
+        e[0].record()
+        o, lse = mi.fwd_blocksparse(q, k, v, md, True, scale)
+        e[1].record()
+        mi.bwd_blocksparse(q, k, v, o, lse, do, md, True, scale)
+        e[2].record()
+        torch.cuda.synchronize()
+        f_ms += e[0].elapsed_time(e[1]) / reps
+        b_ms += e[1].elapsed_time(e[2]) / reps
+    pairs = visible_pairs_blocksparse(mask.numpy(), w.N, True)
+    ff = 4.0 * w.B * w.H * w.d * pairs
+    tf = 3.5 * ff / ((f_ms + b_ms) * 1e-3) / 1e12
+    dense = w.N * (w.N + 1) // 2
+    return {"workload": "%s causal, block mask of 256 x 128 blocks, %d of %d kept (density %.2f + diagonal, "
+                        "seed 9): %.1f%% of the causal pairs" % (w.name, int(mask.sum()), mask.numel(), density,
+                                                                  100.0 * pairs / dense),
+            "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4), "tflops": round(tf, 2),
+            "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -276,6 +322,7 @@ def main():
     }
     out["window"] = bench_window(mi, torch, q, k, v, do, w, 4096)
     out["varlen"] = bench_varlen(mi, torch)
+    out["blocksparse"] = bench_blocksparse(mi, torch, q, k, v, do, w)
     out["kvcache"] = {name: bench_cache(mi, torch, name) for name in ("decode16k", "prefill16k")}
     if args.extra:
         extra = {}

@@ -17,6 +17,7 @@ import os
 import torch
 
 __all__ = ["fwd", "bwd", "merge", "fwd_chunked", "bwd_chunked", "fwd_kvcache", "fwd_varlen", "bwd_varlen",
+           "fwd_blocksparse", "bwd_blocksparse", "block_mask_shape",
            "lib", "MiattnError",
            "library_path", "balanced_rounds"]
 
@@ -55,10 +56,13 @@ def lib():
     L.attn_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, i]
     L.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp, i]
     L.attn_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp, vp, vp, vp, vp, i, i]
+    L.attn_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i]
+    L.attn_bwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, vp, vp, vp, i, i]
     L.attn_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, i, i]
     L.attn_bwd_chunked.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, vp, vp, vp, i, i]
     for fn in ("attn_fwd", "attn_bwd", "attn_bwd_timed", "attn_merge", "attn_fwd_chunked", "attn_bwd_chunked",
-               "attn_fwd_kvcache", "attn_fwd_window", "attn_bwd_window", "attn_fwd_varlen", "attn_bwd_varlen"):
+               "attn_fwd_kvcache", "attn_fwd_window", "attn_bwd_window", "attn_fwd_varlen", "attn_bwd_varlen",
+               "attn_fwd_blocksparse", "attn_bwd_blocksparse"):
         getattr(L, fn).restype = i
     L.attn_last_error.restype = ctypes.c_char_p
     L.attn_last_error.argtypes = []
@@ -312,6 +316,60 @@ def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_len, causal=False, scale=N
                                  max_len, total, H, Hkv, d, int(bool(causal)), int(window), scale,
                                  _stream(q), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _dtype_code(q),
                                  int(bool(accumulate))))
+    return dq, dk, dv
+
+
+BLOCK_ROWS, BLOCK_COLS = 256, 128
+
+
+def block_mask_shape(N):
+    """Shape of the block mask for sequence length N: one entry per block of
+    BLOCK_ROWS query rows x BLOCK_COLS keys."""
+    return ((N + BLOCK_ROWS - 1) // BLOCK_ROWS, (N + BLOCK_COLS - 1) // BLOCK_COLS)
+
+
+def _block_mask(block_mask, N, device):
+    _need(block_mask, "block_mask", torch.uint8, block_mask_shape(N), device)
+    return block_mask
+
+
+def fwd_blocksparse(q, k, v, block_mask, causal=False, scale=None, out=None, out_lse=None):
+    """Block-sparse attention forward (attn_fwd_blocksparse). block_mask: uint8
+    device tensor of block_mask_shape(N); a zero entry removes its block of
+    query rows x keys. Returns (o, lse); rows with no key get o = 0, lse = -inf."""
+    B, N, H, Hkv, d = _dims(q, k, v)
+    _block_mask(block_mask, N, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if out_lse is None else out_lse
+    _need(o, "out", q.dtype, q.shape, q.device)
+    _need(lse, "out_lse", torch.float32, (B, H, N), q.device)
+    _check(lib().attn_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(block_mask), B, H, Hkv,
+                                      N, d, int(bool(causal)), scale, _stream(q), _dtype_code(q)))
+    return o, lse
+
+
+def bwd_blocksparse(q, k, v, o, lse, dout, block_mask, causal=False, scale=None, accumulate=False,
+                    dq=None, dk=None, dv=None):
+    """Backward of fwd_blocksparse with the same block_mask. Returns (dq, dk, dv)."""
+    B, N, H, Hkv, d = _dims(q, k, v)
+    _block_mask(block_mask, N, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _need(o, "o", q.dtype, q.shape, q.device)
+    _need(dout, "dout", q.dtype, q.shape, q.device)
+    _need(lse, "lse", torch.float32, (B, H, N), q.device)
+    gdt = torch.float32 if accumulate else q.dtype
+    mk = (lambda t: torch.zeros(t.shape, dtype=gdt, device=q.device)) if accumulate else \
+         (lambda t: torch.empty(t.shape, dtype=gdt, device=q.device))
+    dq = mk(q) if dq is None else dq
+    dk = mk(k) if dk is None else dk
+    dv = mk(v) if dv is None else dv
+    _need(dq, "dq", gdt, q.shape, q.device)
+    _need(dk, "dk", gdt, k.shape, q.device)
+    _need(dv, "dv", gdt, v.shape, q.device)
+    _check(lib().attn_bwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(block_mask), B, H, Hkv,
+                                      N, d, int(bool(causal)), scale, _stream(q), _ptr(dout), _ptr(dq), _ptr(dk),
+                                      _ptr(dv), _dtype_code(q), int(bool(accumulate))))
     return dq, dk, dv
 
 

@@ -63,7 +63,7 @@ struct DkdvSmem {
   Buf buf[3];
 };
 
-template <int D, bool CAUSAL, bool WIN = false>
+template <int D, bool CAUSAL, bool WIN = false, bool SPARSE = false>
 __global__ __launch_bounds__(DKV_NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(Params p) {
   constexpr int KS = D / 16, DB = D / 32;
@@ -135,7 +135,15 @@ void bwd_dkdv_kernel(Params p) {
     const int q_hi = p.k_start + k0 + DKV_BK - 1 + p.window - 1 - p.q_start;
     nqt_end = min(nqt, max(0, q_hi / DKV_BQ + 1));
   }
-  const int per_head = max(0, nqt_end - first);
+  int per_head = max(0, nqt_end - first);
+  // block-sparse: the query tiles of the block column, ascending, from the
+  // column's first key on (the same list for every head of the group)
+  const int* tl = nullptr;
+  if constexpr (SPARSE) {
+    static_assert(DKV_BK == BS_COLS && DKV_BQ == BS_TILE, "a workgroup covers one block column of the mask");
+    tl = p.bs_col_tiles + (long long)kt * p.bs_ld;
+    per_head = p.bs_col_cnt[kt];
+  }
   const int niter = p.G * per_head;
   const int kpos = p.k_start + kw0 + n;          // this lane's key position
   const int wk_first = p.k_start + kw0;
@@ -223,8 +231,16 @@ void bwd_dkdv_kernel(Params p) {
     }
     if (tid < 128) sm.stat[2][tid >> 6][tid & 63] = (tid < 64) ? INFINITY : 0.f;
   }
+  // block-sparse: query tile of the next tile and of the one after (fetched
+  // an iteration ahead, so the list reads never stall the tile loads)
+  int tq_nx = 0, tq_nx2 = 0, t_nx2 = 0;
+  if constexpr (SPARSE) {
+    t_nx2 = per_head > 2 ? 2 : 0;     // list index of tile 2 (k mod per_head)
+    tq_nx = niter > 1 ? uni(tl[per_head > 1 ? 1 : 0]) : 0;
+    tq_nx2 = niter > 2 ? uni(tl[t_nx2]) : 0;
+  }
   {  // tile 0 (the empty tile if this workgroup has none)
-    const int h = gkv * p.G, q0 = niter > 0 ? first * DKV_BQ : empty_q0;
+    const int h = gkv * p.G, q0 = niter > 0 ? (SPARSE ? uni(tl[0]) : first) * DKV_BQ : empty_q0;
 #pragma unroll
     for (int piece = 0; piece < 2 * NL; ++piece) load_piece(piece, 0, h, q0);
     stat_load(h, q0);
@@ -284,15 +300,22 @@ void bwd_dkdv_kernel(Params p) {
   };
 
   int h_cur = gkv * p.G, t_cur = 0;   // (query head, tile index within the head) of tile k
+  int q0_cur = niter > 0 ? (SPARSE ? uni(tl[0]) : first) * DKV_BQ : empty_q0;   // first row of tile k
   for (int kt_ = 0; kt_ < ntiles; ++kt_) {
     const int cb = kt_ % 3, pb = (kt_ + 2) % 3, nb = (kt_ + 1) % 3;
     const bool real = kt_ < niter;
-    const int q0 = real ? (first + t_cur) * DKV_BQ : empty_q0;
+    const int q0 = SPARSE ? q0_cur : (real ? (first + t_cur) * DKV_BQ : empty_q0);
     // the tile after this one
     int h_nx = h_cur, t_nx = t_cur + 1;
     if (t_nx == per_head) { h_nx = h_cur + 1; t_nx = 0; }
     const bool nx_real = kt_ + 1 < niter;
-    const int q0_nx = nx_real ? (first + t_nx) * DKV_BQ : empty_q0;
+    const int q0_nx = nx_real ? (SPARSE ? tq_nx : first + t_nx) * DKV_BQ : empty_q0;
+    if constexpr (SPARSE) {            // list entry of tile k + 3, read now for the next iteration
+      if (++t_nx2 == per_head) t_nx2 = 0;
+      const int after = kt_ + 3 < niter ? uni(tl[t_nx2]) : 0;
+      tq_nx = tq_nx2;
+      tq_nx2 = after;
+    }
     const int h_ld = nx_real ? h_nx : gkv * p.G;   // a valid head also for the empty tile
     const bool need_mask = CAUSAL && real &&
                            (wk_first + DKV_KW - 1 > p.q_start + q0 ||
@@ -369,6 +392,7 @@ void bwd_dkdv_kernel(Params p) {
     __syncthreads();
     h_cur = h_nx;
     t_cur = t_nx;
+    q0_cur = q0_nx;
   }
 
   // ---- store dK^T, dV^T: lane (g, key n), register r <-> column 32 db + 8 (r/4) + 4g + r%4
@@ -424,7 +448,7 @@ struct DqSmem {
   bf16 v[2][TILE];
 };
 
-template <int D, bool CAUSAL, int NW, bool WIN = false>
+template <int D, bool CAUSAL, int NW, bool WIN = false, bool SPARSE = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void bwd_dq_kernel(Params p) {
   constexpr int BR = NW * 32;
@@ -539,7 +563,21 @@ void bwd_dq_kernel(Params p) {
   // workgroup's first row are skipped too
   int jt0 = 0;
   if constexpr (WIN) jt0 = max(0, p.q_start + q0 - (p.window - 1) - p.k_start) / DQ_BC;
-  if (nkt > jt0) {
+  // block-sparse: the ascending key-tile list of the workgroup's block row
+  // (cut at the diagonal and the last key); its first `npl` entries need no mask
+  const int* tl = nullptr;
+  int nit = 0, npl = 0;
+  if constexpr (SPARSE) {
+    static_assert(BR == BS_ROWS && DQ_BC == BS_TILE, "a workgroup covers one block row of the mask");
+    tl = p.bs_row_tiles + (long long)qt * p.bs_ld;
+    nit = p.bs_row_cnt[qt];
+    npl = min(p.bs_row_plain[qt], nit);
+    if (nit > 0) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) load_piece(i, 0, uni(tl[0]) * DQ_BC);
+      wait_global_loads();
+    }
+  } else if (nkt > jt0) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) load_piece(i, jt0 & 1, jt0 * DQ_BC);
     wait_global_loads();
@@ -557,11 +595,11 @@ void bwd_dq_kernel(Params p) {
   constexpr int PS = 2 * KS, PD = 2 * DB;
   int nplain = min(nkt, p.Nk / DQ_BC);
   if (CAUSAL) nplain = min(nplain, max(0, p.q_start + q0 - p.k_start + 1) / DQ_BC);
-  auto tile = [&](auto mc, int j) {
+  // key tile j from LDS buffer buf, while tile jnext is loaded into the other one
+  auto tile = [&](auto mc, int j, int buf, int jnext) {
     constexpr bool MASKED = decltype(mc)::value;
-    const int buf = j & 1;
     const int kpos0 = p.k_start + j * DQ_BC;
-    const int jn = min(j + 1, nkt - 1) * DQ_BC;      // next tile (the last tile repeats itself)
+    const int jn = jnext * DQ_BC;
     // masked iff key index inside the tile > thr (causal and the ragged end)
     int thr = p.Nk - 1 - j * DQ_BC;
     if (CAUSAL && kpos0 + DQ_BC - 1 > wq_first) thr = min(thr, qpos - kpos0);
@@ -637,18 +675,36 @@ void bwd_dq_kernel(Params p) {
     wait_global_loads();
     __syncthreads();
   };
-  if constexpr (WIN) {
+  auto next = [&](int j) { return min(j + 1, nkt - 1); };   // the last tile repeats itself
+  if constexpr (SPARSE) {
+    // list entries: plain [0, npl), masked [npl, nit); the entry after the
+    // next is read an iteration ahead
+    int jc = nit > 0 ? uni(tl[0]) : 0, jx = nit > 1 ? uni(tl[1]) : jc;
+    int it = 0;
+    for (; it < npl; ++it) {
+      const int jxx = it + 2 < nit ? uni(tl[it + 2]) : jx;
+      tile(std::false_type{}, jc, it & 1, jx);
+      jc = jx;
+      jx = jxx;
+    }
+    for (; it < nit; ++it) {
+      const int jxx = it + 2 < nit ? uni(tl[it + 2]) : jx;
+      tile(std::true_type{}, jc, it & 1, jx);
+      jc = jx;
+      jx = jxx;
+    }
+  } else if constexpr (WIN) {
     // tiles before jlow hold keys before the window of some row of the
     // workgroup: masked prefix [jt0, a), plain [a, b), masked [b, nkt)
     const int jlow = max(0, (p.q_start + q0 + BR - p.window - p.k_start + DQ_BC - 1) / DQ_BC);
     const int a = min(max(jlow, jt0), nkt);
     const int b = max(a, min(nplain, nkt));
-    for (int j = jt0; j < a; ++j) tile(std::true_type{}, j);
-    for (int j = a; j < b; ++j) tile(std::false_type{}, j);
-    for (int j = b; j < nkt; ++j) tile(std::true_type{}, j);
+    for (int j = jt0; j < a; ++j) tile(std::true_type{}, j, j & 1, next(j));
+    for (int j = a; j < b; ++j) tile(std::false_type{}, j, j & 1, next(j));
+    for (int j = b; j < nkt; ++j) tile(std::true_type{}, j, j & 1, next(j));
   } else {
-    for (int j = 0; j < nplain; ++j) tile(std::false_type{}, j);
-    for (int j = nplain; j < nkt; ++j) tile(std::true_type{}, j);
+    for (int j = 0; j < nplain; ++j) tile(std::false_type{}, j, j & 1, next(j));
+    for (int j = nplain; j < nkt; ++j) tile(std::true_type{}, j, j & 1, next(j));
   }
 
   // ---- store dQ = scale * acc^T: lane (g, query n), register r <-> column 32 db + 8 (r/4) + 4g + r%4
@@ -679,7 +735,11 @@ void bwd_dq_kernel(Params p) {
 template <int D>
 hipError_t launch_dkdv_d(const Params& p, hipStream_t s) {
   const dim3 gkv(p.Hkv, (p.Nk + DKV_BK - 1) / DKV_BK, p.B);
-  if (p.causal && p.window > 0)
+  if (p.bs_col_tiles && p.causal)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false, true>), gkv, dim3(DKV_NW * 64), 0, s, p);
+  else if (p.bs_col_tiles)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, false, true>), gkv, dim3(DKV_NW * 64), 0, s, p);
+  else if (p.causal && p.window > 0)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, true>), gkv, dim3(DKV_NW * 64), 0, s, p);
   else if (p.causal)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), gkv, dim3(DKV_NW * 64), 0, s, p);
@@ -692,7 +752,11 @@ template <int D>
 hipError_t launch_dq_d(const Params& p, hipStream_t s) {
   constexpr int NW = 8;
   const dim3 gq(p.H, (p.Nq + NW * 32 - 1) / (NW * 32), p.B);
-  if (p.causal && p.window > 0)
+  if (p.bs_row_tiles && p.causal)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true, NW, false, true>), gq, dim3(NW * 64), 0, s, p);
+  else if (p.bs_row_tiles)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false, NW, false, true>), gq, dim3(NW * 64), 0, s, p);
+  else if (p.causal && p.window > 0)
     hipLaunchKernelGGL((bwd_dq_kernel<D, true, NW, true>), gq, dim3(NW * 64), 0, s, p);
   else if (p.causal)
     hipLaunchKernelGGL((bwd_dq_kernel<D, true, NW>), gq, dim3(NW * 64), 0, s, p);

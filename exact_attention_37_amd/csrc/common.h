@@ -46,7 +46,21 @@ struct Params {
   // Packed variable-length batch: sequence z of the grid owns rows
   // [cu_seqlens[z], cu_seqlens[z + 1]) of a B = 1 layout of N rows; null otherwise.
   const int* cu_seqlens;
+  // Block-sparse attention: one mask entry per block of BS_ROWS query rows x
+  // BS_COLS keys, shared by every batch and head; null otherwise.
+  const uint8_t* bs_mask;   // [ceil(N / BS_ROWS)][bs_nbc], read by the float32 kernels
+  int bs_nbc;               // ceil(N / BS_COLS)
+  // Tile lists built from the mask for the matrix-core kernels (BS_TILE rows
+  // or keys per tile, ascending, cut at the causal diagonal and the last row):
+  const int* bs_row_cnt;    // [nbr] key tiles kept for block row r
+  const int* bs_row_plain;  // [nbr] how many of them need no causal / ragged-end mask
+  const int* bs_row_tiles;  // [nbr][bs_ld]
+  const int* bs_col_cnt;    // [nbc] query tiles kept for block column c
+  const int* bs_col_tiles;  // [nbc][bs_ld]
+  int bs_ld;                // ceil(N / BS_TILE)
 };
+
+constexpr int BS_ROWS = 256, BS_COLS = 128, BS_TILE = 64;
 
 // For a packed variable-length batch, narrows p to sequence s (rows
 // [cu_seqlens[s], cu_seqlens[s + 1]) of the single B = 1 layout; the offsets

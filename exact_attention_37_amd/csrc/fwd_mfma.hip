@@ -52,9 +52,12 @@ struct FwdSmem {
   bf16 v[2][TILE];
 };
 
-template <int D, int NW, bool CAUSAL, typename TO, bool WIN = false>
+template <int D, int NW, bool CAUSAL, typename TO, bool WIN = false, bool SPARSE = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void fwd_mfma_kernel(Params p) {
+  // rows that can still have seen no key mid-loop (sliding window,
+  // block-sparse), or none at all (block-sparse)
+  constexpr bool EMPTY = WIN || SPARSE;
   constexpr int BR = NW * 32;  // query rows per workgroup, 32 per wave
   constexpr int KS = D / 16;   // k-steps of the QK^T product
   constexpr int DB = D / 32;   // 32-column blocks of O
@@ -124,6 +127,15 @@ void fwd_mfma_kernel(Params p) {
   // workgroup's first row are skipped too
   int jt0 = 0;
   if constexpr (WIN) jt0 = max(0, p.q_start + q0 - (p.window - 1) - p.k_start) / BC;
+  // the key tiles taken: jt0 .. nkt-1, or (block-sparse) the ascending list
+  // of the workgroup's block row, already cut at the diagonal and the last key
+  int nit = nkt - jt0;
+  const int* tl = nullptr;
+  if constexpr (SPARSE) {
+    static_assert(BR == BS_ROWS && BC == BS_TILE, "a workgroup covers one block row of the mask");
+    tl = p.bs_row_tiles + (long long)qt * p.bs_ld;
+    nit = p.bs_row_cnt[qt];
+  }
 
   // Direct loads: 1 KB piece s = wave*NL + i of the two tiles (K: s < TILE_KB,
   // then V) covers tile bytes [(s % TILE_KB) KB, +1 KB); lane l fills 16 bytes
@@ -171,19 +183,30 @@ void fwd_mfma_kernel(Params p) {
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
   float m = -INFINITY, l = 0.f;
 
-  if (nkt > jt0) {
+  // block-sparse: the current and the next listed tile (the index of the
+  // one after is fetched an iteration ahead, so its latency stays hidden)
+  int jc = jt0, jx = 0;
+  if constexpr (SPARSE) {
+    jc = nit > 0 ? uni(tl[0]) : 0;
+    jx = nit > 1 ? uni(tl[1]) : jc;
+  }
+  if (nit > 0) {
 #pragma unroll
-    for (int i = 0; i < NL; ++i) load_piece(i, 0, jt0 * BC);
+    for (int i = 0; i < NL; ++i) load_piece(i, 0, jc * BC);
     wait_global_loads();
   }
   __syncthreads();
 
-  for (int j = jt0; j < nkt; ++j) {
-    const int buf = (j - jt0) & 1;
+  for (int it = 0; it < nit; ++it) {
+    const int j = SPARSE ? jc : jt0 + it;
+    const int buf = it & 1;
     const bf16* kt = sm.k[buf];
     const bf16* vt = sm.v[buf];
     const int kpos0 = p.k_start + j * BC;          // absolute position of the tile's first key
-    const int jn = min(j + 1, nkt - 1) * BC;       // next tile (the last tile repeats itself)
+    // next tile (the last tile repeats itself)
+    const int jn = (SPARSE ? jx : min(j + 1, nkt - 1)) * BC;
+    int jxx = 0;
+    if constexpr (SPARSE) jxx = it + 2 < nit ? uni(tl[it + 2]) : jx;
     // No per-wave skip: a per-wave branch makes the register allocator
     // shuttle accumulators between AGPRs and VGPRs every iteration; fully
     // masked waves (diagonal tiles only) compute P = 0 instead.
@@ -239,7 +262,7 @@ void fwd_mfma_kernel(Params p) {
       const float mnew = raise ? mt : m;
       // rows that keep their max keep alpha = 1 (with a window a row's max
       // can still be -inf here, and -inf - -inf has no value)
-      const float alpha = (WIN && !raise) ? 1.f : exp2f(m - mnew);
+      const float alpha = (EMPTY && !raise) ? 1.f : exp2f(m - mnew);
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -248,7 +271,7 @@ void fwd_mfma_kernel(Params p) {
       m = mnew;
     }
     // (a row whose window has not begun yet keeps m = -inf and p = 0)
-    const float mneg = (WIN && m == -INFINITY) ? 0.f : -m;
+    const float mneg = (EMPTY && m == -INFINITY) ? 0.f : -m;
     bf16x8 pf[4];
     float lsum0 = 0.f, lsum1 = 0.f;
 #pragma unroll
@@ -281,12 +304,17 @@ void fwd_mfma_kernel(Params p) {
         [&](int i, bf16x8 a) { acc[i % DB] = mfma32(a, pf[i / DB], acc[i % DB]); });
     wait_global_loads();
     __syncthreads();
+    if constexpr (SPARSE) {
+      jc = jx;
+      jx = jxx;
+    }
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
   const float lt = l + __shfl_xor(l, 32);
   if (row < p.Nq) {
-    const float inv = 1.f / lt;
+    // a row that saw no key (block-sparse) stores o = 0 and lse = -inf
+    const float inv = (SPARSE && lt == 0.f) ? 0.f : 1.f / lt;
     TO* O = (TO*)p.o + (((long long)b * p.N + p.q_start + row) * p.H + h) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -315,7 +343,11 @@ template <int D, int NW, typename TO>
 hipError_t launch_cfg(const Params& p, hipStream_t s) {
   constexpr int BR = NW * 32;
   const dim3 grid(p.H, (p.Nq + BR - 1) / BR, p.B);
-  if (p.causal && p.window > 0)
+  if (p.bs_row_tiles && p.causal)
+    hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, true, TO, false, true>), grid, dim3(NW * 64), 0, s, p);
+  else if (p.bs_row_tiles)
+    hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, false, TO, false, true>), grid, dim3(NW * 64), 0, s, p);
+  else if (p.causal && p.window > 0)
     hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, true, TO, true>), grid, dim3(NW * 64), 0, s, p);
   else if (p.causal)
     hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, true, TO>), grid, dim3(NW * 64), 0, s, p);

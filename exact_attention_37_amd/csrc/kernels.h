@@ -54,4 +54,10 @@ hipError_t launch_convert(const float* src, void* dst, long long n, int dtype, h
 // dst[i] = value for n float32 elements (a kernel, so it can sit in a graph).
 hipError_t launch_fill(float* dst, long long n, float value, hipStream_t s);
 
+// Block-sparse tile lists (the bs_* fields of Params) from a block mask of
+// [nbr = ceil(N / BS_ROWS)][nbc = ceil(N / BS_COLS)] bytes. `ints` must hold
+// bs_list_ints(N) int32 values; fills p's list pointers into it.
+long long bs_list_ints(int N);
+hipError_t launch_bs_lists(const uint8_t* mask, int N, int causal, int* ints, Params& p, hipStream_t s);
+
 }  // namespace miattn

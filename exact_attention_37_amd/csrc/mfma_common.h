@@ -145,6 +145,10 @@ __device__ __forceinline__ void agpr_settle(f32x16& x, f32x16& y) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(x), "+a"(y));
 }
 
+// A value every lane holds alike, moved to a scalar register (offsets of the
+// inline-assembly buffer loads must be scalar).
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 // Waits for every outstanding global load of this wave. Used after the
 // loads of loop-invariant matrix operands: without it the compiler cannot
 // prove them complete across the loop back-edge and inserts vmcnt waits

@@ -172,8 +172,25 @@ int attn_chunk_schedule(int nchunks, int* round_of, int* q_chunk, int* k_chunk, 
 
 namespace {
 
+// Block-sparse set-up: the float32 kernels read the block mask itself, the
+// matrix-core kernels the tile lists built from it (into scratch) on stream s.
+int blocksparse_setup(Params& p, const uint8_t* bmask, int dtype, Scratch& scratch, hipStream_t s) {
+  if (dtype != MIATTN_BF16) {
+    p.bs_mask = bmask;
+    p.bs_nbc = (p.N + miattn::BS_COLS - 1) / miattn::BS_COLS;
+    return MIATTN_OK;
+  }
+  int* ints = (int*)scratch.get((size_t)miattn::bs_list_ints(p.N) * 4);
+  if (!ints) return fail(MIATTN_ENOMEM, "hipMallocAsync failed for the block-sparse tile lists");
+  return launch_status(miattn::launch_bs_lists(bmask, p.N, p.causal, ints, p, s), "block-sparse tile lists");
+}
+
+long long bmask_bytes(int N) {
+  return (long long)((N + miattn::BS_ROWS - 1) / miattn::BS_ROWS) * ((N + miattn::BS_COLS - 1) / miattn::BS_COLS);
+}
+
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N, int d,
-             int causal, float scale, void* stream, int dtype, int window) {
+             int causal, float scale, void* stream, int dtype, int window, const uint8_t* bmask = nullptr) {
   int st = check_common(B, H, Hkv, N, d, dtype);
   if (st) return st;
   if ((st = check_ptrs({q, k, v, o, lse}))) return st;
@@ -185,8 +202,12 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   for (Range r : {span(q, qb), span(k, kb), span(v, kb)})
     if (overlap(ro, r) || overlap(rl, r)) return fail(MIATTN_EINVAL, "o/lse must not alias q, k or v");
   if (overlap(ro, rl)) return fail(MIATTN_EINVAL, "o and lse must not overlap");
+  if (bmask && (overlap(ro, span(bmask, bmask_bytes(N))) || overlap(rl, span(bmask, bmask_bytes(N)))))
+    return fail(MIATTN_EINVAL, "o/lse must not alias block_mask");
   Params p = make_params(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale);
   p.window = window;
+  Scratch scratch((hipStream_t)stream);
+  if (bmask && (st = blocksparse_setup(p, bmask, dtype, scratch, (hipStream_t)stream))) return st;
   if ((st = launch_status(fwd_block(p, dtype, dtype == MIATTN_F32, (hipStream_t)stream), "attn_fwd"))) return st;
   return ok();
 }
@@ -356,7 +377,7 @@ namespace {
 
 int bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H, int Hkv,
              int N, int d, int causal, float scale, void* stream, const void* dout, void* dq, void* dk, void* dv,
-             int dtype, int accumulate, void* const* marks, int window) {
+             int dtype, int accumulate, void* const* marks, int window, const uint8_t* bmask = nullptr) {
   int st = check_common(B, H, Hkv, N, d, dtype);
   if (st) return st;
   if ((st = check_ptrs({q, k, v, o, lse, dout, dq, dk, dv}))) return st;
@@ -373,6 +394,9 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
       if (overlap(out, in)) return fail(MIATTN_EINVAL, "dq/dk/dv must not alias an input");
   if (overlap(rdq, rdk) || overlap(rdq, rdv) || overlap(rdk, rdv))
     return fail(MIATTN_EINVAL, "dq, dk and dv must not overlap");
+  if (bmask)
+    for (Range out : {rdq, rdk, rdv})
+      if (overlap(out, span(bmask, bmask_bytes(N)))) return fail(MIATTN_EINVAL, "dq/dk/dv must not alias block_mask");
 
   hipStream_t s = (hipStream_t)stream;
   Scratch scratch(s);
@@ -386,6 +410,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   p.dsum = dsum;
   p.accumulate = accumulate;
   p.window = window;
+  if (bmask && (st = blocksparse_setup(p, bmask, dtype, scratch, s))) return st;
   if ((st = launch_status(miattn::launch_bwd_pre(o, dout, dsum, B, H, N, d, 0, N, dtype, s), "bwd preprocess")))
     return st;
   if (marks && (st = launch_status(hipEventRecord((hipEvent_t)marks[0], s), "timing mark 0"))) return st;
@@ -424,6 +449,22 @@ int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, 
   if (window < 1) return fail(MIATTN_EINVAL, "window must be >= 1");
   return bwd_impl(q, k, v, o, lse, B, H, Hkv, N, d, 1, scale, stream, dout, dq, dk, dv, dtype, accumulate,
                   nullptr, window);
+}
+
+int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const unsigned char* block_mask, int B, int H, int Hkv, int N, int d, int causal,
+                         float scale, void* stream, int dtype) {
+  if (!block_mask) return fail(MIATTN_EINVAL, "block_mask must not be null");
+  return fwd_impl(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, stream, dtype, 0, block_mask);
+}
+
+int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const unsigned char* block_mask, int B, int H, int Hkv, int N, int d, int causal,
+                         float scale, void* stream, const void* dout, void* dq, void* dk, void* dv, int dtype,
+                         int accumulate) {
+  if (!block_mask) return fail(MIATTN_EINVAL, "block_mask must not be null");
+  return bwd_impl(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, stream, dout, dq, dk, dv, dtype, accumulate,
+                  nullptr, 0, block_mask);
 }
 
 int attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* o, float* lse, int B,

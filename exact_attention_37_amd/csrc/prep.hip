@@ -123,6 +123,52 @@ __global__ __launch_bounds__(256) void fill_kernel(float* __restrict__ dst, long
   }
 }
 
+// Block-sparse tile lists: one wave per block row r (the key tiles of
+// BS_TILE keys whose mask block (r, j / 2) is kept, up to the block row's
+// last query under causal) or per block column c (the query tiles of BS_TILE
+// rows whose mask block (i / 4, c) is kept, from the column's first key on
+// under causal). Lanes test 64 consecutive tiles at a time; a ballot and a
+// prefix count compact the kept ones, so the lists come out ascending.
+__global__ __launch_bounds__(64) void bs_lists_kernel(const uint8_t* __restrict__ mask, int N, int causal,
+                                                      int nbr, int nbc, int ld, int* __restrict__ row_cnt,
+                                                      int* __restrict__ row_plain, int* __restrict__ row_tiles,
+                                                      int* __restrict__ col_cnt, int* __restrict__ col_tiles) {
+  static_assert(BS_ROWS == 4 * BS_TILE && BS_COLS == 2 * BS_TILE, "tiles nest in mask blocks");
+  const int w = blockIdx.x, lane = threadIdx.x;
+  const uint64_t below = (1ull << lane) - 1ull;
+  int cnt = 0, plain = 0;
+  if (w < nbr) {
+    const int r = w;
+    const int last = min(r * BS_ROWS + BS_ROWS - 1, N - 1);
+    // tiles wholly below every row's diagonal and before the ragged end
+    const int plim = min(N / BS_TILE, causal ? r * (BS_ROWS / BS_TILE) : ld);
+    for (int j0 = 0; j0 < ld; j0 += 64) {
+      const int j = j0 + lane;
+      const bool keep = j < ld && (!causal || j * BS_TILE <= last) &&
+                        mask[(long long)r * nbc + j / (BS_COLS / BS_TILE)] != 0;
+      const uint64_t bits = __ballot(keep);
+      if (keep) row_tiles[(long long)r * ld + cnt + __popcll(bits & below)] = j;
+      cnt += __popcll(bits);
+      plain += __popcll(__ballot(keep && j < plim));
+    }
+    if (lane == 0) {
+      row_cnt[r] = cnt;
+      row_plain[r] = plain;
+    }
+  } else {
+    const int c = w - nbr;
+    for (int i0 = 0; i0 < ld; i0 += 64) {
+      const int i = i0 + lane;
+      const bool keep = i < ld && (!causal || i * BS_TILE + BS_TILE - 1 >= c * BS_COLS) &&
+                        mask[(long long)(i / (BS_ROWS / BS_TILE)) * nbc + c] != 0;
+      const uint64_t bits = __ballot(keep);
+      if (keep) col_tiles[(long long)c * ld + cnt + __popcll(bits & below)] = i;
+      cnt += __popcll(bits);
+    }
+    if (lane == 0) col_cnt[c] = cnt;
+  }
+}
+
 inline unsigned blocks_for(long long threads) { return (unsigned)((threads + 255) / 256); }
 
 template <typename TA, typename TB, typename TO>
@@ -176,6 +222,33 @@ hipError_t launch_convert(const float* src, void* dst, long long n, int dtype, h
     hipLaunchKernelGGL((convert_kernel<float>), grid, block, 0, s, src, (float*)dst, n);
   else
     hipLaunchKernelGGL((convert_kernel<bf16>), grid, block, 0, s, src, (bf16*)dst, n);
+  return hipGetLastError();
+}
+
+long long bs_list_ints(int N) {
+  const long long nbr = (N + BS_ROWS - 1) / BS_ROWS, nbc = (N + BS_COLS - 1) / BS_COLS;
+  const long long ld = (N + BS_TILE - 1) / BS_TILE;
+  return 2 * nbr + nbc + (nbr + nbc) * ld;
+}
+
+hipError_t launch_bs_lists(const uint8_t* mask, int N, int causal, int* ints, Params& p, hipStream_t s) {
+  const int nbr = (N + BS_ROWS - 1) / BS_ROWS, nbc = (N + BS_COLS - 1) / BS_COLS;
+  const int ld = (N + BS_TILE - 1) / BS_TILE;
+  int* row_cnt = ints;
+  int* row_plain = row_cnt + nbr;
+  int* col_cnt = row_plain + nbr;
+  int* row_tiles = col_cnt + nbc;
+  int* col_tiles = row_tiles + (long long)nbr * ld;
+  p.bs_mask = mask;
+  p.bs_nbc = nbc;
+  p.bs_row_cnt = row_cnt;
+  p.bs_row_plain = row_plain;
+  p.bs_row_tiles = row_tiles;
+  p.bs_col_cnt = col_cnt;
+  p.bs_col_tiles = col_tiles;
+  p.bs_ld = ld;
+  hipLaunchKernelGGL(bs_lists_kernel, dim3(nbr + nbc), dim3(64), 0, s, mask, N, causal, nbr, nbc, ld, row_cnt,
+                     row_plain, row_tiles, col_cnt, col_tiles);
   return hipGetLastError();
 }
 

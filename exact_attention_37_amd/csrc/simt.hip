@@ -26,6 +26,14 @@ __device__ __forceinline__ long long krow(const Params& p, int b, int row) {
   return ((long long)b * p.N + row) * p.Hkv;
 }
 
+// Block-sparse: whether the mask keeps the block holding query row i and key
+// j (kRows and kTile divide the block sizes, so one test covers a tile).
+__device__ __forceinline__ bool block_kept(const Params& p, int i, int j) {
+  return !p.bs_mask || p.bs_mask[(long long)(i / BS_ROWS) * p.bs_nbc + j / BS_COLS] != 0;
+}
+static_assert(BS_ROWS % kRows == 0 && BS_ROWS % kTile == 0 && BS_COLS % kRows == 0 && BS_COLS % kTile == 0,
+              "row and key tiles nest in mask blocks");
+
 template <typename T, typename TO, int D>
 __global__ __launch_bounds__(kRows) void fwd_simt(Params p) {
   int b = blockIdx.z;
@@ -62,6 +70,7 @@ __global__ __launch_bounds__(kRows) void fwd_simt(Params p) {
   // sliding window: keys before the window of the block's first row are skipped
   const int jbeg = p.window > 0 ? max(0, p.q_start + i0 - (p.window - 1) - p.k_start) / kTile * kTile : 0;
   for (int j0 = jbeg; j0 < kend; j0 += kTile) {
+    if (!block_kept(p, i0, j0)) continue;   // (uniform over the workgroup)
     for (int e = tid; e < kTile * D; e += kRows) {
       const int r = e / D, col = e % D;
       const bool in = j0 + r < p.Nk;
@@ -92,7 +101,7 @@ __global__ __launch_bounds__(kRows) void fwd_simt(Params p) {
   }
   if (i < p.Nq) {
     TO* O = (TO*)p.o + (qrow(p, b, p.q_start + i) + h) * D;
-    const float inv = 1.f / l;
+    const float inv = l > 0.f ? 1.f / l : 0.f;   // a row with no key (block-sparse): o = 0, lse = -inf
 #pragma unroll
     for (int t = 0; t < D; ++t) O[t] = from_f<TO>(acc[t] * inv);
     p.lse[((long long)b * p.H + h) * p.N + p.q_start + i] = (m + log2f(l)) * kLn2;
@@ -149,6 +158,7 @@ __global__ __launch_bounds__(kRows) void bwd_dkdv_simt(Params p) {
     const float* L = p.lse + ((long long)b * p.H + h) * p.N + p.q_start;
     const float* Dv = p.dsum + ((long long)b * p.H + h) * p.N + p.q_start;
     for (int i0 = ibeg; i0 < iend; i0 += kTile) {
+      if (!block_kept(p, i0, j0)) continue;   // (uniform over the workgroup)
       for (int e = tid; e < kTile * D; e += kRows) {
         const int r = e / D, col = e % D;
         const bool in = i0 + r < p.Nq;
@@ -236,6 +246,7 @@ __global__ __launch_bounds__(kRows) void bwd_dq_simt(Params p) {
   const int qpos = p.q_start + i;
   const int jbeg = p.window > 0 ? max(0, p.q_start + i0 - (p.window - 1) - p.k_start) / kTile * kTile : 0;
   for (int j0 = jbeg; j0 < kend; j0 += kTile) {
+    if (!block_kept(p, i0, j0)) continue;   // (uniform over the workgroup)
     for (int e = tid; e < kTile * D; e += kRows) {
       const int r = e / D, col = e % D;
       const bool in = j0 + r < p.Nk;

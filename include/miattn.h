@@ -144,6 +144,34 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
                     int causal, int window, float scale, void* stream, const void* dout, void* dq,
                     void* dk, void* dv, int dtype, int accumulate);
 
+/* Block-sparse attention, forward (FlashAttention abstract page: the
+ * extension to block-sparse attention; FlashAttention-2 reviews page,
+ * reviewer 3's question on sparse block masks): attn_fwd where only the
+ * blocks a block mask keeps are computed. Exact attention under that mask;
+ * an approximation of dense attention.
+ *   block_mask: device uint8 [ceil(N / 256)][ceil(N / 128)], shared by every
+ *               batch and head: entry (r, c) != 0 keeps query rows
+ *               [256 r, 256 r + 256) x keys [128 c, 128 c + 128); applied on
+ *               top of the causal mask when causal = 1. Read on the stream;
+ *               the caller keeps it alive until the call's work completes.
+ * A query row left with no key gets o = 0 and lse = -inf (the merge
+ * identity). Other arguments, layouts and errors as attn_fwd, plus
+ * MIATTN_EINVAL for a null block_mask or outputs overlapping it.
+ * bf16 scratch: int32 tile lists of about (N / 256 + N / 128) * N / 64
+ * entries (stream-ordered allocation). */
+int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const unsigned char* block_mask, int B, int H, int Hkv, int N, int d,
+                         int causal, float scale, void* stream, int dtype);
+
+/* Backward of attn_fwd_blocksparse from its o and lse, with the same
+ * block_mask: dq, dk, dv as attn_bwd (rows with no key get zero
+ * gradients). Arguments, scratch and errors as attn_bwd and
+ * attn_fwd_blocksparse. */
+int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const unsigned char* block_mask, int B, int H, int Hkv, int N, int d,
+                         int causal, float scale, void* stream, const void* dout, void* dq, void* dk,
+                         void* dv, int dtype, int accumulate);
+
 /* Backward pass: from q, k, v, the forward's o and lse, and dout = dL/dO,
  * produces dq, dk, dv without forming the N x N matrix. The forward is not
  * re-run: P is rebuilt tile by tile from the saved lse (DistFlashAttn

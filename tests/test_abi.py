@@ -207,3 +207,20 @@ def test_varlen_rejects_outputs_aliasing_inputs():
     assert varlen_call(True, dk=FAKE * 6) == 1 and b"cu_seqlens" in mi.lib().attn_last_error()
     assert varlen_call(True, dq=FAKE) == 1 and b"alias" in mi.lib().attn_last_error()
     assert varlen_call(True, accumulate=2) == 1 and b"accumulate" in mi.lib().attn_last_error()
+
+
+def test_blocksparse_rejects_bad_arguments():
+    L = mi.lib()
+    q = [vp(FAKE * i) for i in range(1, 6)]
+    assert L.attn_fwd_blocksparse(*q, None, 1, 2, 2, 300, 64, 1, 0.1, None, 1) == 1
+    assert b"block_mask" in L.attn_last_error()
+    assert L.attn_fwd_blocksparse(*q, vp(FAKE * 6), 1, 2, 2, 300, 96, 1, 0.1, None, 1) == 2
+    assert L.attn_fwd_blocksparse(*q, vp(FAKE * 6), 1, 2, 2, 300, 64, 3, 0.1, None, 1) == 1
+    assert L.attn_fwd_blocksparse(*q, vp(FAKE * 4 + 16), 1, 2, 2, 300, 64, 1, 0.1, None, 1) == 1
+    assert b"block_mask" in L.attn_last_error()          # o overlaps the mask
+    g = [vp(FAKE * i) for i in (7, 8, 9, 10)]
+    assert L.attn_bwd_blocksparse(*q, None, 1, 2, 2, 300, 64, 1, 0.1, None, *g, 1, 0) == 1
+    assert L.attn_bwd_blocksparse(*q, vp(FAKE * 8), 1, 2, 2, 300, 64, 1, 0.1, None, *g, 1, 0) == 1
+    assert b"block_mask" in L.attn_last_error()          # dk overlaps the mask
+    assert L.attn_bwd_blocksparse(*q, vp(FAKE * 6), 1, 2, 2, 300, 64, 1, float("nan"), None, *g, 1, 0) == 1
+    assert mi.block_mask_shape(300) == (2, 3) and mi.block_mask_shape(16384) == (64, 128)

@@ -36,6 +36,13 @@ lengths stored back to back): ``packed16k`` -- Llama-7B heads, bf16, causal,
 [256, 4096] until the tokens run out (the last one takes the remainder).
 Draw order: the lengths with ``torch.randint`` one at a time, then Q, K, V,
 dO at [total, heads, d] from the same generator.
+
+Block masks (block-sparse attention): ``draw_block_mask`` keeps each block
+of 256 query rows x 128 keys with probability ``density`` (``torch.rand``
+from its own seeded generator, one value per block in row-major order) and,
+if asked, every block that holds part of the diagonal, so that no row is left
+without keys under the causal mask. The benchmark runs the llama16k tensors
+with a quarter of the blocks kept plus the diagonal (seed 9).
 """
 from __future__ import annotations
 
@@ -181,6 +188,19 @@ def draw_varlen_workload(w: VarlenWorkload, total: int | None = None):
         lengths.append(min(n, left))
         left -= lengths[-1]
     return draw_varlen(lengths, w.H, w.Hkv, w.d, w.seed, gen=g)
+
+
+def draw_block_mask(N: int, density: float, seed: int, diagonal: bool = True,
+                    rows: int = 256, cols: int = 128) -> torch.Tensor:
+    """uint8 CPU tensor [ceil(N / rows), ceil(N / cols)]: 1 = block kept."""
+    nbr, nbc = (N + rows - 1) // rows, (N + cols - 1) // cols
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    m = (torch.rand((nbr, nbc), generator=g) < density).to(torch.uint8)
+    if diagonal:
+        for r in range(nbr):
+            lo, hi = r * rows, min(N, (r + 1) * rows) - 1
+            m[r, lo // cols:hi // cols + 1] = 1
+    return m
 
 
 def as_f64(t: torch.Tensor) -> np.ndarray:
