@@ -301,99 +301,128 @@ void bwd_dkdv_kernel(Params p) {
 
   int h_cur = gkv * p.G, t_cur = 0;   // (query head, tile index within the head) of tile k
   int q0_cur = niter > 0 ? (SPARSE ? uni(tl[0]) : first) * DKV_BQ : empty_q0;   // first row of tile k
-  for (int kt_ = 0; kt_ < ntiles; ++kt_) {
-    const int cb = kt_ % 3, pb = (kt_ + 2) % 3, nb = (kt_ + 1) % 3;
-    const bool real = kt_ < niter;
-    const int q0 = SPARSE ? q0_cur : (real ? (first + t_cur) * DKV_BQ : empty_q0);
-    // the tile after this one
-    int h_nx = h_cur, t_nx = t_cur + 1;
-    if (t_nx == per_head) { h_nx = h_cur + 1; t_nx = 0; }
-    const bool nx_real = kt_ + 1 < niter;
-    const int q0_nx = nx_real ? (SPARSE ? tq_nx : first + t_nx) * DKV_BQ : empty_q0;
-    if constexpr (SPARSE) {            // list entry of tile k + 3, read now for the next iteration
-      if (++t_nx2 == per_head) t_nx2 = 0;
-      const int after = kt_ + 3 < niter ? uni(tl[t_nx2]) : 0;
-      tq_nx = tq_nx2;
-      tq_nx2 = after;
-    }
-    const int h_ld = nx_real ? h_nx : gkv * p.G;   // a valid head also for the empty tile
-    const bool need_mask = CAUSAL && real &&
-                           (wk_first + DKV_KW - 1 > p.q_start + q0 ||
-                            (WIN && p.q_start + q0 + DKV_BQ - 1 - wk_first >= p.window));
-    const int mthr = kpos - (p.q_start + q0);     // query index inside the tile < mthr -> masked
-    // LDS read bases of this iteration (byte addresses; dO at +TILE from Q)
-    const uint32_t cq = lds_addr(sm.buf[0].q) + cb * (uint32_t)sizeof(typename DkdvSmem<D>::Buf);
-    const uint32_t pq = lds_addr(sm.buf[0].q) + pb * (uint32_t)sizeof(typename DkdvSmem<D>::Buf);
-    const uint32_t bs[2] = {lds_opaque(cq + 2 * rd_s[0]), lds_opaque(cq + 2 * rd_s[1])};
-    const uint32_t bt[2] = {lds_opaque(cq + 2 * rd_t[0]), lds_opaque(cq + 2 * rd_t[1])};
-    const uint32_t btp[2] = {lds_opaque(pq + 2 * rd_t[0]), lds_opaque(pq + 2 * rd_t[1])};
-    const uint32_t stb = lds_opaque(stat_lane + cb * (2 * DKV_BQ * 4));
+  // Tile k: one iteration of the pipeline. MASKED iterations apply the
+  // causal (and window) mask to the tile's scores; the driver below gives
+  // each its own loop, so that tiles clear of the diagonal carry no mask
+  // code at all (a mask test inside one loop body is turned into
+  // per-element selects that every tile pays for).
+  int kt_ = 0;
+  auto iteration = [&](auto mc) {
+    constexpr bool MASKED = decltype(mc)::value;
+      const int cb = kt_ % 3, pb = (kt_ + 2) % 3, nb = (kt_ + 1) % 3;
+      const bool real = kt_ < niter;
+      const int q0 = SPARSE ? q0_cur : (real ? (first + t_cur) * DKV_BQ : empty_q0);
+      // the tile after this one
+      int h_nx = h_cur, t_nx = t_cur + 1;
+      if (t_nx == per_head) { h_nx = h_cur + 1; t_nx = 0; }
+      const bool nx_real = kt_ + 1 < niter;
+      const int q0_nx = nx_real ? (SPARSE ? tq_nx : first + t_nx) * DKV_BQ : empty_q0;
+      if constexpr (SPARSE) {            // list entry of tile k + 3, read now for the next iteration
+        if (++t_nx2 == per_head) t_nx2 = 0;
+        const int after = kt_ + 3 < niter ? uni(tl[t_nx2]) : 0;
+        tq_nx = tq_nx2;
+        tq_nx2 = after;
+      }
+      const int h_ld = nx_real ? h_nx : gkv * p.G;   // a valid head also for the empty tile
+      const int mthr = kpos - (p.q_start + q0);     // query index inside the tile < mthr -> masked
+      // LDS read bases of this iteration (byte addresses; dO at +TILE from Q)
+      const uint32_t cq = lds_addr(sm.buf[0].q) + cb * (uint32_t)sizeof(typename DkdvSmem<D>::Buf);
+      const uint32_t pq = lds_addr(sm.buf[0].q) + pb * (uint32_t)sizeof(typename DkdvSmem<D>::Buf);
+      const uint32_t bs[2] = {lds_opaque(cq + 2 * rd_s[0]), lds_opaque(cq + 2 * rd_s[1])};
+      const uint32_t bt[2] = {lds_opaque(cq + 2 * rd_t[0]), lds_opaque(cq + 2 * rd_t[1])};
+      const uint32_t btp[2] = {lds_opaque(pq + 2 * rd_t[0]), lds_opaque(pq + 2 * rd_t[1])};
+      const uint32_t stb = lds_opaque(stat_lane + cb * (2 * DKV_BQ * 4));
 
-    lockstep_products<4 * PL, 4>(
-        [&](auto ic) {
-          constexpr int i = decltype(ic)::value, ph = i / PL, j = i % PL;
-          if constexpr (ph == 0 || ph == 2) {   // S / dP of half ph/2: step j = (ks, which)
-            constexpr int ks = j >> 1;
-            return lds_read16_at(bs[ks & 1] + 2 * ((j & 1) * TILE + (ph / 2) * 32 * ROW + (ks >> 1) * 32));
-          } else {                              // dV / dK: step j = (t, db, which), two transposing reads
-            constexpr int t = (ph == 1 ? 2 : 0) + j / (2 * DB), db = (j >> 1) % DB;
-            constexpr int off = ((j & 1) ? 0 : TILE) + 16 * t * ROW + 32 * db;   // Q^T for dK, dO^T for dV
-            const bf16x4 r0 = lds_read_tr4_at((ph == 1 ? btp[0] : bt[0]) + 2 * off);
-            const bf16x4 r1 = lds_read_tr4_at((ph == 1 ? btp[1] : bt[1]) + 2 * off);
-            return bf16x8{r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
-          }
-        },
-        [&](auto ic, bf16x8 a) {
-          constexpr int i = decltype(ic)::value, ph = i / PL, j = i % PL;
-          if constexpr (ph == 0 || ph == 2) {
-            constexpr int ks = j >> 1;
-            f32x16& acc = (j & 1) ? (ph == 0 ? dp0 : dp1) : (ph == 0 ? s0 : s1);
-            const bf16x8& bop = (j & 1) ? vf[ks] : kf[ks];
-            acc = mfma32(a, bop, ks == 0 ? f32x16{} : acc);
-          } else {
-            constexpr int t = (ph == 1 ? 2 : 0) + j / (2 * DB), db = (j >> 1) % DB;
-            if constexpr (j & 1) mfma32_agpr(dk[db], a, da[t]);
-            else mfma32_agpr(dv[db], a, pa[t]);
-          }
-        },
-        [&](auto ic) {
-          constexpr int i = decltype(ic)::value, ph = i / PL, j = i % PL;
-          // stats for the next phase's group, into slot (ph + 1) & 1
-          if constexpr (j == 0) {
-            if constexpr (ph == 0) stat_read(1, stb, 0, 0);
-            else if constexpr (ph == 1) stat_read(0, stb, 0, 1);
-            else if constexpr (ph == 2) stat_read(1, stb, 1, 0);
-            else stat_read(0, stb, 1, 1);
-          }
-          // softmax sub-steps at steps (2k + 1) PL / 8
-          if constexpr ((j * 8) % PL == 0 && ((j * 8) / PL) % 2 == 1) {
-            constexpr int k = ((j * 8) / PL) / 2;
-            using KC = std::integral_constant<int, k>;
-            using SL = std::integral_constant<int, ph & 1>;
-            if constexpr (ph == 0) softmax_sub(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, KC{}, SL{});
-            else if constexpr (ph == 1) softmax_sub(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, KC{}, SL{});
-            else if constexpr (ph == 2) softmax_sub(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, KC{}, SL{});
-            else softmax_sub(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}, KC{}, SL{});
-          }
-          if constexpr (ph == 0) {            // next tile: direct loads, then its LSE / D
-            constexpr int lo = j * (2 * NL) / PL, hi = (j + 1) * (2 * NL) / PL;
-            [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
-              (load_piece(lo + Ws, nb, h_ld, q0_nx), ...);
-            }(std::make_integer_sequence<int, hi - lo>{});
-            if constexpr (j == PL - 1) stat_load(h_ld, q0_nx);
-          }
-          if constexpr (ph == 3 && j == PL - 1) stat_store(nb);
-          // diagonal tiles: mask each half's scores once its products are done
-          if constexpr ((ph == 0 || ph == 2) && j == PL - 1) {
-            if (need_mask) mask_half(ph == 0 ? s0 : s1, mthr - (ph / 2) * 32);
-          }
-        });
-    wait_global_loads();
-    __syncthreads();
+      lockstep_products<4 * PL, 4>(
+          [&](auto ic) {
+            constexpr int i = decltype(ic)::value, ph = i / PL, j = i % PL;
+            if constexpr (ph == 0 || ph == 2) {   // S / dP of half ph/2: step j = (ks, which)
+              constexpr int ks = j >> 1;
+              return lds_read16_at(bs[ks & 1] + 2 * ((j & 1) * TILE + (ph / 2) * 32 * ROW + (ks >> 1) * 32));
+            } else {                              // dV / dK: step j = (t, db, which), two transposing reads
+              constexpr int t = (ph == 1 ? 2 : 0) + j / (2 * DB), db = (j >> 1) % DB;
+              constexpr int off = ((j & 1) ? 0 : TILE) + 16 * t * ROW + 32 * db;   // Q^T for dK, dO^T for dV
+              const bf16x4 r0 = lds_read_tr4_at((ph == 1 ? btp[0] : bt[0]) + 2 * off);
+              const bf16x4 r1 = lds_read_tr4_at((ph == 1 ? btp[1] : bt[1]) + 2 * off);
+              return bf16x8{r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+            }
+          },
+          [&](auto ic, bf16x8 a) {
+            constexpr int i = decltype(ic)::value, ph = i / PL, j = i % PL;
+            if constexpr (ph == 0 || ph == 2) {
+              constexpr int ks = j >> 1;
+              f32x16& acc = (j & 1) ? (ph == 0 ? dp0 : dp1) : (ph == 0 ? s0 : s1);
+              const bf16x8& bop = (j & 1) ? vf[ks] : kf[ks];
+              acc = mfma32(a, bop, ks == 0 ? f32x16{} : acc);
+            } else {
+              constexpr int t = (ph == 1 ? 2 : 0) + j / (2 * DB), db = (j >> 1) % DB;
+              if constexpr (j & 1) mfma32_agpr(dk[db], a, da[t]);
+              else mfma32_agpr(dv[db], a, pa[t]);
+            }
+          },
+          [&](auto ic) {
+            constexpr int i = decltype(ic)::value, ph = i / PL, j = i % PL;
+            // stats for the next phase's group, into slot (ph + 1) & 1
+            if constexpr (j == 0) {
+              if constexpr (ph == 0) stat_read(1, stb, 0, 0);
+              else if constexpr (ph == 1) stat_read(0, stb, 0, 1);
+              else if constexpr (ph == 2) stat_read(1, stb, 1, 0);
+              else stat_read(0, stb, 1, 1);
+            }
+            // softmax sub-steps at steps (2k + 1) PL / 8
+            if constexpr ((j * 8) % PL == 0 && ((j * 8) / PL) % 2 == 1) {
+              constexpr int k = ((j * 8) / PL) / 2;
+              using KC = std::integral_constant<int, k>;
+              using SL = std::integral_constant<int, ph & 1>;
+              if constexpr (ph == 0) softmax_sub(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, KC{}, SL{});
+              else if constexpr (ph == 1) softmax_sub(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, KC{}, SL{});
+              else if constexpr (ph == 2) softmax_sub(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, KC{}, SL{});
+              else softmax_sub(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}, KC{}, SL{});
+            }
+            if constexpr (ph == 0) {            // next tile: direct loads, then its LSE / D
+              constexpr int lo = j * (2 * NL) / PL, hi = (j + 1) * (2 * NL) / PL;
+              [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
+                (load_piece(lo + Ws, nb, h_ld, q0_nx), ...);
+              }(std::make_integer_sequence<int, hi - lo>{});
+              if constexpr (j == PL - 1) stat_load(h_ld, q0_nx);
+            }
+            if constexpr (ph == 3 && j == PL - 1) stat_store(nb);
+            // diagonal tiles: mask each half's scores once its products are done
+            if constexpr ((ph == 0 || ph == 2) && j == PL - 1) {
+              if constexpr (MASKED) mask_half(ph == 0 ? s0 : s1, mthr - (ph / 2) * 32);
+            }
+          });
+      wait_global_loads();
+      __syncthreads();
     h_cur = h_nx;
     t_cur = t_nx;
     q0_cur = q0_nx;
+    ++kt_;
+  };
+  // The masked tiles of a head: a prefix whose rows start before this
+  // wave's last key (the diagonal) and, under a sliding window, a suffix
+  // whose last row reaches past this wave's first key's window. Rows rise
+  // with the tile index, so both are contiguous. (Per wave: every wave runs
+  // the same number of iterations and barriers.)
+  auto tile_row = [&](int t) { return (SPARSE ? uni(tl[t]) : first + t) * DKV_BQ; };
+  int npre = 0, nsuf = 0;
+  if constexpr (CAUSAL) {
+    while (npre < per_head && wk_first + DKV_KW - 1 > p.q_start + tile_row(npre)) ++npre;
+    if constexpr (WIN) {
+      while (nsuf < per_head - npre &&
+             p.q_start + tile_row(per_head - 1 - nsuf) + DKV_BQ - 1 - wk_first >= p.window)
+        ++nsuf;
+    }
   }
+  for (int hh = 0; hh < p.G && per_head > 0; ++hh) {
+    const int base = hh * per_head;
+    if constexpr (CAUSAL)
+      while (kt_ < base + npre) iteration(std::true_type{});
+    while (kt_ < base + per_head - nsuf) iteration(std::false_type{});
+    if constexpr (WIN)
+      while (kt_ < base + per_head) iteration(std::true_type{});
+  }
+  iteration(std::false_type{});       // the draining tile
 
   // ---- store dK^T, dV^T: lane (g, key n), register r <-> column 32 db + 8 (r/4) + 4g + r%4
 #pragma unroll
