@@ -59,7 +59,7 @@ struct DkdvSmem {
     bf16 q[TILE];
     bf16 o[TILE];              // dO
   };
-  float stat[3][2][DKV_BQ];    // [0]: LSE * log2(e) (+inf past the last row), [1]: D
+  float stat[3][2][DKV_BQ];    // [0]: LSE * log2(e) (+inf past the last row), [1]: -D
   Buf buf[3];
 };
 
@@ -180,7 +180,7 @@ void bwd_dkdv_kernel(Params p) {
   };
   auto stat_store = [&](int buf) {
     if (tid < 128) {
-      const float v = (tid < 64) ? (st_valid ? st * kLog2e : INFINITY) : (st_valid ? st : 0.f);
+      const float v = (tid < 64) ? (st_valid ? st * kLog2e : INFINITY) : (st_valid ? -st : 0.f);
       sm.stat[buf][tid >> 6][tid & 63] = v;
     }
   };
@@ -258,17 +258,29 @@ void bwd_dkdv_kernel(Params p) {
     pa[t] = bf16x8{};
     da[t] = bf16x8{};
   }
-  // LSE (log2 units) and D of the 8 query rows of the group being softmaxed,
+  // LSE (log2 units) of the 8 query rows of the group being softmaxed,
   // double-buffered: slot (phase & 1) is consumed, the other one prefetched
-  f32x4 st_l[2][2], st_d[2][2];
+  f32x4 st_l[2][2];
   const uint32_t stat_lane = lds_addr(&sm.stat[0][0][0]) + 32 * g;   // + rows 8g..8g+7
   // stb: LDS address of this lane's rows in the stats of one buffer
   auto stat_read = [&](int slot, uint32_t stb, int qb, int g2) {
     const int off = (qb * 32 + g2 * 16) * 4;
     st_l[slot][0] = lds_read_f32x4_at(stb + off);
     st_l[slot][1] = lds_read_f32x4_at(stb + off + 16);
-    st_d[slot][0] = lds_read_f32x4_at(stb + DKV_BQ * 4 + off);
-    st_d[slot][1] = lds_read_f32x4_at(stb + DKV_BQ * 4 + off + 16);
+  };
+  // -D of the 16 query rows of half qb that this lane's dP registers hold:
+  // the dP products accumulate onto it, so they produce dP - D directly
+  auto dinit_read = [&](uint32_t stb, int qb) {
+    f32x16 x;
+#pragma unroll
+    for (int g2 = 0; g2 < 2; ++g2)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const f32x4 y = lds_read_f32x4_at(stb + DKV_BQ * 4 + (qb * 32 + g2 * 16) * 4 + 16 * hf);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[8 * g2 + 4 * hf + e] = y[e];
+      }
+    return x;
   };
   stat_read(0, stat_lane + 2 * (2 * DKV_BQ * 4), 1, 1);   // tile -1, half 1, group 1
 
@@ -278,13 +290,13 @@ void bwd_dkdv_kernel(Params p) {
     constexpr int qb = decltype(qbc)::value, g2 = decltype(g2c)::value;
     constexpr int k = decltype(kc)::value, slot = decltype(slotc)::value;
     const f32x16& sv = qb ? s1 : s0;
-    const f32x16& dv_ = qb ? dp1 : dp0;
+    const f32x16& dv_ = qb ? dp1 : dp0;    // dP - D
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int e = 2 * k + u, r = g2 * 8 + e;
       const float x = __builtin_amdgcn_exp2f(fmaf(sv[r], c, -st_l[slot][e >> 2][e & 3]));
       pa[qb * 2 + g2][e] = (bf16)x;
-      da[qb * 2 + g2][e] = (bf16)(x * (dv_[r] - st_d[slot][e >> 2][e & 3]));
+      da[qb * 2 + g2][e] = (bf16)(x * dv_[r]);
     }
   };
   // causal mask on the scores of one half of a diagonal tile: query
@@ -332,6 +344,7 @@ void bwd_dkdv_kernel(Params p) {
       const uint32_t bt[2] = {lds_opaque(cq + 2 * rd_t[0]), lds_opaque(cq + 2 * rd_t[1])};
       const uint32_t btp[2] = {lds_opaque(pq + 2 * rd_t[0]), lds_opaque(pq + 2 * rd_t[1])};
       const uint32_t stb = lds_opaque(stat_lane + cb * (2 * DKV_BQ * 4));
+      const f32x16 di0 = dinit_read(stb, 0), di1 = dinit_read(stb, 1);
 
       lockstep_products<4 * PL, 4>(
           [&](auto ic) {
@@ -353,7 +366,8 @@ void bwd_dkdv_kernel(Params p) {
               constexpr int ks = j >> 1;
               f32x16& acc = (j & 1) ? (ph == 0 ? dp0 : dp1) : (ph == 0 ? s0 : s1);
               const bf16x8& bop = (j & 1) ? vf[ks] : kf[ks];
-              acc = mfma32(a, bop, ks == 0 ? f32x16{} : acc);
+              const f32x16 init = (j & 1) ? (ph == 0 ? di0 : di1) : f32x16{};
+              acc = mfma32(a, bop, ks == 0 ? init : acc);
             } else {
               constexpr int t = (ph == 1 ? 2 : 0) + j / (2 * DB), db = (j >> 1) % DB;
               if constexpr (j & 1) mfma32_agpr(dk[db], a, da[t]);
