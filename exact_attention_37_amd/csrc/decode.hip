@@ -15,11 +15,14 @@
 //  * one single-wave workgroup per (key split, K/V head, block of 32 query
 //    rows, batch); the 32 rows are the (query, head) pairs of one grouped-
 //    query group, so the group's K/V are read from HBM once per split;
-//  * the wave streams 32-key tiles of K and V straight from global memory
-//    into double-buffered LDS (buffer loads with a hardware range check) and
-//    runs the forward's tile step on them: S^T = K Q^T with K rows in sigma32
+//  * the waves stream tiles of K and V straight from global memory into
+//    double-buffered LDS (buffer loads with a hardware range check) and run
+//    the forward's tile step on them: S^T = K Q^T with K rows in sigma32
 //    order so P stays in registers, online softmax with a lazily raised max,
-//    O^T += V^T P^T with V^T from transposing LDS reads;
+//    O^T += V^T P^T with V^T from transposing LDS reads. Tiles hold 32 keys
+//    for one or two waves (decode: the stream is what matters) and 64 keys
+//    when four waves share them (chunked prefill: twice the products per
+//    barrier and per tile step);
 //  * it writes its normalised partial output (float32) and logsumexp; a
 //    second kernel merges the splits of every row.
 #include "common.h"
@@ -30,7 +33,6 @@ namespace miattn {
 
 namespace {
 
-constexpr int DBC = 32;   // keys per tile
 constexpr int NBUF = 2;   // tiles in LDS: the one being used and the next one in flight
 
 // K and V tiles of 32 keys, row-major; rows padded to D + 32 elements with
@@ -38,10 +40,10 @@ constexpr int NBUF = 2;   // tiles in LDS: the one being used and the next one i
 // NBUF buffers: the stream keeps NBUF - 1 tiles in flight per wave. (Four
 // buffers, three tiles in flight, measured no faster on the decode workload
 // and slower on chunked prefill, which then fits fewer waves per CU.)
-template <int D>
+template <int D, int KB>
 struct DecSmem {
   static constexpr int ROW = D + 32;
-  static constexpr int TILE = DBC * ROW;
+  static constexpr int TILE = 32 * KB * ROW;   // KB blocks of 32 keys
   bf16 k[NBUF][TILE];
   bf16 v[NBUF][TILE];
 };
@@ -50,17 +52,19 @@ struct DecSmem {
 // (gfx9 encoding: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt not waited on)
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-template <int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(NW * 64) void fwd_split_kernel(SplitParams p) {
+template <int D, bool CAUSAL, int NW, int KB>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(KB)))   // KB = 2: two waves per SIMD
+void fwd_split_kernel(SplitParams p) {
   constexpr int KS = D / 16;   // k-steps of the QK^T product
   constexpr int DB = D / 32;   // 32-column blocks of O
-  constexpr int ROW = DecSmem<D>::ROW, TILE = DecSmem<D>::TILE;
+  constexpr int DBC = 32 * KB; // keys per tile
+  constexpr int ROW = DecSmem<D, KB>::ROW, TILE = DecSmem<D, KB>::TILE;
   constexpr int TILE_KB = TILE * 2 / 1024;          // 1 KB direct loads per tensor tile
   static_assert(TILE * 2 % 1024 == 0, "whole 1 KB pieces");
   constexpr int PIECES = 2 * TILE_KB;               // load instructions per tile (K, V)
   static_assert(PIECES % NW == 0, "tile loads split evenly over the waves");
   constexpr int NL = PIECES / NW;                   // per wave
-  __shared__ __attribute__((aligned(16))) DecSmem<D> sm;
+  __shared__ __attribute__((aligned(16))) DecSmem<D, KB> sm;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
@@ -171,25 +175,31 @@ __global__ __launch_bounds__(NW * 64) void fwd_split_kernel(SplitParams p) {
     const bf16* kt = sm.k[buf];
     const bf16* vt = sm.v[buf];
 
-    // ---- S^T = K Q^T: register r of lane (g, n) <-> key key0 + sigma_row(g, r)
-    f32x16 s = f32x16{};
-    pipelined_products<KS, 4>(
-        [&](int ks) { return lds_read16(kt + rd_s[ks & 1], (ks >> 1) * 32); },
-        [&](int ks, bf16x8 a) { s = mfma32(a, qf[ks], s); });
+    // ---- S^T = K Q^T: register r of block kb of lane (g, n) <-> key key0 + 32 kb + sigma_row(g, r)
+    f32x16 s[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
+    pipelined_products<KB * KS, 4>(
+        [&](int i) { return lds_read16(kt + rd_s[(i % KS) & 1], (i / KS) * 32 * ROW + ((i % KS) >> 1) * 32); },
+        [&](int i, bf16x8 a) { s[i / KS] = mfma32(a, qf[i % KS], s[i / KS]); });
 
     // ---- mask: keys past k_hi, and (causal) keys after the query's position
     int thr = k_hi - 1 - key0;
     if (CAUSAL) thr = min(thr, qpos - key0);
     if (__builtin_amdgcn_ballot_w64(thr < DBC - 1) != 0) {
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr)
-        if (sigma_row(g, rr) > thr) s[rr] = -INFINITY;
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+          if (32 * kb + sigma_row(g, rr) > thr) s[kb][rr] = -INFINITY;
     }
 
     // ---- online softmax; rows that have seen no key yet keep m = -inf and p = 0
-    float mx = s[0];
+    float mx = s[0][0];
 #pragma unroll
-    for (int rr = 1; rr < 16; ++rr) mx = fmaxf(mx, s[rr]);
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb][rr]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mt = mx * c;
     const bool raise = mt > m + 8.f;
@@ -206,23 +216,25 @@ __global__ __launch_bounds__(NW * 64) void fwd_split_kernel(SplitParams p) {
       m = mnew;
     }
     const float mneg = m == -INFINITY ? 0.f : -m;
-    bf16x8 pf[2];
+    bf16x8 pf[2 * KB];
     float lsum = 0.f;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      bf16x8 x;
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(s[half * 8 + e], c, mneg));
-        lsum += pv;
-        x[e] = (bf16)pv;
+      for (int half = 0; half < 2; ++half) {
+        bf16x8 x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][half * 8 + e], c, mneg));
+          lsum += pv;
+          x[e] = (bf16)pv;
+        }
+        pf[2 * kb + half] = x;
       }
-      pf[half] = x;
-    }
     l += lsum;
 
-    // ---- O^T += V^T P^T: step i = (kq, db)
-    pipelined_products<2 * DB, 4>(
+    // ---- O^T += V^T P^T: step i = (kq, db), kq = 16-key block of the tile
+    pipelined_products<2 * KB * DB, 4>(
         [&](int st) {
           const int kq = st / DB, db = st % DB;
           const bf16x4 r0 = lds_read_tr4(vt + rd_t[0] + 16 * kq * ROW + 32 * db);
@@ -303,12 +315,13 @@ __global__ __launch_bounds__(64) void split_merge_kernel(SplitParams p) {
 
 template <int D, int NW>
 void launch_split_nw(const SplitParams& p, hipStream_t s) {
+  constexpr int KB = NW >= 4 ? 2 : 1;    // 64-key tiles when four waves share them
   const int rbs = (p.Nq * p.G + 31) / 32;
   const dim3 grid(p.nsplit, p.Hkv * ((rbs + NW - 1) / NW), p.B);
   if (p.causal)
-    hipLaunchKernelGGL((fwd_split_kernel<D, true, NW>), grid, dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((fwd_split_kernel<D, true, NW, KB>), grid, dim3(NW * 64), 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_split_kernel<D, false, NW>), grid, dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((fwd_split_kernel<D, false, NW, KB>), grid, dim3(NW * 64), 0, s, p);
 }
 
 template <int D>
