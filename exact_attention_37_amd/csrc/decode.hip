@@ -200,7 +200,7 @@ void fwd_split_kernel(SplitParams p) {
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb][rr]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_halves(mx);
     const float mt = mx * c;
     const bool raise = mt > m + 8.f;
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
@@ -246,7 +246,7 @@ void fwd_split_kernel(SplitParams p) {
 
   // ---- partial result of this split: normalised O (float32) and logsumexp;
   // a row without visible keys here gives (0, -inf), the merge's identity
-  const float lt = l + __shfl_xor(l, 32);
+  const float lt = sum_halves(l);
   if (valid) {
     const long long row = ((long long)split * p.B + b) * p.Nq + i;   // [split][b][i]
     float* O = p.o_part + (row * p.H + h) * D;

@@ -255,7 +255,7 @@ void fwd_mfma_kernel(Params p) {
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_halves(mx);
     const float mt = mx * c;
     const bool raise = mt > m + 8.f;
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
@@ -311,7 +311,7 @@ void fwd_mfma_kernel(Params p) {
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
-  const float lt = l + __shfl_xor(l, 32);
+  const float lt = sum_halves(l);
   if (row < p.Nq) {
     // a row that saw no key (block-sparse) stores o = 0 and lse = -inf
     const float inv = (SPARSE && lt == 0.f) ? 0.f : 1.f / lt;

@@ -145,6 +145,19 @@ __device__ __forceinline__ void agpr_settle(f32x16& x, f32x16& y) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(x), "+a"(y));
 }
 
+// The value of lane l ^ 32 combined with lane l's own, through one
+// v_permlane32_swap (no LDS round trip): swapping a register with itself
+// leaves the lower half's values in result 0 and the upper half's in
+// result 1 of every lane (checked on the device by a lane-layout probe).
+__device__ __forceinline__ float max_halves(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
 // A value every lane holds alike, moved to a scalar register (offsets of the
 // inline-assembly buffer loads must be scalar).
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
