@@ -75,8 +75,14 @@ def cpu_baseline(workload, heads=3):
     oracle.backward(qq, kk, vv, dd, True, scale)
     dt = time.perf_counter() - t0
     ff, fb = flops(1, heads, w.N, w.d, True)
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), model)
+    except OSError:
+        pass
     return {"value": round((ff + fb) / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "seconds": round(dt, 2),
+            "kind": "oracle", "seconds": round(dt, 2), "cpu_model": model, "host_cpus": os.cpu_count(),
             "sample": "%d query heads (B=1, N=%d, d=%d, causal) fwd+bwd in float64; "
                       "FLOPs counted as for the GPU" % (heads, w.N, w.d)}
 
