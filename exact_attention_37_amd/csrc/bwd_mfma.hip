@@ -388,10 +388,12 @@ void bwd_dkdv_kernel(Params p) {
               constexpr int k = ((j * 8) / PL) / 2;
               using KC = std::integral_constant<int, k>;
               using SL = std::integral_constant<int, ph & 1>;
-              if constexpr (ph == 0) softmax_sub(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, KC{}, SL{});
-              else if constexpr (ph == 1) softmax_sub(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, KC{}, SL{});
-              else if constexpr (ph == 2) softmax_sub(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, KC{}, SL{});
-              else softmax_sub(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}, KC{}, SL{});
+              using I0 = std::integral_constant<int, 0>;
+              using I1 = std::integral_constant<int, 1>;
+              if constexpr (ph == 0) softmax_sub(I1{}, I1{}, KC{}, SL{});
+              else if constexpr (ph == 1) softmax_sub(I0{}, I0{}, KC{}, SL{});
+              else if constexpr (ph == 2) softmax_sub(I0{}, I1{}, KC{}, SL{});
+              else softmax_sub(I1{}, I0{}, KC{}, SL{});
             }
             if constexpr (ph == 0) {            // next tile: direct loads, then its LSE / D
               constexpr int lo = j * (2 * NL) / PL, hi = (j + 1) * (2 * NL) / PL;

@@ -45,7 +45,8 @@ int check_common(int B, int H, int Hkv, int N, int d, int dtype) {
     return fail(MIATTN_EINVAL, "B, H, Hkv and N must be >= 1");
   if (H % Hkv != 0) return fail(MIATTN_EINVAL, "H must be a multiple of Hkv");
   if (d != 64 && d != 128) return fail(MIATTN_EUNSUPPORTED, "head dimension d must be 64 or 128");
-  if (dtype != MIATTN_F32 && dtype != MIATTN_BF16) return fail(MIATTN_EUNSUPPORTED, "dtype must be MIATTN_F32 or MIATTN_BF16");
+  if (dtype != MIATTN_F32 && dtype != MIATTN_BF16)
+    return fail(MIATTN_EUNSUPPORTED, "dtype must be MIATTN_F32 or MIATTN_BF16");
   if (B > 65535 || H > 65535) return fail(MIATTN_EUNSUPPORTED, "B and H must be <= 65535");
   // [B, H, N] statistics and row positions are indexed with 32-bit ints; the
   // matrix-core kernels address one sequence of a tensor (plus one tile past

@@ -1,5 +1,7 @@
 // Memory-bound helper kernels: the backward preprocess rowsum(dO * O), the
 // LSE merge of partial outputs, dtype conversion and fills.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -190,16 +192,18 @@ hipError_t launch_bwd_pre(const void* o, const void* dout, float* dsum, int B, i
                           int row0, int nrows, int dtype, hipStream_t s) {
   const long long threads = (long long)B * nrows * H * (d / 8);
   const dim3 grid(blocks_for(threads)), block(256);
+  auto go = [&](auto tc, auto dc) {
+    using T = decltype(tc);
+    constexpr int D = decltype(dc)::value;
+    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), grid, block, 0, s, (const T*)o, (const T*)dout, dsum, B, H, N, row0,
+                       nrows);
+  };
   if (dtype == 0) {
-    if (d == 64)
-      hipLaunchKernelGGL((bwd_pre_kernel<float, 64>), grid, block, 0, s, (const float*)o, (const float*)dout, dsum, B, H, N, row0, nrows);
-    else
-      hipLaunchKernelGGL((bwd_pre_kernel<float, 128>), grid, block, 0, s, (const float*)o, (const float*)dout, dsum, B, H, N, row0, nrows);
+    if (d == 64) go(float{}, std::integral_constant<int, 64>{});
+    else go(float{}, std::integral_constant<int, 128>{});
   } else {
-    if (d == 64)
-      hipLaunchKernelGGL((bwd_pre_kernel<bf16, 64>), grid, block, 0, s, (const bf16*)o, (const bf16*)dout, dsum, B, H, N, row0, nrows);
-    else
-      hipLaunchKernelGGL((bwd_pre_kernel<bf16, 128>), grid, block, 0, s, (const bf16*)o, (const bf16*)dout, dsum, B, H, N, row0, nrows);
+    if (d == 64) go(bf16{}, std::integral_constant<int, 64>{});
+    else go(bf16{}, std::integral_constant<int, 128>{});
   }
   return hipGetLastError();
 }

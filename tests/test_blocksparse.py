@@ -108,3 +108,17 @@ def test_llama16k_quarter_density_sampled():
     has_key = torch.isfinite(lse[0]).T.unsqueeze(-1)                    # [N, H, 1]
     sdo = (do[0].double().to(DEV) * has_key).sum(0)
     assert torch.all((dvs.sum(0) - sdo).abs() <= 2.0 ** -7 * dvs.abs().sum(0))
+
+
+def test_backward_accumulate_adds_into_float32_gradients():
+    q, k, v, do = draw(1, 4, 2, 700, 128, seed=46)
+    mask = draw_block_mask(700, 0.5, seed=5).to(DEV)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = mi.fwd_blocksparse(qd, kd, vd, mask, True, 0.1)
+    g = mi.bwd_blocksparse(qd, kd, vd, o, lse, dod, mask, True, 0.1)
+    base = [torch.full(t.shape, -0.5, dtype=torch.float32, device=DEV) for t in (qd, kd, vd)]
+    acc = mi.bwd_blocksparse(qd, kd, vd, o, lse, dod, mask, True, 0.1, accumulate=True,
+                             dq=base[0].clone(), dk=base[1].clone(), dv=base[2].clone())
+    torch.cuda.synchronize()
+    for a, b, x in zip(acc, g, base):
+        check_bf16("accumulated", f64(a - x), f64(b))

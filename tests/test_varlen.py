@@ -131,3 +131,17 @@ def test_packed16k_sampled():
         check_bf16("dk[s=%d,g=%d]" % (s, gk), f64(dk[a:e][rows, gk]), rk)
         check_bf16("dv[s=%d,g=%d]" % (s, gk), f64(dv[a:e][rows, gk]), rv)
         print("sequence", s, "rows", rows, "ok", flush=True)
+
+
+def test_backward_accumulate_adds_into_float32_gradients():
+    q, k, v, do, cu = draw_varlen([300, 77, 513], 4, 2, 128, seed=45)
+    qd, kd, vd, dod, cud = (t.to(DEV) for t in (q, k, v, do, cu))
+    o, lse = mi.fwd_varlen(qd, kd, vd, cud, 513, True, 0.1)
+    g = mi.bwd_varlen(qd, kd, vd, o, lse, dod, cud, 513, True, 0.1)
+    base = [torch.full(t.shape, 0.25, dtype=torch.float32, device=DEV) for t in (qd, kd, vd)]
+    acc = mi.bwd_varlen(qd, kd, vd, o, lse, dod, cud, 513, True, 0.1, accumulate=True,
+                        dq=base[0].clone(), dk=base[1].clone(), dv=base[2].clone())
+    torch.cuda.synchronize()
+    for a, b, x in zip(acc, g, base):
+        # the bf16 gradients are the float32 sums rounded once
+        check_bf16("accumulated", f64(a - x), f64(b))
