@@ -70,9 +70,14 @@ void fwd_split_kernel(SplitParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
   const int lane = tid & 63;
   const int g = lane >> 5, n = lane & 31;
-  const int split = blockIdx.x;
-  const int gkv = (int)blockIdx.y % p.Hkv;
-  const int rb = ((int)blockIdx.y / p.Hkv) * NW + wave;   // this wave's block of 32 rows
+  // grid: (split, head x row-block group, batch); with 64-key tiles (chunked
+  // prefill) the first two are swapped, so that the workgroups of one split
+  // over all heads and row blocks run side by side (measured faster there,
+  // and slower for decode)
+  const int split = KB == 2 ? (int)blockIdx.y : (int)blockIdx.x;
+  const int hg = KB == 2 ? (int)blockIdx.x : (int)blockIdx.y;
+  const int gkv = hg % p.Hkv;
+  const int rb = (hg / p.Hkv) * NW + wave;   // this wave's block of 32 rows
   const int b = blockIdx.z;
 
   // ---- the wave's 32 columns: row r = 32 rb + n of the group = (query i, head h)
@@ -317,7 +322,8 @@ template <int D, int NW>
 void launch_split_nw(const SplitParams& p, hipStream_t s) {
   constexpr int KB = NW >= 4 ? 2 : 1;    // 64-key tiles when four waves share them
   const int rbs = (p.Nq * p.G + 31) / 32;
-  const dim3 grid(p.nsplit, p.Hkv * ((rbs + NW - 1) / NW), p.B);
+  const unsigned hgs = p.Hkv * ((rbs + NW - 1) / NW);
+  const dim3 grid(KB == 2 ? hgs : p.nsplit, KB == 2 ? p.nsplit : hgs, p.B);
   if (p.causal)
     hipLaunchKernelGGL((fwd_split_kernel<D, true, NW, KB>), grid, dim3(NW * 64), 0, s, p);
   else
