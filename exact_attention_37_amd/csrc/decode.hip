@@ -52,7 +52,22 @@ struct DecSmem {
 // (gfx9 encoding: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt not waited on)
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-template <int D, bool CAUSAL, int NW, int KB>
+// Balanced splits: the valid keys of all sequences, taken in order, form
+// one range of T = sum_b L_b keys per (K/V head, row block); workgroup w of
+// P covers keys [T w / P, T (w + 1) / P) of it, so every workgroup streams
+// the same number of keys whatever the length mix. Its partial for sequence
+// b goes to slot w + b: the pairs (w, b) whose ranges overlap form a
+// staircase, so w + b is unique among them.
+__device__ __forceinline__ long long range_start(long long T, int w, int P) { return T * w / P; }
+// the workgroup whose range holds key x of the joint range (0 <= x < T)
+__device__ __forceinline__ int range_of(long long T, long long x, int P) {
+  int w = (int)(x * P / T);
+  while (w + 1 < P && range_start(T, w + 1, P) <= x) ++w;
+  while (w > 0 && range_start(T, w, P) > x) --w;
+  return w;
+}
+
+template <int D, bool CAUSAL, int NW, int KB, bool BAL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(KB)))   // KB = 2: two waves per SIMD
 void fwd_split_kernel(SplitParams p) {
   constexpr int KS = D / 16;   // k-steps of the QK^T product
@@ -78,7 +93,6 @@ void fwd_split_kernel(SplitParams p) {
   const int hg = KB == 2 ? (int)blockIdx.x : (int)blockIdx.y;
   const int gkv = hg % p.Hkv;
   const int rb = (hg / p.Hkv) * NW + wave;   // this wave's block of 32 rows
-  const int b = blockIdx.z;
 
   // ---- the wave's 32 columns: row r = 32 rb + n of the group = (query i, head h)
   const int M = p.Nq * p.G;
@@ -86,61 +100,11 @@ void fwd_split_kernel(SplitParams p) {
   const bool valid = r < M;
   const int rc = valid ? r : M - 1;
   const int i = rc / p.G, h = gkv * p.G + rc % p.G;
-  const int L = p.k_lens ? min(max(p.k_lens[b], 0), p.Nk) : p.Nk;   // valid cache rows
-  const int qpos = L - p.Nq + i;                  // position of query i in the sequence
-
   const long long qrs = (long long)p.H * D, krs = (long long)p.Hkv * D;
-  const bf16* Q = (const bf16*)p.q + ((long long)b * p.Nq) * qrs;
-  const bf16* K = (const bf16*)p.k + ((long long)b * p.Nk) * krs + (long long)gkv * D;
-  const bf16* V = (const bf16*)p.v + ((long long)b * p.Nk) * krs + (long long)gkv * D;
 
   float c = fabsf(p.scale) * kLog2e;
   float qsign = p.scale < 0.f ? -1.f : 1.f;
   if (p.scale == 0.f) { c = 1.f; qsign = 0.f; }
-
-  // Q^T operand (B of S^T = K Q^T): lane (g, n) holds Q[i][h][16 ks + 8 g .. +8]
-  bf16x8 qf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    bf16x8 x = *(const bf16x8*)(Q + (long long)i * qrs + (long long)h * D + ks * 16 + g * 8);
-    if (qsign != 1.f) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = (bf16)((float)x[e] * qsign);
-    }
-    qf[ks] = x;
-  }
-  wait_global_loads();
-
-  // ---- this split's keys [k_lo, k_hi)
-  const int k_lo = split * p.chunk;
-  const int k_hi = min(L, k_lo + p.chunk);
-  const int ntile = k_hi > k_lo ? (k_hi - k_lo + DBC - 1) / DBC : 0;
-
-  // Direct loads: piece s = wave * NL + j of a tile (K: s < TILE_KB, then V)
-  // covers tensor tile bytes [(s % TILE_KB) KB, +1 KB); lane l fills 16 bytes
-  // at 16 l: tile row rr, logical chunk ch (padding from chunk 0), read from
-  // byte loff[j] = 2 (rr * row stride + 8 ch) past the tile's first key. Keys
-  // past the cache's last row read as zeros (buffer range check); keys past
-  // k_hi are masked.
-  uint32_t loff[NL];
-#pragma unroll
-  for (int j = 0; j < NL; ++j) {
-    const int off = ((wave * NL + j) % TILE_KB) * 1024 + 16 * lane;
-    const int rr = off / (ROW * 2), pch = (off % (ROW * 2)) / 16;
-    const int col = pch < D / 8 ? ((pch ^ ((rr >> 2) & 3)) << 3) : 0;
-    loff[j] = (uint32_t)(rr * krs + col) * 2u;
-  }
-  const uint32_t kbytes = (uint32_t)(((p.Nk - 1) * krs + D) * 2);
-  const u32x4 rk = rsrc_words(K, kbytes), rv = rsrc_words(V, kbytes);
-  auto load_tile = [&](int buf, int key0) {
-#pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      const int s_ = wave * NL + j;                // wave-uniform
-      const bool is_v = s_ >= TILE_KB;
-      buffer_load_lds16_async(is_v ? rv : rk, loff[j], (uint32_t)(key0 * krs) * 2u,
-                              lds_addr((is_v ? sm.v[buf] : sm.k[buf]) + (s_ % TILE_KB) * 512));
-    }
-  };
 
   // per-lane LDS read offsets (elements), as in the forward kernel
   const int srow = sigma32(n), sf = (srow >> 2) & 3;
@@ -157,6 +121,55 @@ void fwd_split_kernel(SplitParams p) {
       rd_t[rd] = r_ * ROW + (chunk << 3) + 4 * (j & 1);
     }
   }
+
+  // Direct loads: piece s = wave * NL + j of a tile (K: s < TILE_KB, then V)
+  // covers tensor tile bytes [(s % TILE_KB) KB, +1 KB); lane l fills 16 bytes
+  // at 16 l: tile row rr, logical chunk ch (padding from chunk 0), read from
+  // byte loff[j] = 2 (rr * row stride + 8 ch) past the tile's first key. Keys
+  // past the cache's last row read as zeros (buffer range check); keys past
+  // k_hi are masked.
+  uint32_t loff[NL];
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    const int off = ((wave * NL + j) % TILE_KB) * 1024 + 16 * lane;
+    const int rr = off / (ROW * 2), pch = (off % (ROW * 2)) / 16;
+    const int col = pch < D / 8 ? ((pch ^ ((rr >> 2) & 3)) << 3) : 0;
+    loff[j] = (uint32_t)(rr * krs + col) * 2u;
+  }
+
+  // Keys [k_lo, k_hi) of sequence b; the partial goes to slot pslot.
+  auto run = [&](int b, int k_lo, int k_hi, long long pslot) {
+  const int L = p.k_lens ? min(max(p.k_lens[b], 0), p.Nk) : p.Nk;   // valid cache rows
+  const int qpos = L - p.Nq + i;                  // position of query i in the sequence
+  const bf16* Q = (const bf16*)p.q + ((long long)b * p.Nq) * qrs;
+  const bf16* K = (const bf16*)p.k + ((long long)b * p.Nk) * krs + (long long)gkv * D;
+  const bf16* V = (const bf16*)p.v + ((long long)b * p.Nk) * krs + (long long)gkv * D;
+
+  // Q^T operand (B of S^T = K Q^T): lane (g, n) holds Q[i][h][16 ks + 8 g .. +8]
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    bf16x8 x = *(const bf16x8*)(Q + (long long)i * qrs + (long long)h * D + ks * 16 + g * 8);
+    if (qsign != 1.f) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = (bf16)((float)x[e] * qsign);
+    }
+    qf[ks] = x;
+  }
+  wait_global_loads();
+
+  const int ntile = k_hi > k_lo ? (k_hi - k_lo + DBC - 1) / DBC : 0;
+  const uint32_t kbytes = (uint32_t)(((p.Nk - 1) * krs + D) * 2);
+  const u32x4 rk = rsrc_words(K, kbytes), rv = rsrc_words(V, kbytes);
+  auto load_tile = [&](int buf, int key0) {
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int s_ = wave * NL + j;                // wave-uniform
+      const bool is_v = s_ >= TILE_KB;
+      buffer_load_lds16_async(is_v ? rv : rk, loff[j], (uint32_t)(key0 * krs) * 2u,
+                              lds_addr((is_v ? sm.v[buf] : sm.k[buf]) + (s_ % TILE_KB) * 512));
+    }
+  };
 
   f32x16 acc[DB];
 #pragma unroll
@@ -253,7 +266,7 @@ void fwd_split_kernel(SplitParams p) {
   // a row without visible keys here gives (0, -inf), the merge's identity
   const float lt = sum_halves(l);
   if (valid) {
-    const long long row = ((long long)split * p.B + b) * p.Nq + i;   // [split][b][i]
+    const long long row = pslot * p.Nq + i;        // [slot][i]
     float* O = p.o_part + (row * p.H + h) * D;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
@@ -266,8 +279,35 @@ void fwd_split_kernel(SplitParams p) {
         *(f32x4*)(O + db * 32 + run * 8 + g * 4) = x;
       }
     if (g == 0)
-      p.lse_part[(((long long)split * p.B + b) * p.H + h) * p.Nq + i] =
-          lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+      p.lse_part[(pslot * p.H + h) * p.Nq + i] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+  }
+  };
+
+  if constexpr (!BAL) {
+    // this split's keys of the batch entry
+    const int b = blockIdx.z;
+    const int L = p.k_lens ? min(max(p.k_lens[b], 0), p.Nk) : p.Nk;
+    const int k_lo = split * p.chunk;
+    run(b, k_lo, min(L, k_lo + p.chunk), (long long)split * p.B + b);
+  } else {
+    // this workgroup's range of the joint key range, sequence by sequence
+    const long long* pre = p.pre;
+    const long long T = pre[p.B];
+    const int P = p.nsplit, w = split;
+    const long long s0 = range_start(T, w, P), s1 = range_start(T, w + 1, P);
+    if (s0 >= s1) return;
+    int lo = 0, hi = p.B;                         // last b with pre[b] <= s0
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) / 2;
+      if (pre[mid] <= s0) lo = mid; else hi = mid;
+    }
+    for (int b = lo; b < p.B && pre[b] < s1; ++b) {
+      const long long a = max(s0, pre[b]), e = min(s1, pre[b + 1]);
+      if (e > a) {
+        __syncthreads();                          // every wave is done with the previous sequence's tiles
+        run(b, (int)(a - pre[b]), (int)(e - pre[b]), (long long)w + b);
+      }
+    }
   }
 }
 
@@ -318,6 +358,76 @@ __global__ __launch_bounds__(64) void split_merge_kernel(SplitParams p) {
   if (lane == 0) p.lse[((long long)b * p.H + h) * p.Nq + i] = lse;
 }
 
+// Merge for balanced splits: row (b, i, h) combines the partials of the
+// workgroups whose ranges overlap sequence b's keys [pre[b], pre[b+1]) of
+// the joint range (slot w + b), as split_merge_kernel does over splits.
+template <int D>
+__global__ __launch_bounds__(64) void bal_merge_kernel(SplitParams p) {
+  const int lane = threadIdx.x;
+  const int row = blockIdx.x;                     // (b, i, h), h fastest
+  const int h = row % p.H, i = (row / p.H) % p.Nq, b = row / (p.H * p.Nq);
+  const long long* pre = p.pre;
+  const long long T = pre[p.B], a = pre[b], e = pre[b + 1];
+  const int P = p.nsplit;
+  const int w0 = a < e ? range_of(T, a, P) : 0, nw = a < e ? range_of(T, e - 1, P) - w0 + 1 : 0;
+  // a workgroup with an empty range wrote nothing
+  auto lse_at = [&](int t) {
+    const int w = w0 + t;
+    if (range_start(T, w, P) == range_start(T, w + 1, P)) return -INFINITY;
+    return p.lse_part[(((long long)w + b) * p.H + h) * p.Nq + i];
+  };
+  float mx = -INFINITY;
+  for (int t = lane; t < nw; t += 64) mx = fmaxf(mx, lse_at(t));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  float tot = 0.f;
+  if (mx != -INFINITY)
+    for (int t = lane; t < nw; t += 64) tot += expf(lse_at(t) - mx);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
+  const float lse = mx == -INFINITY ? -INFINITY : mx + logf(tot);
+  constexpr int CPL = D / 64;                     // columns per lane
+  float acc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+  if (mx != -INFINITY) {
+    for (int t0 = 0; t0 < nw; t0 += 64) {
+      const float w_l = t0 + lane < nw ? expf(lse_at(t0 + lane) - lse) : 0.f;
+      const int cnt = min(64, nw - t0);
+      for (int t = 0; t < cnt; ++t) {
+        const float wt = __shfl(w_l, t);
+        if (wt == 0.f) continue;                  // (wave-uniform) nothing to add, or an empty range
+        const float* src = p.o_part + ((((long long)w0 + t0 + t + b) * p.Nq + i) * p.H + h) * D + lane;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[c] += wt * src[64 * c];
+      }
+    }
+  }
+  bf16* O = (bf16*)p.o + (((long long)b * p.Nq + i) * p.H + h) * D + lane;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) O[64 * c] = (bf16)acc[c];
+  if (lane == 0) p.lse[((long long)b * p.H + h) * p.Nq + i] = lse;
+}
+
+// pre[b] = sum of the valid lengths of sequences 0 .. b-1 (pre[0] = 0,
+// pre[B] = T), lengths clamped to [0, Nk]; one wave, 64 sequences a step.
+__global__ __launch_bounds__(64) void bal_prefix_kernel(const int* k_lens, int B, int Nk, long long* pre) {
+  const int lane = threadIdx.x;
+  long long base = 0;
+  if (lane == 0) pre[0] = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int b = b0 + lane;
+    int x = b < B ? (k_lens ? min(max(k_lens[b], 0), Nk) : Nk) : 0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {            // inclusive scan over the wave
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (b < B) pre[b + 1] = base + x;
+    base += __shfl(x, 63);
+  }
+}
+
 template <int D, int NW>
 void launch_split_nw(const SplitParams& p, hipStream_t s) {
   constexpr int KB = NW >= 4 ? 2 : 1;    // 64-key tiles when four waves share them
@@ -325,13 +435,25 @@ void launch_split_nw(const SplitParams& p, hipStream_t s) {
   const unsigned hgs = p.Hkv * ((rbs + NW - 1) / NW);
   const dim3 grid(KB == 2 ? hgs : p.nsplit, KB == 2 ? p.nsplit : hgs, p.B);
   if (p.causal)
-    hipLaunchKernelGGL((fwd_split_kernel<D, true, NW, KB>), grid, dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((fwd_split_kernel<D, true, NW, KB, false>), grid, dim3(NW * 64), 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_split_kernel<D, false, NW, KB>), grid, dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((fwd_split_kernel<D, false, NW, KB, false>), grid, dim3(NW * 64), 0, s, p);
 }
 
 template <int D>
 hipError_t launch_split_d(const SplitParams& p, hipStream_t s) {
+  if (p.pre) {                                    // balanced ranges: one block of 32 rows per group
+    hipLaunchKernelGGL(bal_prefix_kernel, dim3(1), dim3(64), 0, s, p.k_lens, p.B, p.Nk, p.pre);
+    const dim3 grid(p.nsplit, p.Hkv, 1);
+    if (p.causal)
+      hipLaunchKernelGGL((fwd_split_kernel<D, true, 1, 1, true>), grid, dim3(64), 0, s, p);
+    else
+      hipLaunchKernelGGL((fwd_split_kernel<D, false, 1, 1, true>), grid, dim3(64), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bal_merge_kernel<D>), dim3(p.B * p.Nq * p.H), dim3(64), 0, s, p);
+    return hipGetLastError();
+  }
   // waves per workgroup = blocks of 32 rows sharing each K/V tile
   const int rbs = (p.Nq * p.G + 31) / 32;
   if (rbs >= 4) launch_split_nw<D, 4>(p, s);

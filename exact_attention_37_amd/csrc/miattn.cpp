@@ -328,25 +328,47 @@ int attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, co
     if (overlap(ro, r) || overlap(rl, r)) return fail(MIATTN_EINVAL, "o/lse must not alias q, k_cache or v_cache");
   if (overlap(ro, rl)) return fail(MIATTN_EINVAL, "o and lse must not overlap");
 
-  // Splits: enough single-wave workgroups to keep every CU streaming (about
-  // 8 per CU), each split at least 256 keys; keys per split a multiple of the
-  // 32-key tile.
   const int G = H / Hkv;
-  const long long groups = (long long)B * Hkv * ((Nq * G + 31) / 32);
-  if (nsplit == 0) {
-    const long long want = (2048 + groups - 1) / groups;
-    const long long most = (Nk + 255) / 256;
-    nsplit = (int)std::max(1LL, std::min(want, most));
-  }
-  int chunk = (Nk + nsplit - 1) / nsplit;
-  chunk = (chunk + 31) / 32 * 32;
-  nsplit = (Nk + chunk - 1) / chunk;     // no empty trailing split
-
+  const int rbs = (Nq * G + 31) / 32;           // blocks of 32 rows per K/V head group
   hipStream_t s = (hipStream_t)stream;
   Scratch scratch(s);
   const long long rows = (long long)B * Nq * H;
-  float* o_part = (float*)scratch.get((size_t)nsplit * rows * d * 4);
-  float* lse_part = (float*)scratch.get((size_t)nsplit * rows * 4);
+  long long* pre = nullptr;
+  int chunk = 0;
+  long long slots;                              // partial results per row
+  if (rbs == 1) {
+    // Decode-shaped (one block of rows per group): balanced ranges. The
+    // valid keys of all sequences form one joint range per K/V head, cut into
+    // nsplit equal ranges; by default one range per resident single-wave
+    // workgroup (four per CU), each at least 256 keys.
+    if (nsplit == 0) {
+      int dev = 0, ncu = 256;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        ncu = 256;
+      const long long most = std::max(1LL, (long long)B * Nk / 256);
+      nsplit = (int)std::max(1LL, std::min({(long long)4 * ncu / Hkv, most, 1024LL}));
+    }
+    slots = (long long)nsplit + B;
+    pre = (long long*)scratch.get((size_t)(B + 1) * 8);
+    if (!pre) return fail(MIATTN_ENOMEM, "hipMallocAsync failed for the length prefix sums");
+  } else {
+    // Splits: enough workgroups to keep every CU busy (about 2048 single-wave
+    // equivalents), each split at least 256 keys; keys per split a multiple
+    // of the 32-key tile.
+    const long long groups = (long long)B * Hkv * rbs;
+    if (nsplit == 0) {
+      const long long want = (2048 + groups - 1) / groups;
+      const long long most = (Nk + 255) / 256;
+      nsplit = (int)std::max(1LL, std::min(want, most));
+    }
+    chunk = (Nk + nsplit - 1) / nsplit;
+    chunk = (chunk + 31) / 32 * 32;
+    nsplit = (Nk + chunk - 1) / chunk;     // no empty trailing split
+    slots = (long long)nsplit * B;
+  }
+  float* o_part = (float*)scratch.get((size_t)(slots * rows / B) * d * 4);
+  float* lse_part = (float*)scratch.get((size_t)(slots * rows / B) * 4);
   if (!o_part || !lse_part) return fail(MIATTN_ENOMEM, "hipMallocAsync failed for the split partials");
   miattn::SplitParams p{};
   p.q = q;
@@ -368,6 +390,7 @@ int attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, co
   p.scale = scale;
   p.nsplit = nsplit;
   p.chunk = chunk;
+  p.pre = pre;
   if ((st = launch_status(miattn::launch_fwd_split(p, s), "attn_fwd_kvcache"))) return st;
   return ok();
 }

@@ -90,12 +90,21 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *                   sees cache rows j <= that position (the new rows are the
  *                   last Nq positions of the sequence). A row that sees no
  *                   key gets o = 0 and lse = -inf.
- *   nsplit        : number of key chunks, 1..1024, or 0 to let the library
- *                   choose (about 2048 single-wave workgroups in all, each
- *                   chunk at least 256 keys). Chunks are rounded up to a
- *                   multiple of 32 keys, which can lower the count.
+ *   nsplit        : 1..1024, or 0 to let the library choose. With at most
+ *                   32 query rows per K/V head group (Nq * H / Hkv <= 32,
+ *                   decoding) it is the number of equal key ranges that the
+ *                   valid keys of all batch entries, taken in order, are cut
+ *                   into per K/V head, so that the work is the same for every
+ *                   range whatever the length mix (default: four ranges per
+ *                   compute unit over the K/V heads, each >= 256 keys).
+ *                   Otherwise it is the number of equal chunks of every
+ *                   entry's cache (default: about 2048 single-wave workgroups
+ *                   in all, each chunk >= 256 keys, rounded up to a multiple
+ *                   of 32 keys, which can lower the count). The result does
+ *                   not depend on it beyond float32 rounding.
  *   dtype         : MIATTN_BF16 only (MIATTN_EUNSUPPORTED otherwise).
- * Scratch: float32 partials, nsplit * B * Nq * H * (d + 1) * 4 bytes.
+ * Scratch: float32 partials of (nsplit + B) [ranges] or nsplit * B [chunks]
+ * slots of Nq * H * (d + 1) values, plus B + 1 int64 prefix sums [ranges].
  * o and lse must not alias q, k_cache or v_cache. */
 int attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, const int* k_lens,
                      void* o, float* lse, int B, int H, int Hkv, int Nq, int Nk, int d, int causal,

@@ -39,6 +39,9 @@ CASES = [
     (2, 4, 2, 1, 64, 64, [0, 64], True, 0),            # an empty cache: o = 0, lse = -inf
     (1, 8, 8, 2, 5000, 128, [4999], False, 40),        # many small splits
     (1, 4, 4, 3, 600, 64, [546], True, 19),            # last split (keys 544, 545) unseen by row 0
+    (6, 8, 2, 1, 3000, 128, [3000, 0, 1, 33, 2999, 70], True, 0),   # skewed mix: ranges cross sequences
+    (4, 8, 4, 2, 900, 64, [900, 5, 0, 64], True, 13),  # 13 ranges over 969 keys, two new rows
+    (3, 4, 2, 1, 50, 128, [50, 1, 2], False, 64),      # more ranges than keys: some ranges empty
 ]
 
 
