@@ -139,148 +139,148 @@ void fwd_split_kernel(SplitParams p) {
 
   // Keys [k_lo, k_hi) of sequence b; the partial goes to slot pslot.
   auto run = [&](int b, int k_lo, int k_hi, long long pslot) {
-  const int L = p.k_lens ? min(max(p.k_lens[b], 0), p.Nk) : p.Nk;   // valid cache rows
-  const int qpos = L - p.Nq + i;                  // position of query i in the sequence
-  const bf16* Q = (const bf16*)p.q + ((long long)b * p.Nq) * qrs;
-  const bf16* K = (const bf16*)p.k + ((long long)b * p.Nk) * krs + (long long)gkv * D;
-  const bf16* V = (const bf16*)p.v + ((long long)b * p.Nk) * krs + (long long)gkv * D;
+    const int L = p.k_lens ? min(max(p.k_lens[b], 0), p.Nk) : p.Nk;   // valid cache rows
+    const int qpos = L - p.Nq + i;                  // position of query i in the sequence
+    const bf16* Q = (const bf16*)p.q + ((long long)b * p.Nq) * qrs;
+    const bf16* K = (const bf16*)p.k + ((long long)b * p.Nk) * krs + (long long)gkv * D;
+    const bf16* V = (const bf16*)p.v + ((long long)b * p.Nk) * krs + (long long)gkv * D;
 
-  // Q^T operand (B of S^T = K Q^T): lane (g, n) holds Q[i][h][16 ks + 8 g .. +8]
-  bf16x8 qf[KS];
+    // Q^T operand (B of S^T = K Q^T): lane (g, n) holds Q[i][h][16 ks + 8 g .. +8]
+    bf16x8 qf[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    bf16x8 x = *(const bf16x8*)(Q + (long long)i * qrs + (long long)h * D + ks * 16 + g * 8);
-    if (qsign != 1.f) {
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 x = *(const bf16x8*)(Q + (long long)i * qrs + (long long)h * D + ks * 16 + g * 8);
+      if (qsign != 1.f) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = (bf16)((float)x[e] * qsign);
+        for (int e = 0; e < 8; ++e) x[e] = (bf16)((float)x[e] * qsign);
+      }
+      qf[ks] = x;
     }
-    qf[ks] = x;
-  }
-  wait_global_loads();
+    wait_global_loads();
 
-  const int ntile = k_hi > k_lo ? (k_hi - k_lo + DBC - 1) / DBC : 0;
-  const uint32_t kbytes = (uint32_t)(((p.Nk - 1) * krs + D) * 2);
-  const u32x4 rk = rsrc_words(K, kbytes), rv = rsrc_words(V, kbytes);
-  auto load_tile = [&](int buf, int key0) {
+    const int ntile = k_hi > k_lo ? (k_hi - k_lo + DBC - 1) / DBC : 0;
+    const uint32_t kbytes = (uint32_t)(((p.Nk - 1) * krs + D) * 2);
+    const u32x4 rk = rsrc_words(K, kbytes), rv = rsrc_words(V, kbytes);
+    auto load_tile = [&](int buf, int key0) {
 #pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      const int s_ = wave * NL + j;                // wave-uniform
-      const bool is_v = s_ >= TILE_KB;
-      buffer_load_lds16_async(is_v ? rv : rk, loff[j], (uint32_t)(key0 * krs) * 2u,
-                              lds_addr((is_v ? sm.v[buf] : sm.k[buf]) + (s_ % TILE_KB) * 512));
-    }
-  };
+      for (int j = 0; j < NL; ++j) {
+        const int s_ = wave * NL + j;                // wave-uniform
+        const bool is_v = s_ >= TILE_KB;
+        buffer_load_lds16_async(is_v ? rv : rk, loff[j], (uint32_t)(key0 * krs) * 2u,
+                                lds_addr((is_v ? sm.v[buf] : sm.k[buf]) + (s_ % TILE_KB) * 512));
+      }
+    };
 
-  f32x16 acc[DB];
+    f32x16 acc[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-  float m = -INFINITY, l = 0.f;
+    for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+    float m = -INFINITY, l = 0.f;
 
-  static_assert(NBUF <= 4 && (NBUF - 2) * NL < 64, "vmcnt range");
-  for (int t = 0; t < NBUF - 1 && t < ntile; ++t) load_tile(t, k_lo + t * DBC);
-  for (int t = 0; t < ntile; ++t) {
-    const int buf = t % NBUF;
-    const int key0 = k_lo + t * DBC;
-    // wait for tile t; the (at most NBUF - 2) tiles issued after it may stay in flight
-    const int later = min(NBUF - 2, ntile - 1 - t);
-    if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NL));
-    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NL));
-    else wait_global_loads();
-    // every wave's pieces of tile t are in LDS, and every wave is done with
-    // the buffer that the next loads overwrite
-    __syncthreads();
-    if (t + NBUF - 1 < ntile) load_tile((t + NBUF - 1) % NBUF, key0 + (NBUF - 1) * DBC);
-    const bf16* kt = sm.k[buf];
-    const bf16* vt = sm.v[buf];
+    static_assert(NBUF <= 4 && (NBUF - 2) * NL < 64, "vmcnt range");
+    for (int t = 0; t < NBUF - 1 && t < ntile; ++t) load_tile(t, k_lo + t * DBC);
+    for (int t = 0; t < ntile; ++t) {
+      const int buf = t % NBUF;
+      const int key0 = k_lo + t * DBC;
+      // wait for tile t; the (at most NBUF - 2) tiles issued after it may stay in flight
+      const int later = min(NBUF - 2, ntile - 1 - t);
+      if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NL));
+      else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NL));
+      else wait_global_loads();
+      // every wave's pieces of tile t are in LDS, and every wave is done with
+      // the buffer that the next loads overwrite
+      __syncthreads();
+      if (t + NBUF - 1 < ntile) load_tile((t + NBUF - 1) % NBUF, key0 + (NBUF - 1) * DBC);
+      const bf16* kt = sm.k[buf];
+      const bf16* vt = sm.v[buf];
 
-    // ---- S^T = K Q^T: register r of block kb of lane (g, n) <-> key key0 + 32 kb + sigma_row(g, r)
-    f32x16 s[KB];
+      // ---- S^T = K Q^T: register r of block kb of lane (g, n) <-> key key0 + 32 kb + sigma_row(g, r)
+      f32x16 s[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
-    pipelined_products<KB * KS, 4>(
-        [&](int i) { return lds_read16(kt + rd_s[(i % KS) & 1], (i / KS) * 32 * ROW + ((i % KS) >> 1) * 32); },
-        [&](int i, bf16x8 a) { s[i / KS] = mfma32(a, qf[i % KS], s[i / KS]); });
+      for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
+      pipelined_products<KB * KS, 4>(
+          [&](int i) { return lds_read16(kt + rd_s[(i % KS) & 1], (i / KS) * 32 * ROW + ((i % KS) >> 1) * 32); },
+          [&](int i, bf16x8 a) { s[i / KS] = mfma32(a, qf[i % KS], s[i / KS]); });
 
-    // ---- mask: keys past k_hi, and (causal) keys after the query's position
-    int thr = k_hi - 1 - key0;
-    if (CAUSAL) thr = min(thr, qpos - key0);
-    if (__builtin_amdgcn_ballot_w64(thr < DBC - 1) != 0) {
+      // ---- mask: keys past k_hi, and (causal) keys after the query's position
+      int thr = k_hi - 1 - key0;
+      if (CAUSAL) thr = min(thr, qpos - key0);
+      if (__builtin_amdgcn_ballot_w64(thr < DBC - 1) != 0) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr)
+            if (32 * kb + sigma_row(g, rr) > thr) s[kb][rr] = -INFINITY;
+      }
+
+      // ---- online softmax; rows that have seen no key yet keep m = -inf and p = 0
+      float mx = s[0][0];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr)
-          if (32 * kb + sigma_row(g, rr) > thr) s[kb][rr] = -INFINITY;
+        for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb][rr]);
+      mx = max_halves(mx);
+      const float mt = mx * c;
+      const bool raise = mt > m + 8.f;
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+        const float mnew = raise ? mt : m;
+        // rows that keep their max keep alpha = 1: a row that has seen no key
+        // yet has m = -inf, and -inf - -inf has no value
+        const float alpha = raise ? exp2f(m - mnew) : 1.f;
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) acc[db][rr] *= alpha;
+        m = mnew;
+      }
+      const float mneg = m == -INFINITY ? 0.f : -m;
+      bf16x8 pf[2 * KB];
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          bf16x8 x;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][half * 8 + e], c, mneg));
+            lsum += pv;
+            x[e] = (bf16)pv;
+          }
+          pf[2 * kb + half] = x;
+        }
+      l += lsum;
+
+      // ---- O^T += V^T P^T: step i = (kq, db), kq = 16-key block of the tile
+      pipelined_products<2 * KB * DB, 4>(
+          [&](int st) {
+            const int kq = st / DB, db = st % DB;
+            const bf16x4 r0 = lds_read_tr4(vt + rd_t[0] + 16 * kq * ROW + 32 * db);
+            const bf16x4 r1 = lds_read_tr4(vt + rd_t[1] + 16 * kq * ROW + 32 * db);
+            return bf16x8{r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+          },
+          [&](int st, bf16x8 a) { acc[st % DB] = mfma32(a, pf[st / DB], acc[st % DB]); });
     }
 
-    // ---- online softmax; rows that have seen no key yet keep m = -inf and p = 0
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb][rr]);
-    mx = max_halves(mx);
-    const float mt = mx * c;
-    const bool raise = mt > m + 8.f;
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-      const float mnew = raise ? mt : m;
-      // rows that keep their max keep alpha = 1: a row that has seen no key
-      // yet has m = -inf, and -inf - -inf has no value
-      const float alpha = raise ? exp2f(m - mnew) : 1.f;
-      l *= alpha;
+    // ---- partial result of this split: normalised O (float32) and logsumexp;
+    // a row without visible keys here gives (0, -inf), the merge's identity
+    const float lt = sum_halves(l);
+    if (valid) {
+      const long long row = pslot * p.Nq + i;        // [slot][i]
+      float* O = p.o_part + (row * p.H + h) * D;
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) acc[db][rr] *= alpha;
-      m = mnew;
-    }
-    const float mneg = m == -INFINITY ? 0.f : -m;
-    bf16x8 pf[2 * KB];
-    float lsum = 0.f;
+        for (int run = 0; run < 4; ++run) {
+          f32x4 x;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        bf16x8 x;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][half * 8 + e], c, mneg));
-          lsum += pv;
-          x[e] = (bf16)pv;
+          for (int e = 0; e < 4; ++e) x[e] = acc[db][run * 4 + e] * inv;
+          *(f32x4*)(O + db * 32 + run * 8 + g * 4) = x;
         }
-        pf[2 * kb + half] = x;
-      }
-    l += lsum;
-
-    // ---- O^T += V^T P^T: step i = (kq, db), kq = 16-key block of the tile
-    pipelined_products<2 * KB * DB, 4>(
-        [&](int st) {
-          const int kq = st / DB, db = st % DB;
-          const bf16x4 r0 = lds_read_tr4(vt + rd_t[0] + 16 * kq * ROW + 32 * db);
-          const bf16x4 r1 = lds_read_tr4(vt + rd_t[1] + 16 * kq * ROW + 32 * db);
-          return bf16x8{r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
-        },
-        [&](int st, bf16x8 a) { acc[st % DB] = mfma32(a, pf[st / DB], acc[st % DB]); });
-  }
-
-  // ---- partial result of this split: normalised O (float32) and logsumexp;
-  // a row without visible keys here gives (0, -inf), the merge's identity
-  const float lt = sum_halves(l);
-  if (valid) {
-    const long long row = pslot * p.Nq + i;        // [slot][i]
-    float* O = p.o_part + (row * p.H + h) * D;
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int run = 0; run < 4; ++run) {
-        f32x4 x;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = acc[db][run * 4 + e] * inv;
-        *(f32x4*)(O + db * 32 + run * 8 + g * 4) = x;
-      }
-    if (g == 0)
-      p.lse_part[(pslot * p.H + h) * p.Nq + i] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
-  }
+      if (g == 0)
+        p.lse_part[(pslot * p.H + h) * p.Nq + i] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+    }
   };
 
   if constexpr (!BAL) {
