@@ -21,8 +21,9 @@
 //    order so P stays in registers, online softmax with a lazily raised max,
 //    O^T += V^T P^T with V^T from transposing LDS reads. Tiles hold 32 keys
 //    for one or two waves (decode: the stream is what matters) and 64 keys
-//    when four waves share them (chunked prefill: twice the products per
-//    barrier and per tile step);
+//    when four or eight waves share them (chunked prefill: twice the
+//    products per barrier and per tile step; eight waves, 256 rows, halve
+//    the tile loads per product again);
 //  * it writes its normalised partial output (float32) and logsumexp; a
 //    second kernel merges the splits of every row.
 #include "common.h"
@@ -430,7 +431,7 @@ __global__ __launch_bounds__(64) void bal_prefix_kernel(const int* k_lens, int B
 
 template <int D, int NW>
 void launch_split_nw(const SplitParams& p, hipStream_t s) {
-  constexpr int KB = NW >= 4 ? 2 : 1;    // 64-key tiles when four waves share them
+  constexpr int KB = NW >= 4 ? 2 : 1;    // 64-key tiles when four or more waves share them
   const int rbs = (p.Nq * p.G + 31) / 32;
   const unsigned hgs = p.Hkv * ((rbs + NW - 1) / NW);
   const dim3 grid(KB == 2 ? hgs : p.nsplit, KB == 2 ? p.nsplit : hgs, p.B);
@@ -456,7 +457,8 @@ hipError_t launch_split_d(const SplitParams& p, hipStream_t s) {
   }
   // waves per workgroup = blocks of 32 rows sharing each K/V tile
   const int rbs = (p.Nq * p.G + 31) / 32;
-  if (rbs >= 4) launch_split_nw<D, 4>(p, s);
+  if (rbs >= 8) launch_split_nw<D, 8>(p, s);
+  else if (rbs >= 4) launch_split_nw<D, 4>(p, s);
   else if (rbs >= 2) launch_split_nw<D, 2>(p, s);
   else launch_split_nw<D, 1>(p, s);
   hipError_t e = hipGetLastError();
