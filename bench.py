@@ -27,7 +27,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 # rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; calibrated against a plain
 # 1 GiB device copy in the same process), valid only for the kernel sources
 # whose SHA-1 is recorded with it (profiles/llama16k_causal_bf16_traffic.md).
-DKDV_TRAFFIC = {"sources_sha1": "3a050b7ba52128d55e98b0b86f03345b55bf62b0", "bytes": 2850749435}   # fetch 2.582 GB + write 0.268 GB
+DKDV_TRAFFIC = {"sources_sha1": "02c55b8c877cce605ac0ff0cc5db472b5a646934", "bytes": 2849466418}   # fetch 2.581 GB + write 0.268 GB
 DKDV_SOURCES = ("exact_attention_37_amd/csrc/bwd_mfma.hip", "exact_attention_37_amd/csrc/mfma_common.h",
                 "exact_attention_37_amd/csrc/common.h")
 

@@ -18,7 +18,7 @@ import torch
 
 __all__ = ["fwd", "bwd", "merge", "fwd_chunked", "bwd_chunked", "fwd_kvcache", "fwd_varlen", "bwd_varlen",
            "fwd_blocksparse", "bwd_blocksparse", "block_mask_shape",
-           "lib", "MiattnError",
+           "release_scratch", "lib", "MiattnError",
            "library_path", "balanced_rounds"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -68,6 +68,8 @@ def lib():
     L.attn_last_error.argtypes = []
     L.attn_version.restype = ctypes.c_char_p
     L.attn_version.argtypes = []
+    L.attn_release_scratch.argtypes = [vp]
+    L.attn_release_scratch.restype = i
     ip = ctypes.POINTER(ctypes.c_int)
     L.attn_chunk_schedule.argtypes = [i, ip, ip, ip, i]
     L.attn_chunk_schedule.restype = i
@@ -371,6 +373,14 @@ def bwd_blocksparse(q, k, v, o, lse, dout, block_mask, causal=False, scale=None,
                                       N, d, int(bool(causal)), scale, _stream(q), _ptr(dout), _ptr(dq), _ptr(dk),
                                       _ptr(dv), _dtype_code(q), int(bool(accumulate))))
     return dq, dk, dv
+
+
+def release_scratch(stream=None):
+    """Frees the scratch buffer the library keeps for `stream` (a
+    torch.cuda.Stream, default the current stream) on the current device, in
+    stream order (attn_release_scratch)."""
+    s = torch.cuda.current_stream() if stream is None else stream
+    _check(lib().attn_release_scratch(ctypes.c_void_p(s.cuda_stream)))
 
 
 def balanced_rounds(P):

@@ -36,9 +36,16 @@
  *   MIATTN_ENOMEM       a stream-ordered scratch allocation failed.
  *
  * Ownership: the caller allocates and owns every buffer passed in. The
- * library keeps no pointer after a call returns beyond the work enqueued on
- * `stream`. Scratch that a call needs is taken with hipMallocAsync on
- * `stream` and released with hipFreeAsync on the same stream.
+ * library keeps no pointer to them after a call returns beyond the work
+ * enqueued on `stream`. Scratch that a call needs comes from one device
+ * buffer that the library keeps per (device, stream) and uses only in that
+ * stream's order. A call that needs more takes the rest with hipMallocAsync
+ * on `stream`, then replaces the buffer with one of its full size (the old
+ * one freed with hipFreeAsync on `stream`): after the largest call, calls
+ * allocate nothing. Calls made while `stream` is being captured into a graph
+ * use stream-ordered allocations only, which the graph then owns. The buffer
+ * lives until attn_release_scratch(stream); call that before destroying a
+ * stream the library was used on.
  */
 #ifndef MIATTN_H
 #define MIATTN_H
@@ -274,6 +281,12 @@ const char* attn_last_error(void);
 
 /* Library version string. */
 const char* attn_version(void);
+
+/* Frees the scratch buffer kept for `stream` on the current device, in
+ * stream order (hipFreeAsync on `stream`); the next call on the stream
+ * allocates again. Nothing to free is not an error. Errors: MIATTN_ELAUNCH
+ * if the HIP runtime reports one. */
+int attn_release_scratch(void* stream);
 
 #ifdef __cplusplus
 }
