@@ -60,6 +60,27 @@ constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4
 // b goes to slot w + b: the pairs (w, b) whose ranges overlap form a
 // staircase, so w + b is unique among them.
 __device__ __forceinline__ long long range_start(long long T, int w, int P) { return T * w / P; }
+// valid cache rows of sequence b, clamped to [0, Nk]
+__device__ __forceinline__ int valid_len(const SplitParams& p, int b) {
+  return p.k_lens ? min(max(p.k_lens[b], 0), p.Nk) : p.Nk;
+}
+__device__ __forceinline__ long long wave_sum(long long x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+// a value every lane holds alike, as a scalar
+__device__ __forceinline__ long long uni64(long long x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long long)x >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+// T = the sum of the valid lengths, taken by one wave 64 sequences a step
+__device__ __forceinline__ long long total_len(const SplitParams& p, int lane) {
+  long long T = 0;
+  for (int b0 = 0; b0 < p.B; b0 += 64) T += wave_sum(b0 + lane < p.B ? valid_len(p, b0 + lane) : 0);
+  return uni64(T);
+}
 // the workgroup whose range holds key x of the joint range (0 <= x < T)
 __device__ __forceinline__ int range_of(long long T, long long x, int P) {
   int w = (int)(x * P / T);
@@ -291,23 +312,45 @@ void fwd_split_kernel(SplitParams p) {
     const int k_lo = split * p.chunk;
     run(b, k_lo, min(L, k_lo + p.chunk), (long long)split * p.B + b);
   } else {
-    // this workgroup's range of the joint key range, sequence by sequence
-    const long long* pre = p.pre;
-    const long long T = pre[p.B];
+    // this workgroup's range [s0, s1) of the joint key range, sequence by
+    // sequence; sequence b holds joint keys [start_b, start_b + L_b)
+    static_assert(NW == 1, "balanced ranges: one wave per workgroup");
+    const long long T = total_len(p, lane);
     const int P = p.nsplit, w = split;
     const long long s0 = range_start(T, w, P), s1 = range_start(T, w + 1, P);
     if (s0 >= s1) return;
-    int lo = 0, hi = p.B;                         // last b with pre[b] <= s0
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) / 2;
-      if (pre[mid] <= s0) lo = mid; else hi = mid;
-    }
-    for (int b = lo; b < p.B && pre[b] < s1; ++b) {
-      const long long a = max(s0, pre[b]), e = min(s1, pre[b + 1]);
-      if (e > a) {
-        __syncthreads();                          // every wave is done with the previous sequence's tiles
-        run(b, (int)(a - pre[b]), (int)(e - pre[b]), (long long)w + b);
+    // the first sequence that ends after s0, and its start: an inclusive scan
+    // of the lengths, 64 sequences a step
+    int b = p.B;
+    long long start = 0, base = 0;
+    for (int b0 = 0; b0 < p.B; b0 += 64) {
+      const long long x = b0 + lane < p.B ? valid_len(p, b0 + lane) : 0;
+      long long incl = x;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const long long y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
       }
+      // lanes past the last sequence hold the step's total, so the first hit is a sequence
+      const unsigned long long hit = __ballot(base + incl > s0);
+      if (hit) {
+        const int l = __ffsll(hit) - 1;
+        b = b0 + l;
+        start = base + __shfl(incl - x, l);
+        break;
+      }
+      base += __shfl(incl, 63);
+    }
+    b = uni(b);
+    start = uni64(start);
+    for (; b < p.B && start < s1; ++b) {
+      const int L = valid_len(p, b);
+      const long long a = max(s0, start), e = min(s1, start + L);
+      if (e > a) {
+        __syncthreads();                          // done with the previous sequence's tiles
+        run(b, (int)(a - start), (int)(e - start), (long long)w + b);
+      }
+      start += L;
     }
   }
 }
@@ -360,15 +403,23 @@ __global__ __launch_bounds__(64) void split_merge_kernel(SplitParams p) {
 }
 
 // Merge for balanced splits: row (b, i, h) combines the partials of the
-// workgroups whose ranges overlap sequence b's keys [pre[b], pre[b+1]) of
-// the joint range (slot w + b), as split_merge_kernel does over splits.
+// workgroups whose ranges overlap sequence b's keys [a, a + L_b) of the
+// joint range (slot w + b), as split_merge_kernel does over splits.
 template <int D>
 __global__ __launch_bounds__(64) void bal_merge_kernel(SplitParams p) {
   const int lane = threadIdx.x;
   const int row = blockIdx.x;                     // (b, i, h), h fastest
   const int h = row % p.H, i = (row / p.H) % p.Nq, b = row / (p.H * p.Nq);
-  const long long* pre = p.pre;
-  const long long T = pre[p.B], a = pre[b], e = pre[b + 1];
+  long long T = 0, a = 0;                         // all lengths; those before sequence b
+  for (int b0 = 0; b0 < p.B; b0 += 64) {
+    const int bb = b0 + lane;
+    const long long x = bb < p.B ? valid_len(p, bb) : 0;
+    T += wave_sum(x);
+    a += wave_sum(bb < b ? x : 0);
+  }
+  T = uni64(T);
+  a = uni64(a);
+  const long long e = a + valid_len(p, b);
   const int P = p.nsplit;
   const int w0 = a < e ? range_of(T, a, P) : 0, nw = a < e ? range_of(T, e - 1, P) - w0 + 1 : 0;
   // a workgroup with an empty range wrote nothing
@@ -410,25 +461,6 @@ __global__ __launch_bounds__(64) void bal_merge_kernel(SplitParams p) {
   if (lane == 0) p.lse[((long long)b * p.H + h) * p.Nq + i] = lse;
 }
 
-// pre[b] = sum of the valid lengths of sequences 0 .. b-1 (pre[0] = 0,
-// pre[B] = T), lengths clamped to [0, Nk]; one wave, 64 sequences a step.
-__global__ __launch_bounds__(64) void bal_prefix_kernel(const int* k_lens, int B, int Nk, long long* pre) {
-  const int lane = threadIdx.x;
-  long long base = 0;
-  if (lane == 0) pre[0] = 0;
-  for (int b0 = 0; b0 < B; b0 += 64) {
-    const int b = b0 + lane;
-    int x = b < B ? (k_lens ? min(max(k_lens[b], 0), Nk) : Nk) : 0;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {            // inclusive scan over the wave
-      const int y = __shfl_up(x, o);
-      if (lane >= o) x += y;
-    }
-    if (b < B) pre[b + 1] = base + x;
-    base += __shfl(x, 63);
-  }
-}
-
 template <int D, int NW>
 void launch_split_nw(const SplitParams& p, hipStream_t s) {
   constexpr int KB = NW >= 4 ? 2 : 1;    // 64-key tiles when four or more waves share them
@@ -443,8 +475,7 @@ void launch_split_nw(const SplitParams& p, hipStream_t s) {
 
 template <int D>
 hipError_t launch_split_d(const SplitParams& p, hipStream_t s) {
-  if (p.pre) {                                    // balanced ranges: one block of 32 rows per group
-    hipLaunchKernelGGL(bal_prefix_kernel, dim3(1), dim3(64), 0, s, p.k_lens, p.B, p.Nk, p.pre);
+  if (p.balanced) {                               // balanced ranges: one block of 32 rows per group
     const dim3 grid(p.nsplit, p.Hkv, 1);
     if (p.causal)
       hipLaunchKernelGGL((fwd_split_kernel<D, true, 1, 1, true>), grid, dim3(64), 0, s, p);

@@ -45,11 +45,11 @@ struct SplitParams {
   int B, H, Hkv, G, Nq, Nk, d, causal;
   float scale;
   int nsplit, chunk;
-  // Balanced ranges (one block of <= 32 rows per K/V head group): scratch of
-  // B + 1 prefix sums of the valid lengths; nsplit = ranges per K/V head,
-  // partial slots w + b (nsplit + B of them). Null: nsplit chunks of `chunk`
-  // keys per sequence, partial slots split * B + b.
-  long long* pre;
+  // Nonzero: balanced ranges (one block of <= 32 rows per K/V head group):
+  // nsplit = ranges per K/V head of the joint key range, partial slots w + b
+  // (nsplit + B of them). Zero: nsplit chunks of `chunk` keys per sequence,
+  // partial slots split * B + b.
+  int balanced;
 };
 hipError_t launch_fwd_split(const SplitParams& p, hipStream_t s);
 

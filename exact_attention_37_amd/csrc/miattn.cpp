@@ -404,7 +404,6 @@ int attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, co
   hipStream_t s = (hipStream_t)stream;
   Scratch scratch(s);
   const long long rows = (long long)B * Nq * H;
-  long long* pre = nullptr;
   int chunk = 0;
   long long slots;                              // partial results per row
   if (rbs == 1) {
@@ -421,8 +420,6 @@ int attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, co
       nsplit = (int)std::max(1LL, std::min({(long long)4 * ncu / Hkv, most, 1024LL}));
     }
     slots = (long long)nsplit + B;
-    pre = (long long*)scratch.get((size_t)(B + 1) * 8);
-    if (!pre) return fail(MIATTN_ENOMEM, "hipMallocAsync failed for the length prefix sums");
   } else {
     // Splits: enough workgroups to keep every CU busy (about 2048 single-wave
     // equivalents), each split at least 256 keys; keys per split a multiple
@@ -461,7 +458,7 @@ int attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, co
   p.scale = scale;
   p.nsplit = nsplit;
   p.chunk = chunk;
-  p.pre = pre;
+  p.balanced = rbs == 1;
   if ((st = launch_status(miattn::launch_fwd_split(p, s), "attn_fwd_kvcache"))) return st;
   return ok();
 }

@@ -111,7 +111,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *                   not depend on it beyond float32 rounding.
  *   dtype         : MIATTN_BF16 only (MIATTN_EUNSUPPORTED otherwise).
  * Scratch: float32 partials of (nsplit + B) [ranges] or nsplit * B [chunks]
- * slots of Nq * H * (d + 1) values, plus B + 1 int64 prefix sums [ranges].
+ * slots of Nq * H * (d + 1) values.
  * o and lse must not alias q, k_cache or v_cache. */
 int attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, const int* k_lens,
                      void* o, float* lse, int B, int H, int Hkv, int Nq, int Nk, int d, int causal,
