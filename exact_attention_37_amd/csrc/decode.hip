@@ -59,7 +59,16 @@ constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4
 // the same number of keys whatever the length mix. Its partial for sequence
 // b goes to slot w + b: the pairs (w, b) whose ranges overlap form a
 // staircase, so w + b is unique among them.
-__device__ __forceinline__ long long range_start(long long T, int w, int P) { return T * w / P; }
+// floor(n / d) for 0 <= n < 2^53 and 0 < d < 2^53: the correctly rounded
+// double quotient is at most one away from it, so one step either way, with
+// exact integer products, fixes it (far shorter than a 64-bit division)
+__device__ __forceinline__ long long floor_div(long long n, long long d) {
+  long long q = (long long)((double)n / (double)d);
+  if (q * d > n) --q;
+  else if ((q + 1) * d <= n) ++q;
+  return q;
+}
+__device__ __forceinline__ long long range_start(long long T, int w, int P) { return floor_div(T * w, P); }
 // valid cache rows of sequence b, clamped to [0, Nk]
 __device__ __forceinline__ int valid_len(const SplitParams& p, int b) {
   return p.k_lens ? min(max(p.k_lens[b], 0), p.Nk) : p.Nk;
@@ -80,13 +89,6 @@ __device__ __forceinline__ long long total_len(const SplitParams& p, int lane) {
   long long T = 0;
   for (int b0 = 0; b0 < p.B; b0 += 64) T += wave_sum(b0 + lane < p.B ? valid_len(p, b0 + lane) : 0);
   return uni64(T);
-}
-// the workgroup whose range holds key x of the joint range (0 <= x < T)
-__device__ __forceinline__ int range_of(long long T, long long x, int P) {
-  int w = (int)(x * P / T);
-  while (w + 1 < P && range_start(T, w + 1, P) <= x) ++w;
-  while (w > 0 && range_start(T, w, P) > x) --w;
-  return w;
 }
 
 template <int D, bool CAUSAL, int NW, int KB, bool BAL>
@@ -355,6 +357,30 @@ void fwd_split_kernel(SplitParams p) {
   }
 }
 
+// acc[c] += sum over t < n of weight_t * row_t[lane + 64 c], with weight_t
+// held by lane t of w_l and row_t = src(t). Eight rows' loads are in flight
+// at a time; indices past n repeat the last row, and a zero weight (past n,
+// or a partial that no workgroup wrote) selects nothing rather than
+// multiplying whatever the row holds.
+template <int CPL, class SRC>
+__device__ __forceinline__ void accumulate_partials(float (&acc)[CPL], float w_l, int n, int lane, SRC src) {
+  for (int t = 0; t < n; t += 8) {
+    float x[8][CPL];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float* r = src(min(t + u, n - 1)) + lane;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) x[u][c] = r[64 * c];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float wt = t + u < n ? __shfl(w_l, t + u) : 0.f;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[c] += wt != 0.f ? wt * x[u][c] : 0.f;
+    }
+  }
+}
+
 // Merge of the splits of every (b, query, head) row: with M the largest
 // partial logsumexp, lse = M + ln sum_s e^(lse_s - M) and
 // o = sum_s e^(lse_s - lse) o_s; a row with no visible key gives o = 0,
@@ -369,13 +395,16 @@ __global__ __launch_bounds__(64) void split_merge_kernel(SplitParams p) {
   const int h = row % p.H, i = (row / p.H) % p.Nq, b = row / (p.H * p.Nq);
   const long long ps = (long long)p.B * p.Nq * p.H;   // rows per split
   auto lse_at = [&](int s) { return p.lse_part[(((long long)s * p.B + b) * p.H + h) * p.Nq + i]; };
-  float mx = -INFINITY;
-  for (int s = lane; s < p.nsplit; s += 64) mx = fmaxf(mx, lse_at(s));
+  const float l0 = lane < p.nsplit ? lse_at(lane) : -INFINITY;   // the first 64 splits, read once
+  float mx = l0;
+  for (int s = lane + 64; s < p.nsplit; s += 64) mx = fmaxf(mx, lse_at(s));
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
   float tot = 0.f;
-  if (mx != -INFINITY)
-    for (int s = lane; s < p.nsplit; s += 64) tot += expf(lse_at(s) - mx);
+  if (mx != -INFINITY) {
+    tot = expf(l0 - mx);
+    for (int s = lane + 64; s < p.nsplit; s += 64) tot += expf(lse_at(s) - mx);
+  }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
   const float lse = mx == -INFINITY ? -INFINITY : mx + logf(tot);
@@ -385,15 +414,9 @@ __global__ __launch_bounds__(64) void split_merge_kernel(SplitParams p) {
   for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
   if (mx != -INFINITY) {
     for (int s0 = 0; s0 < p.nsplit; s0 += 64) {
-      const int sl = s0 + lane;
-      const float w_l = sl < p.nsplit ? expf(lse_at(sl) - lse) : 0.f;
-      const int n = min(64, p.nsplit - s0);
-      for (int t = 0; t < n; ++t) {
-        const float w = __shfl(w_l, t);
-        const float* src = p.o_part + ((s0 + t) * ps + row) * D + lane;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) acc[c] += w * src[64 * c];
-      }
+      const float ls = s0 == 0 ? l0 : (s0 + lane < p.nsplit ? lse_at(s0 + lane) : -INFINITY);
+      accumulate_partials(acc, expf(ls - lse), min(64, p.nsplit - s0), lane,
+                          [&](int t) { return p.o_part + ((s0 + t) * ps + row) * D; });
     }
   }
   bf16* O = (bf16*)p.o + (((long long)b * p.Nq + i) * p.H + h) * D + lane;
@@ -421,20 +444,26 @@ __global__ __launch_bounds__(64) void bal_merge_kernel(SplitParams p) {
   a = uni64(a);
   const long long e = a + valid_len(p, b);
   const int P = p.nsplit;
-  const int w0 = a < e ? range_of(T, a, P) : 0, nw = a < e ? range_of(T, e - 1, P) - w0 + 1 : 0;
-  // a workgroup with an empty range wrote nothing
+  // the last range that starts at or before joint key x: range w starts at
+  // or before x exactly when T w < (x + 1) P, so no search is needed
+  auto last_range = [&](long long x) { return (int)min((long long)P - 1, floor_div((x + 1) * P - 1, T)); };
+  const int w0 = a < e ? last_range(a) : 0, nw = a < e ? last_range(e - 1) - w0 + 1 : 0;
+  // a workgroup with an empty range (possible only when T < P) wrote nothing
   auto lse_at = [&](int t) {
     const int w = w0 + t;
-    if (range_start(T, w, P) == range_start(T, w + 1, P)) return -INFINITY;
+    if (T < P && range_start(T, w, P) == range_start(T, w + 1, P)) return -INFINITY;
     return p.lse_part[(((long long)w + b) * p.H + h) * p.Nq + i];
   };
-  float mx = -INFINITY;
-  for (int t = lane; t < nw; t += 64) mx = fmaxf(mx, lse_at(t));
+  const float l0 = lane < nw ? lse_at(lane) : -INFINITY;   // the first 64 ranges, read once
+  float mx = l0;
+  for (int t = lane + 64; t < nw; t += 64) mx = fmaxf(mx, lse_at(t));
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
   float tot = 0.f;
-  if (mx != -INFINITY)
-    for (int t = lane; t < nw; t += 64) tot += expf(lse_at(t) - mx);
+  if (mx != -INFINITY) {
+    tot = expf(l0 - mx);
+    for (int t = lane + 64; t < nw; t += 64) tot += expf(lse_at(t) - mx);
+  }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
   const float lse = mx == -INFINITY ? -INFINITY : mx + logf(tot);
@@ -444,15 +473,11 @@ __global__ __launch_bounds__(64) void bal_merge_kernel(SplitParams p) {
   for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
   if (mx != -INFINITY) {
     for (int t0 = 0; t0 < nw; t0 += 64) {
-      const float w_l = t0 + lane < nw ? expf(lse_at(t0 + lane) - lse) : 0.f;
-      const int cnt = min(64, nw - t0);
-      for (int t = 0; t < cnt; ++t) {
-        const float wt = __shfl(w_l, t);
-        if (wt == 0.f) continue;                  // (wave-uniform) nothing to add, or an empty range
-        const float* src = p.o_part + ((((long long)w0 + t0 + t + b) * p.Nq + i) * p.H + h) * D + lane;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) acc[c] += wt * src[64 * c];
-      }
+      const float lt = t0 == 0 ? l0 : (t0 + lane < nw ? lse_at(t0 + lane) : -INFINITY);
+      const float w_l = expf(lt - lse);           // 0 for lanes past nw and empty ranges
+      accumulate_partials(acc, w_l, min(64, nw - t0), lane, [&](int t) {
+        return p.o_part + ((((long long)w0 + t0 + t + b) * p.Nq + i) * p.H + h) * D;
+      });
     }
   }
   bf16* O = (bf16*)p.o + (((long long)b * p.Nq + i) * p.H + h) * D + lane;
@@ -461,40 +486,35 @@ __global__ __launch_bounds__(64) void bal_merge_kernel(SplitParams p) {
   if (lane == 0) p.lse[((long long)b * p.H + h) * p.Nq + i] = lse;
 }
 
-template <int D, int NW>
+template <int D, int NW, bool BAL>
 void launch_split_nw(const SplitParams& p, hipStream_t s) {
   constexpr int KB = NW >= 4 ? 2 : 1;    // 64-key tiles when four or more waves share them
   const int rbs = (p.Nq * p.G + 31) / 32;
   const unsigned hgs = p.Hkv * ((rbs + NW - 1) / NW);
-  const dim3 grid(KB == 2 ? hgs : p.nsplit, KB == 2 ? p.nsplit : hgs, p.B);
+  const dim3 grid(KB == 2 ? hgs : p.nsplit, KB == 2 ? p.nsplit : hgs, BAL ? 1 : p.B);
   if (p.causal)
-    hipLaunchKernelGGL((fwd_split_kernel<D, true, NW, KB, false>), grid, dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((fwd_split_kernel<D, true, NW, KB, BAL>), grid, dim3(NW * 64), 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_split_kernel<D, false, NW, KB, false>), grid, dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((fwd_split_kernel<D, false, NW, KB, BAL>), grid, dim3(NW * 64), 0, s, p);
 }
 
 template <int D>
 hipError_t launch_split_d(const SplitParams& p, hipStream_t s) {
   if (p.balanced) {                               // balanced ranges: one block of 32 rows per group
-    const dim3 grid(p.nsplit, p.Hkv, 1);
-    if (p.causal)
-      hipLaunchKernelGGL((fwd_split_kernel<D, true, 1, 1, true>), grid, dim3(64), 0, s, p);
-    else
-      hipLaunchKernelGGL((fwd_split_kernel<D, false, 1, 1, true>), grid, dim3(64), 0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bal_merge_kernel<D>), dim3(p.B * p.Nq * p.H), dim3(64), 0, s, p);
-    return hipGetLastError();
+    launch_split_nw<D, 1, true>(p, s);
+  } else {                                        // waves per workgroup = blocks of 32 rows sharing each tile
+    const int rbs = (p.Nq * p.G + 31) / 32;
+    if (rbs >= 8) launch_split_nw<D, 8, false>(p, s);
+    else if (rbs >= 4) launch_split_nw<D, 4, false>(p, s);
+    else if (rbs >= 2) launch_split_nw<D, 2, false>(p, s);
+    else launch_split_nw<D, 1, false>(p, s);
   }
-  // waves per workgroup = blocks of 32 rows sharing each K/V tile
-  const int rbs = (p.Nq * p.G + 31) / 32;
-  if (rbs >= 8) launch_split_nw<D, 8>(p, s);
-  else if (rbs >= 4) launch_split_nw<D, 4>(p, s);
-  else if (rbs >= 2) launch_split_nw<D, 2>(p, s);
-  else launch_split_nw<D, 1>(p, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((split_merge_kernel<D>), dim3(p.B * p.Nq * p.H), dim3(64), 0, s, p);
+  if (p.balanced)
+    hipLaunchKernelGGL((bal_merge_kernel<D>), dim3(p.B * p.Nq * p.H), dim3(64), 0, s, p);
+  else
+    hipLaunchKernelGGL((split_merge_kernel<D>), dim3(p.B * p.Nq * p.H), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -408,9 +408,10 @@ int attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, co
   long long slots;                              // partial results per row
   if (rbs == 1) {
     // Decode-shaped (one block of rows per group): balanced ranges. The
-    // valid keys of all sequences form one joint range per K/V head, cut into
-    // nsplit equal ranges; by default one range per resident single-wave
-    // workgroup (four per CU), each at least 256 keys.
+    // valid keys of all sequences form one joint range per K/V head, cut
+    // into nsplit equal ranges, so every workgroup streams the same number
+    // of keys whatever the length mix; by default one range per resident
+    // single-wave workgroup (four per CU), each at least 256 keys.
     if (nsplit == 0) {
       int dev = 0, ncu = 256;
       if (hipGetDevice(&dev) != hipSuccess ||
@@ -421,9 +422,12 @@ int attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, co
     }
     slots = (long long)nsplit + B;
   } else {
-    // Splits: enough workgroups to keep every CU busy (about 2048 single-wave
-    // equivalents), each split at least 256 keys; keys per split a multiple
-    // of the 32-key tile.
+    // Larger groups: nsplit equal chunks of every sequence, enough workgroups
+    // to keep every CU busy (about 2048 single-wave equivalents), each chunk
+    // at least 256 keys and a multiple of the 32-key tile. (Balanced ranges
+    // were measured here too: they even out the split kernel, but ranges that
+    // straddle sequences leave each row more partials, and the merge then
+    // costs more than the split kernel saves.)
     const long long groups = (long long)B * Hkv * rbs;
     if (nsplit == 0) {
       const long long want = (2048 + groups - 1) / groups;

@@ -42,6 +42,8 @@ CASES = [
     (6, 8, 2, 1, 3000, 128, [3000, 0, 1, 33, 2999, 70], True, 0),   # skewed mix: ranges cross sequences
     (4, 8, 4, 2, 900, 64, [900, 5, 0, 64], True, 13),  # 13 ranges over 969 keys, two new rows
     (3, 4, 2, 1, 50, 128, [50, 1, 2], False, 64),      # more ranges than keys: some ranges empty
+    (5, 8, 2, 40, 2000, 64, [2000, 0, 41, 1500, 7], True, 0),   # 160 rows per group (4 waves); empty and short caches
+    (3, 16, 2, 40, 1200, 128, [1200, 300, 77], True, 13),       # 320 rows per group (8 waves); ranges cross sequences
 ]
 
 
@@ -76,3 +78,21 @@ def test_cache_workload_matches_oracle(name):
     if w.Nq > 1:   # prefill: check the first two sequences in full
         q, k, v, lens = q[:2], k[:2], v[:2], lens[:2]
     run_case(q, k, v, lens, True, w.d ** -0.5, 0)
+
+
+@pytest.mark.slow
+def test_prefill16k_full_call_sampled_sequences():
+    # the whole workload in one call, as bench.py times it; two of its
+    # sequences (the shortest and the last) checked in full against the oracle
+    w = CACHE_WORKLOADS["prefill16k"]
+    q, k, v, lens = draw_cache_workload(w)
+    qd, kd, vd, ld = (t.to(DEV) for t in (q, k, v, lens))
+    o, lse = mi.fwd_kvcache(qd, kd, vd, ld, True, w.d ** -0.5, 0)
+    torch.cuda.synchronize()
+    for b in (1, 3):
+        sl = slice(b, b + 1)
+        ro, rl = oracle.forward_kvcache(as_f64(q[sl]), as_f64(k[sl]), as_f64(v[sl]), [int(lens[b])],
+                                        True, w.d ** -0.5)
+        check_bf16("o[b=%d]" % b, f64(o[sl]), ro)
+        check_abs("lse[b=%d]" % b, f64(lse[sl]), rl, BF16_LSE_ABS)
+        print("sequence", b, "length", int(lens[b]), "ok", flush=True)
