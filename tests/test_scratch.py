@@ -81,3 +81,36 @@ def test_release_without_a_buffer_and_calls_after_release():
     torch.cuda.synchronize()
     assert all(torch.equal(x, y) for x, y in zip(a, b))
     mi.release_scratch()
+
+
+def test_graph_replays_match_eager_and_survive_buffer_growth():
+    # Captured calls take stream-ordered allocations that the graph owns, so
+    # a later eager call that grows (and frees) the kept buffer cannot pull
+    # memory out from under a replay. Every replay is checked against the
+    # eager result, with eager work and synchronisations in between.
+    c = calls()
+    eager = {name: fresh(c[name]) for name in ("decode", "bwd")}
+    mi.release_scratch()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm-up on the capture's stream, outside the capture
+        c["decode"](); c["bwd"]()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dec = c["decode"]()
+        bw = c["bwd"]()
+    for rep in range(4):
+        c["prefill"]()                     # eager: grows this stream's kept buffer
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(dec, eager["decode"]):
+            assert torch.equal(a, b), "decode, replay %d" % rep
+        for a, b in zip(bw, eager["bwd"]):
+            assert torch.equal(a, b), "bwd, replay %d" % rep
+        print("replay", rep, "ok", flush=True)
+    mi.release_scratch()
+    mi.release_scratch(side)
+    torch.cuda.synchronize()
