@@ -26,7 +26,11 @@
 //  * bwd_dq: one workgroup per query tile of one (b, h), the forward's
 //    structure: S^T = K Q^T and dP^T = V dO^T from row-major K and V tiles,
 //    then dQ^T += K^T dS^T with K^T read from the same K tile by
-//    transposing LDS reads.
+//    transposing LDS reads. It uses the 16x16x32 product shape, which
+//    sustains more FLOP/s at the chip's power limit; its softmax work per
+//    product is low enough for the shape's fewer free VALU issue slots, and
+//    each wave's two 16-row query blocks share every K/V fragment, so LDS
+//    bytes per FLOP match the 32x32 shape's.
 #include "common.h"
 #include "kernels.h"
 #include "mfma_common.h"
@@ -481,10 +485,11 @@ void bwd_dkdv_kernel(Params p) {
 
 constexpr int DQ_BC = 64;   // keys per tile
 
-// K and V tiles (64 keys), row-major in the padded, chunk-swizzled layout of
-// DkdvSmem: the sigma32-ordered row reads of S^T = K Q^T and dP^T = V dO^T
-// and the transposing reads of K^T for dQ^T = K^T dS^T are conflict-free,
-// and both tiles are written by direct global -> LDS loads.
+// K and V tiles (64 keys), row-major; rows padded to D + 32 elements with
+// the low two bits of the 16-byte chunk index XORed by swz16(row), so that
+// the pi16-ordered row reads of S^T = K Q^T and dP^T = V dO^T and the
+// transposing reads of K^T for dQ^T = K^T dS^T are conflict-free. Both tiles
+// are written by direct global -> LDS loads.
 template <int D>
 struct DqSmem {
   static constexpr int ROW = D + 32;
@@ -497,7 +502,8 @@ template <int D, bool CAUSAL, int NW, bool WIN = false, bool SPARSE = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void bwd_dq_kernel(Params p) {
   constexpr int BR = NW * 32;
-  constexpr int KS = D / 16, DB = D / 32;
+  constexpr int KS = D / 32;          // 32-wide k-steps of S^T = K Q^T and dP^T = V dO^T
+  constexpr int DM = D / 16;          // 16-row blocks of dQ^T
   constexpr int ROW = DqSmem<D>::ROW, TILE = DqSmem<D>::TILE;
   constexpr int TILES_KB = 2 * TILE * 2 / 1024;     // K and V, in 1 KB direct loads
   static_assert(TILES_KB % NW == 0, "tile loads split evenly over the waves");
@@ -508,7 +514,7 @@ void bwd_dq_kernel(Params p) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
   const int lane = tid & 63;
-  const int g = lane >> 5, n = lane & 31;
+  const int q4 = lane >> 4, i16 = lane & 15;
   const int ntq = gridDim.y;
   const int qt = CAUSAL ? (ntq - 1 - (int)blockIdx.y) : (int)blockIdx.y;
   const int h = xcd_head(blockIdx.x, p.H);
@@ -531,25 +537,31 @@ void bwd_dq_kernel(Params p) {
   float qsign = p.scale < 0.f ? -1.f : 1.f;
   if (p.scale == 0.f) { c = 1.f; qsign = 0.f; }
 
-  // Q and dO as B operands of S^T = K Q^T and dP^T = V dO^T: lane (g, n) holds row wq0+n, columns 16ks+8g..
-  const int row = wq0 + n;
-  const int rc = min(row, p.Nq - 1);
-  bf16x8 qf[KS], of[KS];
+  // Q and dO as B operands of S^T = K Q^T and dP^T = V dO^T: lane (q4, i16)
+  // holds row wq0 + 16 nb + i16 (query block nb), columns 32 ks + 8 q4 ..
+  bf16x8 qf[2][KS], of[2][KS];
+  float lse2[2], dsum[2];
+  int qpos[2];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    bf16x8 x = *(const bf16x8*)(Q + rc * qrs + ks * 16 + g * 8);
-    if (qsign != 1.f) {
+  for (int nb = 0; nb < 2; ++nb) {
+    const int r_ = wq0 + 16 * nb + i16;
+    const int rc = min(r_, p.Nq - 1);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = (bf16)((float)x[e] * qsign);
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 x = *(const bf16x8*)(Q + rc * qrs + ks * 32 + q4 * 8);
+      if (qsign != 1.f) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (bf16)((float)x[e] * qsign);
+      }
+      qf[nb][ks] = x;
+      of[nb][ks] = *(const bf16x8*)(dO + rc * qrs + ks * 32 + q4 * 8);
     }
-    qf[ks] = x;
-    of[ks] = *(const bf16x8*)(dO + rc * qrs + ks * 16 + g * 8);
+    const long long si = ((long long)b * p.H + h) * p.N + p.q_start + rc;
+    lse2[nb] = p.lse[si] * kLog2e;
+    dsum[nb] = p.dsum[si];
+    qpos[nb] = p.q_start + r_;
   }
-  const long long si = ((long long)b * p.H + h) * p.N + p.q_start + rc;
-  const float lse2 = p.lse[si] * kLog2e;
-  const float dsum = p.dsum[si];
   wait_global_loads();
-  const int qpos = p.q_start + row;
 
   int nkt = (p.Nk + DQ_BC - 1) / DQ_BC;
   if (CAUSAL) {
@@ -561,14 +573,15 @@ void bwd_dq_kernel(Params p) {
 
   // Direct loads: 1 KB piece s = wave*NL + i of the two tiles (K: s < TILE_KB,
   // then V) covers tile bytes [(s % TILE_KB) KB, +1 KB); lane l fills 16 bytes
-  // at 16 l: tile row r, logical chunk ch (padding from chunk 0), read from
-  // byte loff[i] = 2 (r * row stride + 8 ch) past the tile's first key.
+  // at 16 l: tile row r, physical chunk pch holding logical chunk
+  // pch ^ swz16(r) (padding chunks from chunk 0), read from byte
+  // loff[i] = 2 (r * row stride + 8 * logical chunk) past the tile's first key.
   uint32_t loff[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int off = ((wave * NL + i) % TILE_KB) * 1024 + 16 * lane;
     const int r_ = off / (ROW * 2), pch = (off % (ROW * 2)) / 16;
-    const int col = pch < D / 8 ? ((pch ^ ((r_ >> 2) & 3)) << 3) : 0;
+    const int col = pch < D / 8 ? ((pch ^ swz16(r_)) << 3) : 0;
     loff[i] = (uint32_t)(r_ * krs + col) * 2u;
   }
   // keys past the last one read as zeros (buffer range check); the mask drops them
@@ -581,28 +594,27 @@ void bwd_dq_kernel(Params p) {
                             lds_addr((is_v ? sm.v[buf] : sm.k[buf]) + (sl % TILE_KB) * 512));
   };
 
-  // per-lane LDS read bases (elements): K / V rows sigma32(n) (+32 kb), logical
-  // chunk 2 ks + g -> base for ks parity e; K^T transposing reads: lane j of
-  // 16-lane group (g, hf) addresses key row 16t + 8g + 4rd + j/4, columns
-  // 32db + 16hf + 4(j%4).
-  const int srow = sigma32(n), sf = (srow >> 2) & 3;
-  int rd_s[2];
+  // per-lane LDS read offsets (elements). K / V fragment (key block mb,
+  // k-step ks): row pi16(mb, i16), logical chunk 4 ks + q4 -> physical
+  // 4 ks + (q4 ^ swz16(row)) (swz16 does not depend on mb). K^T fragment
+  // (d block md, key chunk kc), read rd: lane j of 16-lane group q4
+  // addresses key row 32 kc + 8 q4 + 4 rd + j/4, columns 16 md + 4 (j%4);
+  // the swizzle touches bit 0 of md, hence one offset per md parity.
+  const int krow0 = pi16(0, i16);
+  const int rd_k = krow0 * ROW + 8 * (q4 ^ swz16(krow0));
+  int rd_t[2][2];
 #pragma unroll
-  for (int e = 0; e < 2; ++e) rd_s[e] = srow * ROW + (((2 * e + g) ^ sf) << 3);
-  int rd_t[2];
-  {
-    const int G4 = lane >> 4, j = lane & 15, hf = G4 & 1;
+  for (int mp = 0; mp < 2; ++mp)
 #pragma unroll
     for (int rd = 0; rd < 2; ++rd) {
-      const int r_ = 8 * g + 4 * rd + (j >> 2);
-      const int chunk = (2 * hf + ((j & 3) >> 1)) ^ ((2 * g + rd) & 3);
-      rd_t[rd] = r_ * ROW + (chunk << 3) + 4 * (j & 1);
+      const int r_ = 8 * q4 + 4 * rd + (i16 >> 2);
+      const int lc = 2 * mp + ((i16 & 3) >> 1);
+      rd_t[mp][rd] = r_ * ROW + 8 * (lc ^ swz16(r_)) + 4 * (i16 & 1);
     }
-  }
 
-  f32x16 acc[DB];
+  f32x4 acc[DM][2];   // dQ^T: [16-row d block][query block]
 #pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  for (int md = 0; md < DM; ++md) acc[md][0] = acc[md][1] = f32x4{};
 
   // sliding window (causal): key tiles wholly before the window of the
   // workgroup's first row are skipped too
@@ -629,15 +641,16 @@ void bwd_dq_kernel(Params p) {
   }
   __syncthreads();
 
-  // Lock steps per key tile (PS = 2 KS products per key block, PD = 2 DB per 16 keys):
+  // Lock steps per key tile (PS = 2 KS steps per 32-key chunk, PD = DM per chunk;
+  // every step is one K/V or K^T fragment and its two products, one per query block):
   //   phase 0 (PS steps): S^T, dP^T of keys 0-31    + direct loads of the next tile
   //   phase 1 (PS steps): S^T, dP^T of keys 32-63   + dS of keys 0-31
   //   phase 2 (PD steps): dQ^T over keys 0-31       + dS of keys 32-63
   //   phase 3 (PD steps): dQ^T over keys 32-63
   // Key tiles before nplain lie entirely below the causal diagonal of every
   // row of the workgroup and before the ragged end: they run a body without
-  // the mask test; the rest (at most 5 tiles) run the masked body.
-  constexpr int PS = 2 * KS, PD = 2 * DB;
+  // the mask test; the rest run the masked body.
+  constexpr int PS = 2 * KS * 2, PD = DM;   // (2 key blocks of 16) x KS x (S, dP)
   int nplain = min(nkt, p.Nk / DQ_BC);
   if (CAUSAL) nplain = min(nplain, max(0, p.q_start + q0 - p.k_start + 1) / DQ_BC);
   // key tile j from LDS buffer buf, while tile jnext is loaded into the other one
@@ -645,76 +658,91 @@ void bwd_dq_kernel(Params p) {
     constexpr bool MASKED = decltype(mc)::value;
     const int kpos0 = p.k_start + j * DQ_BC;
     const int jn = jnext * DQ_BC;
-    // masked iff key index inside the tile > thr (causal and the ragged end)
-    int thr = p.Nk - 1 - j * DQ_BC;
-    if (CAUSAL && kpos0 + DQ_BC - 1 > wq_first) thr = min(thr, qpos - kpos0);
-    int lo = 0;   // sliding window: key index inside the tile < lo is before the row's window
-    if constexpr (WIN) lo = qpos - (p.window - 1) - kpos0;
+    // masked iff key index inside the tile > thr (causal and the ragged end),
+    // or < lo under a sliding window (before the row's window)
+    int thr[2], lo[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      thr[nb] = p.Nk - 1 - j * DQ_BC;
+      if (CAUSAL && kpos0 + DQ_BC - 1 > wq_first) thr[nb] = min(thr[nb], qpos[nb] - kpos0);
+      lo[nb] = 0;
+      if constexpr (WIN) lo[nb] = qpos[nb] - (p.window - 1) - kpos0;
+    }
     const bf16* kt = sm.k[buf];
     const bf16* vt = sm.v[buf];
-    f32x16 s[2], dp[2];
-    s[0] = f32x16{}; dp[0] = f32x16{}; s[1] = f32x16{}; dp[1] = f32x16{};
-    bf16x8 dsb[4];
+    f32x4 s[4][2], dp[4][2];   // [key block mb][query block nb]
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) s[mb][0] = s[mb][1] = dp[mb][0] = dp[mb][1] = f32x4{};
+    bf16x8 dsb[2][2];          // dS^T as the B operand: [key chunk kc][query block nb]
 
-    // dS for elements 2w, 2w+1 (w = 0..7) of key block kb: lane (g, query n),
-    // register r <-> key 32 kb + sigma_row(g, r)
-    auto ds_sub = [&](auto kbc, auto wc) {
-      constexpr int kb = decltype(kbc)::value, w = decltype(wc)::value;
+    // dS for key chunk kc, slice w of 8 (query block w / 4, register pair
+    // 2 (w % 4)): register r of key block mb holds key 32 (mb/2) + 8 q4 +
+    // 4 (mb%2) + r, i.e. element 4 (mb%2) + r of the chunk's B operand
+    auto ds_sub = [&](auto kcc, auto wc) {
+      constexpr int kc = decltype(kcc)::value, w = decltype(wc)::value;
+      constexpr int nb = w / 4, e0 = 2 * (w % 4);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int r = 2 * w + u;
-        const float x = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -lse2));
+        const int e = e0 + u, mb = 2 * kc + (e >> 2), r = e & 3;
+        const float x = __builtin_amdgcn_exp2f(fmaf(s[mb][nb][r], c, -lse2[nb]));
         float pv = x;
         if constexpr (MASKED) {
-          const int kin = kb * 32 + ((r < 8) ? (g * 8 + r) : (16 + g * 8 + r - 8));
-          pv = (kin > thr || (WIN && kin < lo)) ? 0.f : x;
+          const int kin = 32 * kc + 8 * q4 + e;
+          pv = (kin > thr[nb] || (WIN && kin < lo[nb])) ? 0.f : x;
         }
-        dsb[kb * 2 + (r >> 3)][r & 7] = (bf16)(pv * (dp[kb][r] - dsum));
+        dsb[kc][nb][e] = (bf16)(pv * (dp[mb][nb][r] - dsum[nb]));
       }
     };
 
     lockstep_products<2 * PS + 2 * PD, 4>(
         [&](auto ic) {
           constexpr int i = decltype(ic)::value;
-          if constexpr (i < 2 * PS) {            // S^T / dP^T: (kb, ks, which)
-            constexpr int kb = i / PS, jj = i % PS, ks = jj >> 1;
-            const bf16* t = (jj & 1) ? vt : kt;
-            return lds_read16(t + rd_s[ks & 1], kb * 32 * ROW + (ks >> 1) * 32);
-          } else {                                // dQ^T: (t, db) with t = key block of 16
-            constexpr int ii = i - 2 * PS, t = ii / DB, db = ii % DB;
-            const bf16x4 r0 = lds_read_tr4(kt + rd_t[0] + 16 * t * ROW + 32 * db);
-            const bf16x4 r1 = lds_read_tr4(kt + rd_t[1] + 16 * t * ROW + 32 * db);
+          if constexpr (i < 2 * PS) {            // S^T / dP^T: (mb, ks, which)
+            constexpr int mb = i / (2 * KS), jj = i % (2 * KS), ks = jj >> 1;
+            constexpr int moff = (32 * (mb >> 1) + 4 * (mb & 1)) * ROW + 32 * ks;
+            return lds_read16((jj & 1) ? vt : kt, rd_k + moff);
+          } else {                                // dQ^T: (kc, md)
+            constexpr int ii = i - 2 * PS, kc = ii / DM, md = ii % DM;
+            constexpr int off = 32 * kc * ROW + 32 * (md >> 1);
+            const bf16x4 r0 = lds_read_tr4(kt + rd_t[md & 1][0] + off);
+            const bf16x4 r1 = lds_read_tr4(kt + rd_t[md & 1][1] + off);
             return bf16x8{r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
           }
         },
         [&](auto ic, bf16x8 a) {
           constexpr int i = decltype(ic)::value;
           if constexpr (i < 2 * PS) {
-            constexpr int kb = i / PS, jj = i % PS, ks = jj >> 1;
-            if constexpr (jj & 1) dp[kb] = mfma32(a, of[ks], dp[kb]);
-            else s[kb] = mfma32(a, qf[ks], s[kb]);
+            constexpr int mb = i / (2 * KS), jj = i % (2 * KS), ks = jj >> 1;
+            if constexpr (jj & 1) {
+              dp[mb][0] = mfma16(a, of[0][ks], dp[mb][0]);
+              dp[mb][1] = mfma16(a, of[1][ks], dp[mb][1]);
+            } else {
+              s[mb][0] = mfma16(a, qf[0][ks], s[mb][0]);
+              s[mb][1] = mfma16(a, qf[1][ks], s[mb][1]);
+            }
           } else {
-            constexpr int ii = i - 2 * PS, t = ii / DB, db = ii % DB;
-            acc[db] = mfma32(a, dsb[t], acc[db]);
+            constexpr int ii = i - 2 * PS, kc = ii / DM, md = ii % DM;
+            acc[md][0] = mfma16(a, dsb[kc][0], acc[md][0]);
+            acc[md][1] = mfma16(a, dsb[kc][1], acc[md][1]);
           }
         },
         [&](auto ic) {
           constexpr int i = decltype(ic)::value;
           if constexpr (i < PS) {                 // phase 0: next tile's direct loads
-            constexpr int lo = i * NL / PS, hi = (i + 1) * NL / PS;
+            constexpr int lo_ = i * NL / PS, hi_ = (i + 1) * NL / PS;
             [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
-              (load_piece(lo + Ws, buf ^ 1, jn), ...);
-            }(std::make_integer_sequence<int, hi - lo>{});
-          } else if constexpr (i < 2 * PS) {      // phase 1: dS of key block 0
-            constexpr int ii = i - PS, lo = ii * 8 / PS, hi = (ii + 1) * 8 / PS;
+              (load_piece(lo_ + Ws, buf ^ 1, jn), ...);
+            }(std::make_integer_sequence<int, hi_ - lo_>{});
+          } else if constexpr (i < 2 * PS) {      // phase 1: dS of key chunk 0
+            constexpr int ii = i - PS, lo_ = ii * 8 / PS, hi_ = (ii + 1) * 8 / PS;
             [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
-              (ds_sub(std::integral_constant<int, 0>{}, std::integral_constant<int, lo + Ws>{}), ...);
-            }(std::make_integer_sequence<int, hi - lo>{});
-          } else if constexpr (i < 2 * PS + PD) { // phase 2: dS of key block 1
-            constexpr int ii = i - 2 * PS, lo = ii * 8 / PD, hi = (ii + 1) * 8 / PD;
+              (ds_sub(std::integral_constant<int, 0>{}, std::integral_constant<int, lo_ + Ws>{}), ...);
+            }(std::make_integer_sequence<int, hi_ - lo_>{});
+          } else if constexpr (i < 2 * PS + PD) { // phase 2: dS of key chunk 1
+            constexpr int ii = i - 2 * PS, lo_ = ii * 8 / PD, hi_ = (ii + 1) * 8 / PD;
             [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
-              (ds_sub(std::integral_constant<int, 1>{}, std::integral_constant<int, lo + Ws>{}), ...);
-            }(std::make_integer_sequence<int, hi - lo>{});
+              (ds_sub(std::integral_constant<int, 1>{}, std::integral_constant<int, lo_ + Ws>{}), ...);
+            }(std::make_integer_sequence<int, hi_ - lo_>{});
           }
         });
     wait_global_loads();
@@ -743,35 +771,36 @@ void bwd_dq_kernel(Params p) {
     // workgroup: masked prefix [jt0, a), plain [a, b), masked [b, nkt)
     const int jlow = max(0, (p.q_start + q0 + BR - p.window - p.k_start + DQ_BC - 1) / DQ_BC);
     const int a = min(max(jlow, jt0), nkt);
-    const int b = max(a, min(nplain, nkt));
+    const int b_ = max(a, min(nplain, nkt));
     for (int j = jt0; j < a; ++j) tile(std::true_type{}, j, j & 1, next(j));
-    for (int j = a; j < b; ++j) tile(std::false_type{}, j, j & 1, next(j));
-    for (int j = b; j < nkt; ++j) tile(std::true_type{}, j, j & 1, next(j));
+    for (int j = a; j < b_; ++j) tile(std::false_type{}, j, j & 1, next(j));
+    for (int j = b_; j < nkt; ++j) tile(std::true_type{}, j, j & 1, next(j));
   } else {
     for (int j = 0; j < nplain; ++j) tile(std::false_type{}, j, j & 1, next(j));
     for (int j = nplain; j < nkt; ++j) tile(std::true_type{}, j, j & 1, next(j));
   }
 
-  // ---- store dQ = scale * acc^T: lane (g, query n), register r <-> column 32 db + 8 (r/4) + 4g + r%4
-  if (row < p.Nq) {
-    const long long off = (((long long)b * p.N + p.q_start + row) * p.H + h) * D;
+  // ---- store dQ = scale * acc^T: lane (q4, i16), register r of block (md, nb)
+  // <-> row wq0 + 16 nb + i16, column 16 md + 4 q4 + r
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+  for (int nb = 0; nb < 2; ++nb) {
+    const int r_ = wq0 + 16 * nb + i16;
+    if (r_ >= p.Nq) continue;
+    const long long off = (((long long)b * p.N + p.q_start + r_) * p.H + h) * D;
 #pragma unroll
-      for (int run = 0; run < 4; ++run) {
-        const int col = db * 32 + run * 8 + g * 4;
-        if (p.accumulate) {
-          f32x4* a = (f32x4*)((float*)p.dq + off + col);
-          f32x4 x = *a;
+    for (int md = 0; md < DM; ++md) {
+      const int col = 16 * md + 4 * q4;
+      if (p.accumulate) {
+        f32x4* a = (f32x4*)((float*)p.dq + off + col);
+        f32x4 x = *a;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] += acc[db][run * 4 + e] * p.scale;
-          *a = x;
-        } else {
-          bf16x4 x;
+        for (int e = 0; e < 4; ++e) x[e] += acc[md][nb][e] * p.scale;
+        *a = x;
+      } else {
+        bf16x4 x;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = (bf16)(acc[db][run * 4 + e] * p.scale);
-          *(bf16x4*)((bf16*)p.dq + off + col) = x;
-        }
+        for (int e = 0; e < 4; ++e) x[e] = (bf16)(acc[md][nb][e] * p.scale);
+        *(bf16x4*)((bf16*)p.dq + off + col) = x;
       }
     }
   }
