@@ -358,27 +358,34 @@ void fwd_split_kernel(SplitParams p) {
 }
 
 // acc[c] += sum over t < n of weight_t * row_t[lane + 64 c], with weight_t
-// held by lane t of w_l and row_t = src(t). Eight rows' loads are in flight
-// at a time; indices past n repeat the last row, and a zero weight (past n,
-// or a partial that no workgroup wrote) selects nothing rather than
+// held by lane t of w_l and row_t = src(t). U rows' loads are in flight at
+// a time; indices past n repeat the last row, and a zero weight (past n, or
+// a partial that no workgroup wrote) selects nothing rather than
 // multiplying whatever the row holds.
-template <int CPL, class SRC>
-__device__ __forceinline__ void accumulate_partials(float (&acc)[CPL], float w_l, int n, int lane, SRC src) {
-  for (int t = 0; t < n; t += 8) {
-    float x[8][CPL];
+template <int U, int CPL, class SRC>
+__device__ __forceinline__ void accumulate_batches(float (&acc)[CPL], float w_l, int n, int lane, SRC src) {
+  for (int t = 0; t < n; t += U) {
+    float x[U][CPL];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < U; ++u) {
       const float* r = src(min(t + u, n - 1)) + lane;
 #pragma unroll
       for (int c = 0; c < CPL; ++c) x[u][c] = r[64 * c];
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < U; ++u) {
       const float wt = t + u < n ? __shfl(w_l, t + u) : 0.f;
 #pragma unroll
       for (int c = 0; c < CPL; ++c) acc[c] += wt != 0.f ? wt * x[u][c] : 0.f;
     }
   }
+}
+// (rows with at most four partials, as in chunked prefill, take batches of
+// four: eight would double their loads with repeats)
+template <int CPL, class SRC>
+__device__ __forceinline__ void accumulate_partials(float (&acc)[CPL], float w_l, int n, int lane, SRC src) {
+  if (n <= 4) accumulate_batches<4>(acc, w_l, n, lane, src);
+  else accumulate_batches<8>(acc, w_l, n, lane, src);
 }
 
 // Merge of the splits of every (b, query, head) row: with M the largest
