@@ -39,8 +39,6 @@ namespace miattn {
 
 namespace {
 
-constexpr int PAD = LDS_PAD;
-
 // ============================================================ dK, dV
 
 constexpr int DKV_NW = 4;            // waves per workgroup
@@ -223,7 +221,6 @@ void bwd_dkdv_kernel(Params p) {
   // (zero rows, LSE = +inf) drains the pipeline. Each phase prefetches the
   // LSE / D values the next phase's softmax group needs.
   constexpr int PL = D / 8;          // lock steps per phase
-  const int ntiles = niter + 1;      // plus the draining tile
   const int empty_q0 = nqt * DKV_BQ; // rows past the end: zeros, LSE = +inf
 
   // buffer 2 = tile -1: zero Q / dO, LSE = +inf, D = 0
