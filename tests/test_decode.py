@@ -42,6 +42,8 @@ CASES = [
     (6, 8, 2, 1, 3000, 128, [3000, 0, 1, 33, 2999, 70], True, 0),   # skewed mix: ranges cross sequences
     (4, 8, 4, 2, 900, 64, [900, 5, 0, 64], True, 13),  # 13 ranges over 969 keys, two new rows
     (3, 4, 2, 1, 50, 128, [50, 1, 2], False, 64),      # more ranges than keys: some ranges empty
+    (150, 4, 2, 1, 300, 64, "drawn", True, 0),        # 150 sequences, lengths 0..300: the length scans take three 64-wide steps
+    (2, 8, 2, 1, 4000, 128, [4000, 10], False, 200),   # a sequence spanning about 200 ranges: merges past 64
     (5, 8, 2, 40, 2000, 64, [2000, 0, 41, 1500, 7], True, 0),   # 160 rows per group (4 waves); empty and short caches
     (3, 16, 2, 40, 1200, 128, [1200, 300, 77], True, 13),       # 320 rows per group (8 waves); ranges cross sequences
 ]
@@ -50,8 +52,9 @@ CASES = [
 @pytest.mark.parametrize("case", CASES, ids=[str(i) for i in range(len(CASES))])
 def test_kvcache_matches_oracle(case):
     B, H, Hkv, Nq, Nk, d, lens, causal, nsplit = case
-    q, k, v, _ = draw_cache(B, H, Hkv, Nq, Nk, d, seed=100 + len(str(case)) + Nk)
-    lt = None if lens is None else torch.tensor(lens, dtype=torch.int32)
+    q, k, v, drawn = draw_cache(B, H, Hkv, Nq, Nk, d, seed=100 + len(str(case)) + Nk,
+                                min_len=0 if lens == "drawn" else None)
+    lt = drawn if lens == "drawn" else (None if lens is None else torch.tensor(lens, dtype=torch.int32))
     run_case(q, k, v, lt, causal, d ** -0.5, nsplit)
 
 
