@@ -483,10 +483,8 @@ void bwd_dkdv_kernel(Params p) {
 constexpr int DQ_BC = 64;   // keys per tile
 
 // K and V tiles (64 keys), row-major; rows padded to D + 32 elements with
-// the low two bits of the 16-byte chunk index XORed by swz16(row), so that
-// the pi16-ordered row reads of S^T = K Q^T and dP^T = V dO^T and the
-// transposing reads of K^T for dQ^T = K^T dS^T are conflict-free. Both tiles
-// are written by direct global -> LDS loads.
+// the low two bits of the 16-byte chunk index XORed by swz_s4(row) (below).
+// Both tiles are written by direct global -> LDS loads.
 template <int D>
 struct DqSmem {
   static constexpr int ROW = D + 32;
@@ -494,6 +492,17 @@ struct DqSmem {
   bf16 k[2][TILE];
   bf16 v[2][TILE];
 };
+
+// Stride-4 key order of the dQ kernel's tiles: A-operand row i = 4q + r of
+// 16-key block mb is tile row q + 4 r + 16 (mb % 2) (+ 32 per 32-key chunk),
+// so the accumulators of blocks 2c and 2c + 1 give lane group q the keys
+// 32 c + q + 4 e, e = 0..7, in register order; the K^T operand of the dQ
+// product is read with the same key order. With the chunk swizzle
+// (row / 4) % 4 the row reads of S^T = K Q^T and dP^T = V dO^T have no bank
+// conflicts and the transposing reads of K^T have half as many as the row
+// reads of a key order with 8 consecutive keys per lane group (measured
+// with the SQ_LDS_BANK_CONFLICT counter on the device).
+__device__ __forceinline__ int swz_s4(int row) { return (row >> 2) & 3; }
 
 template <int D, bool CAUSAL, int NW, bool WIN = false, bool SPARSE = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
@@ -571,14 +580,14 @@ void bwd_dq_kernel(Params p) {
   // Direct loads: 1 KB piece s = wave*NL + i of the two tiles (K: s < TILE_KB,
   // then V) covers tile bytes [(s % TILE_KB) KB, +1 KB); lane l fills 16 bytes
   // at 16 l: tile row r, physical chunk pch holding logical chunk
-  // pch ^ swz16(r) (padding chunks from chunk 0), read from byte
+  // pch ^ swz_s4(r) (padding chunks from chunk 0), read from byte
   // loff[i] = 2 (r * row stride + 8 * logical chunk) past the tile's first key.
   uint32_t loff[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int off = ((wave * NL + i) % TILE_KB) * 1024 + 16 * lane;
     const int r_ = off / (ROW * 2), pch = (off % (ROW * 2)) / 16;
-    const int col = pch < D / 8 ? ((pch ^ swz16(r_)) << 3) : 0;
+    const int col = pch < D / 8 ? ((pch ^ swz_s4(r_)) << 3) : 0;
     loff[i] = (uint32_t)(r_ * krs + col) * 2u;
   }
   // keys past the last one read as zeros (buffer range check); the mask drops them
@@ -592,21 +601,23 @@ void bwd_dq_kernel(Params p) {
   };
 
   // per-lane LDS read offsets (elements). K / V fragment (key block mb,
-  // k-step ks): row pi16(mb, i16), logical chunk 4 ks + q4 -> physical
-  // 4 ks + (q4 ^ swz16(row)) (swz16 does not depend on mb). K^T fragment
-  // (d block md, key chunk kc), read rd: lane j of 16-lane group q4
-  // addresses key row 32 kc + 8 q4 + 4 rd + j/4, columns 16 md + 4 (j%4);
-  // the swizzle touches bit 0 of md, hence one offset per md parity.
-  const int krow0 = pi16(0, i16);
-  const int rd_k = krow0 * ROW + 8 * (q4 ^ swz16(krow0));
+  // k-step ks): row i16 / 4 + 4 (i16 % 4) + 16 (mb % 2) + 32 (mb / 2),
+  // logical chunk 4 ks + q4 -> physical 4 ks + (q4 ^ swz_s4(row)) (swz_s4
+  // depends on neither mb nor the 32-key chunk). K^T fragment (d block md,
+  // key chunk kc), read rd: lane j of 16-lane group q4 addresses key row
+  // 32 kc + q4 + 16 rd + 4 (j/4), columns 16 md + 4 (j%4); element 4 rd + t
+  // of the result is key 32 kc + q4 + 4 (4 rd + t), the order of dS^T. The
+  // swizzle touches bit 0 of md, hence one offset per md parity.
+  const int krow0 = (i16 >> 2) + 4 * (i16 & 3);
+  const int rd_k = krow0 * ROW + 8 * (q4 ^ swz_s4(krow0));
   int rd_t[2][2];
 #pragma unroll
   for (int mp = 0; mp < 2; ++mp)
 #pragma unroll
     for (int rd = 0; rd < 2; ++rd) {
-      const int r_ = 8 * q4 + 4 * rd + (i16 >> 2);
+      const int r_ = q4 + 16 * rd + 4 * (i16 >> 2);
       const int lc = 2 * mp + ((i16 & 3) >> 1);
-      rd_t[mp][rd] = r_ * ROW + 8 * (lc ^ swz16(r_)) + 4 * (i16 & 1);
+      rd_t[mp][rd] = r_ * ROW + 8 * (lc ^ swz_s4(r_)) + 4 * (i16 & 1);
     }
 
   f32x4 acc[DM][2];   // dQ^T: [16-row d block][query block]
@@ -673,8 +684,8 @@ void bwd_dq_kernel(Params p) {
     bf16x8 dsb[2][2];          // dS^T as the B operand: [key chunk kc][query block nb]
 
     // dS for key chunk kc, slice w of 8 (query block w / 4, register pair
-    // 2 (w % 4)): register r of key block mb holds key 32 (mb/2) + 8 q4 +
-    // 4 (mb%2) + r, i.e. element 4 (mb%2) + r of the chunk's B operand
+    // 2 (w % 4)): register r of key block mb holds key 32 (mb/2) + q4 +
+    // 4 (4 (mb%2) + r), i.e. element e = 4 (mb%2) + r of the chunk's B operand
     auto ds_sub = [&](auto kcc, auto wc) {
       constexpr int kc = decltype(kcc)::value, w = decltype(wc)::value;
       constexpr int nb = w / 4, e0 = 2 * (w % 4);
@@ -684,7 +695,7 @@ void bwd_dq_kernel(Params p) {
         const float x = __builtin_amdgcn_exp2f(fmaf(s[mb][nb][r], c, -lse2[nb]));
         float pv = x;
         if constexpr (MASKED) {
-          const int kin = 32 * kc + 8 * q4 + e;
+          const int kin = 32 * kc + q4 + 4 * e;
           pv = (kin > thr[nb] || (WIN && kin < lo[nb])) ? 0.f : x;
         }
         dsb[kc][nb][e] = (bf16)(pv * (dp[mb][nb][r] - dsum[nb]));
@@ -696,7 +707,7 @@ void bwd_dq_kernel(Params p) {
           constexpr int i = decltype(ic)::value;
           if constexpr (i < 2 * PS) {            // S^T / dP^T: (mb, ks, which)
             constexpr int mb = i / (2 * KS), jj = i % (2 * KS), ks = jj >> 1;
-            constexpr int moff = (32 * (mb >> 1) + 4 * (mb & 1)) * ROW + 32 * ks;
+            constexpr int moff = (32 * (mb >> 1) + 16 * (mb & 1)) * ROW + 32 * ks;
             return lds_read16((jj & 1) ? vt : kt, rd_k + moff);
           } else {                                // dQ^T: (kc, md)
             constexpr int ii = i - 2 * PS, kc = ii / DM, md = ii % DM;

@@ -91,20 +91,6 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Row of a 64-row tile read as A-operand row i of 16-row block mb, so that
-// the product's accumulator gives lane group q the rows 32 (mb/2) + 8 q +
-// 4 (mb%2) + r: blocks 2c and 2c + 1 together hold rows 32 c + 8 q .. + 7,
-// which is the B-operand layout of a product contracting over those rows.
-__device__ __forceinline__ int pi16(int mb, int i) {
-  return 32 * (mb >> 1) + 8 * (i >> 2) + 4 * (mb & 1) + (i & 3);
-}
-
-// XOR applied to the low two bits of a row's 16-byte chunk index in the LDS
-// tiles of the 16x16x32 kernels (rows padded to D + 32 elements). With it
-// the pi16-ordered ds_read_b128 row reads (16 lanes: rows 8b + c, b, c in
-// 0..3, one chunk) and the transposing ds_read_b64_tr_b16 reads (32 lanes:
-// 8 rows 8q + t, two chunks) both touch every bank once.
-__device__ __forceinline__ int swz16(int row) { return 2 * ((row >> 3) & 1) + ((row >> 4) & 1); }
 
 // Direct global -> LDS load of 16 bytes per lane: the wave writes 1 KB of
 // LDS contiguously, lane l at lds_base + 16 l; lds_base must be the same in
