@@ -243,7 +243,7 @@ def bench_blocksparse(mi, torch, q, k, v, do, w, density=0.25, reps=10):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: libmiattn has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
     import torch
