@@ -568,6 +568,18 @@ int attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float
   int st = check_common(B, H, H, N, d, dtype);
   if (st) return st;
   if ((st = check_ptrs({o_a, lse_a, o_b, lse_b, o, lse}))) return st;
+  // in place means exactly in place: an output may equal an input of its own
+  // kind (each element is read before the same thread writes it) but must not
+  // overlap any input at another offset, nor the other output
+  const long long ob = (long long)B * N * H * d * esize(dtype), lb = (long long)B * H * N * 4;
+  const Range ro = span(o, ob), rl = span(lse, lb);
+  const Range roa = span(o_a, ob), rob = span(o_b, ob), rla = span(lse_a, lb), rlb = span(lse_b, lb);
+  if ((o != o_a && overlap(ro, roa)) || (o != o_b && overlap(ro, rob)) || overlap(ro, rla) || overlap(ro, rlb))
+    return fail(MIATTN_EINVAL, "o must equal o_a or o_b or overlap no input");
+  if ((lse != lse_a && overlap(rl, rla)) || (lse != lse_b && overlap(rl, rlb)) || overlap(rl, roa) ||
+      overlap(rl, rob))
+    return fail(MIATTN_EINVAL, "lse must equal lse_a or lse_b or overlap no input");
+  if (overlap(ro, rl)) return fail(MIATTN_EINVAL, "o and lse must not overlap");
   const int t = dtype == MIATTN_BF16 ? 1 : 0;
   if ((st = launch_status(miattn::launch_merge(o_a, lse_a, o_b, lse_b, o, lse, B, H, N, d, 0, N, t, t, t,
                                                (hipStream_t)stream),

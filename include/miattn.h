@@ -238,7 +238,10 @@ int attn_bwd_timed(const void* q, const void* k, const void* v, const void* o, c
  * Rows where both lse are -inf give o = 0, lse = -inf.
  * o_a, o_b, o: [B, N, H, d] of `dtype`; lse_a, lse_b, lse: [B, H, N] float32.
  * In-place use is allowed: o may equal o_a or o_b, lse may equal lse_a or
- * lse_b (each element is read before it is written by the same thread). */
+ * lse_b (each element is read before it is written by the same thread).
+ * Errors: MIATTN_EINVAL for an output that overlaps an input at any other
+ * offset, overlaps an input of the other kind, or overlaps the other output;
+ * the size, pointer and dtype errors of attn_fwd. */
 int attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
                void* o, float* lse, int B, int H, int N, int d, int dtype, void* stream);
 

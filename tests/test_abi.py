@@ -224,3 +224,21 @@ def test_blocksparse_rejects_bad_arguments():
     assert b"block_mask" in L.attn_last_error()          # dk overlaps the mask
     assert L.attn_bwd_blocksparse(*q, vp(FAKE * 6), 1, 2, 2, 300, 64, 1, float("nan"), None, *g, 1, 0) == 1
     assert mi.block_mask_shape(300) == (2, 3) and mi.block_mask_shape(16384) == (64, 128)
+
+
+def test_merge_refuses_partial_overlap():
+    """o may be o_a or o_b exactly (in place) but may not overlap an input at
+    another offset; lse likewise; o and lse may not overlap each other."""
+    L = mi.lib()
+    B, H, N, d = 1, 2, 8, 64            # o: 2048 bytes (bf16), lse: 64 bytes
+    oa, la, ob, lb, o, l = (FAKE * i for i in range(1, 7))
+    call = lambda o_, l_: L.attn_merge(vp(oa), vp(la), vp(ob), vp(lb), vp(o_), vp(l_), B, H, N, d, 1, None)
+    # (valid combinations would enqueue the merge on these fake addresses, so
+    # only refused ones are called here; in-place merges run in the GPU tests)
+    assert call(oa + 16, l) == 1 and b"o must" in L.attn_last_error()
+    assert call(ob - 1024, l) == 1 and b"o must" in L.attn_last_error()
+    assert call(la - 16, l) == 1 and b"o must" in L.attn_last_error()
+    assert call(o, la + 16) == 1 and b"lse must" in L.attn_last_error()
+    assert call(o, oa + 32) == 1 and b"lse must" in L.attn_last_error()
+    assert call(o, o + 1024) == 1 and b"must not overlap" in L.attn_last_error()
+

@@ -12,8 +12,8 @@ import torch
 import exact_attention_37_amd as mi
 import oracle
 from workloads import WORKLOADS, draw, draw_workload, as_f64
-from tests.helpers import (check_bf16, check_abs, check_rel, f64, default_scale,
-                           BF16_LSE_ABS)
+from tests.helpers import (check_bf16, check_abs, check_rel, check_rows_rel, f64, default_scale,
+                           BF16_ABS, BF16_LSE_ABS, BF16_CAST)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -23,10 +23,25 @@ def to_dev(*ts):
     return [t.to(DEV) for t in ts]
 
 
-def run_fwd_bwd(q, k, v, do, causal, scale):
+def nan_like(t, dtype=None):
+    """A device tensor shaped like t, filled with NaN: an output element the
+    kernels never write keeps its NaN and fails every comparison."""
+    return torch.full(t.shape, float("nan"), dtype=dtype or t.dtype, device=DEV)
+
+
+def run_fwd_bwd(q, k, v, do, causal, scale, accumulate=False):
+    """Forward and backward through the C ABI into NaN-filled outputs
+    (accumulate=True: float32 gradients added onto zeros)."""
     qd, kd, vd, dod = to_dev(q, k, v, do)
-    o, lse = mi.fwd(qd, kd, vd, causal, scale)
-    dq, dk, dv = mi.bwd(qd, kd, vd, o, lse, dod, causal, scale)
+    B, N, H, _ = q.shape
+    o = nan_like(qd)
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=DEV)
+    mi.fwd(qd, kd, vd, causal, scale, out=o, out_lse=lse)
+    if accumulate:
+        dq, dk, dv = (torch.zeros(t.shape, dtype=torch.float32, device=DEV) for t in (qd, kd, vd))
+    else:
+        dq, dk, dv = nan_like(qd), nan_like(kd), nan_like(vd)
+    mi.bwd(qd, kd, vd, o, lse, dod, causal, scale, accumulate=accumulate, dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     return [f64(t) for t in (o, lse, dq, dk, dv)]
 
@@ -49,6 +64,16 @@ def compare_full(gpu, ref, dtype):
         else:
             errs[n] = check_bf16(n, g, r)
     print("errors", {k: "%.3g" % v for k, v in errs.items()}, flush=True)
+    return errs
+
+
+def compare_flat_grads(gpu, ref):
+    """float32 gradients of bf16 inputs (accumulate mode, no output cast) held
+    to the flat max-abs bar of the stated tolerance: the kernels' own
+    computation error, without the rounding of a bf16 output."""
+    errs = {n: check_abs(n + " (fp32 out, flat bar)", g, r, BF16_ABS)
+            for n, g, r in zip(("dq", "dk", "dv"), gpu[2:], ref[2:])}
+    print("fp32-output gradient errors", {k: "%.3g" % v for k, v in errs.items()}, flush=True)
     return errs
 
 
@@ -84,6 +109,32 @@ def test_small_shapes_match_oracle(shape, causal, dtype):
     q, k, v, do = draw(B, H, Hkv, N, d, seed=100 + N, dtype=dtype)
     scale = default_scale(d)
     compare_full(run_fwd_bwd(q, k, v, do, causal, scale), oracle_full(q, k, v, do, causal, scale), dtype)
+
+
+# A negative scale is folded into Q (forward, dQ) or K (dK/dV) and scale 0 is
+# run as Q = 0 with scale 1: every kernel's sign handling is exercised here.
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("scale", [-0.125, 0.0], ids=["neg", "zero"])
+@pytest.mark.parametrize("shape", [(2, 4, 2, 200, 128), (1, 4, 1, 130, 64)], ids=lambda s: "B%dH%dKV%dN%dd%d" % s)
+def test_negative_and_zero_scale_match_oracle(shape, scale, causal, dtype):
+    B, H, Hkv, N, d = shape
+    q, k, v, do = draw(B, H, Hkv, N, d, seed=300 + N, dtype=dtype)
+    compare_full(run_fwd_bwd(q, k, v, do, causal, scale), oracle_full(q, k, v, do, causal, scale), dtype)
+
+
+# Gradients written as float32 (accumulate mode) carry no output cast, so
+# they are held to the flat 2e-2: the shapes include the one whose bf16 dV
+# needs the cast allowance (B2H4KV1N200d128, causal).
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("shape", [(2, 4, 1, 200, 128), (1, 8, 2, 300, 64), (2, 2, 1, 127, 64), (1, 2, 2, 520, 128)],
+                         ids=lambda s: "B%dH%dKV%dN%dd%d" % s)
+def test_float32_gradients_meet_flat_bar(shape, causal):
+    B, H, Hkv, N, d = shape
+    q, k, v, do = draw(B, H, Hkv, N, d, seed=100 + N, dtype=torch.bfloat16)
+    scale = default_scale(d)
+    compare_flat_grads(run_fwd_bwd(q, k, v, do, causal, scale, accumulate=True),
+                       oracle_full(q, k, v, do, causal, scale))
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -129,23 +180,44 @@ def test_workload_matches_oracle_everywhere(name):
     q, k, v, do = draw_workload(w)
     scale = default_scale(w.d)
     causal = w.causal[0]
-    compare_full(run_fwd_bwd(q, k, v, do, causal, scale), oracle_full(q, k, v, do, causal, scale), w.torch_dtype)
+    ref = oracle_full(q, k, v, do, causal, scale)
+    compare_full(run_fwd_bwd(q, k, v, do, causal, scale), ref, w.torch_dtype)
+    # the same gradients as float32 (no output cast), held to the flat bar
+    compare_flat_grads(run_fwd_bwd(q, k, v, do, causal, scale, accumulate=True), ref)
 
 
 # ---------------------------------------------------------------- long context, sampled
 
-def sampled_check(q, k, v, do, o, lse, dq, dk, dv, scale, heads, kv_heads, rows, cols, b=0):
-    """Compare GPU outputs on selected rows with the oracle's row-by-row values."""
+def sampled_check(q, k, v, do, o, lse, dq, dk, dv, scale, heads, kv_heads, rows, cols, b=0, flat_grads=False):
+    """Compare GPU outputs on selected rows with the oracle's row-by-row values.
+    flat_grads: dq/dk/dv are float32 (accumulate mode) and held to the flat bar."""
+    abs_check = (lambda n, g_, r_: check_abs(n, g_, r_, BF16_ABS)) if flat_grads else check_bf16
+    N = q.shape[1]
+    # rows that see at least LONG keys, key rows seen by at least LONG queries:
+    # there the outputs are averages of many terms, small against the
+    # absolute bar, and are also held to the per-row relative bound
+    long_r = np.asarray(rows) + 1 >= LONG
+    long_c = None if cols is None else N - np.asarray(cols) >= LONG
+
+    def grad_check(n, g_, r_, sel):
+        abs_check(n, g_, r_)
+        check_rows_rel(n, g_[sel], r_[sel])
+
     for h in heads:
-        ro, rl = oracle.forward_rows(q, k, v, True, scale, b, h, rows)
-        check_bf16("o[h=%d]" % h, f64(o[b, rows, h]), ro)
-        check_abs("lse[h=%d]" % h, f64(lse[b, h, rows]), rl, BF16_LSE_ABS)
+        if o is not None:
+            ro, rl = oracle.forward_rows(q, k, v, True, scale, b, h, rows)
+            check_bf16("o[h=%d]" % h, f64(o[b, rows, h]), ro)
+            check_rows_rel("o[h=%d]" % h, f64(o[b, rows, h])[long_r], ro[long_r])
+            check_abs("lse[h=%d]" % h, f64(lse[b, h, rows]), rl, BF16_LSE_ABS)
         rq = oracle.backward_dq_rows(q, k, v, do, True, scale, b, h, rows)
-        check_bf16("dq[h=%d]" % h, f64(dq[b, rows, h]), rq)
+        grad_check("dq[h=%d]" % h, f64(dq[b, rows, h]), rq, long_r)
     for g in kv_heads:
         rk, rv = oracle.backward_dkdv_rows(q, k, v, do, True, scale, b, g, cols)
-        check_bf16("dk[g=%d]" % g, f64(dk[b, cols, g]), rk)
-        check_bf16("dv[g=%d]" % g, f64(dv[b, cols, g]), rv)
+        grad_check("dk[g=%d]" % g, f64(dk[b, cols, g]), rk, long_c)
+        grad_check("dv[g=%d]" % g, f64(dv[b, cols, g]), rv, long_c)
+
+
+LONG = 1024
 
 
 def gradient_sum_properties(dk, dv, do, G):
@@ -165,20 +237,71 @@ def gradient_sum_properties(dk, dv, do, G):
     assert torch.all((sv - sdo).abs() <= bound_v), float(((sv - sdo).abs() - bound_v).max())
 
 
+def device_check_bf16(name, got, ref, tol=BF16_ABS):
+    """check_bf16 for two large device tensors (GPU result against GPU result),
+    evaluated in float32 on the device slice by slice: every element within
+    tol + 2^-8 |ref|, and finite."""
+    worst, err = -1.0, 0.0
+    for a, r in zip(got.reshape(-1).split(1 << 26), ref.reshape(-1).split(1 << 26)):
+        a, r = a.float(), r.float()
+        assert bool(torch.isfinite(a).all()), "%s has non-finite values" % name
+        diff = (a - r).abs()
+        err = max(err, float(diff.max()))
+        worst = max(worst, float((diff - (tol + BF16_CAST * r.abs())).max()))
+    assert worst <= 0.0, "%s: max abs err %.4g exceeds %.3g + 2^-8|ref|" % (name, err, tol)
+    return err
+
+
+def device_check_abs(name, got, ref, tol):
+    err = 0.0
+    for a, r in zip(got.reshape(-1).split(1 << 26), ref.reshape(-1).split(1 << 26)):
+        a, r = a.float(), r.float()
+        assert bool(torch.isfinite(a).all()), "%s has non-finite values" % name
+        err = max(err, float((a - r).abs().max()))
+    assert err <= tol, "%s: max abs err %.4g > %.3g" % (name, err, tol)
+    return err
+
+
+# 16K rows sampled at the first rows, both sides of the 64-row tile and
+# 256-row workgroup boundaries, the middle and the end; key rows at both
+# sides of the 128-key workgroup boundaries
+L16_ROWS = np.array([0, 1, 63, 64, 255, 256, 4095, 8191, 8192, 12000, 16127, 16128, 16383])
+L16_COLS = np.array([0, 5, 127, 128, 255, 256, 9000, 16255, 16256, 16382, 16383])
+L16_HEADS = (0, 5, 9, 13, 17, 22, 27, 31)
+L16_KV_HEADS = (0, 11, 17, 31)
+
+
 @pytest.mark.slow
 def test_llama16k_single_pass_sampled():
     w = WORKLOADS["llama16k"]
     q, k, v, do = draw_workload(w)
     scale = default_scale(w.d)
     qd, kd, vd, dod = to_dev(q, k, v, do)
-    o, lse = mi.fwd(qd, kd, vd, True, scale)
-    dq, dk, dv = mi.bwd(qd, kd, vd, o, lse, dod, True, scale)
+    o, lse = nan_like(qd), torch.full((w.B, w.H, w.N), float("nan"), dtype=torch.float32, device=DEV)
+    mi.fwd(qd, kd, vd, True, scale, out=o, out_lse=lse)
+    dq, dk, dv = nan_like(qd), nan_like(kd), nan_like(vd)
+    mi.bwd(qd, kd, vd, o, lse, dod, True, scale, dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
-    rows = np.array([0, 1, 63, 64, 4095, 8191, 12000, w.N - 1])
-    cols = np.array([0, 5, 127, 128, 9000, w.N - 2, w.N - 1])
+    for n, t in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
+        assert bool(torch.isfinite(t).all()), "%s has unwritten (NaN) elements" % n
     qq, kk, vv, dd = (as_f64(t) for t in (q, k, v, do))
-    sampled_check(qq, kk, vv, dd, o, lse, dq, dk, dv, scale, heads=(0, 31), kv_heads=(17,), rows=rows, cols=cols)
+    sampled_check(qq, kk, vv, dd, o, lse, dq, dk, dv, scale, heads=L16_HEADS, kv_heads=L16_KV_HEADS,
+                  rows=L16_ROWS, cols=L16_COLS)
     gradient_sum_properties(dk.cpu(), dv.cpu(), do, w.G)
+
+
+@pytest.mark.slow
+def test_llama16k_float32_gradients_meet_flat_bar():
+    w = WORKLOADS["llama16k"]
+    q, k, v, do = draw_workload(w)
+    scale = default_scale(w.d)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    o, lse = mi.fwd(qd, kd, vd, True, scale)
+    dq, dk, dv = mi.bwd(qd, kd, vd, o, lse, dod, True, scale, accumulate=True)
+    torch.cuda.synchronize()
+    qq, kk, vv, dd = (as_f64(t) for t in (q, k, v, do))
+    sampled_check(qq, kk, vv, dd, None, None, dq, dk, dv, scale, heads=(0, 17, 31), kv_heads=(0, 31),
+                  rows=L16_ROWS, cols=L16_COLS, flat_grads=True)
 
 
 @pytest.mark.slow
@@ -198,22 +321,91 @@ def test_llama16k_chunked_equals_single_pass():
         check_bf16(n + " chunked vs single", f64(a), f64(b))
 
 
+def gqa64k_golden():
+    """The oracle's dK/dV of gqa64k at key rows in chunks 5-7 (2 K/V heads),
+    written by tests/golden/make_gqa64k_dkdv.py from the oracle alone."""
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "gqa64k_dkdv_cols.npz")
+    z = np.load(path, allow_pickle=False)
+    return {key: z[key] for key in z.files}
+
+
+def inputs_sha1(tensors):
+    import hashlib
+    h = hashlib.sha1()
+    for t in tensors:
+        h.update(t.contiguous().view(-1).view(dtype=torch.int16).numpy().tobytes())
+    return h.hexdigest()
+
+
 @pytest.mark.slow
 def test_gqa64k_chunked_sampled():
+    """The 8-chunk driver against the oracle: rows of every chunk, and key rows
+    in chunks 5, 6 and 7, whose gradients are summed over 3, 2 and 1 chunk
+    pairs, on K/V heads 0 and 7 (all four query heads of each group)."""
     w = WORKLOADS["gqa64k"]
     q, k, v, do = draw_workload(w)
+    gold = gqa64k_golden()
+    assert str(gold["inputs_sha1"]) == inputs_sha1((q, k, v, do)), "inputs differ from the stored oracle values"
     scale = default_scale(w.d)
     qd, kd, vd, dod = to_dev(q, k, v, do)
     o, lse = mi.fwd_chunked(qd, kd, vd, w.chunks, scale)
     dq, dk, dv = mi.bwd_chunked(qd, kd, vd, o, lse, dod, w.chunks, scale)
     torch.cuda.synchronize()
     N = w.N
-    rows = np.array([0, 8191, 8192, 30000, 57344, N - 1])
-    # key rows in the last chunk keep the oracle's column work bounded (queries >= key)
-    cols = np.array([N - 8192, N - 4097, N - 2, N - 1])
+    rows = np.array([0, 8191, 8192, 30000, 40960, 57344, N - 1])
     qq, kk, vv, dd = (as_f64(t) for t in (q, k, v, do))
-    sampled_check(qq, kk, vv, dd, o, lse, dq, dk, dv, scale, heads=(0, 13, 31), kv_heads=(7,), rows=rows, cols=cols)
+    sampled_check(qq, kk, vv, dd, o, lse, dq, dk, dv, scale, heads=(0, 13, 31), kv_heads=(), rows=rows, cols=None)
+    cols = gold["cols"]
+    long_c = N - cols >= LONG
+    for i, g in enumerate(gold["kv_heads"]):
+        for n, t, r in (("dk", dk, gold["dk"][i]), ("dv", dv, gold["dv"][i])):
+            got = f64(t[0, cols, g])
+            check_bf16("%s[g=%d] cols %s" % (n, g, cols.tolist()), got, r)
+            err = check_rows_rel("%s[g=%d]" % (n, g), got[long_c], r[long_c])
+            print("%s[g=%d] per-key rel err %.3g" % (n, g, err), flush=True)
     gradient_sum_properties(dk.cpu(), dv.cpu(), do, w.G)
+
+
+@pytest.mark.slow
+def test_gqa64k_chunked_equals_single_pass():
+    """8 chunks in balanced rounds equal one causal pass over all 65536 rows,
+    element by element over every output."""
+    w = WORKLOADS["gqa64k"]
+    q, k, v, do = draw_workload(w)
+    scale = default_scale(w.d)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    del q, k, v, do
+    o1, l1 = mi.fwd(qd, kd, vd, True, scale)
+    o8, l8 = mi.fwd_chunked(qd, kd, vd, w.chunks, scale)
+    torch.cuda.synchronize()
+    device_check_bf16("o chunked vs single", o8, o1)
+    device_check_abs("lse chunked vs single", l8, l1, BF16_LSE_ABS)
+    dq1, dk1, dv1 = mi.bwd(qd, kd, vd, o1, l1, dod, True, scale)
+    dq8, dk8, dv8 = mi.bwd_chunked(qd, kd, vd, o8, l8, dod, w.chunks, scale)
+    torch.cuda.synchronize()
+    for n, a, b in (("dq", dq8, dq1), ("dk", dk8, dk1), ("dv", dv8, dv1)):
+        print(n, "chunked vs single max abs %.3g" % device_check_bf16(n + " chunked vs single", a, b), flush=True)
+
+
+# Chunk driver against the oracle over every output, at sizes the oracle
+# finishes in seconds: GQA with 8 chunks (each key chunk's gradient summed
+# over up to 8 pairs), chunks of 300 rows (ragged inside every tile), fp32.
+@pytest.mark.parametrize("case", [
+    (1, 8, 2, 2048, 128, 8, torch.bfloat16),
+    (2, 4, 4, 1200, 64, 4, torch.bfloat16),
+    (1, 4, 1, 1040, 128, 2, torch.bfloat16),
+    (1, 2, 1, 512, 64, 4, torch.float32),
+], ids=lambda c: "B%dH%dKV%dN%dd%d-P%d-%s" % (c[:6] + ("bf16" if c[6] == torch.bfloat16 else "f32",)))
+def test_chunked_matches_oracle_everywhere(case):
+    B, H, Hkv, N, d, P, dtype = case
+    q, k, v, do = draw(B, H, Hkv, N, d, seed=500 + N, dtype=dtype)
+    scale = default_scale(d)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    o, lse = mi.fwd_chunked(qd, kd, vd, P, scale)
+    dq, dk, dv = mi.bwd_chunked(qd, kd, vd, o, lse, dod, P, scale)
+    torch.cuda.synchronize()
+    compare_full([f64(t) for t in (o, lse, dq, dk, dv)], oracle_full(q, k, v, do, True, scale), dtype)
 
 
 # ---------------------------------------------------------------- merge
