@@ -16,7 +16,7 @@ import os
 
 import torch
 
-__all__ = ["fwd", "bwd", "merge", "fwd_chunked", "bwd_chunked", "fwd_kvcache", "fwd_varlen", "bwd_varlen",
+__all__ = ["fwd", "bwd", "bwd_noalloc", "merge", "fwd_chunked", "bwd_chunked", "fwd_kvcache", "fwd_varlen", "bwd_varlen",
            "fwd_blocksparse", "bwd_blocksparse", "block_mask_shape",
            "release_scratch", "lib", "MiattnError",
            "library_path", "balanced_rounds"]
@@ -49,6 +49,7 @@ def lib():
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i]
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, vp, vp, vp, i, i]
+    L.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, vp, vp, vp, i, i]
     L.attn_bwd_timed.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, vp, vp, vp, i, i, vp]
     L.attn_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i]
     L.attn_bwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, vp, vp, vp, i, i]
@@ -60,7 +61,7 @@ def lib():
     L.attn_bwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, vp, vp, vp, i, i]
     L.attn_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, i, i]
     L.attn_bwd_chunked.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, vp, vp, vp, i, i]
-    for fn in ("attn_fwd", "attn_bwd", "attn_bwd_timed", "attn_merge", "attn_fwd_chunked", "attn_bwd_chunked",
+    for fn in ("attn_fwd", "attn_bwd", "attn_bwd_noalloc", "attn_bwd_timed", "attn_merge", "attn_fwd_chunked", "attn_bwd_chunked",
                "attn_fwd_kvcache", "attn_fwd_window", "attn_bwd_window", "attn_fwd_varlen", "attn_bwd_varlen",
                "attn_fwd_blocksparse", "attn_bwd_blocksparse"):
         getattr(L, fn).restype = i
@@ -186,6 +187,24 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, accumulate=False, dq=No
                 m.record()
         ev = (ctypes.c_void_p * 2)(*[ctypes.c_void_p(m.cuda_event) for m in marks])
         _check(lib().attn_bwd_timed(*args, ev))
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, lse, dout, causal, scale, dq, dk, dv, accumulate=False):
+    """attn_bwd_noalloc: the backward into caller-given dq, dk, dv with the
+    library's fixed per-device rowsum array, allocating nothing (B * H * N at
+    most 4194304). Returns (dq, dk, dv)."""
+    B, N, H, Hkv, d = _dims(q, k, v)
+    _need(o, "o", q.dtype, q.shape, q.device)
+    _need(dout, "dout", q.dtype, q.shape, q.device)
+    _need(lse, "lse", torch.float32, (B, H, N), q.device)
+    gdt = torch.float32 if accumulate else q.dtype
+    _need(dq, "dq", gdt, q.shape, q.device)
+    _need(dk, "dk", gdt, k.shape, q.device)
+    _need(dv, "dv", gdt, v.shape, q.device)
+    _check(lib().attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
+                                  int(bool(causal)), float(scale), _stream(q), _ptr(dout), _ptr(dq), _ptr(dk),
+                                  _ptr(dv), _dtype_code(q), int(bool(accumulate))))
     return dq, dk, dv
 
 

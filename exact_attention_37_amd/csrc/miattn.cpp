@@ -9,6 +9,7 @@
 #include <string>
 #include <map>
 #include <mutex>
+#include <optional>
 #include <utility>
 #include <vector>
 
@@ -471,9 +472,13 @@ int attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, co
 
 namespace {
 
+// fixed_dsum: a caller-provided rowsum buffer of at least B * H * N floats;
+// then the call takes no scratch from the per-stream buffer and allocates
+// nothing (bmask must be null).
 int bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H, int Hkv,
              int N, int d, int causal, float scale, void* stream, const void* dout, void* dq, void* dk, void* dv,
-             int dtype, int accumulate, void* const* marks, int window, const uint8_t* bmask = nullptr) {
+             int dtype, int accumulate, void* const* marks, int window, const uint8_t* bmask = nullptr,
+             float* fixed_dsum = nullptr) {
   int st = check_common(B, H, Hkv, N, d, dtype);
   if (st) return st;
   if ((st = check_ptrs({q, k, v, o, lse, dout, dq, dk, dv}))) return st;
@@ -495,9 +500,13 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
       if (overlap(out, span(bmask, bmask_bytes(N)))) return fail(MIATTN_EINVAL, "dq/dk/dv must not alias block_mask");
 
   hipStream_t s = (hipStream_t)stream;
-  Scratch scratch(s);
-  float* dsum = (float*)scratch.get((size_t)B * H * N * 4);
-  if (!dsum) return fail(MIATTN_ENOMEM, "hipMallocAsync failed for the rowsum vector");
+  std::optional<Scratch> scratch;
+  float* dsum = fixed_dsum;
+  if (!dsum) {
+    scratch.emplace(s);
+    dsum = (float*)scratch->get((size_t)B * H * N * 4);
+    if (!dsum) return fail(MIATTN_ENOMEM, "hipMallocAsync failed for the rowsum vector");
+  }
   Params p = make_params(q, k, v, const_cast<void*>(o), const_cast<float*>(lse), B, H, Hkv, N, d, causal, scale);
   p.dout = dout;
   p.dq = dq;
@@ -506,7 +515,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   p.dsum = dsum;
   p.accumulate = accumulate;
   p.window = window;
-  if (bmask && (st = blocksparse_setup(p, bmask, dtype, scratch, s))) return st;
+  if (bmask && (!scratch || (st = blocksparse_setup(p, bmask, dtype, *scratch, s))))
+    return st ? st : fail(MIATTN_EINVAL, "block masks need library scratch");
   if ((st = launch_status(miattn::launch_bwd_pre(o, dout, dsum, B, H, N, d, 0, N, dtype, s), "bwd preprocess")))
     return st;
   if (marks && (st = launch_status(hipEventRecord((hipEvent_t)marks[0], s), "timing mark 0"))) return st;
@@ -521,9 +531,59 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   return ok();
 }
 
+// ---- attn_bwd_noalloc: the rowsum vector in a fixed device array
+
+// Rows (B * H * N) the fixed array holds: 16 MiB of float32 per device,
+// enough for a [B, H, N] rowsum vector of 4M rows (the 64K-row, 32-head
+// workload needs 2M).
+constexpr long long kNoallocRows = 1LL << 22;
+
+// One copy per device, held from the library's load to the end of the
+// process. Host code never uses this name as an address (on the host it is
+// only a stand-in for the device symbol): kernels get the device address
+// that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) float scratch[kNoallocRows];
+
+constexpr int kMaxDevices = 64;
+std::mutex noalloc_mu;
+float* noalloc_addr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) into *out; returns a status.
+int noalloc_scratch(float** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MIATTN_ELAUNCH, "hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MIATTN_EUNSUPPORTED, "attn_bwd_noalloc supports device indices below 64");
+  std::lock_guard<std::mutex> g(noalloc_mu);
+  if (!noalloc_addr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(MIATTN_ELAUNCH, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    noalloc_addr[dev] = (float*)ptr;
+  }
+  *out = noalloc_addr[dev];
+  return MIATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
+                     int Hkv, int N, int d, int causal, float scale, void* stream, const void* dout, void* dq,
+                     void* dk, void* dv, int dtype, int accumulate) {
+  int st = check_common(B, H, Hkv, N, d, dtype);
+  if (st) return st;
+  if ((long long)B * H * N > kNoallocRows)
+    return fail(MIATTN_EINVAL, "attn_bwd_noalloc: B * H * N = " + std::to_string((long long)B * H * N) +
+                                   " exceeds the fixed scratch of " + std::to_string(kNoallocRows) + " rows");
+  float* dsum = nullptr;
+  if ((st = noalloc_scratch(&dsum))) return st;
+  return bwd_impl(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, stream, dout, dq, dk, dv, dtype, accumulate,
+                  nullptr, 0, nullptr, dsum);
+}
 
 int attn_bwd_timed(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
                    int Hkv, int N, int d, int causal, float scale, void* stream, const void* dout, void* dq,

@@ -213,6 +213,26 @@ int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, 
                     void* stream, const void* dout, void* dq, void* dk, void* dv,
                     int dtype, int accumulate);
 
+/* attn_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments, layouts, results and errors as attn_bwd, but the one
+ * scratch buffer of the backward, the float32 [B, H, N] rowsum vector
+ * D = rowsum(dout * o), lives in a fixed device array of 4194304 floats
+ * (16 MiB) that the library holds on every device it runs on until the
+ * process ends. The call allocates and frees nothing. Its address is looked
+ * up once per device, at the first call with that device current.
+ * Errors: MIATTN_EINVAL if B * H * N exceeds 4194304 (the message gives both
+ * numbers), before anything is enqueued; MIATTN_ELAUNCH if the array's
+ * address cannot be obtained. Every call on one device shares that device's
+ * array, and D is written in full by each call before it is read, so
+ * consecutive calls need no clearing; calls that overlap in time on one
+ * device (concurrent streams, several host threads) race on it and must be
+ * ordered by the caller. */
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     int B, int H, int Hkv, int N, int d, int causal, float scale,
+                     void* stream, const void* dout, void* dq, void* dk, void* dv,
+                     int dtype, int accumulate);
+
 /* attn_bwd with per-kernel timing marks, for measurement tools: the same
  * arguments, results and errors as attn_bwd, and additionally
  *   marks[0] is recorded on `stream` after the rowsum(dout * o) kernel,

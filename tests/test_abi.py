@@ -242,3 +242,14 @@ def test_merge_refuses_partial_overlap():
     assert call(o, oa + 32) == 1 and b"lse must" in L.attn_last_error()
     assert call(o, o + 1024) == 1 and b"must not overlap" in L.attn_last_error()
 
+
+def test_noalloc_backward_refuses_oversized_rowsum():
+    """attn_bwd_noalloc's fixed rowsum array holds 4194304 rows (B * H * N);
+    a larger call is refused before anything is enqueued."""
+    L = mi.lib()
+    base = [vp(FAKE * i) for i in range(1, 6)]
+    g = [vp(FAKE * i) for i in range(6, 10)]
+    assert L.attn_bwd_noalloc(*base, 1, 64, 64, 70000, 64, 1, 0.125, None, *g, 1, 0) == 1
+    assert b"exceeds the fixed scratch of 4194304 rows" in L.attn_last_error()
+    assert L.attn_bwd_noalloc(*base, 2, 32, 8, 65537, 128, 1, 0.125, None, *g, 1, 0) == 1
+    assert L.attn_bwd_noalloc(*base, 1, 32, 8, 65536, 96, 1, 0.125, None, *g, 1, 0) == 2
