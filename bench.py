@@ -5,11 +5,14 @@ One step = one forward (attn_fwd) and one backward (attn_bwd) of causal
 exact attention over the Llama-7B-shaped 16K workload (B=1, H=Hkv=32,
 N=16384, d=128, bf16, iid N(0,1) synthetic inputs resident in HBM). Prints
 one JSON line. FLOPs: forward 4*B*H*N^2*d halved for the causal mask,
-backward 2.5x the forward. The line also carries "kvcache": the key/value-
-cache forward (attn_fwd_kvcache) on a decode and a chunked-prefill workload,
-each against its own roofline.
+backward 2.5x the forward. The line also carries the other workloads, each
+against its own roofline: "configs" (the GPT-2 and BERT shapes, the 16K
+sequence as 4 chunks and the 64K GQA sequence as 8 chunks), the sliding-
+window, packed variable-length and block-sparse variants, the key/value-
+cache forward on a decode and a chunked-prefill workload, and the causal
+forward at the FlashAttention-2 ablation shape (context only).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--extra]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
 """
 import argparse
 import json
@@ -47,7 +50,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline leg")
-    ap.add_argument("--extra", action="store_true", help="also time the chunked workloads")
+    ap.add_argument("--main-only", action="store_true",
+                    help="time only the main step (for profiler runs): no secondary workloads")
     ap.add_argument("--workload", default="llama16k")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run 3 plain device copies of MIB MiB (a known-size "
@@ -240,6 +244,123 @@ def bench_blocksparse(mi, torch, q, k, v, do, w, density=0.25, reps=10):
             "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2)}
 
 
+def time_fwd_bwd(torch, fwd, bwd, reps, flush=None):
+    """Average event-timed forward and backward (ms) over `reps` calls. With
+    `flush` (a device tensor), it is overwritten before every rep, outside the
+    timed events, so that the inputs are not served from the caches."""
+    # all reps are enqueued before one synchronisation, so the host's call
+    # overhead overlaps the device work instead of landing between events
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for e in evs:
+        if flush is not None:
+            flush.fill_(1)
+        e[0].record()
+        out = fwd()
+        e[1].record()
+        bwd(*out)
+        e[2].record()
+    torch.cuda.synchronize()
+    f_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / reps
+    b_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / reps
+    return f_ms, b_ms
+
+
+def algorithmic_bytes(w):
+    """Bytes of the forward and the backward with every tensor touched once:
+    forward reads Q, K, V and writes O, LSE; backward reads Q, K, V, O, dO,
+    LSE, writes dQ, dK, dV and writes and reads the rowsum vector D."""
+    e = 4 if w.dtype == "f32" else 2
+    nq = w.B * w.N * w.H * w.d * e
+    nk = w.B * w.N * w.Hkv * w.d * e
+    nl = w.B * w.H * w.N * 4
+    return 2 * nq + 2 * nk + nl, 4 * nq + 4 * nk + 3 * nl
+
+
+def bench_workload(mi, torch, name, reps=20):
+    """fwd+bwd on a whole small workload (GPT-2 or BERT shape): TFLOP/s against
+    the bf16 peak and against its own roofline min(peak, intensity x HBM
+    bandwidth). These working sets (150-400 MB) fit largely in the 256 MB
+    last-level cache, so a second timing overwrites a 1 GiB buffer before
+    every rep."""
+    from workloads import WORKLOADS, draw_workload, flops
+    w = WORKLOADS[name]
+    causal = w.causal[0]
+    q, k, v, do = [t.to("cuda:0") for t in draw_workload(w)]
+    scale = w.d ** -0.5
+    o, lse = torch.empty_like(q), torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fwd = lambda: mi.fwd(q, k, v, causal, scale, out=o, out_lse=lse)
+    bwd = lambda o_, l_: mi.bwd(q, k, v, o_, l_, do, causal, scale, dq=dq, dk=dk, dv=dv)
+    time_fwd_bwd(torch, fwd, bwd, 3)
+    f_ms, b_ms = time_fwd_bwd(torch, fwd, bwd, reps)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=q.device)
+    fc_ms, bc_ms = time_fwd_bwd(torch, fwd, bwd, reps, flush=flush)
+    del flush
+    ff, fb = flops(w.B, w.H, w.N, w.d, causal)
+    bf_, bb = algorithmic_bytes(w)
+    ridge_tf = (ff + fb) / (bf_ + bb) * PEAK_HBM_GBS / 1e3        # intensity x bandwidth, TFLOP/s
+    roof_tf = min(PEAK_BF16_TFLOPS, ridge_tf)
+    tf = (ff + fb) / ((f_ms + b_ms) * 1e-3) / 1e12
+    tfc = (ff + fb) / ((fc_ms + bc_ms) * 1e-3) / 1e12
+    return {"workload": "%s: B=%d H=%d Hkv=%d N=%d d=%d %s, fwd+bwd" % (
+                w.name, w.B, w.H, w.Hkv, w.N, w.d, "causal" if causal else "non-causal"),
+            "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4), "tflops": round(tf, 2),
+            "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
+            "roofline": {"bound": "mfma" if roof_tf >= PEAK_BF16_TFLOPS else "hbm", "achieved": round(tf, 2),
+                         "peak": round(roof_tf, 1), "unit": "TFLOP/s", "frac": round(tf / roof_tf, 4),
+                         "algorithmic_bytes": int(bf_ + bb)},
+            "cold": {"fwd_ms": round(fc_ms, 4), "bwd_ms": round(bc_ms, 4), "tflops": round(tfc, 2),
+                     "note": "1 GiB buffer overwritten before every rep"}}
+
+
+def bench_chunked(mi, torch, name, reps=3):
+    """The chunk-pair driver (attn_fwd_chunked / attn_bwd_chunked) on a
+    chunked workload; FLOPs counted as for the whole problem."""
+    from workloads import WORKLOADS, draw_workload, flops
+    w = WORKLOADS[name]
+    q, k, v, do = [t.to("cuda:0") for t in draw_workload(w)]
+    scale = w.d ** -0.5
+    fwd = lambda: mi.fwd_chunked(q, k, v, w.chunks, scale)
+    bwd = lambda o_, l_: mi.bwd_chunked(q, k, v, o_, l_, do, w.chunks, scale)
+    time_fwd_bwd(torch, fwd, bwd, 2)
+    f_ms, b_ms = time_fwd_bwd(torch, fwd, bwd, reps)
+    ff, fb = flops(w.B, w.H, w.N, w.d, True)
+    tf = (ff + fb) / ((f_ms + b_ms) * 1e-3) / 1e12
+    out = {"workload": "%s: B=%d H=%d Hkv=%d N=%d d=%d causal, %d chunks of %d rows in balanced rounds, fwd+bwd" % (
+               w.name, w.B, w.H, w.Hkv, w.N, w.d, w.chunks, w.N // w.chunks),
+           "fwd_ms": round(f_ms, 3), "bwd_ms": round(b_ms, 3), "tflops": round(tf, 2),
+           "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
+           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+    del q, k, v, do
+    return out
+
+
+def bench_fa2_ablation_shape(mi, torch, reps=20):
+    """Causal forward at the shape of the FlashAttention-2 authors' ablation
+    table (B = 8 and 1, H = 16, N = 2048, d = 128): context only, next to
+    their A100 figures."""
+    from workloads import draw, flops
+    out = {}
+    for B in (8, 1):
+        q, k, v, _ = [t.to("cuda:0") for t in draw(B, 16, 16, 2048, 128, seed=10 + B)]
+        o, lse = torch.empty_like(q), torch.empty((B, 16, 2048), dtype=torch.float32, device=q.device)
+        for _ in range(3):
+            mi.fwd(q, k, v, True, 128 ** -0.5, out=o, out_lse=lse)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            mi.fwd(q, k, v, True, 128 ** -0.5, out=o, out_lse=lse)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        ff, _ = flops(B, 16, 2048, 128, True)
+        out["B%d" % B] = {"fwd_ms": round(ms, 4), "tflops": round(ff / (ms * 1e-3) / 1e12, 2)}
+    out["workload"] = "causal forward, H=16, N=2048, d=128, bf16 (the FlashAttention-2 ablation shape; context only)"
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -251,7 +372,7 @@ def main():
     from workloads import WORKLOADS, draw_workload, flops
 
     w = WORKLOADS[args.workload]
-    causal = True
+    causal = w.causal[0]
     scale = w.d ** -0.5
     q, k, v, do = [t.to("cuda:0") for t in draw_workload(w)]
     o = torch.empty_like(q)
@@ -315,7 +436,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "%s: B=%d H=%d Hkv=%d N=%d d=%d causal, fwd+bwd" % (w.name, w.B, w.H, w.Hkv, w.N, w.d),
+        "config": {"workload": "%s: B=%d H=%d Hkv=%d N=%d d=%d %s, fwd+bwd" % (w.name, w.B, w.H, w.Hkv, w.N, w.d, "causal" if causal else "non-causal"),
                    "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)"},
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
@@ -326,41 +447,22 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dkdv_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
     }
-    out["window"] = bench_window(mi, torch, q, k, v, do, w, 4096)
-    out["varlen"] = bench_varlen(mi, torch)
-    out["blocksparse"] = bench_blocksparse(mi, torch, q, k, v, do, w)
-    out["kvcache"] = {name: bench_cache(mi, torch, name) for name in ("decode16k", "prefill16k")}
-    if args.extra:
-        extra = {}
-        for name in ("llama16k", "gqa64k"):
-            we = WORKLOADS[name]
-            tq, tk, tv, tdo = [t.to("cuda:0") for t in draw_workload(we)]
-            sc = we.d ** -0.5
-            for _ in range(2):
-                oo, ll = mi.fwd_chunked(tq, tk, tv, we.chunks, sc)
-                mi.bwd_chunked(tq, tk, tv, oo, ll, tdo, we.chunks, sc)
-            torch.cuda.synchronize()
-            reps = 3
-            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-            f_ms = b_ms = 0.0
-            for _ in range(reps):
-                e0.record()
-                oo, ll = mi.fwd_chunked(tq, tk, tv, we.chunks, sc)
-                e1.record()
-                mi.bwd_chunked(tq, tk, tv, oo, ll, tdo, we.chunks, sc)
-                e2.record()
-                torch.cuda.synchronize()
-                f_ms += e0.elapsed_time(e1) / reps
-                b_ms += e1.elapsed_time(e2) / reps
-            a, bb = flops(we.B, we.H, we.N, we.d, True)
-            extra[name + "_chunked%d" % we.chunks] = {
-                "fwd_ms": round(f_ms, 3), "bwd_ms": round(b_ms, 3),
-                "tflops": round((a + bb) / ((f_ms + b_ms) * 1e-3) / 1e12, 2)}
-            del tq, tk, tv, tdo, oo, ll
-        out["extra"] = extra
+    if not args.main_only:
+        out["window"] = bench_window(mi, torch, q, k, v, do, w, 4096)
+        out["varlen"] = bench_varlen(mi, torch)
+        out["blocksparse"] = bench_blocksparse(mi, torch, q, k, v, do, w)
+        out["kvcache"] = {name: bench_cache(mi, torch, name) for name in ("decode16k", "prefill16k")}
+        del q, k, v, do, o, lse, dq, dk, dv
+        out["configs"] = {
+            "gpt2": bench_workload(mi, torch, "gpt2"),
+            "bert": bench_workload(mi, torch, "bert"),
+            "llama16k_chunked4": bench_chunked(mi, torch, "llama16k"),
+            "gqa64k_chunked8": bench_chunked(mi, torch, "gqa64k"),
+        }
+        out["fa2_ablation_shape"] = bench_fa2_ablation_shape(mi, torch)
     if args.calib_copy:
         nbytes = args.calib_copy << 20
-        src = torch.ones(nbytes, dtype=torch.uint8, device=q.device)
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)

@@ -152,11 +152,13 @@ void fwd_mfma_kernel(Params p) {
   // keys past the last one read as zeros (buffer range check); the mask drops them
   const uint32_t kbytes = (uint32_t)(((p.Nk - 1) * krs + D) * 2);
   const u32x4 rk = rsrc_words(K, kbytes), rv = rsrc_words(V, kbytes);
-  auto load_piece = [&](int i, int buf, int j0) {
+  // piece i of this wave: K of the tile starting at key jk0 into K buffer kb,
+  // or V of the tile starting at key jv0 into V buffer vb
+  auto load_piece = [&](int i, int kb, int jk0, int vb, int jv0) {
     const int sl = wave * NL + i;                  // wave-uniform
     const bool is_v = sl >= TILE_KB;
-    buffer_load_lds16_async(is_v ? rv : rk, loff[i], (uint32_t)(j0 * krs) * 2u,
-                            lds_addr((is_v ? sm.v[buf] : sm.k[buf]) + (sl % TILE_KB) * 512));
+    buffer_load_lds16_async(is_v ? rv : rk, loff[i], (uint32_t)((is_v ? jv0 : jk0) * krs) * 2u,
+                            lds_addr((is_v ? sm.v[vb] : sm.k[kb]) + (sl % TILE_KB) * 512));
   };
 
   // ---- per-lane LDS read bases (elements): K rows sigma32(n) (+32 kb), logical
@@ -183,80 +185,79 @@ void fwd_mfma_kernel(Params p) {
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
   float m = -INFINITY, l = 0.f;
 
-  // block-sparse: the current and the next listed tile (the index of the
-  // one after is fetched an iteration ahead, so its latency stays hidden)
-  int jc = jt0, jx = 0;
-  if constexpr (SPARSE) {
-    jc = nit > 0 ? uni(tl[0]) : 0;
-    jx = nit > 1 ? uni(tl[1]) : jc;
-  }
+  // Tiles are taken in list order it = 0 .. nit-1 (tile_of(it): contiguous
+  // from jt0, or the block-sparse list). K and V of tile it sit in K / V
+  // buffer it & 1. The loop is software-pipelined across tiles, so that
+  // every phase of matrix-core products carries independent vector work:
+  //   phase A: S^T of tile it+1 (K from LDS)  + exp / row sum / bf16 P of tile it
+  //            + direct loads of K(it+2) and V(it+1)
+  //   phase B: O^T += V^T P^T of tile it      + max scan of tile it+1's scores
+  // then the running max is raised for tile it+1 (rescaling the
+  // accumulator, which now holds tile it), one wait for the loads and one
+  // barrier. K is thereby loaded two tiles ahead and V one tile ahead: K(it+2)
+  // overwrites K(it), whose products ran in the previous iteration, and
+  // V(it+1) overwrites V(it-1). Tiles past the last repeat the last one.
+  // Block-sparse list entries are read two iterations ahead.
+  int t1 = 0, t2 = 0, t3 = 0;     // tile_of(it + 1), tile_of(it + 2), tile_of(it + 3)
+  auto list_at = [&](int it) { return SPARSE ? uni(tl[min(it, nit - 1)]) : jt0 + min(it, nit - 1); };
+  int t0 = 0;
   if (nit > 0) {
-#pragma unroll
-    for (int i = 0; i < NL; ++i) load_piece(i, 0, jc * BC);
-    wait_global_loads();
+    t0 = list_at(0);
+    t1 = list_at(1);
+    t2 = list_at(2);
+    t3 = list_at(3);
   }
-  __syncthreads();
 
-  for (int it = 0; it < nit; ++it) {
-    const int j = SPARSE ? jc : jt0 + it;
-    const int buf = it & 1;
-    const bf16* kt = sm.k[buf];
-    const bf16* vt = sm.v[buf];
-    const int kpos0 = p.k_start + j * BC;          // absolute position of the tile's first key
-    // next tile (the last tile repeats itself)
-    const int jn = (SPARSE ? jx : min(j + 1, nkt - 1)) * BC;
-    int jxx = 0;
-    if constexpr (SPARSE) jxx = it + 2 < nit ? uni(tl[it + 2]) : jx;
-    // No per-wave skip: a per-wave branch makes the register allocator
-    // shuttle accumulators between AGPRs and VGPRs every iteration; fully
-    // masked waves (diagonal tiles only) compute P = 0 instead.
-
-    // ---- S^T = K Q^T for 2 blocks of 32 keys (lock steps, with the next
-    // tile's direct loads in between): step i = (kb, ks)
-    f32x16 s[2];
-    s[0] = f32x16{};
-    s[1] = f32x16{};
+  // ---- S^T = K Q^T of one tile from K buffer kb into sx, lock-stepped with ex(step)
+  auto scores = [&](f32x16 (&sx)[2], int kbuf, auto ex) {
+    const bf16* kt = sm.k[kbuf];
+    sx[0] = f32x16{};
+    sx[1] = f32x16{};
     lockstep_products<2 * KS, 4>(
         [&](auto ic) {
-          constexpr int i = decltype(ic)::value, kb = i / KS, ks = i % KS;
+          constexpr int i = decltype(ic)::value, kb = i % 2, ks = i / 2;
           return lds_read16(kt + rd_s[ks & 1], kb * 32 * ROW + (ks >> 1) * 32);
         },
         [&](auto ic, bf16x8 a) {
-          constexpr int i = decltype(ic)::value, kb = i / KS, ks = i % KS;
-          s[kb] = mfma32(a, qf[ks], s[kb]);
+          constexpr int i = decltype(ic)::value, kb = i % 2, ks = i / 2;
+          sx[kb] = mfma32(a, qf[ks], sx[kb]);
         },
-        [&](auto ic) {
-          constexpr int i = decltype(ic)::value;
-          constexpr int lo = i * NL / (2 * KS), hi = (i + 1) * NL / (2 * KS);
-          [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
-            (load_piece(lo + Ws, buf ^ 1, jn), ...);
-          }(std::make_integer_sequence<int, hi - lo>{});
-        });
-
-    // ---- mask: key index inside the tile > thr (causal diagonal, ragged end)
-    // or, under a sliding window, < lo (before the row's window)
+        ex);
+  };
+  // ---- mask of one tile's scores: key index inside the tile > thr (causal
+  // diagonal, ragged end) or, under a sliding window, < lo (before the row's window)
+  auto mask_tile = [&](f32x16 (&sx)[2], int j) {
+    const int kpos0 = p.k_start + j * BC;          // absolute position of the tile's first key
     int thr = p.Nk - 1 - j * BC;
     if (CAUSAL && kpos0 + BC - 1 > wq_first) thr = min(thr, qpos - kpos0);
     int lo = 0;
     if constexpr (WIN) lo = qpos - (p.window - 1) - kpos0;
     if (__builtin_amdgcn_ballot_w64(thr < BC - 1 || (WIN && lo > 0)) != 0) {
+      // key index kb * 32 + sigma_row(g, r) = 8 g + kb * 32 + r (+ 8 for r >= 8):
+      // the lane's part moves into the thresholds, the rest is a constant
+      const int thr_g = thr - 8 * g, lo_g = lo - 8 * g;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int kin = kb * 32 + sigma_row(g, r);
-          if (kin > thr || (WIN && kin < lo)) s[kb][r] = -INFINITY;
+          const int kc = kb * 32 + r + (r >= 8 ? 8 : 0);
+          if (kc > thr_g || (WIN && kc < lo_g)) sx[kb][r] = -INFINITY;
         }
     }
-
-    // ---- online softmax: lane (g, query n), register r of block kb <-> key 32 kb + sigma_row(g, r)
-    float mx = s[0][0];
+  };
+  // ---- running max over a tile's scores, in NS slices (slice k of NS)
+  float mx = -INFINITY;
+  auto max_slice = [&](const f32x16 (&sx)[2], auto kc, auto nsc) {
+    constexpr int k = decltype(kc)::value, ns = decltype(nsc)::value;
+    constexpr int lo = k * 32 / ns, hi = (k + 1) * 32 / ns;
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    mx = max_halves(mx);
-    const float mt = mx * c;
+    for (int e = lo; e < hi; ++e) mx = fmaxf(mx, sx[e / 16][e % 16]);
+  };
+  // raise the running max to the tile's max (lane (g, query n)) when it
+  // exceeds the kept one by more than 8 (log2 units), rescaling acc and l
+  auto raise_max = [&]() {
+    const float mt = max_halves(mx) * c;
+    mx = -INFINITY;
     const bool raise = mt > m + 8.f;
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
       const float mnew = raise ? mt : m;
@@ -270,44 +271,102 @@ void fwd_mfma_kernel(Params p) {
         for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
       m = mnew;
     }
+  };
+  // ---- P of the current tile sc: sub-step w of 16 = (kb, half, element
+  // pair), the float32 probabilities summed into the row sum before the bf16 cast
+  bf16x8 pf[4];
+  float lsum0 = 0.f, lsum1 = 0.f, mneg = 0.f;
+  auto exp_sub = [&](const f32x16 (&sc)[2], auto wc) {
+    constexpr int w = decltype(wc)::value, kb = w / 8, half = (w / 4) % 2, e = 2 * (w % 4);
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][half * 8 + e], c, mneg));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][half * 8 + e + 1], c, mneg));
+    lsum0 += p0;
+    lsum1 += p1;
+    pf[kb * 2 + half][e] = (bf16)p0;
+    pf[kb * 2 + half][e + 1] = (bf16)p1;
+  };
+  // exp sub-steps [i * 16 / n, (i + 1) * 16 / n) for step i of n
+  auto exp_steps = [&](const f32x16 (&sc)[2], auto ic, auto nc) {
+    constexpr int i = decltype(ic)::value, n_ = decltype(nc)::value;
+    constexpr int lo = i * 16 / n_, hi = (i + 1) * 16 / n_;
+    [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
+      (exp_sub(sc, std::integral_constant<int, lo + Ws>{}), ...);
+    }(std::make_integer_sequence<int, hi - lo>{});
+  };
+
+  // scores of the current tile (sa) and of the next one (sb); the loop is
+  // unrolled twice so that the two swap roles without copies
+  f32x16 sa[2], sb[2];
+  if (nit > 0) {
+    // prologue: K, V of tiles 0 and 1 into buffers 0 and 1, then S^T of
+    // tile 0, its mask and max (a barrier before the loop's first loads,
+    // which overwrite K(0))
+#pragma unroll
+    for (int i = 0; i < NL; ++i) load_piece(i, 0, t0 * BC, 0, t0 * BC);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) load_piece(i, 1, t1 * BC, 1, t1 * BC);
+    wait_global_loads();
+    __syncthreads();
+    scores(sa, 0, [](auto) {});
+    mask_tile(sa, t0);
+    max_slice(sa, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+    raise_max();
+    __syncthreads();
+  }
+
+  // one tile: sc holds its (masked) scores, sn receives the next tile's
+  auto iteration = [&](int it, const f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    const int vb = it & 1;
+    const bf16* vt = sm.v[vb];
+    const bool has_next = it + 1 < nit;
     // (a row whose window has not begun yet keeps m = -inf and p = 0)
-    const float mneg = (EMPTY && m == -INFINITY) ? 0.f : -m;
-    bf16x8 pf[4];
-    float lsum0 = 0.f, lsum1 = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        bf16x8 x;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][half * 8 + e], c, mneg));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][half * 8 + e + 1], c, mneg));
-          lsum0 += p0;
-          lsum1 += p1;
-          x[e] = (bf16)p0;
-          x[e + 1] = (bf16)p1;
-        }
-        pf[kb * 2 + half] = x;
-      }
+    mneg = (EMPTY && m == -INFINITY) ? 0.f : -m;
+    lsum0 = lsum1 = 0.f;
+    // ---- phase A: S^T of tile it+1 with P of tile it and the next loads
+    if (has_next) {
+      const int jk = t2 * BC, jv = t1 * BC;
+      scores(sn, vb ^ 1, [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        exp_steps(sc, ic, std::integral_constant<int, 2 * KS>{});
+        constexpr int lo = i * NL / (2 * KS), hi = (i + 1) * NL / (2 * KS);
+        [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
+          (load_piece(lo + Ws, vb, jk, vb ^ 1, jv), ...);
+        }(std::make_integer_sequence<int, hi - lo>{});
+      });
+      mask_tile(sn, t1);
+    } else {
+      [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
+        (exp_sub(sc, std::integral_constant<int, Ws>{}), ...);
+      }(std::make_integer_sequence<int, 16>{});
     }
     l += lsum0 + lsum1;
 
-    // ---- O^T += V^T P^T: V^T by transposing reads; step i = (kq, db)
-    pipelined_products<4 * DB, 4>(
-        [&](int i) {
-          const int kq = i / DB, db = i % DB;
+    // ---- phase B: O^T += V^T P^T of tile it (V^T by transposing reads;
+    // step i = (kq, db)) with the max scan of tile it+1
+    lockstep_products<4 * DB, 4>(
+        [&](auto ic) {
+          constexpr int i = decltype(ic)::value, kq = i / DB, db = i % DB;
           const bf16x4 r0 = lds_read_tr4(vt + rd_t[0] + 16 * kq * ROW + 32 * db);
           const bf16x4 r1 = lds_read_tr4(vt + rd_t[1] + 16 * kq * ROW + 32 * db);
           return bf16x8{r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
         },
-        [&](int i, bf16x8 a) { acc[i % DB] = mfma32(a, pf[i / DB], acc[i % DB]); });
+        [&](auto ic, bf16x8 a) {
+          constexpr int i = decltype(ic)::value, kq = i / DB, db = i % DB;
+          acc[db] = mfma32(a, pf[kq], acc[db]);
+        },
+        [&](auto ic) {
+          if (has_next) max_slice(sn, ic, std::integral_constant<int, 4 * DB>{});
+        });
+    if (has_next) raise_max();
+    t1 = t2;
+    t2 = t3;
+    t3 = list_at(it + 4);
     wait_global_loads();
     __syncthreads();
-    if constexpr (SPARSE) {
-      jc = jx;
-      jx = jxx;
-    }
+  };
+  for (int it = 0; it < nit; it += 2) {
+    iteration(it, sa, sb);
+    if (it + 1 < nit) iteration(it + 1, sb, sa);
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
