@@ -452,26 +452,30 @@ void bwd_dkdv_kernel(Params p) {
 #pragma unroll
       for (int run = 0; run < 4; ++run) {
         const int col = db * 32 + run * 8 + g * 4;
-        if (p.accumulate) {
-          f32x4* a = (f32x4*)((float*)p.dk + off + col);
-          f32x4* v = (f32x4*)((float*)p.dv + off + col);
-          f32x4 xa = *a, xv = *v;
+        f32x4 xa, xv;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            xa[e] += dk[db][run * 4 + e] * p.scale;
-            xv[e] += dv[db][run * 4 + e];
-          }
-          *a = xa;
-          *v = xv;
+        for (int e = 0; e < 4; ++e) {
+          xa[e] = dk[db][run * 4 + e] * p.scale;
+          xv[e] = dv[db][run * 4 + e];
+        }
+        if (p.acc_kv == ACC_ADD || p.acc_kv == ACC_LAST) {   // plus the float32 sums so far
+          const float* sk = p.acc_kv == ACC_ADD ? (const float*)p.dk : p.k_part;
+          const float* sv = p.acc_kv == ACC_ADD ? (const float*)p.dv : p.v_part;
+          xa += *(const f32x4*)(sk + off + col);
+          xv += *(const f32x4*)(sv + off + col);
+        }
+        if (p.acc_kv == ACC_ADD || p.acc_kv == ACC_FIRST) {
+          *(f32x4*)((float*)p.dk + off + col) = xa;
+          *(f32x4*)((float*)p.dv + off + col) = xv;
         } else {
-          bf16x4 xa, xv;
+          bf16x4 ya, yv;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            xa[e] = (bf16)(dk[db][run * 4 + e] * p.scale);
-            xv[e] = (bf16)dv[db][run * 4 + e];
+            ya[e] = (bf16)xa[e];
+            yv[e] = (bf16)xv[e];
           }
-          *(bf16x4*)((bf16*)p.dk + off + col) = xa;
-          *(bf16x4*)((bf16*)p.dv + off + col) = xv;
+          *(bf16x4*)((bf16*)p.dk + off + col) = ya;
+          *(bf16x4*)((bf16*)p.dv + off + col) = yv;
         }
       }
     }
@@ -798,17 +802,18 @@ void bwd_dq_kernel(Params p) {
 #pragma unroll
     for (int md = 0; md < DM; ++md) {
       const int col = 16 * md + 4 * q4;
-      if (p.accumulate) {
-        f32x4* a = (f32x4*)((float*)p.dq + off + col);
-        f32x4 x = *a;
+      f32x4 x;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] += acc[md][nb][e] * p.scale;
-        *a = x;
+      for (int e = 0; e < 4; ++e) x[e] = acc[md][nb][e] * p.scale;
+      if (p.acc_q == ACC_ADD || p.acc_q == ACC_LAST)    // plus the float32 sum so far
+        x += *(const f32x4*)((p.acc_q == ACC_ADD ? (const float*)p.dq : p.q_part) + off + col);
+      if (p.acc_q == ACC_ADD || p.acc_q == ACC_FIRST) {
+        *(f32x4*)((float*)p.dq + off + col) = x;
       } else {
-        bf16x4 x;
+        bf16x4 y;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = (bf16)(acc[md][nb][e] * p.scale);
-        *(bf16x4*)((bf16*)p.dq + off + col) = x;
+        for (int e = 0; e < 4; ++e) y[e] = (bf16)x[e];
+        *(bf16x4*)((bf16*)p.dq + off + col) = y;
       }
     }
   }

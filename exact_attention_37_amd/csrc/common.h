@@ -42,7 +42,22 @@ struct Params {
   int causal;        // mask keys whose absolute position exceeds the query's
   float scale;
   int accumulate;        // backward: add into float32 dq/dk/dv
+  // Store modes of the matrix-core backward kernels, for dq (acc_q) and for
+  // dk / dv (acc_kv): ACC_STORE writes the input dtype, ACC_ADD adds into
+  // float32, ACC_FIRST writes float32 without reading, ACC_LAST adds the
+  // float32 running sums q_part / k_part / v_part (same layouts) and writes
+  // the input dtype. Chunk pairs use FIRST / ADD / LAST per chunk.
+  int acc_q, acc_kv;
+  const float* q_part;
+  const float* k_part;
+  const float* v_part;
   int window;            // > 0 (causal only): key visible iff query position - window < key position
+  // Forward (matrix-core kernel) of a chunk pair: merge the block's result
+  // into the running result of the same rows over earlier key chunks, float32
+  // [B, N, H, d] and [B, H, N] (the attn_merge arithmetic), and store the
+  // merged rows to o / lse, which may be these very buffers; null otherwise.
+  const float* mrg_o;
+  const float* mrg_lse;
   // Packed variable-length batch: sequence z of the grid owns rows
   // [cu_seqlens[z], cu_seqlens[z + 1]) of a B = 1 layout of N rows; null otherwise.
   const int* cu_seqlens;
@@ -61,6 +76,7 @@ struct Params {
 };
 
 constexpr int BS_ROWS = 256, BS_COLS = 128, BS_TILE = 64;
+constexpr int ACC_STORE = 0, ACC_ADD = 1, ACC_FIRST = 2, ACC_LAST = 3;
 
 // For a packed variable-length batch, narrows p to sequence s (rows
 // [cu_seqlens[s], cu_seqlens[s + 1]) of the single B = 1 layout; the offsets

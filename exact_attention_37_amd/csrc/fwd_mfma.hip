@@ -374,27 +374,54 @@ void fwd_mfma_kernel(Params p) {
   if (row < p.Nq) {
     // a row that saw no key (block-sparse) stores o = 0 and lse = -inf
     const float inv = (SPARSE && lt == 0.f) ? 0.f : 1.f / lt;
-    TO* O = (TO*)p.o + (((long long)b * p.N + p.q_start + row) * p.H + h) * D;
+    const long long ro = (((long long)b * p.N + p.q_start + row) * p.H + h) * D;
+    const long long li = ((long long)b * p.H + h) * p.N + p.q_start + row;
+    float lse_row = (m + __log2f(lt)) * kLn2;
+    // chunk pair: softmax over the union of the earlier key chunks and this
+    // block's keys, from the running result (weight wa) and this block's
+    // normalised rows (weight wb), the same arithmetic as the merge kernel
+    const float* R = p.mrg_o ? p.mrg_o + ro : nullptr;
+    float wa = 0.f, wb = 1.f;
+    if (R) {
+      const float la = p.mrg_lse[li], lb = lse_row;
+      const float mm = fmaxf(la, lb);
+      wb = 0.f;
+      lse_row = -INFINITY;
+      if (mm != -INFINITY) {
+        const float ea = __expf(la - mm), eb = __expf(lb - mm);
+        const float tot = ea + eb;
+        lse_row = mm + __logf(tot);
+        const float itot = 1.f / tot;
+        wa = ea * itot;
+        wb = eb * itot;
+      }
+    }
+    TO* O = (TO*)p.o + ro;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       // accumulator rows (r/4)*8 + g*4 + r%4: four runs of 4 columns
 #pragma unroll
       for (int run = 0; run < 4; ++run) {
-        TO* dst = O + db * 32 + run * 8 + g * 4;
+        const int col = db * 32 + run * 8 + g * 4;
+        float z[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[e] = acc[db][run * 4 + e] * inv;
+        if (R) {
+          const f32x4 x = *(const f32x4*)(R + col);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[e] = wa * x[e] + wb * z[e];
+        }
         if constexpr (sizeof(TO) == 2) {
-          bf16x4 x;
+          bf16x4 y;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = (bf16)(acc[db][run * 4 + e] * inv);
-          *(bf16x4*)dst = x;
+          for (int e = 0; e < 4; ++e) y[e] = (bf16)z[e];
+          *(bf16x4*)(O + col) = y;
         } else {
-          f32x4 x;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = acc[db][run * 4 + e] * inv;
-          *(f32x4*)dst = x;
+          *(f32x4*)(O + col) = f32x4{z[0], z[1], z[2], z[3]};
         }
       }
     }
-    if (g == 0) p.lse[((long long)b * p.H + h) * p.N + p.q_start + row] = (m + __log2f(lt)) * kLn2;
+    if (g == 0) p.lse[li] = lse_row;
   }
 }
 

@@ -372,6 +372,7 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
   p.dv = dv;
   p.dsum = dsum;
   p.accumulate = accumulate;
+  p.acc_q = p.acc_kv = accumulate;
   // rowsum(dout * o) is per token: the packed rows as one sequence
   if ((st = launch_status(miattn::launch_bwd_pre(o, dout, dsum, 1, H, total, d, 0, total, dtype, s),
                           "bwd preprocess")))
@@ -514,6 +515,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   p.dv = dv;
   p.dsum = dsum;
   p.accumulate = accumulate;
+  p.acc_q = p.acc_kv = accumulate;
   p.window = window;
   if (bmask && (!scratch || (st = blocksparse_setup(p, bmask, dtype, *scratch, s))))
     return st ? st : fail(MIATTN_EINVAL, "block masks need library scratch");
@@ -665,12 +667,16 @@ int attn_fwd_chunked(const void* q, const void* k, const void* v, void* o, float
   const int R = N / nchunks;
   const long long no = (long long)B * N * H * d, nl = (long long)B * H * N;
   Scratch scratch(s);
-  // running (merged-so-far) result per query chunk, and one partial per pair
+  // running (merged-so-far) result per query chunk; the float32 path also
+  // keeps one partial per pair for the merge kernel (the bf16 forward kernel
+  // merges into the running result in its epilogue)
+  const bool fused = dtype == MIATTN_BF16;
   float* run_o = (float*)scratch.get(no * 4);
   float* run_l = (float*)scratch.get(nl * 4);
-  float* part_o = (float*)scratch.get(no * 4);
-  float* part_l = (float*)scratch.get(nl * 4);
-  if (!run_o || !run_l || !part_o || !part_l) return fail(MIATTN_ENOMEM, "hipMallocAsync failed for chunk partials");
+  float* part_o = fused ? nullptr : (float*)scratch.get(no * 4);
+  float* part_l = fused ? nullptr : (float*)scratch.get(nl * 4);
+  if (!run_o || !run_l || (!fused && (!part_o || !part_l)))
+    return fail(MIATTN_ENOMEM, "hipMallocAsync failed for chunk partials");
 
   std::vector<int> done(nchunks, 0);   // pairs merged into each query chunk so far
   for (const auto& round : balanced_rounds(nchunks)) {
@@ -691,6 +697,13 @@ int attn_fwd_chunked(const void* q, const void* k, const void* v, void* o, float
         p.o = run_o;
         p.lse = run_l;
         if ((st = launch_status(fwd_block(p, dtype, true, s), "chunk forward"))) return st;
+      } else if (fused) {
+        // this pair merged into the running result by the forward kernel
+        p.mrg_o = run_o;
+        p.mrg_lse = run_l;
+        p.o = last ? o : (void*)run_o;
+        p.lse = last ? lse : run_l;
+        if ((st = launch_status(miattn::launch_fwd_mfma(p, !last, s), "chunk forward"))) return st;
       } else {
         p.o = part_o;
         p.lse = part_l;
@@ -734,11 +747,24 @@ int attn_bwd_chunked(const void* q, const void* k, const void* v, const void* o,
   float* ak = (float*)scratch.get(nk * 4);
   float* av = (float*)scratch.get(nk * 4);
   if (!dsum || !aq || !ak || !av) return fail(MIATTN_ENOMEM, "hipMallocAsync failed for gradient accumulators");
-  if ((st = launch_status(miattn::launch_fill(aq, nq, 0.f, s), "clear"))) return st;
-  if ((st = launch_status(miattn::launch_fill(ak, nk, 0.f, s), "clear"))) return st;
-  if ((st = launch_status(miattn::launch_fill(av, nk, 0.f, s), "clear"))) return st;
+  // bf16: the matrix-core kernels keep the per-chunk float32 sums themselves
+  // (the first pair of a chunk stores, later ones add, the last one adds and
+  // writes the bf16 result); float32: zeroed accumulators, added into by
+  // every pair, converted at the end
+  const bool fused = dtype == MIATTN_BF16;
+  if (!fused) {
+    if ((st = launch_status(miattn::launch_fill(aq, nq, 0.f, s), "clear"))) return st;
+    if ((st = launch_status(miattn::launch_fill(ak, nk, 0.f, s), "clear"))) return st;
+    if ((st = launch_status(miattn::launch_fill(av, nk, 0.f, s), "clear"))) return st;
+  }
   if ((st = launch_status(miattn::launch_bwd_pre(o, dout, dsum, B, H, N, d, 0, N, dtype, s), "bwd preprocess")))
     return st;
+  // pairs seen so far per query chunk (i + 1 in all) and per key chunk (nchunks - j)
+  std::vector<int> seen_q(nchunks, 0), seen_k(nchunks, 0);
+  auto mode = [](int seen, int total) {
+    return total == 1 ? miattn::ACC_STORE
+                      : seen == 0 ? miattn::ACC_FIRST : seen == total - 1 ? miattn::ACC_LAST : miattn::ACC_ADD;
+  };
   for (const auto& round : balanced_rounds(nchunks)) {
     for (const auto& pr : round) {
       const int i = pr.first, j = pr.second;
@@ -753,12 +779,29 @@ int attn_bwd_chunked(const void* q, const void* k, const void* v, const void* o,
       p.dv = av;
       p.dsum = dsum;
       p.accumulate = 1;
-      if ((st = launch_status(bwd_block(p, dtype, s), "chunk backward"))) return st;
+      if (fused) {
+        p.acc_q = mode(seen_q[i]++, i + 1);
+        p.acc_kv = mode(seen_k[j]++, nchunks - j);
+        p.q_part = aq;
+        p.k_part = ak;
+        p.v_part = av;
+        if (p.acc_q == miattn::ACC_STORE || p.acc_q == miattn::ACC_LAST) p.dq = dq;
+        if (p.acc_kv == miattn::ACC_STORE || p.acc_kv == miattn::ACC_LAST) {
+          p.dk = dk;
+          p.dv = dv;
+        }
+        if ((st = launch_status(miattn::launch_bwd_mfma(p, s), "chunk backward"))) return st;
+      } else {
+        p.acc_q = p.acc_kv = miattn::ACC_ADD;
+        if ((st = launch_status(bwd_block(p, dtype, s), "chunk backward"))) return st;
+      }
     }
   }
-  if ((st = launch_status(miattn::launch_convert(aq, dq, nq, dtype, s), "dq convert"))) return st;
-  if ((st = launch_status(miattn::launch_convert(ak, dk, nk, dtype, s), "dk convert"))) return st;
-  if ((st = launch_status(miattn::launch_convert(av, dv, nk, dtype, s), "dv convert"))) return st;
+  if (!fused) {
+    if ((st = launch_status(miattn::launch_convert(aq, dq, nq, dtype, s), "dq convert"))) return st;
+    if ((st = launch_status(miattn::launch_convert(ak, dk, nk, dtype, s), "dk convert"))) return st;
+    if ((st = launch_status(miattn::launch_convert(av, dv, nk, dtype, s), "dv convert"))) return st;
+  }
   return ok();
 }
 

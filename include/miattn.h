@@ -275,17 +275,23 @@ int attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float
  * so every round carries the same amount of work (the DistFlashAttn reviews
  * page, review 1 point 1 and review 3: redistributing causal work from later
  * to earlier workers). nchunks must be even (or 1) and divide N.
- * Same arguments and outputs as attn_fwd with causal = 1. Scratch: float32
- * partial and running outputs, [B, N, H, d] and [B, H, N] each. */
+ * Same arguments and outputs as attn_fwd with causal = 1. For MIATTN_BF16 the
+ * forward kernel of each pair merges its rows into the query chunk's running
+ * float32 result as it stores them (the last pair writes o and lse); for
+ * MIATTN_F32 each pair's float32 partial is merged by the merge kernel.
+ * Scratch: the float32 running output and LSE, [B, N, H, d] and [B, H, N]
+ * (MIATTN_F32: twice that, for the partials). */
 int attn_fwd_chunked(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int H, int Hkv, int N, int d, float scale,
                      void* stream, int dtype, int nchunks);
 
 /* Backward pass over the same chunk pairs and rounds as attn_fwd_chunked:
  * every pair's gradients are taken with the final o and lse of its query
- * chunk and summed in float32. Same arguments and outputs as attn_bwd with
- * causal = 1 and accumulate = 0. Scratch: float32 dq, dk, dv accumulators
- * and the [B, H, N] rowsum vector. */
+ * chunk and summed in float32 (MIATTN_BF16: the first pair of a chunk stores
+ * its float32 sums, later pairs add to them and the last one adds and writes
+ * the bf16 result; MIATTN_F32: zeroed accumulators, converted at the end).
+ * Same arguments and outputs as attn_bwd with causal = 1 and accumulate = 0.
+ * Scratch: float32 dq, dk, dv sums and the [B, H, N] rowsum vector. */
 int attn_bwd_chunked(const void* q, const void* k, const void* v, const void* o, const float* lse,
                      int B, int H, int Hkv, int N, int d, float scale,
                      void* stream, const void* dout, void* dq, void* dk, void* dv,
