@@ -58,6 +58,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     tmp = OUT + ".tmp"
     _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs, verbose)
     os.replace(tmp, OUT)
+    # host AddressSanitizer build of the C ABI (CPU-only ABI tests)
+    _run(["bash", os.path.join(PKG, "build_asan.sh")], verbose)
     return OUT
 
 
