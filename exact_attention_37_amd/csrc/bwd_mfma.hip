@@ -80,8 +80,13 @@ void bwd_dkdv_kernel(Params p) {
   const int lane = tid & 63;
   const int g = lane >> 5, n = lane & 31;
   const int gkv = blockIdx.x;          // all tiles of one K/V head share an XCD
-  const int kt = blockIdx.y;           // tile 0 has the most causal work: dispatched first
+  int kt = blockIdx.y;                 // tile 0 has the most causal work: dispatched first
   int b = blockIdx.z;
+  if (p.vl_ktiles) {                   // packed batch: (sequence, tile) from the work list
+    if ((int)blockIdx.y >= p.vl_ktiles[0]) return;
+    b = p.vl_ktiles[2 + 2 * blockIdx.y];
+    kt = p.vl_ktiles[3 + 2 * blockIdx.y];
+  }
   const int k0 = kt * DKV_BK;
   if (p.cu_seqlens) {                  // packed batch: z is the sequence
     if (!narrow_to_sequence(p, b, k0)) return;
@@ -526,9 +531,14 @@ void bwd_dq_kernel(Params p) {
   const int lane = tid & 63;
   const int q4 = lane >> 4, i16 = lane & 15;
   const int ntq = gridDim.y;
-  const int qt = CAUSAL ? (ntq - 1 - (int)blockIdx.y) : (int)blockIdx.y;
+  int qt = CAUSAL ? (ntq - 1 - (int)blockIdx.y) : (int)blockIdx.y;
   const int h = xcd_head(blockIdx.x, p.H);
   int b = blockIdx.z;
+  if (p.vl_qtiles) {                   // packed batch: (sequence, tile) from the work list
+    if ((int)blockIdx.y >= p.vl_qtiles[0]) return;
+    b = p.vl_qtiles[2 + 2 * blockIdx.y];
+    qt = p.vl_qtiles[3 + 2 * blockIdx.y];
+  }
   const int kvh = h / p.G;
   const int q0 = qt * BR;
   if (p.cu_seqlens) {                  // packed batch: z is the sequence
@@ -821,7 +831,7 @@ void bwd_dq_kernel(Params p) {
 
 template <int D>
 hipError_t launch_dkdv_d(const Params& p, hipStream_t s) {
-  const dim3 gkv(p.Hkv, (p.Nk + DKV_BK - 1) / DKV_BK, p.B);
+  const dim3 gkv(p.Hkv, p.vl_ktiles ? p.vl_kcap : (p.Nk + DKV_BK - 1) / DKV_BK, p.vl_ktiles ? 1 : p.B);
   if (p.bs_col_tiles && p.causal)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false, true>), gkv, dim3(DKV_NW * 64), 0, s, p);
   else if (p.bs_col_tiles)
@@ -838,7 +848,7 @@ hipError_t launch_dkdv_d(const Params& p, hipStream_t s) {
 template <int D>
 hipError_t launch_dq_d(const Params& p, hipStream_t s) {
   constexpr int NW = 8;
-  const dim3 gq(p.H, (p.Nq + NW * 32 - 1) / (NW * 32), p.B);
+  const dim3 gq(p.H, p.vl_qtiles ? p.vl_qcap : (p.Nq + NW * 32 - 1) / (NW * 32), p.vl_qtiles ? 1 : p.B);
   if (p.bs_row_tiles && p.causal)
     hipLaunchKernelGGL((bwd_dq_kernel<D, true, NW, false, true>), gq, dim3(NW * 64), 0, s, p);
   else if (p.bs_row_tiles)

@@ -61,6 +61,13 @@ struct Params {
   // Packed variable-length batch: sequence z of the grid owns rows
   // [cu_seqlens[z], cu_seqlens[z + 1]) of a B = 1 layout of N rows; null otherwise.
   const int* cu_seqlens;
+  // Packed batch, matrix-core kernels: device-built work lists of (sequence,
+  // tile) entries, [0] = count, entry e at [2 + 2e], [3 + 2e] (query tiles of
+  // the forward / dQ workgroups; key tiles of the dK/dV workgroups), and the
+  // grid extent reserved for them; null otherwise.
+  const int* vl_qtiles;
+  const int* vl_ktiles;
+  int vl_qcap, vl_kcap;
   // Block-sparse attention: one mask entry per block of BS_ROWS query rows x
   // BS_COLS keys, shared by every batch and head; null otherwise.
   const uint8_t* bs_mask;   // [ceil(N / BS_ROWS)][bs_nbc], read by the float32 kernels

@@ -75,9 +75,14 @@ void fwd_mfma_kernel(Params p) {
 
   // ---- workgroup -> (b, h, query tile), heaviest causal tiles first
   const int ntq = gridDim.y;
-  const int qt = CAUSAL ? (ntq - 1 - (int)blockIdx.y) : (int)blockIdx.y;
+  int qt = CAUSAL ? (ntq - 1 - (int)blockIdx.y) : (int)blockIdx.y;
   const int h = xcd_head(blockIdx.x, p.H);
   int b = blockIdx.z;
+  if (p.vl_qtiles) {                              // packed batch: (sequence, tile) from the work list
+    if ((int)blockIdx.y >= p.vl_qtiles[0]) return;
+    b = p.vl_qtiles[2 + 2 * blockIdx.y];
+    qt = p.vl_qtiles[3 + 2 * blockIdx.y];
+  }
   const int kvh = h / p.G;
   const int q0 = qt * BR;                         // first local query row of the tile
   if (p.cu_seqlens) {                             // packed batch: z is the sequence
@@ -428,7 +433,7 @@ void fwd_mfma_kernel(Params p) {
 template <int D, int NW, typename TO>
 hipError_t launch_cfg(const Params& p, hipStream_t s) {
   constexpr int BR = NW * 32;
-  const dim3 grid(p.H, (p.Nq + BR - 1) / BR, p.B);
+  const dim3 grid(p.H, p.vl_qtiles ? p.vl_qcap : (p.Nq + BR - 1) / BR, p.vl_qtiles ? 1 : p.B);
   if (p.bs_row_tiles && p.causal)
     hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, true, TO, false, true>), grid, dim3(NW * 64), 0, s, p);
   else if (p.bs_row_tiles)

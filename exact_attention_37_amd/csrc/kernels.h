@@ -65,4 +65,11 @@ hipError_t launch_fill(float* dst, long long n, float value, hipStream_t s);
 long long bs_list_ints(int N);
 hipError_t launch_bs_lists(const uint8_t* mask, int N, int causal, int* ints, Params& p, hipStream_t s);
 
+// Packed batches: entries reserved for the work list of tiles of `rows`
+// rows (ceil(total / rows) + nseq), and the one-workgroup kernel that fills
+// it from the device offsets (2 + 2 * cap int32 values at `list`).
+int varlen_list_cap(int total, int rows, int nseq);
+hipError_t launch_varlen_tiles(const int* cu_seqlens, int nseq, int total, int rows, int desc, int* list,
+                               hipStream_t s);
+
 }  // namespace miattn

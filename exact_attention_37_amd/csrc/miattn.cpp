@@ -258,6 +258,31 @@ int blocksparse_setup(Params& p, const uint8_t* bmask, int dtype, Scratch& scrat
   return launch_status(miattn::launch_bs_lists(bmask, p.N, p.causal, ints, p, s), "block-sparse tile lists");
 }
 
+// Packed batch, matrix-core kernels: the work lists of (sequence, tile)
+// entries, built on the device from cu_seqlens into scratch: query tiles of
+// the forward / dQ workgroups (256 rows, heaviest causal tile of a sequence
+// first) and, for the backward, key tiles of the dK/dV workgroups (128 keys,
+// first tile first). The grids reserve ceil(total / rows) + nseq entries.
+int varlen_lists(Params& p, Scratch& scratch, bool backward, hipStream_t s) {
+  const int total = p.N, nseq = p.B;
+  const int qcap = miattn::varlen_list_cap(total, 256, nseq);
+  int* ql = (int*)scratch.get((size_t)(2 + 2 * (long long)qcap) * 4);
+  if (!ql) return fail(MIATTN_ENOMEM, "hipMallocAsync failed for the packed-batch work list");
+  int st = launch_status(miattn::launch_varlen_tiles(p.cu_seqlens, nseq, total, 256, 1, ql, s), "work list");
+  if (st) return st;
+  p.vl_qtiles = ql;
+  p.vl_qcap = qcap;
+  if (!backward) return MIATTN_OK;
+  const int kcap = miattn::varlen_list_cap(total, 128, nseq);
+  int* kl = (int*)scratch.get((size_t)(2 + 2 * (long long)kcap) * 4);
+  if (!kl) return fail(MIATTN_ENOMEM, "hipMallocAsync failed for the packed-batch work list");
+  if ((st = launch_status(miattn::launch_varlen_tiles(p.cu_seqlens, nseq, total, 128, 0, kl, s), "work list")))
+    return st;
+  p.vl_ktiles = kl;
+  p.vl_kcap = kcap;
+  return MIATTN_OK;
+}
+
 long long bmask_bytes(int N) {
   return (long long)((N + miattn::BS_ROWS - 1) / miattn::BS_ROWS) * ((N + miattn::BS_COLS - 1) / miattn::BS_COLS);
 }
@@ -324,8 +349,10 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
   p.Nq = p.Nk = max_len;       // grid extent; each workgroup narrows to its sequence
   p.window = window;
   p.cu_seqlens = cu_seqlens;
-  if ((st = launch_status(fwd_block(p, dtype, dtype == MIATTN_F32, (hipStream_t)stream), "attn_fwd_varlen")))
-    return st;
+  hipStream_t s = (hipStream_t)stream;
+  Scratch scratch(s);
+  if (dtype == MIATTN_BF16 && (st = varlen_lists(p, scratch, false, s))) return st;
+  if ((st = launch_status(fwd_block(p, dtype, dtype == MIATTN_F32, s), "attn_fwd_varlen"))) return st;
   return ok();
 }
 
@@ -373,6 +400,7 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
   p.dsum = dsum;
   p.accumulate = accumulate;
   p.acc_q = p.acc_kv = accumulate;
+  if (dtype == MIATTN_BF16 && (st = varlen_lists(p, scratch, true, s))) return st;
   // rowsum(dout * o) is per token: the packed rows as one sequence
   if ((st = launch_status(miattn::launch_bwd_pre(o, dout, dsum, 1, H, total, d, 0, total, dtype, s),
                           "bwd preprocess")))

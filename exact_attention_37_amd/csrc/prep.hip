@@ -171,6 +171,49 @@ __global__ __launch_bounds__(64) void bs_lists_kernel(const uint8_t* __restrict_
   }
 }
 
+// Work list of a packed variable-length batch: every sequence s (rows
+// [cu[s], cu[s+1]) clamped to [0, N], as in narrow_to_sequence) contributes
+// ceil(length / rows) tiles, sequences in order and within a sequence from
+// the last tile down (desc) or from tile 0 up. Entry e is (list[2 + 2e],
+// list[3 + 2e]) = (sequence, tile); list[0] is the number of entries. At
+// most cap entries are written (malformed offsets can ask for more).
+__global__ __launch_bounds__(1024) void varlen_tiles_kernel(const int* __restrict__ cu, int nseq, int N, int rows,
+                                                           int desc, int cap, int* __restrict__ list) {
+  __shared__ int wsum[16];
+  __shared__ int base;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) base = 0;
+  __syncthreads();
+  for (int s0 = 0; s0 < nseq; s0 += 1024) {
+    const int sq = s0 + tid;
+    int nt = 0;
+    if (sq < nseq) {
+      const int e = min(max(cu[sq + 1], 0), N);
+      const int a = min(max(cu[sq], 0), e);
+      nt = (e - a + rows - 1) / rows;
+    }
+    int x = nt;                                  // inclusive scan over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    int wofs = 0;
+    for (int w = 0; w < wave; ++w) wofs += wsum[w];
+    const int off = base + wofs + x - nt;        // exclusive offset of this sequence
+    for (int k = 0; k < nt && off + k < cap; ++k) {
+      list[2 + 2 * (off + k)] = sq;
+      list[3 + 2 * (off + k)] = desc ? nt - 1 - k : k;
+    }
+    __syncthreads();
+    if (tid == 1023) base = off + nt;
+    __syncthreads();
+  }
+  if (tid == 0) list[0] = min(base, cap);
+}
+
 inline unsigned blocks_for(long long threads) { return (unsigned)((threads + 255) / 256); }
 
 template <typename TA, typename TB, typename TO>
@@ -253,6 +296,15 @@ hipError_t launch_bs_lists(const uint8_t* mask, int N, int causal, int* ints, Pa
   p.bs_ld = ld;
   hipLaunchKernelGGL(bs_lists_kernel, dim3(nbr + nbc), dim3(64), 0, s, mask, N, causal, nbr, nbc, ld, row_cnt,
                      row_plain, row_tiles, col_cnt, col_tiles);
+  return hipGetLastError();
+}
+
+int varlen_list_cap(int total, int rows, int nseq) { return (total + rows - 1) / rows + nseq; }
+
+hipError_t launch_varlen_tiles(const int* cu_seqlens, int nseq, int total, int rows, int desc, int* list,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(varlen_tiles_kernel, dim3(1), dim3(1024), 0, s, cu_seqlens, nseq, total, rows, desc,
+                     varlen_list_cap(total, rows, nseq), list);
   return hipGetLastError();
 }
 
