@@ -65,8 +65,13 @@ struct DkdvSmem {
   Buf buf[3];
 };
 
+// Waves per SIMD of the dK/dV kernel: its K/V operands and dK/dV
+// accumulators fill one wave's registers at d = 128; at d = 64 they fit
+// twice, and two workgroups share a CU.
+template <int D> constexpr int dkdv_waves() { return D == 64 ? 2 : 1; }
+
 template <int D, bool CAUSAL, bool WIN = false, bool SPARSE = false>
-__global__ __launch_bounds__(DKV_NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(DKV_NW * 64) __attribute__((amdgpu_waves_per_eu(dkdv_waves<D>(), dkdv_waves<D>())))
 void bwd_dkdv_kernel(Params p) {
   constexpr int KS = D / 16, DB = D / 32;
   constexpr int ROW = DkdvSmem<D>::ROW, TILE = DkdvSmem<D>::TILE;
@@ -350,7 +355,9 @@ void bwd_dkdv_kernel(Params p) {
       const uint32_t bt[2] = {lds_opaque(cq + 2 * rd_t[0]), lds_opaque(cq + 2 * rd_t[1])};
       const uint32_t btp[2] = {lds_opaque(pq + 2 * rd_t[0]), lds_opaque(pq + 2 * rd_t[1])};
       const uint32_t stb = lds_opaque(stat_lane + cb * (2 * DKV_BQ * 4));
-      const f32x16 di0 = dinit_read(stb, 0), di1 = dinit_read(stb, 1);
+      // -D of half 0 now; that of half 1 two steps before its first product
+      const f32x16 di0 = dinit_read(stb, 0);
+      f32x16 di1;
 
       lockstep_products<4 * PL, 4>(
           [&](auto ic) {
@@ -408,6 +415,7 @@ void bwd_dkdv_kernel(Params p) {
               }(std::make_integer_sequence<int, hi - lo>{});
               if constexpr (j == PL - 1) stat_load(h_ld, q0_nx);
             }
+            if constexpr (ph == 1 && j == PL - 2) di1 = dinit_read(stb, 1);
             if constexpr (ph == 3 && j == PL - 1) stat_store(nb);
             // diagonal tiles: mask each half's scores once its products are done
             if constexpr ((ph == 0 || ph == 2) && j == PL - 1) {
@@ -514,7 +522,7 @@ struct DqSmem {
 __device__ __forceinline__ int swz_s4(int row) { return (row >> 2) & 3; }
 
 template <int D, bool CAUSAL, int NW, bool WIN = false, bool SPARSE = false>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(Params p) {
   constexpr int BR = NW * 32;
   constexpr int KS = D / 32;          // 32-wide k-steps of S^T = K Q^T and dP^T = V dO^T
@@ -847,13 +855,17 @@ hipError_t launch_dkdv_d(const Params& p, hipStream_t s) {
 
 template <int D>
 hipError_t launch_dq_d(const Params& p, hipStream_t s) {
-  constexpr int NW = 8;
+  if (p.bs_row_tiles) {   // one 256-row block row of the mask per workgroup
+    const dim3 gq(p.H, (p.Nq + BS_ROWS - 1) / BS_ROWS, p.B);
+    if (p.causal)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, true, 8, false, true>), gq, dim3(8 * 64), 0, s, p);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, false, 8, false, true>), gq, dim3(8 * 64), 0, s, p);
+    return hipGetLastError();
+  }
+  constexpr int NW = query_waves(D);
   const dim3 gq(p.H, p.vl_qtiles ? p.vl_qcap : (p.Nq + NW * 32 - 1) / (NW * 32), p.vl_qtiles ? 1 : p.B);
-  if (p.bs_row_tiles && p.causal)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, true, NW, false, true>), gq, dim3(NW * 64), 0, s, p);
-  else if (p.bs_row_tiles)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, false, NW, false, true>), gq, dim3(NW * 64), 0, s, p);
-  else if (p.causal && p.window > 0)
+  if (p.causal && p.window > 0)
     hipLaunchKernelGGL((bwd_dq_kernel<D, true, NW, true>), gq, dim3(NW * 64), 0, s, p);
   else if (p.causal)
     hipLaunchKernelGGL((bwd_dq_kernel<D, true, NW>), gq, dim3(NW * 64), 0, s, p);

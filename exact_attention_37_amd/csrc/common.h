@@ -85,6 +85,13 @@ struct Params {
 constexpr int BS_ROWS = 256, BS_COLS = 128, BS_TILE = 64;
 constexpr int ACC_STORE = 0, ACC_ADD = 1, ACC_FIRST = 2, ACC_LAST = 3;
 
+// Waves (32 query rows each) of the forward and dQ matrix-core workgroups:
+// 8 at d = 128 (one workgroup per CU, two waves per SIMD); 4 at d = 64,
+// where two workgroups share a CU so that one's prologue and epilogue
+// overlap the other's products. Packed-batch work lists use the same rows.
+constexpr int query_waves(int d) { return d == 64 ? 4 : 8; }
+constexpr int query_tile_rows(int d) { return 32 * query_waves(d); }
+
 // For a packed variable-length batch, narrows p to sequence s (rows
 // [cu_seqlens[s], cu_seqlens[s + 1]) of the single B = 1 layout; the offsets
 // are clamped to [0, N] so malformed ones cannot move any access out of the

@@ -53,7 +53,7 @@ struct FwdSmem {
 };
 
 template <int D, int NW, bool CAUSAL, typename TO, bool WIN = false, bool SPARSE = false>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_mfma_kernel(Params p) {
   // rows that can still have seen no key mid-loop (sliding window,
   // block-sparse), or none at all (block-sparse)
@@ -430,15 +430,21 @@ void fwd_mfma_kernel(Params p) {
   }
 }
 
+// NW waves per workgroup (32 query rows each); the block-sparse kernels
+// cover one 256-row block row of the mask per workgroup (8 waves)
 template <int D, int NW, typename TO>
 hipError_t launch_cfg(const Params& p, hipStream_t s) {
+  if (p.bs_row_tiles) {
+    const dim3 grid(p.H, (p.Nq + BS_ROWS - 1) / BS_ROWS, p.B);
+    if (p.causal)
+      hipLaunchKernelGGL((fwd_mfma_kernel<D, 8, true, TO, false, true>), grid, dim3(8 * 64), 0, s, p);
+    else
+      hipLaunchKernelGGL((fwd_mfma_kernel<D, 8, false, TO, false, true>), grid, dim3(8 * 64), 0, s, p);
+    return hipGetLastError();
+  }
   constexpr int BR = NW * 32;
   const dim3 grid(p.H, p.vl_qtiles ? p.vl_qcap : (p.Nq + BR - 1) / BR, p.vl_qtiles ? 1 : p.B);
-  if (p.bs_row_tiles && p.causal)
-    hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, true, TO, false, true>), grid, dim3(NW * 64), 0, s, p);
-  else if (p.bs_row_tiles)
-    hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, false, TO, false, true>), grid, dim3(NW * 64), 0, s, p);
-  else if (p.causal && p.window > 0)
+  if (p.causal && p.window > 0)
     hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, true, TO, true>), grid, dim3(NW * 64), 0, s, p);
   else if (p.causal)
     hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, true, TO>), grid, dim3(NW * 64), 0, s, p);
@@ -450,8 +456,9 @@ hipError_t launch_cfg(const Params& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd_mfma(const Params& p, bool out_f32, hipStream_t s) {
-  if (p.d == 128) return out_f32 ? launch_cfg<128, 8, float>(p, s) : launch_cfg<128, 8, bf16>(p, s);
-  return out_f32 ? launch_cfg<64, 8, float>(p, s) : launch_cfg<64, 8, bf16>(p, s);
+  constexpr int W128 = query_waves(128), W64 = query_waves(64);
+  if (p.d == 128) return out_f32 ? launch_cfg<128, W128, float>(p, s) : launch_cfg<128, W128, bf16>(p, s);
+  return out_f32 ? launch_cfg<64, W64, float>(p, s) : launch_cfg<64, W64, bf16>(p, s);
 }
 
 }  // namespace miattn

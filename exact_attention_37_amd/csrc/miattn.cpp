@@ -260,15 +260,16 @@ int blocksparse_setup(Params& p, const uint8_t* bmask, int dtype, Scratch& scrat
 
 // Packed batch, matrix-core kernels: the work lists of (sequence, tile)
 // entries, built on the device from cu_seqlens into scratch: query tiles of
-// the forward / dQ workgroups (256 rows, heaviest causal tile of a sequence
-// first) and, for the backward, key tiles of the dK/dV workgroups (128 keys,
-// first tile first). The grids reserve ceil(total / rows) + nseq entries.
+// the forward / dQ workgroups (query_tile_rows(d) rows, heaviest causal tile
+// of a sequence first) and, for the backward, key tiles of the dK/dV
+// workgroups (128 keys, first tile first). The grids reserve
+// ceil(total / rows) + nseq entries.
 int varlen_lists(Params& p, Scratch& scratch, bool backward, hipStream_t s) {
-  const int total = p.N, nseq = p.B;
-  const int qcap = miattn::varlen_list_cap(total, 256, nseq);
+  const int total = p.N, nseq = p.B, qrows = miattn::query_tile_rows(p.d);
+  const int qcap = miattn::varlen_list_cap(total, qrows, nseq);
   int* ql = (int*)scratch.get((size_t)(2 + 2 * (long long)qcap) * 4);
   if (!ql) return fail(MIATTN_ENOMEM, "hipMallocAsync failed for the packed-batch work list");
-  int st = launch_status(miattn::launch_varlen_tiles(p.cu_seqlens, nseq, total, 256, 1, ql, s), "work list");
+  int st = launch_status(miattn::launch_varlen_tiles(p.cu_seqlens, nseq, total, qrows, 1, ql, s), "work list");
   if (st) return st;
   p.vl_qtiles = ql;
   p.vl_qcap = qcap;
