@@ -700,9 +700,16 @@ void bwd_dq_kernel(Params p) {
     }
     const bf16* kt = sm.k[buf];
     const bf16* vt = sm.v[buf];
-    f32x4 s[4][2], dp[4][2];   // [key block mb][query block nb]
+    // [key block mb][query block nb]; the dP^T products accumulate onto -D
+    // of their query (every register of a lane holds the same query), so
+    // they leave dP - D
+    f32x4 s[4][2], dp[4][2];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) s[mb][0] = s[mb][1] = dp[mb][0] = dp[mb][1] = f32x4{};
+    for (int mb = 0; mb < 4; ++mb) {
+      s[mb][0] = s[mb][1] = f32x4{};
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) dp[mb][nb] = f32x4{-dsum[nb], -dsum[nb], -dsum[nb], -dsum[nb]};
+    }
     bf16x8 dsb[2][2];          // dS^T as the B operand: [key chunk kc][query block nb]
 
     // dS for key chunk kc, slice w of 8 (query block w / 4, register pair
@@ -720,7 +727,7 @@ void bwd_dq_kernel(Params p) {
           const int kin = 32 * kc + q4 + 4 * e;
           pv = (kin > thr[nb] || (WIN && kin < lo[nb])) ? 0.f : x;
         }
-        dsb[kc][nb][e] = (bf16)(pv * (dp[mb][nb][r] - dsum[nb]));
+        dsb[kc][nb][e] = (bf16)(pv * dp[mb][nb][r]);
       }
     };
 
