@@ -184,11 +184,13 @@ void bwd_dkdv_kernel(Params p) {
   };
   float st;          // LSE (tid < 64) or D (64 <= tid < 128) of row q0 + tid % 64
   bool st_valid;
+  // LSE (tid < 64) or D (64 <= tid < 128) of batch entry b from row q_start
+  // on; a row is h * N + row past it (32-bit: B * H * N < 2^31)
+  const float* st_base = ((tid & 64) ? p.dsum : p.lse) + (long long)b * p.H * p.N + p.q_start;
   auto stat_load = [&](int h, int q0) {
     const int row = q0 + (tid & 63);
     st_valid = row < p.Nq;
-    const long long si = ((long long)b * p.H + h) * p.N + p.q_start + min(row, p.Nq - 1);
-    st = ((tid & 64) ? p.dsum : p.lse)[si];
+    st = st_base[h * p.N + min(row, p.Nq - 1)];
   };
   auto stat_store = [&](int buf) {
     if (tid < 128) {
@@ -330,9 +332,10 @@ void bwd_dkdv_kernel(Params p) {
   // code at all (a mask test inside one loop body is turned into
   // per-element selects that every tile pays for).
   int kt_ = 0;
+  int cb = 0;                          // LDS buffer of tile k (k % 3, kept incrementally)
   auto iteration = [&](auto mc) {
     constexpr bool MASKED = decltype(mc)::value;
-      const int cb = kt_ % 3, pb = (kt_ + 2) % 3, nb = (kt_ + 1) % 3;
+      const int pb = cb == 0 ? 2 : cb - 1, nb = cb == 2 ? 0 : cb + 1;
       const bool real = kt_ < niter;
       const int q0 = SPARSE ? q0_cur : (real ? (first + t_cur) * DKV_BQ : empty_q0);
       // the tile after this one
@@ -428,6 +431,7 @@ void bwd_dkdv_kernel(Params p) {
     t_cur = t_nx;
     q0_cur = q0_nx;
     ++kt_;
+    cb = cb == 2 ? 0 : cb + 1;
   };
   // The masked tiles of a head: a prefix whose rows start before this
   // wave's last key (the diagonal) and, under a sliding window, a suffix
