@@ -175,12 +175,16 @@ void bwd_dkdv_kernel(Params p) {
   }
   const uint32_t qbytes = (uint32_t)(p.Nq * qrs * 2);
   const u32x4 rq = rsrc_words(Qb, qbytes), ro = rsrc_words(Ob, qbytes);
+  // LDS byte address of buffer 0's Q tile, converted from the generic
+  // pointer once (buffers follow at sizeof(Buf), dO at + 2 TILE in each)
+  const uint32_t lds_q0 = lds_addr(sm.buf[0].q);
+  constexpr uint32_t BUF_BYTES = (uint32_t)sizeof(typename DkdvSmem<D>::Buf);
   auto load_piece = [&](int piece, int buf, int h, int q0) {   // piece < 2 NL: Q then dO
     const int i = piece % NL;
     const bool is_o = piece >= NL;
     const uint32_t soff = (uint32_t)(q0 * qrs + h * D) * 2u;
     buffer_load_lds16_async(is_o ? ro : rq, loff[i], soff,
-                            lds_addr((is_o ? sm.buf[buf].o : sm.buf[buf].q) + (wave * NL + i) * 512));
+                            lds_q0 + buf * BUF_BYTES + (is_o ? 2u * TILE : 0u) + (uint32_t)(wave * NL + i) * 1024u);
   };
   float st;          // LSE (tid < 64) or D (64 <= tid < 128) of row q0 + tid % 64
   bool st_valid;
@@ -352,8 +356,8 @@ void bwd_dkdv_kernel(Params p) {
       const int h_ld = nx_real ? h_nx : gkv * p.G;   // a valid head also for the empty tile
       const int mthr = kpos - (p.q_start + q0);     // query index inside the tile < mthr -> masked
       // LDS read bases of this iteration (byte addresses; dO at +TILE from Q)
-      const uint32_t cq = lds_addr(sm.buf[0].q) + cb * (uint32_t)sizeof(typename DkdvSmem<D>::Buf);
-      const uint32_t pq = lds_addr(sm.buf[0].q) + pb * (uint32_t)sizeof(typename DkdvSmem<D>::Buf);
+      const uint32_t cq = lds_q0 + cb * BUF_BYTES;
+      const uint32_t pq = lds_q0 + pb * BUF_BYTES;
       const uint32_t bs[2] = {lds_opaque(cq + 2 * rd_s[0]), lds_opaque(cq + 2 * rd_s[1])};
       const uint32_t bt[2] = {lds_opaque(cq + 2 * rd_t[0]), lds_opaque(cq + 2 * rd_t[1])};
       const uint32_t btp[2] = {lds_opaque(pq + 2 * rd_t[0]), lds_opaque(pq + 2 * rd_t[1])};
@@ -424,7 +428,8 @@ void bwd_dkdv_kernel(Params p) {
             if constexpr ((ph == 0 || ph == 2) && j == PL - 1) {
               if constexpr (MASKED) mask_half(ph == 0 ? s0 : s1, mthr - (ph / 2) * 32);
             }
-          });
+          },
+          std::true_type{});
       wait_global_loads();
       __syncthreads();
     h_cur = h_nx;

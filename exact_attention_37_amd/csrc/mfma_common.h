@@ -244,25 +244,31 @@ __device__ __forceinline__ void products_pattern() {
 // matrix cores are busy, also with a single wave per SIMD. The steps are
 // expanded at compile time: rd, mm and ex receive std::integral_constant
 // step indices, so every per-step decision is resolved by `if constexpr`.
-template <int I, int N, int R, class RD, class MM, class EX>
+//
+// PAIRED: at even steps the product also waits for the next step's operand
+// (an empty asm statement that reads it). LDS reads complete in order, so
+// one wait then covers two products and the odd steps issue none: half the
+// s_waitcnt instructions, for kernels whose issue slots are the limit.
+template <int I, int N, int R, bool PAIRED, class RD, class MM, class EX>
 __device__ __forceinline__ void lockstep_step(bf16x8 (&ring)[R], RD& rd, MM& mm, EX& ex) {
   if constexpr (I < N) {
     const bf16x8 a = ring[I % R];
+    if constexpr (PAIRED && I % 2 == 0 && I + 1 < N) asm volatile("" ::"v"(ring[(I + 1) % R]));
     if constexpr (I + R < N) ring[I % R] = rd(std::integral_constant<int, I + R>{});
     mm(std::integral_constant<int, I>{}, a);
     ex(std::integral_constant<int, I>{});
     __builtin_amdgcn_sched_barrier(0);
-    lockstep_step<I + 1, N, R>(ring, rd, mm, ex);
+    lockstep_step<I + 1, N, R, PAIRED>(ring, rd, mm, ex);
   }
 }
 
-template <int N, int R, class RD, class MM, class EX>
-__device__ __forceinline__ void lockstep_products(RD rd, MM mm, EX ex) {
+template <int N, int R, class RD, class MM, class EX, bool PAIRED = false>
+__device__ __forceinline__ void lockstep_products(RD rd, MM mm, EX ex, std::bool_constant<PAIRED> = {}) {
   bf16x8 ring[R];
   [&]<int... Is>(std::integer_sequence<int, Is...>) {
     ((ring[Is] = rd(std::integral_constant<int, Is>{})), ...);
   }(std::make_integer_sequence<int, R>{});
-  lockstep_step<0, N, R>(ring, rd, mm, ex);
+  lockstep_step<0, N, R, PAIRED>(ring, rd, mm, ex);
 }
 
 // Workgroup x index -> head index, so that with H % 8 == 0 all heads that
