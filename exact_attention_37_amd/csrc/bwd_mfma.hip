@@ -790,7 +790,8 @@ void bwd_dq_kernel(Params p) {
               (ds_sub(std::integral_constant<int, 1>{}, std::integral_constant<int, lo_ + Ws>{}), ...);
             }(std::make_integer_sequence<int, hi_ - lo_>{});
           }
-        });
+        },
+        std::true_type{});
     wait_global_loads();
     __syncthreads();
   };

@@ -227,7 +227,7 @@ void fwd_mfma_kernel(Params p) {
           constexpr int i = decltype(ic)::value, kb = i % 2, ks = i / 2;
           sx[kb] = mfma32(a, qf[ks], sx[kb]);
         },
-        ex);
+        ex, std::true_type{});
   };
   // ---- mask of one tile's scores: key index inside the tile > thr (causal
   // diagonal, ragged end) or, under a sliding window, < lo (before the row's window)
@@ -361,7 +361,8 @@ void fwd_mfma_kernel(Params p) {
         },
         [&](auto ic) {
           if (has_next) max_slice(sn, ic, std::integral_constant<int, 4 * DB>{});
-        });
+        },
+        std::true_type{});
     if (has_next) raise_max();
     t1 = t2;
     t2 = t3;
