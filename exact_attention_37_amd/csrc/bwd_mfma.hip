@@ -508,12 +508,12 @@ void bwd_dkdv_kernel(Params p) {
 
 constexpr int DQ_BC = 64;   // keys per tile
 
-// K and V tiles (64 keys), row-major; rows padded to D + 32 elements with
-// the low two bits of the 16-byte chunk index XORed by swz_s4(row) (below).
-// Both tiles are written by direct global -> LDS loads.
+// K and V tiles (64 keys), row-major; rows padded to D + 32 (d = 128) or
+// D + 16 (d = 64) elements, the 16-byte chunk index XORed by swz_dq<D>(row)
+// (below). Both tiles are written by direct global -> LDS loads.
 template <int D>
 struct DqSmem {
-  static constexpr int ROW = D + 32;
+  static constexpr int ROW = D == 64 ? D + 16 : D + 32;
   static constexpr int TILE = DQ_BC * ROW;
   bf16 k[2][TILE];
   bf16 v[2][TILE];
@@ -523,12 +523,29 @@ struct DqSmem {
 // 16-key block mb is tile row q + 4 r + 16 (mb % 2) (+ 32 per 32-key chunk),
 // so the accumulators of blocks 2c and 2c + 1 give lane group q the keys
 // 32 c + q + 4 e, e = 0..7, in register order; the K^T operand of the dQ
-// product is read with the same key order. With the chunk swizzle
-// (row / 4) % 4 the row reads of S^T = K Q^T and dP^T = V dO^T have no bank
-// conflicts and the transposing reads of K^T have half as many as the row
-// reads of a key order with 8 consecutive keys per lane group (measured
-// with the SQ_LDS_BANK_CONFLICT counter on the device).
-__device__ __forceinline__ int swz_s4(int row) { return (row >> 2) & 3; }
+// product is read with the same key order.
+//
+// LDS has 64 banks of 4 bytes. An 8-byte read (plain or transposing) is
+// served 32 lanes at a time (lanes 0-31, then 32-63); a 16-byte read 16
+// lanes at a time: within each half-wave, the lane quads (lane / 4) % 8
+// whose three index bits have even parity, then those with odd parity
+// (measured on the device with SQ_LDS_BANK_CONFLICT, two lanes on one bank
+// at a time). The row reads of S^T = K Q^T and dP^T = V dO^T touch rows
+// 0..15 (+16 k) with one logical chunk; a transposing read of K^T touches,
+// per 32 lanes, rows q + 4 m (q = two neighbours, m = 0..3) with one 32-byte
+// chunk pair each. With the row strides above, rows 4 apart start on the
+// same bank, so the swizzle has to spread those rows over different chunk
+// pairs while keeping the rows of each 16-byte phase on different chunk
+// columns. It depends on bits 2 and 3 of the row only (so every row a lane
+// reads shares it) and sets at most one chunk-index bit above bit 1: the top
+// bit of the row's chunks (bit 3 for d = 128, bit 2 for d = 64). Both read
+// patterns are then free of bank conflicts (exhaustive check of all
+// swizzles linear in the row's low bits against the rules above).
+template <int D>
+__device__ __forceinline__ int swz_dq(int row) {
+  if constexpr (D == 128) return (((row >> 2) & 1) * 2) ^ (((row >> 3) & 1) * 8);
+  else return ((row >> 3) & 1) * 4;
+}
 
 template <int D, bool CAUSAL, int NW, bool WIN = false, bool SPARSE = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -538,8 +555,8 @@ void bwd_dq_kernel(Params p) {
   constexpr int DM = D / 16;          // 16-row blocks of dQ^T
   constexpr int ROW = DqSmem<D>::ROW, TILE = DqSmem<D>::TILE;
   constexpr int TILES_KB = 2 * TILE * 2 / 1024;     // K and V, in 1 KB direct loads
-  static_assert(TILES_KB % NW == 0, "tile loads split evenly over the waves");
-  constexpr int NL = TILES_KB / NW;                // per wave
+  static_assert(TILE * 2 % 1024 == 0, "whole 1 KB pieces");
+  constexpr int NL = (TILES_KB + NW - 1) / NW;     // per wave (the last waves may have fewer)
   constexpr int TILE_KB = TILES_KB / 2;
   __shared__ __attribute__((aligned(16))) DqSmem<D> sm;
 
@@ -609,16 +626,17 @@ void bwd_dq_kernel(Params p) {
   const int wq_first = p.q_start + wq0;
 
   // Direct loads: 1 KB piece s = wave*NL + i of the two tiles (K: s < TILE_KB,
-  // then V) covers tile bytes [(s % TILE_KB) KB, +1 KB); lane l fills 16 bytes
-  // at 16 l: tile row r, physical chunk pch holding logical chunk
-  // pch ^ swz_s4(r) (padding chunks from chunk 0), read from byte
-  // loff[i] = 2 (r * row stride + 8 * logical chunk) past the tile's first key.
+  // then V; pieces s >= TILES_KB do not exist) covers tile bytes
+  // [(s % TILE_KB) KB, +1 KB); lane l fills 16 bytes at 16 l: tile row r,
+  // physical chunk pch holding logical chunk pch ^ swz_dq(r) (padding chunks
+  // from chunk 0), read from byte loff[i] = 2 (r * row stride + 8 * logical
+  // chunk) past the tile's first key.
   uint32_t loff[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int off = ((wave * NL + i) % TILE_KB) * 1024 + 16 * lane;
     const int r_ = off / (ROW * 2), pch = (off % (ROW * 2)) / 16;
-    const int col = pch < D / 8 ? ((pch ^ swz_s4(r_)) << 3) : 0;
+    const int col = pch < D / 8 ? ((pch ^ swz_dq<D>(r_)) << 3) : 0;
     loff[i] = (uint32_t)(r_ * krs + col) * 2u;
   }
   // keys past the last one read as zeros (buffer range check); the mask drops them
@@ -626,30 +644,43 @@ void bwd_dq_kernel(Params p) {
   const u32x4 rk = rsrc_words(K, kbytes), rv = rsrc_words(V, kbytes);
   auto load_piece = [&](int i, int buf, int j0) {
     const int sl = wave * NL + i;                  // wave-uniform
+    if (TILES_KB % NW != 0 && sl >= TILES_KB) return;
     const bool is_v = sl >= TILE_KB;
     buffer_load_lds16_async(is_v ? rv : rk, loff[i], (uint32_t)(j0 * krs) * 2u,
                             lds_addr((is_v ? sm.v[buf] : sm.k[buf]) + (sl % TILE_KB) * 512));
   };
 
-  // per-lane LDS read offsets (elements). K / V fragment (key block mb,
-  // k-step ks): row i16 / 4 + 4 (i16 % 4) + 16 (mb % 2) + 32 (mb / 2),
-  // logical chunk 4 ks + q4 -> physical 4 ks + (q4 ^ swz_s4(row)) (swz_s4
-  // depends on neither mb nor the 32-key chunk). K^T fragment (d block md,
-  // key chunk kc), read rd: lane j of 16-lane group q4 addresses key row
-  // 32 kc + q4 + 16 rd + 4 (j/4), columns 16 md + 4 (j%4); element 4 rd + t
-  // of the result is key 32 kc + q4 + 4 (4 rd + t), the order of dS^T. The
-  // swizzle touches bit 0 of md, hence one offset per md parity.
+  // per-lane LDS read offsets (elements). Every row a lane reads has the
+  // same bits 2 and 3, hence one swizzle per lane: its bits 0-1 (slo) move
+  // the chunk within its group of 4, its higher part (if any) flips the top
+  // bit of the group index (the group index ^ (half its range)).
+  // K / V fragment (key block mb, k-step ks): row i16 / 4 + 4 (i16 % 4) +
+  // 16 (mb % 2) + 32 (mb / 2), logical chunk 4 ks + q4 -> physical
+  // 4 (ks ^ flip) + (q4 ^ slo): base rd_k[0] for the first KS / 2 k-steps,
+  // rd_k[1] for the rest. K^T fragment (d block md, key chunk kc), read rd:
+  // lane j of 16-lane group q4 addresses key row 32 kc + q4 + 16 rd + 4 (j/4),
+  // logical columns 16 md + 4 (j%4); element 4 rd + t of the result is key
+  // 32 kc + q4 + 4 (4 rd + t), the order of dS^T. Its chunk 2 md + (j%4)/2 =
+  // 4 (md / 2) + (2 (md % 2) + (j%4)/2) -> base rd_t[md % 2][(md / 2) / (DM / 4)].
   const int krow0 = (i16 >> 2) + 4 * (i16 & 3);
-  const int rd_k = krow0 * ROW + 8 * (q4 ^ swz_s4(krow0));
+  int rd_k[2];
+  {
+    const int sk = swz_dq<D>(krow0), slo = sk & 3, flip = sk >> 2 ? KS / 2 : 0;
+    const int base = krow0 * ROW + 8 * (q4 ^ slo);
+    rd_k[0] = base + 32 * flip;
+    rd_k[1] = base + 32 * (KS / 2 - flip);
+  }
   int rd_t[2][2];
+  {
+    const int r_ = q4 + 4 * (i16 >> 2);
+    const int st = swz_dq<D>(r_), slo = st & 3, flip = st >> 2 ? DM / 4 : 0;
 #pragma unroll
-  for (int mp = 0; mp < 2; ++mp)
-#pragma unroll
-    for (int rd = 0; rd < 2; ++rd) {
-      const int r_ = q4 + 16 * rd + 4 * (i16 >> 2);
-      const int lc = 2 * mp + ((i16 & 3) >> 1);
-      rd_t[mp][rd] = r_ * ROW + 8 * (lc ^ swz_s4(r_)) + 4 * (i16 & 1);
+    for (int mp = 0; mp < 2; ++mp) {
+      const int base = r_ * ROW + 8 * ((2 * mp + ((i16 & 3) >> 1)) ^ slo) + 4 * (i16 & 1);
+      rd_t[mp][0] = base + 32 * flip;
+      rd_t[mp][1] = base + 32 * (DM / 4 - flip);
     }
+  }
 
   f32x4 acc[DM][2];   // dQ^T: [16-row d block][query block]
 #pragma unroll
@@ -745,13 +776,14 @@ void bwd_dq_kernel(Params p) {
           constexpr int i = decltype(ic)::value;
           if constexpr (i < 2 * PS) {            // S^T / dP^T: (mb, ks, which)
             constexpr int mb = i / (2 * KS), jj = i % (2 * KS), ks = jj >> 1;
-            constexpr int moff = (32 * (mb >> 1) + 16 * (mb & 1)) * ROW + 32 * ks;
-            return lds_read16((jj & 1) ? vt : kt, rd_k + moff);
+            constexpr int moff = (32 * (mb >> 1) + 16 * (mb & 1)) * ROW + 32 * (ks % (KS / 2));
+            return lds_read16((jj & 1) ? vt : kt, rd_k[ks / (KS / 2)] + moff);
           } else {                                // dQ^T: (kc, md)
             constexpr int ii = i - 2 * PS, kc = ii / DM, md = ii % DM;
-            constexpr int off = 32 * kc * ROW + 32 * (md >> 1);
-            const bf16x4 r0 = lds_read_tr4(kt + rd_t[md & 1][0] + off);
-            const bf16x4 r1 = lds_read_tr4(kt + rd_t[md & 1][1] + off);
+            constexpr int hh = (md >> 1) / (DM / 4);
+            constexpr int off = 32 * kc * ROW + 32 * ((md >> 1) % (DM / 4));
+            const bf16x4 r0 = lds_read_tr4(kt + rd_t[md & 1][hh] + off);
+            const bf16x4 r1 = lds_read_tr4(kt + rd_t[md & 1][hh] + off + 16 * ROW);
             return bf16x8{r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
           }
         },
