@@ -30,7 +30,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 # rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; calibrated against a plain
 # 1 GiB device copy in the same process), valid only for the kernel sources
 # whose SHA-1 is recorded with it (profiles/llama16k_causal_bf16_traffic.md).
-DKDV_TRAFFIC = {"sources_sha1": "6fe3998e62202ed0045565930a90cc049fe8dbc8", "bytes": 2849653404}   # fetch 2.581 GB + write 0.268 GB
+DKDV_TRAFFIC = {"sources_sha1": "7b44e3def9c3d90bdf96c8cc6ecfdefec7ea539e", "bytes": 2851422862}   # fetch 2.582 GB + write 0.269 GB
 DKDV_SOURCES = ("exact_attention_37_amd/csrc/bwd_mfma.hip", "exact_attention_37_amd/csrc/mfma_common.h",
                 "exact_attention_37_amd/csrc/common.h")
 
