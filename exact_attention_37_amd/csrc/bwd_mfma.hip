@@ -85,15 +85,18 @@ void bwd_dkdv_kernel(Params p) {
   const int lane = tid & 63;
   const int g = lane >> 5, n = lane & 31;
   const int gkv = blockIdx.x;          // all tiles of one K/V head share an XCD
-  int kt = blockIdx.y;                 // tile 0 has the most causal work: dispatched first
-  int b = blockIdx.z;
+  // key tile (tile 0, with the most causal work, first) and batch entry from
+  // the grid (tile_grid_index(), mfma_common.h)
+  const int tix = tile_grid_index<CAUSAL>();
+  int kt = tix;
+  int b = batch_grid_index<CAUSAL>();
   if (p.vl_ktiles) {                   // packed batch: (sequence, tile) from the work list
-    if ((int)blockIdx.y >= p.vl_ktiles[0]) return;
-    b = p.vl_ktiles[2 + 2 * blockIdx.y];
-    kt = p.vl_ktiles[3 + 2 * blockIdx.y];
+    if (tix >= p.vl_ktiles[0]) return;
+    b = p.vl_ktiles[2 + 2 * tix];
+    kt = p.vl_ktiles[3 + 2 * tix];
   }
   const int k0 = kt * DKV_BK;
-  if (p.cu_seqlens) {                  // packed batch: z is the sequence
+  if (p.cu_seqlens) {                  // packed batch: b is the sequence (from the work list)
     if (!narrow_to_sequence(p, b, k0)) return;
     b = 0;
   }
@@ -564,18 +567,18 @@ void bwd_dq_kernel(Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
   const int lane = tid & 63;
   const int q4 = lane >> 4, i16 = lane & 15;
-  const int ntq = gridDim.y;
-  int qt = CAUSAL ? (ntq - 1 - (int)blockIdx.y) : (int)blockIdx.y;
+  const int tix = tile_grid_index<CAUSAL>(), ntq = tile_grid_count<CAUSAL>();
+  int qt = CAUSAL ? (ntq - 1 - tix) : tix;
   const int h = xcd_head(blockIdx.x, p.H);
-  int b = blockIdx.z;
+  int b = batch_grid_index<CAUSAL>();
   if (p.vl_qtiles) {                   // packed batch: (sequence, tile) from the work list
-    if ((int)blockIdx.y >= p.vl_qtiles[0]) return;
-    b = p.vl_qtiles[2 + 2 * blockIdx.y];
-    qt = p.vl_qtiles[3 + 2 * blockIdx.y];
+    if (tix >= p.vl_qtiles[0]) return;
+    b = p.vl_qtiles[2 + 2 * tix];
+    qt = p.vl_qtiles[3 + 2 * tix];
   }
   const int kvh = h / p.G;
   const int q0 = qt * BR;
-  if (p.cu_seqlens) {                  // packed batch: z is the sequence
+  if (p.cu_seqlens) {                  // packed batch: b is the sequence (from the work list)
     if (!narrow_to_sequence(p, b, q0)) return;
     b = 0;
   }
@@ -888,7 +891,7 @@ void bwd_dq_kernel(Params p) {
 
 template <int D>
 hipError_t launch_dkdv_d(const Params& p, hipStream_t s) {
-  const dim3 gkv(p.Hkv, p.vl_ktiles ? p.vl_kcap : (p.Nk + DKV_BK - 1) / DKV_BK, p.vl_ktiles ? 1 : p.B);
+  const dim3 gkv = tile_grid(p.Hkv, p.vl_ktiles ? 1 : p.B, p.vl_ktiles ? p.vl_kcap : (p.Nk + DKV_BK - 1) / DKV_BK, p.causal);
   if (p.bs_col_tiles && p.causal)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false, true>), gkv, dim3(DKV_NW * 64), 0, s, p);
   else if (p.bs_col_tiles)
@@ -905,7 +908,7 @@ hipError_t launch_dkdv_d(const Params& p, hipStream_t s) {
 template <int D>
 hipError_t launch_dq_d(const Params& p, hipStream_t s) {
   if (p.bs_row_tiles) {   // one 256-row block row of the mask per workgroup
-    const dim3 gq(p.H, (p.Nq + BS_ROWS - 1) / BS_ROWS, p.B);
+    const dim3 gq = tile_grid(p.H, p.B, (p.Nq + BS_ROWS - 1) / BS_ROWS, p.causal);
     if (p.causal)
       hipLaunchKernelGGL((bwd_dq_kernel<D, true, 8, false, true>), gq, dim3(8 * 64), 0, s, p);
     else
@@ -913,7 +916,7 @@ hipError_t launch_dq_d(const Params& p, hipStream_t s) {
     return hipGetLastError();
   }
   constexpr int NW = query_waves(D);
-  const dim3 gq(p.H, p.vl_qtiles ? p.vl_qcap : (p.Nq + NW * 32 - 1) / (NW * 32), p.vl_qtiles ? 1 : p.B);
+  const dim3 gq = tile_grid(p.H, p.vl_qtiles ? 1 : p.B, p.vl_qtiles ? p.vl_qcap : (p.Nq + NW * 32 - 1) / (NW * 32), p.causal);
   if (p.causal && p.window > 0)
     hipLaunchKernelGGL((bwd_dq_kernel<D, true, NW, true>), gq, dim3(NW * 64), 0, s, p);
   else if (p.causal)

@@ -73,19 +73,20 @@ void fwd_mfma_kernel(Params p) {
   const int lane = tid & 63;
   const int g = lane >> 5, n = lane & 31;
 
-  // ---- workgroup -> (b, h, query tile), heaviest causal tiles first
-  const int ntq = gridDim.y;
-  int qt = CAUSAL ? (ntq - 1 - (int)blockIdx.y) : (int)blockIdx.y;
+  // ---- workgroup -> (b, h, query tile); tile_grid_index() (mfma_common.h) picks
+  // the grid dimension that holds the tile
+  const int tix = tile_grid_index<CAUSAL>(), ntq = tile_grid_count<CAUSAL>();
+  int qt = CAUSAL ? (ntq - 1 - tix) : tix;
   const int h = xcd_head(blockIdx.x, p.H);
-  int b = blockIdx.z;
+  int b = batch_grid_index<CAUSAL>();
   if (p.vl_qtiles) {                              // packed batch: (sequence, tile) from the work list
-    if ((int)blockIdx.y >= p.vl_qtiles[0]) return;
-    b = p.vl_qtiles[2 + 2 * blockIdx.y];
-    qt = p.vl_qtiles[3 + 2 * blockIdx.y];
+    if (tix >= p.vl_qtiles[0]) return;
+    b = p.vl_qtiles[2 + 2 * tix];
+    qt = p.vl_qtiles[3 + 2 * tix];
   }
   const int kvh = h / p.G;
   const int q0 = qt * BR;                         // first local query row of the tile
-  if (p.cu_seqlens) {                             // packed batch: z is the sequence
+  if (p.cu_seqlens) {                             // packed batch: b is the sequence (from the work list)
     if (!narrow_to_sequence(p, b, q0)) return;
     b = 0;
   }
@@ -436,7 +437,7 @@ void fwd_mfma_kernel(Params p) {
 template <int D, int NW, typename TO>
 hipError_t launch_cfg(const Params& p, hipStream_t s) {
   if (p.bs_row_tiles) {
-    const dim3 grid(p.H, (p.Nq + BS_ROWS - 1) / BS_ROWS, p.B);
+    const dim3 grid = tile_grid(p.H, p.B, (p.Nq + BS_ROWS - 1) / BS_ROWS, p.causal);
     if (p.causal)
       hipLaunchKernelGGL((fwd_mfma_kernel<D, 8, true, TO, false, true>), grid, dim3(8 * 64), 0, s, p);
     else
@@ -444,7 +445,7 @@ hipError_t launch_cfg(const Params& p, hipStream_t s) {
     return hipGetLastError();
   }
   constexpr int BR = NW * 32;
-  const dim3 grid(p.H, p.vl_qtiles ? p.vl_qcap : (p.Nq + BR - 1) / BR, p.vl_qtiles ? 1 : p.B);
+  const dim3 grid = tile_grid(p.H, p.vl_qtiles ? 1 : p.B, p.vl_qtiles ? p.vl_qcap : (p.Nq + BR - 1) / BR, p.causal);
   if (p.causal && p.window > 0)
     hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, true, TO, true>), grid, dim3(NW * 64), 0, s, p);
   else if (p.causal)

@@ -278,4 +278,20 @@ __device__ __forceinline__ int xcd_head(int x, int H) {
   return (H & 7) == 0 ? (x & 7) * (H >> 3) + (x >> 3) : x;
 }
 
+// Grid order of the matrix-core kernels. Causal: (head, batch, tile) with the
+// tile index slowest, so that the heaviest tiles of every (b, h) are
+// dispatched first and the light ones fill the end of the run (a batch-major
+// order leaves the heavy tiles of the last batch entries to the end).
+// Non-causal: (head, tile, batch); every tile weighs the same, and the
+// workgroups of one (b, h) run together and share its K/V in the L2.
+template <bool CAUSAL>
+__device__ __forceinline__ int tile_grid_index() { return CAUSAL ? (int)blockIdx.z : (int)blockIdx.y; }
+template <bool CAUSAL>
+__device__ __forceinline__ int tile_grid_count() { return CAUSAL ? (int)gridDim.z : (int)gridDim.y; }
+template <bool CAUSAL>
+__device__ __forceinline__ int batch_grid_index() { return CAUSAL ? (int)blockIdx.y : (int)blockIdx.z; }
+inline dim3 tile_grid(int heads, int batch, int tiles, int causal) {
+  return causal ? dim3(heads, batch, tiles) : dim3(heads, tiles, batch);
+}
+
 }  // namespace miattn
