@@ -382,8 +382,8 @@ def main():
 
     def step(ev=None):
         # events (all on torch's current stream, which is the stream the
-        # library launches on): before fwd | after fwd | after the rowsum
-        # kernel | after the dK/dV kernel | after the dQ kernel
+        # library launches on): before fwd | after fwd | after the dQ kernel
+        # (which also forms the rowsum D) | after the dK/dV kernel | after bwd
         if ev is not None:
             ev[0].record()
         mi.fwd(q, k, v, causal, scale, out=o, out_lse=lse)
@@ -407,7 +407,7 @@ def main():
     def avg(a, b):
         return sum(e[a].elapsed_time(e[b]) for e in evs) / args.steps
     fwd_ms, bwd_ms = avg(0, 1), avg(1, 4)
-    pre_ms, dkdv_ms, dq_ms = avg(1, 2), avg(2, 3), avg(3, 4)
+    dq_ms, dkdv_ms = avg(1, 2), avg(2, 3)
     ms = wall * 1e3 / args.steps
 
     ff, fb = flops(w.B, w.H, w.N, w.d, causal)
@@ -441,8 +441,7 @@ def main():
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
         "fwd_tflops": round(fwd_tf, 2), "bwd_tflops": round(bwd_tf, 2),
-        "kernel_ms": {"fwd_mfma": round(fwd_ms, 4), "bwd_pre": round(pre_ms, 4),
-                      "bwd_dkdv": round(dkdv_ms, 4), "bwd_dq": round(dq_ms, 4)},
+        "kernel_ms": {"fwd_mfma": round(fwd_ms, 4), "bwd_dq": round(dq_ms, 4), "bwd_dkdv": round(dkdv_ms, 4)},
         "roofline": {"bound": "mfma", "kernel": "bwd_dkdv_kernel", "achieved": round(dkdv_tf, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dkdv_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},

@@ -155,7 +155,8 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, accumulate=False, dq=No
     accumulate=True: dq/dk/dv are float32 tensors (given or zero-initialised)
     that the gradients are added to; otherwise they have q's dtype.
     marks: optional pair of torch.cuda.Event, recorded on the stream after the
-    rowsum kernel and after the dK/dV kernel (attn_bwd_timed).
+    backward's first and second kernel (attn_bwd_timed): for bf16 the dQ
+    kernel (which also forms the rowsum of dout * o) and the dK/dV kernel.
     window > 0: backward of causal sliding-window attention (attn_bwd_window).
     """
     B, N, H, Hkv, d = _dims(q, k, v)

@@ -599,6 +599,16 @@ void bwd_dq_kernel(Params p) {
   bf16x8 qf[2][KS], of[2][KS];
   float lse2[2], dsum[2];
   int qpos[2];
+  long long si[2];
+  // With p.fuse_dsum the kernel forms D = rowsum(dO * O) of its rows itself
+  // (FlashAttention-2 reviews page, reviewer 2 point 2: the backward needs
+  // only the saved O and logsumexp): each lane sums its 8 KS products of the
+  // row, and the four lane groups q4 that share the row add their sums.
+  // Every query row belongs to exactly one workgroup of this kernel, which
+  // writes its D for the dK/dV kernel that runs after it.
+  const bool fuse = p.fuse_dsum != 0;
+  const bf16* Ob = (const bf16*)p.o + ((long long)b * p.N + p.q_start) * qrs + (long long)h * D;
+  bf16x8 ov[2][KS];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int r_ = wq0 + 16 * nb + i16;
@@ -612,13 +622,28 @@ void bwd_dq_kernel(Params p) {
       }
       qf[nb][ks] = x;
       of[nb][ks] = *(const bf16x8*)(dO + rc * qrs + ks * 32 + q4 * 8);
+      if (fuse) ov[nb][ks] = *(const bf16x8*)(Ob + rc * qrs + ks * 32 + q4 * 8);
     }
-    const long long si = ((long long)b * p.H + h) * p.N + p.q_start + rc;
-    lse2[nb] = p.lse[si] * kLog2e;
-    dsum[nb] = p.dsum[si];
+    si[nb] = ((long long)b * p.H + h) * p.N + p.q_start + rc;
+    lse2[nb] = p.lse[si[nb]] * kLog2e;
+    if (!fuse) dsum[nb] = p.dsum[si[nb]];
     qpos[nb] = p.q_start + r_;
   }
   wait_global_loads();
+  if (fuse) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      float x = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x = fmaf((float)of[nb][ks][e], (float)ov[nb][ks][e], x);
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      dsum[nb] = x;
+      if (q4 == 0 && wq0 + 16 * nb + i16 < p.Nq) p.dsum[si[nb]] = x;
+    }
+  }
 
   int nkt = (p.Nk + DQ_BC - 1) / DQ_BC;
   if (CAUSAL) {

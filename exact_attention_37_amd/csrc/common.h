@@ -34,6 +34,7 @@ struct Params {
   void* dk;
   void* dv;
   float* dsum;       // backward: rowsum(dout * o), [B, H, N]
+  int fuse_dsum;     // backward, bf16: the dQ kernel forms dsum for its rows from o and dout and writes it
   int B, H, Hkv, G;
   int N;             // full sequence length: row strides and [B,H,N] strides
   int Nq, Nk;        // rows of this block

@@ -401,7 +401,14 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
   p.dsum = dsum;
   p.accumulate = accumulate;
   p.acc_q = p.acc_kv = accumulate;
-  if (dtype == MIATTN_BF16 && (st = varlen_lists(p, scratch, true, s))) return st;
+  if (dtype == MIATTN_BF16) {
+    if ((st = varlen_lists(p, scratch, true, s))) return st;
+    // D = rowsum(dout * o) formed by the dQ kernel, for every row of a sequence
+    p.fuse_dsum = 1;
+    if ((st = launch_status(miattn::launch_bwd_dq_mfma(p, s), "attn_bwd_varlen dQ"))) return st;
+    if ((st = launch_status(miattn::launch_bwd_dkdv_mfma(p, s), "attn_bwd_varlen dK/dV"))) return st;
+    return ok();
+  }
   // rowsum(dout * o) is per token: the packed rows as one sequence
   if ((st = launch_status(miattn::launch_bwd_pre(o, dout, dsum, 1, H, total, d, 0, total, dtype, s),
                           "bwd preprocess")))
@@ -548,14 +555,18 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   p.window = window;
   if (bmask && (!scratch || (st = blocksparse_setup(p, bmask, dtype, *scratch, s))))
     return st ? st : fail(MIATTN_EINVAL, "block masks need library scratch");
-  if ((st = launch_status(miattn::launch_bwd_pre(o, dout, dsum, B, H, N, d, 0, N, dtype, s), "bwd preprocess")))
-    return st;
-  if (marks && (st = launch_status(hipEventRecord((hipEvent_t)marks[0], s), "timing mark 0"))) return st;
   if (dtype == MIATTN_BF16) {
+    // the dQ kernel also forms D = rowsum(dout * o) of its rows and writes
+    // it; the dK/dV kernel, which reads D, runs after it
+    p.fuse_dsum = 1;
+    if ((st = launch_status(miattn::launch_bwd_dq_mfma(p, s), "attn_bwd dQ"))) return st;
+    if (marks && (st = launch_status(hipEventRecord((hipEvent_t)marks[0], s), "timing mark 0"))) return st;
     if ((st = launch_status(miattn::launch_bwd_dkdv_mfma(p, s), "attn_bwd dK/dV"))) return st;
     if (marks && (st = launch_status(hipEventRecord((hipEvent_t)marks[1], s), "timing mark 1"))) return st;
-    if ((st = launch_status(miattn::launch_bwd_dq_mfma(p, s), "attn_bwd dQ"))) return st;
   } else {
+    if ((st = launch_status(miattn::launch_bwd_pre(o, dout, dsum, B, H, N, d, 0, N, dtype, s), "bwd preprocess")))
+      return st;
+    if (marks && (st = launch_status(hipEventRecord((hipEvent_t)marks[0], s), "timing mark 0"))) return st;
     if ((st = launch_status(bwd_block(p, dtype, s), "attn_bwd"))) return st;
     if (marks && (st = launch_status(hipEventRecord((hipEvent_t)marks[1], s), "timing mark 1"))) return st;
   }

@@ -235,14 +235,16 @@ int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
 
 /* attn_bwd with per-kernel timing marks, for measurement tools: the same
  * arguments, results and errors as attn_bwd, and additionally
- *   marks[0] is recorded on `stream` after the rowsum(dout * o) kernel,
- *   marks[1] after the dK/dV kernel (the dQ kernel follows),
+ *   marks[0] is recorded on `stream` after the backward's first kernel,
+ *   marks[1] after its second,
  * where marks[0], marks[1] are hipEvent_t handles (passed as void*) that the
  * caller created and owns. marks == NULL records nothing. For dtype
- * MIATTN_BF16 the two intervals between an event the caller records before
- * the call, marks[0], marks[1] and one recorded after it are the durations
- * of the three kernels of the backward; for MIATTN_F32 marks[1] follows the
- * single float32 backward block and the last interval is empty.
+ * MIATTN_BF16 the first kernel is the dQ kernel (which also forms the
+ * rowsum D = rowsum(dout * o) of its rows) and the second the dK/dV kernel:
+ * the intervals between an event the caller records before the call,
+ * marks[0] and marks[1] are their durations, and an event recorded after the
+ * call adds an empty interval. For MIATTN_F32 the first kernel is the rowsum
+ * kernel and the second the float32 backward block.
  * MIATTN_ELAUNCH also covers a failed hipEventRecord. */
 int attn_bwd_timed(const void* q, const void* k, const void* v, const void* o, const float* lse,
                    int B, int H, int Hkv, int N, int d, int causal, float scale,
