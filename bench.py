@@ -30,7 +30,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 # rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; calibrated against a plain
 # 1 GiB device copy in the same process), valid only for the kernel sources
 # whose SHA-1 is recorded with it (profiles/llama16k_causal_bf16_traffic.md).
-DKDV_TRAFFIC = {"sources_sha1": "7b44e3def9c3d90bdf96c8cc6ecfdefec7ea539e", "bytes": 2851422862}   # fetch 2.582 GB + write 0.269 GB
+DKDV_TRAFFIC = {"sources_sha1": "89b684de4e531cee033c0792351dd6ba73b418c1", "bytes": 2850574126}   # fetch 2.582 GB + write 0.268 GB
 DKDV_SOURCES = ("exact_attention_37_amd/csrc/bwd_mfma.hip", "exact_attention_37_amd/csrc/mfma_common.h",
                 "exact_attention_37_amd/csrc/common.h")
 
@@ -293,6 +293,18 @@ def bench_workload(mi, torch, name, reps=20):
     bwd = lambda o_, l_: mi.bwd(q, k, v, o_, l_, do, causal, scale, dq=dq, dk=dk, dv=dv)
     time_fwd_bwd(torch, fwd, bwd, 3)
     f_ms, b_ms = time_fwd_bwd(torch, fwd, bwd, reps)
+    # the throughput: steps back to back, one event pair around all of them
+    # (an event between two kernels costs a few microseconds of device time,
+    # much of a 0.1 ms step)
+    steps = 50
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        bwd(*fwd())
+    e1.record()
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / steps
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=q.device)
     fc_ms, bc_ms = time_fwd_bwd(torch, fwd, bwd, reps, flush=flush)
     del flush
@@ -300,11 +312,14 @@ def bench_workload(mi, torch, name, reps=20):
     bf_, bb = algorithmic_bytes(w)
     ridge_tf = (ff + fb) / (bf_ + bb) * PEAK_HBM_GBS / 1e3        # intensity x bandwidth, TFLOP/s
     roof_tf = min(PEAK_BF16_TFLOPS, ridge_tf)
-    tf = (ff + fb) / ((f_ms + b_ms) * 1e-3) / 1e12
+    tf = (ff + fb) / (step_ms * 1e-3) / 1e12
     tfc = (ff + fb) / ((fc_ms + bc_ms) * 1e-3) / 1e12
     return {"workload": "%s: B=%d H=%d Hkv=%d N=%d d=%d %s, fwd+bwd" % (
                 w.name, w.B, w.H, w.Hkv, w.N, w.d, "causal" if causal else "non-causal"),
-            "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4), "tflops": round(tf, 2),
+            "step_ms": round(step_ms, 4),
+            "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
+            "split_note": "fwd_ms, bwd_ms: each phase between its own events; tflops from step_ms (%d steps back to back)" % steps,
+            "tflops": round(tf, 2),
             "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
             "roofline": {"bound": "mfma" if roof_tf >= PEAK_BF16_TFLOPS else "hbm", "achieved": round(tf, 2),
                          "peak": round(roof_tf, 1), "unit": "TFLOP/s", "frac": round(tf / roof_tf, 4),
