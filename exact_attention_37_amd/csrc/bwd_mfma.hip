@@ -930,7 +930,7 @@ hipError_t launch_dkdv_d(const Params& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int NW = query_waves(D)>
 hipError_t launch_dq_d(const Params& p, hipStream_t s) {
   if (p.bs_row_tiles) {   // one 256-row block row of the mask per workgroup
     const dim3 gq = tile_grid(p.H, p.B, (p.Nq + BS_ROWS - 1) / BS_ROWS, p.causal);
@@ -940,7 +940,6 @@ hipError_t launch_dq_d(const Params& p, hipStream_t s) {
       hipLaunchKernelGGL((bwd_dq_kernel<D, false, 8, false, true>), gq, dim3(8 * 64), 0, s, p);
     return hipGetLastError();
   }
-  constexpr int NW = query_waves(D);
   const dim3 gq = tile_grid(p.H, p.vl_qtiles ? 1 : p.B, p.vl_qtiles ? p.vl_qcap : (p.Nq + NW * 32 - 1) / (NW * 32), p.causal);
   if (p.causal && p.window > 0)
     hipLaunchKernelGGL((bwd_dq_kernel<D, true, NW, true>), gq, dim3(NW * 64), 0, s, p);
@@ -958,6 +957,8 @@ hipError_t launch_bwd_dkdv_mfma(const Params& p, hipStream_t s) {
 }
 
 hipError_t launch_bwd_dq_mfma(const Params& p, hipStream_t s) {
+  if (p.d == 128 && !p.vl_qtiles && !p.bs_row_tiles && small_query_grid(128, p.B, p.H, p.Nq, device_cu_count()))
+    return launch_dq_d<128, 4>(p, s);
   return p.d == 128 ? launch_dq_d<128>(p, s) : launch_dq_d<64>(p, s);
 }
 

@@ -92,6 +92,14 @@ constexpr int ACC_STORE = 0, ACC_ADD = 1, ACC_FIRST = 2, ACC_LAST = 3;
 // overlap the other's products. Packed-batch work lists use the same rows.
 constexpr int query_waves(int d) { return d == 64 ? 4 : 8; }
 constexpr int query_tile_rows(int d) { return 32 * query_waves(d); }
+// A dense (not packed, not block-sparse) forward or dQ launch at d = 128
+// whose eight-wave workgroups would not give every compute unit one takes
+// four-wave workgroups (128 rows) instead: twice the workgroups, two per CU
+// (small batch x heads: the FlashAttention-2 reviews page, authors' common
+// response, ablation (B), parallelism over the sequence).
+inline bool small_query_grid(int d, int B, int H, int Nq, int cus) {
+  return d == 128 && (long long)B * H * ((Nq + 255) / 256) < cus;
+}
 
 // For a packed variable-length batch, narrows p to sequence s (rows
 // [cu_seqlens[s], cu_seqlens[s + 1]) of the single B = 1 layout; the offsets

@@ -58,6 +58,7 @@ hipError_t launch_convert(const float* src, void* dst, long long n, int dtype, h
 
 // dst[i] = value for n float32 elements (a kernel, so it can sit in a graph).
 hipError_t launch_fill(float* dst, long long n, float value, hipStream_t s);
+int device_cu_count();   // compute units of the current device (cached per device)
 
 // Block-sparse tile lists (the bs_* fields of Params) from a block mask of
 // [nbr = ceil(N / BS_ROWS)][nbc = ceil(N / BS_COLS)] bytes. `ints` must hold

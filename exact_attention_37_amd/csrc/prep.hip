@@ -1,5 +1,6 @@
 // Memory-bound helper kernels: the backward preprocess rowsum(dO * O), the
 // LSE merge of partial outputs, dtype conversion and fills.
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -306,6 +307,18 @@ hipError_t launch_varlen_tiles(const int* cu_seqlens, int nseq, int total, int r
   hipLaunchKernelGGL(varlen_tiles_kernel, dim3(1), dim3(1024), 0, s, cu_seqlens, nseq, total, rows, desc,
                      varlen_list_cap(total, rows, nseq), list);
   return hipGetLastError();
+}
+
+int device_cu_count() {
+  // per device, read once: the attribute query is a host call
+  static std::atomic<int> counts[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = counts[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  counts[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 hipError_t launch_fill(float* dst, long long n, float value, hipStream_t s) {
