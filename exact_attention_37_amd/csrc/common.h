@@ -93,12 +93,13 @@ constexpr int ACC_STORE = 0, ACC_ADD = 1, ACC_FIRST = 2, ACC_LAST = 3;
 constexpr int query_waves(int d) { return d == 64 ? 4 : 8; }
 constexpr int query_tile_rows(int d) { return 32 * query_waves(d); }
 // A dense (not packed, not block-sparse) forward or dQ launch at d = 128
-// whose eight-wave workgroups would not give every compute unit one takes
+// with fewer eight-wave workgroups than two per compute unit takes
 // four-wave workgroups (128 rows) instead: twice the workgroups, two per CU
-// (small batch x heads: the FlashAttention-2 reviews page, authors' common
-// response, ablation (B), parallelism over the sequence).
+// at a time, and finer pieces for the causal load balance (small batch x
+// heads: the FlashAttention-2 reviews page, authors' common response,
+// ablation (B), parallelism over the sequence).
 inline bool small_query_grid(int d, int B, int H, int Nq, int cus) {
-  return d == 128 && (long long)B * H * ((Nq + 255) / 256) < cus;
+  return d == 128 && (long long)B * H * ((Nq + 255) / 256) < 2LL * cus;
 }
 
 // For a packed variable-length batch, narrows p to sequence s (rows
