@@ -957,7 +957,8 @@ hipError_t launch_bwd_dkdv_mfma(const Params& p, hipStream_t s) {
 }
 
 hipError_t launch_bwd_dq_mfma(const Params& p, hipStream_t s) {
-  if (p.d == 128 && !p.vl_qtiles && !p.bs_row_tiles && small_query_grid(128, p.B, p.H, p.Nq, device_cu_count()))
+  // four-wave workgroups at d = 128 for packed batches (kVarlenQueryWaves) and small grids
+  if (p.d == 128 && !p.bs_row_tiles && (p.vl_qtiles || small_query_grid(128, p.B, p.H, p.Nq, device_cu_count())))
     return launch_dq_d<128, 4>(p, s);
   return p.d == 128 ? launch_dq_d<128>(p, s) : launch_dq_d<64>(p, s);
 }

@@ -91,13 +91,15 @@ constexpr int ACC_STORE = 0, ACC_ADD = 1, ACC_FIRST = 2, ACC_LAST = 3;
 // where two workgroups share a CU so that one's prologue and epilogue
 // overlap the other's products. Packed-batch work lists use the same rows.
 constexpr int query_waves(int d) { return d == 64 ? 4 : 8; }
-constexpr int query_tile_rows(int d) { return 32 * query_waves(d); }
 // A dense (not packed, not block-sparse) forward or dQ launch at d = 128
 // with fewer eight-wave workgroups than two per compute unit takes
 // four-wave workgroups (128 rows) instead: twice the workgroups, two per CU
 // at a time, and finer pieces for the causal load balance (small batch x
 // heads: the FlashAttention-2 reviews page, authors' common response,
 // ablation (B), parallelism over the sequence).
+// Packed batches (short sequences) take four-wave (128-row) query
+// workgroups at both head sizes: half the masked diagonal per workgroup.
+constexpr int kVarlenQueryWaves = 4;
 inline bool small_query_grid(int d, int B, int H, int Nq, int cus) {
   return d == 128 && (long long)B * H * ((Nq + 255) / 256) < 2LL * cus;
 }

@@ -459,7 +459,8 @@ hipError_t launch_cfg(const Params& p, hipStream_t s) {
 
 hipError_t launch_fwd_mfma(const Params& p, bool out_f32, hipStream_t s) {
   constexpr int W128 = query_waves(128), W64 = query_waves(64);
-  if (p.d == 128 && !p.vl_qtiles && !p.bs_row_tiles && small_query_grid(128, p.B, p.H, p.Nq, device_cu_count()))
+  // four-wave workgroups at d = 128 for packed batches (kVarlenQueryWaves) and small grids
+  if (p.d == 128 && !p.bs_row_tiles && (p.vl_qtiles || small_query_grid(128, p.B, p.H, p.Nq, device_cu_count())))
     return out_f32 ? launch_cfg<128, 4, float>(p, s) : launch_cfg<128, 4, bf16>(p, s);
   if (p.d == 128) return out_f32 ? launch_cfg<128, W128, float>(p, s) : launch_cfg<128, W128, bf16>(p, s);
   return out_f32 ? launch_cfg<64, W64, float>(p, s) : launch_cfg<64, W64, bf16>(p, s);

@@ -260,12 +260,12 @@ int blocksparse_setup(Params& p, const uint8_t* bmask, int dtype, Scratch& scrat
 
 // Packed batch, matrix-core kernels: the work lists of (sequence, tile)
 // entries, built on the device from cu_seqlens into scratch: query tiles of
-// the forward / dQ workgroups (query_tile_rows(d) rows, heaviest causal tile
+// the forward / dQ workgroups (32 kVarlenQueryWaves rows, heaviest causal tile
 // of a sequence first) and, for the backward, key tiles of the dK/dV
 // workgroups (128 keys, first tile first). The grids reserve
 // ceil(total / rows) + nseq entries.
 int varlen_lists(Params& p, Scratch& scratch, bool backward, hipStream_t s) {
-  const int total = p.N, nseq = p.B, qrows = miattn::query_tile_rows(p.d);
+  const int total = p.N, nseq = p.B, qrows = 32 * miattn::kVarlenQueryWaves;
   const int qcap = miattn::varlen_list_cap(total, qrows, nseq);
   int* ql = (int*)scratch.get((size_t)(2 + 2 * (long long)qcap) * 4);
   if (!ql) return fail(MIATTN_ENOMEM, "hipMallocAsync failed for the packed-batch work list");
