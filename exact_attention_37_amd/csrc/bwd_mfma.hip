@@ -3,7 +3,7 @@
 // The backward rebuilds P tile by tile from the saved logsumexp instead of
 // re-running the forward (DistFlashAttn reviews page, review 1 point 3;
 // FlashAttention-2 reviews page, reviewer 2, point 2) and never forms the
-// N x N matrix. With D_i = rowsum(dO_i * O_i) computed beforehand:
+// N x N matrix. With D_i = rowsum(dO_i * O_i):
 //     P = exp(scale Q K^T - LSE),  dP = dO V^T,  dS = P (dP - D)
 //     dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K
 // Grouped-query heads: dK and dV of a K/V head are summed over the query
@@ -14,6 +14,8 @@
 // with another workgroup, so no atomics are needed and results are bitwise
 // deterministic. Accumulating dQ across key tiles with float32 atomics would
 // cost as much memory traffic as the whole computation takes on MI355X.
+// The dQ kernel runs first: each of its workgroups also forms D of its own
+// query rows (it already holds their dO) and writes it for the dK/dV kernel.
 //  * bwd_dkdv: one workgroup per 128 keys of one (b, K/V head); each of its 4
 //    waves holds 32 keys' K and V as matrix-core operands and their dK, dV
 //    accumulators in registers, and streams 64-row tiles of Q and dO

@@ -8,8 +8,9 @@
 // (FlashAttention-2 reviews page, reviewer 4, section 3.1).
 //
 // Work split (MI355X-specific, not from the pages):
-//  * a workgroup of 8 waves (two per SIMD) owns 256 query rows of one (b, h);
-//    each wave owns 32 rows, so its row max and row sum never leave the wave
+//  * a workgroup of 8 waves (256 query rows; 4 waves and 128 rows at d = 64,
+//    two workgroups per CU) owns query rows of one (b, h), two waves per
+//    SIMD; each wave owns 32 rows, so its row max and row sum never leave the wave
 //    (the pages' warp partitioning, with 64-lane wavefronts);
 //  * K and V tiles of BC=64 keys are double-buffered in LDS, one barrier per
 //    tile; the next tile is loaded straight from global memory into LDS
@@ -27,9 +28,12 @@
 //  * the row sum is accumulated from the float32 probabilities before they
 //    are rounded to bf16 for the P V product, so the saved logsumexp keeps
 //    float32 accuracy even for rows with few keys;
-//  * causal workgroups are launched heaviest first, and with H % 8 == 0 the
-//    heads are permuted so that every workgroup of one K/V head group lands
-//    on the same XCD (workgroups are dealt to the 8 XCDs round-robin).
+//  * causal grids are ordered (head, batch, tile) so that the heaviest
+//    tiles of every (batch, head) are dispatched first, and with H % 8 == 0
+//    the heads are permuted so that every workgroup of one K/V head group
+//    lands on the same XCD (workgroups are dealt to the 8 XCDs round-robin);
+//  * at d = 128 small grids and packed batches take four-wave (128-row)
+//    workgroups (small_query_grid(), kVarlenQueryWaves).
 #include "common.h"
 #include "kernels.h"
 #include "mfma_common.h"

@@ -1,5 +1,7 @@
-// Memory-bound helper kernels: the backward preprocess rowsum(dO * O), the
-// LSE merge of partial outputs, dtype conversion and fills.
+// Memory-bound helper kernels: the backward preprocess rowsum(dO * O) (the
+// float32 backward and the chunk driver; the bf16 backward forms it in its dQ
+// kernel), the LSE merge of partial outputs, dtype conversion and fills, and
+// the packed-batch work lists.
 #include <atomic>
 #include <type_traits>
 
