@@ -28,8 +28,13 @@ FLAGS = ["-O3", "-fPIC", "-std=c++20", "--offload-arch=" + ARCH,
 
 # Per-source extra flags. The backward kernels keep their softmax inputs in
 # VGPRs when MFMA results are allocated in VGPR form (otherwise every tile's
-# S and dP are copied out of AGPRs before the vector work).
-EXTRA = {"bwd_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# S and dP are copied out of AGPRs before the vector work). The matrix-core
+# kernels' occupancy is fixed by their launch bounds, so the scheduler is
+# told to weigh latency only (metric bias 0): 2-3% faster forward and dK/dV
+# kernels at d = 64, unchanged at d = 128, identical results.
+LATENCY = ["-mllvm", "-amdgpu-schedule-metric-bias=0"]
+EXTRA = {"bwd_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"] + LATENCY,
+         "fwd_mfma.hip": LATENCY}
 
 
 def _run(cmd, verbose):
