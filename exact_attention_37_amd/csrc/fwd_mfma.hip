@@ -21,10 +21,14 @@
 //    next product O^T += V^T P^T. P never moves between lanes.
 //  * V^T operands of the P V product come from transposing LDS reads of the
 //    row-major V tile, so V is stored once, as loaded;
-//  * the running max is only raised when a row's tile max exceeds it by more
-//    than 8 (log2 units); otherwise the old max is kept, p <= 2^8, and the
-//    accumulator is not rescaled. The result is unchanged (numerator and
-//    denominator share the max), and most tiles skip the rescale entirely;
+//  * the running max is not rescanned per tile: P is formed with the max
+//    kept so far and the tile is accepted when every lane's probability sum
+//    is at most 2^8 (so p <= 2^8); only a tile that fails raises the max,
+//    rescales the accumulator and forms its P again. The result is unchanged
+//    (numerator and denominator share the max), and the max scan leaves the
+//    loop;
+//  * each of the loop's two phases of products (S^T of the next tile, P V of
+//    the current one) carries half a tile of exponentials, one per product;
 //  * the row sum is accumulated from the float32 probabilities before they
 //    are rounded to bf16 for the P V product, so the saved logsumexp keeps
 //    float32 accuracy even for rows with few keys;
@@ -197,17 +201,26 @@ void fwd_mfma_kernel(Params p) {
 
   // Tiles are taken in list order it = 0 .. nit-1 (tile_of(it): contiguous
   // from jt0, or the block-sparse list). K and V of tile it sit in K / V
-  // buffer it & 1. The loop is software-pipelined across tiles, so that
-  // every phase of matrix-core products carries independent vector work:
-  //   phase A: S^T of tile it+1 (K from LDS)  + exp / row sum / bf16 P of tile it
+  // buffer it & 1. The loop is software-pipelined across tiles, and each of
+  // its two phases of matrix-core products carries half a tile of softmax:
+  //   phase A: S^T of tile it+1 (K from LDS)  + P of keys 32..63 of tile it
   //            + direct loads of K(it+2) and V(it+1)
-  //   phase B: O^T += V^T P^T of tile it      + max scan of tile it+1's scores
-  // then the running max is raised for tile it+1 (rescaling the
-  // accumulator, which now holds tile it), one wait for the loads and one
-  // barrier. K is thereby loaded two tiles ahead and V one tile ahead: K(it+2)
-  // overwrites K(it), whose products ran in the previous iteration, and
-  // V(it+1) overwrites V(it-1). Tiles past the last repeat the last one.
+  //   phase B: O^T += V^T P^T of tile it      + P of keys 0..31 of tile it+1
+  // then one wait for the loads and one barrier. K is thereby loaded two
+  // tiles ahead and V one tile ahead: K(it+2) overwrites K(it), whose
+  // products ran in the previous iteration, and V(it+1) overwrites V(it-1).
+  // Tiles past the last repeat the last one (the extra scores are unused).
   // Block-sparse list entries are read two iterations ahead.
+  //
+  // The running max m is not rescanned per tile. P is formed with the max
+  // kept so far, and a tile is accepted when every lane's sum of its
+  // probabilities is at most 2^8, which bounds every probability by 2^8, as
+  // a max raised lazily by a margin of 8 would. The scores of the first
+  // tile set m. A tile that fails the test (a score more than about 8 above
+  // m in log2 units; a window row that has seen no key yet) takes a slow
+  // path: its max raises m, the accumulator and row sum are rescaled, and
+  // its probabilities are formed again. The result is the same softmax:
+  // numerator and denominator share m.
   int t1 = 0, t2 = 0, t3 = 0;     // tile_of(it + 1), tile_of(it + 2), tile_of(it + 3)
   auto list_at = [&](int it) { return SPARSE ? uni(tl[min(it, nit - 1)]) : jt0 + min(it, nit - 1); };
   int t0 = 0;
@@ -255,25 +268,47 @@ void fwd_mfma_kernel(Params p) {
         }
     }
   };
-  // ---- running max over a tile's scores, in NS slices (slice k of NS)
-  float mx = -INFINITY;
-  auto max_slice = [&](const f32x16 (&sx)[2], auto kc, auto nsc) {
-    constexpr int k = decltype(kc)::value, ns = decltype(nsc)::value;
-    constexpr int lo = k * 32 / ns, hi = (k + 1) * 32 / ns;
+  // ---- max of a tile's scores over the row (lane (g, query n) and lane
+  // (1 - g, n) hold the row's two key halves), in log2 units
+  auto tile_max = [&](const f32x16 (&sx)[2]) {
+    float mx = -INFINITY;
 #pragma unroll
-    for (int e = lo; e < hi; ++e) mx = fmaxf(mx, sx[e / 16][e % 16]);
+    for (int e = 0; e < 32; ++e) mx = fmaxf(mx, sx[e / 16][e % 16]);
+    return max_halves(mx) * c;
   };
-  // raise the running max to the tile's max (lane (g, query n)) when it
-  // exceeds the kept one by more than 8 (log2 units), rescaling acc and l
-  auto raise_max = [&]() {
-    const float mt = max_halves(mx) * c;
-    mx = -INFINITY;
-    const bool raise = mt > m + 8.f;
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-      const float mnew = raise ? mt : m;
-      // rows that keep their max keep alpha = 1 (with a window a row's max
-      // can still be -inf here, and -inf - -inf has no value)
-      const float alpha = (EMPTY && !raise) ? 1.f : exp2f(m - mnew);
+  // ---- probabilities: element r of score half kb of sx -> pf[2 kb + r / 8][r % 8],
+  // summed into ls in float32 before the bf16 rounding. Empty asm uses pin
+  // the results of a lock-stepped call to its step, so that the compiler
+  // cannot move the exponentials out of the products they run beside.
+  float mneg = 0.f;               // -m (0 for a row that has seen no key)
+  auto prob = [&](const f32x16 (&sx)[2], bf16x8 (&pf)[4], float& ls, auto kbc, auto rc) {
+    constexpr int kb = decltype(kbc)::value, r = decltype(rc)::value;
+    const float x = __builtin_amdgcn_exp2f(fmaf(sx[kb][r], c, mneg));
+    ls += x;
+    pf[2 * kb + r / 8][r % 8] = (bf16)x;
+    if constexpr (r % 2 == 1) asm volatile("" : "+v"(pf[2 * kb + r / 8]), "+v"(ls));
+  };
+  // elements [i * 16 / n, (i + 1) * 16 / n) of half kb: step i of n
+  auto prob_steps = [&](const f32x16 (&sx)[2], bf16x8 (&pf)[4], float& ls, auto kbc, auto ic, auto nc) {
+    constexpr int i = decltype(ic)::value, n_ = decltype(nc)::value;
+    constexpr int lo = i * 16 / n_, hi = (i + 1) * 16 / n_;
+    [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
+      (prob(sx, pf, ls, kbc, std::integral_constant<int, lo + Ws>{}), ...);
+    }(std::make_integer_sequence<int, hi - lo>{});
+  };
+  auto prob_all = [&](const f32x16 (&sx)[2], bf16x8 (&pf)[4], float& ls, auto kbc) {
+    [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
+      (prob(sx, pf, ls, kbc, std::integral_constant<int, Ws>{}), ...);
+    }(std::make_integer_sequence<int, 16>{});
+  };
+  using KB0 = std::integral_constant<int, 0>;
+  using KB1 = std::integral_constant<int, 1>;
+  // ---- slow path for a tile that failed the test: raise m to the tile's max,
+  // rescale the accumulator and row sum, form the tile's probabilities again
+  auto redo_tile = [&](const f32x16 (&sx)[2], bf16x8 (&pf)[4], float& ls) {
+    const float mnew = fmaxf(m, tile_max(sx));
+    if (mnew != m) {                // from m = -inf (no key seen yet): alpha = 0, acc and l are 0
+      const float alpha = exp2f(m - mnew);
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -281,36 +316,23 @@ void fwd_mfma_kernel(Params p) {
         for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
       m = mnew;
     }
-  };
-  // ---- P of the current tile sc: sub-step w of 16 = (kb, half, element
-  // pair), the float32 probabilities summed into the row sum before the bf16 cast
-  bf16x8 pf[4];
-  float lsum0 = 0.f, lsum1 = 0.f, mneg = 0.f;
-  auto exp_sub = [&](const f32x16 (&sc)[2], auto wc) {
-    constexpr int w = decltype(wc)::value, kb = w / 8, half = (w / 4) % 2, e = 2 * (w % 4);
-    const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][half * 8 + e], c, mneg));
-    const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][half * 8 + e + 1], c, mneg));
-    lsum0 += p0;
-    lsum1 += p1;
-    pf[kb * 2 + half][e] = (bf16)p0;
-    pf[kb * 2 + half][e + 1] = (bf16)p1;
-  };
-  // exp sub-steps [i * 16 / n, (i + 1) * 16 / n) for step i of n
-  auto exp_steps = [&](const f32x16 (&sc)[2], auto ic, auto nc) {
-    constexpr int i = decltype(ic)::value, n_ = decltype(nc)::value;
-    constexpr int lo = i * 16 / n_, hi = (i + 1) * 16 / n_;
-    [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
-      (exp_sub(sc, std::integral_constant<int, lo + Ws>{}), ...);
-    }(std::make_integer_sequence<int, hi - lo>{});
+    mneg = (EMPTY && m == -INFINITY) ? 0.f : -m;
+    ls = 0.f;
+    prob_all(sx, pf, ls, KB0{});
+    prob_all(sx, pf, ls, KB1{});
   };
 
-  // scores of the current tile (sa) and of the next one (sb); the loop is
-  // unrolled twice so that the two swap roles without copies
+  // scores of the current tile (sa) and of the next one (sb), probabilities
+  // of the current tile (pa) and of the next one (pb), row-sum partials of
+  // the first half (lsa) and second half (lsb) of a tile; the loop is
+  // unrolled twice so that the two sets swap roles without copies
   f32x16 sa[2], sb[2];
+  bf16x8 pa[4], pb[4];
+  float lsa = 0.f, lsb = 0.f;
   if (nit > 0) {
     // prologue: K, V of tiles 0 and 1 into buffers 0 and 1, then S^T of
-    // tile 0, its mask and max (a barrier before the loop's first loads,
-    // which overwrite K(0))
+    // tile 0, its mask, its max as m and the probabilities of its first
+    // half (a barrier before the loop's first loads, which overwrite K(0))
 #pragma unroll
     for (int i = 0; i < NL; ++i) load_piece(i, 0, t0 * BC, 0, t0 * BC);
 #pragma unroll
@@ -319,40 +341,39 @@ void fwd_mfma_kernel(Params p) {
     __syncthreads();
     scores(sa, 0, [](auto) {});
     mask_tile(sa, t0);
-    max_slice(sa, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
-    raise_max();
+    m = tile_max(sa);
+    mneg = (EMPTY && m == -INFINITY) ? 0.f : -m;
+    prob_all(sa, pa, lsa, KB0{});
     __syncthreads();
   }
 
-  // one tile: sc holds its (masked) scores, sn receives the next tile's
-  auto iteration = [&](int it, const f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+  // one tile: sc holds its (masked) scores and pc[0..1] the probabilities of
+  // its first half (lsa their sum); sn, pn[0..1] and lsa receive the next tile's
+  auto iteration = [&](int it, const f32x16 (&sc)[2], f32x16 (&sn)[2], bf16x8 (&pc)[4], bf16x8 (&pn)[4]) {
     const int vb = it & 1;
     const bf16* vt = sm.v[vb];
-    const bool has_next = it + 1 < nit;
-    // (a row whose window has not begun yet keeps m = -inf and p = 0)
-    mneg = (EMPTY && m == -INFINITY) ? 0.f : -m;
-    lsum0 = lsum1 = 0.f;
-    // ---- phase A: S^T of tile it+1 with P of tile it and the next loads
-    if (has_next) {
+    // ---- phase A: S^T of tile it+1 with P of the second half of tile it and the next loads
+    lsb = 0.f;
+    {
       const int jk = t2 * BC, jv = t1 * BC;
       scores(sn, vb ^ 1, [&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        exp_steps(sc, ic, std::integral_constant<int, 2 * KS>{});
+        prob_steps(sc, pc, lsb, KB1{}, ic, std::integral_constant<int, 2 * KS>{});
         constexpr int lo = i * NL / (2 * KS), hi = (i + 1) * NL / (2 * KS);
         [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
           (load_piece(lo + Ws, vb, jk, vb ^ 1, jv), ...);
         }(std::make_integer_sequence<int, hi - lo>{});
       });
-      mask_tile(sn, t1);
-    } else {
-      [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
-        (exp_sub(sc, std::integral_constant<int, Ws>{}), ...);
-      }(std::make_integer_sequence<int, 16>{});
     }
-    l += lsum0 + lsum1;
+    // ---- the test of tile it (every lane's probability sum at most 2^8)
+    float ls = lsa + lsb;
+    if (__builtin_amdgcn_ballot_w64(ls > 256.f || (EMPTY && m == -INFINITY)) != 0) redo_tile(sc, pc, ls);
+    l += ls;
+    mask_tile(sn, t1);
 
     // ---- phase B: O^T += V^T P^T of tile it (V^T by transposing reads;
-    // step i = (kq, db)) with the max scan of tile it+1
+    // step i = (kq, db)) with P of the first half of tile it+1
+    lsa = 0.f;
     lockstep_products<4 * DB, 4>(
         [&](auto ic) {
           constexpr int i = decltype(ic)::value, kq = i / DB, db = i % DB;
@@ -362,13 +383,10 @@ void fwd_mfma_kernel(Params p) {
         },
         [&](auto ic, bf16x8 a) {
           constexpr int i = decltype(ic)::value, kq = i / DB, db = i % DB;
-          acc[db] = mfma32(a, pf[kq], acc[db]);
+          acc[db] = mfma32(a, pc[kq], acc[db]);
         },
-        [&](auto ic) {
-          if (has_next) max_slice(sn, ic, std::integral_constant<int, 4 * DB>{});
-        },
+        [&](auto ic) { prob_steps(sn, pn, lsa, KB0{}, ic, std::integral_constant<int, 4 * DB>{}); },
         std::true_type{});
-    if (has_next) raise_max();
     t1 = t2;
     t2 = t3;
     t3 = list_at(it + 4);
@@ -376,8 +394,8 @@ void fwd_mfma_kernel(Params p) {
     __syncthreads();
   };
   for (int it = 0; it < nit; it += 2) {
-    iteration(it, sa, sb);
-    if (it + 1 < nit) iteration(it + 1, sb, sa);
+    iteration(it, sa, sb, pa, pb);
+    if (it + 1 < nit) iteration(it + 1, sb, sa, pb, pa);
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
