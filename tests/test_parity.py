@@ -162,6 +162,35 @@ def test_peaked_rows(causal):
         check_rel(n, g_, r_, 1e-2)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_rising_scores(causal, d):
+    # Scores that climb by about 12 (log2 units) from one 64-key tile to the
+    # next: Q's first coordinate is 4 and K's is 24 x the key's tile index, so
+    # each new tile holds scores far above the running max. Every tile then
+    # takes the forward's path that raises the max, rescales the accumulator
+    # and forms its probabilities again (its probability sums overflow the
+    # bound the running max is kept under). Gradients grow with |Q| as in the
+    # peaked rows above and are held to the same normwise relative bound. dQ's
+    # first coordinate is left out: it is scale * 24 t * (sum of dS over the
+    # dominant tile t), a cancellation whose exact value is near 0 and whose
+    # computed value carries the error of D = rowsum(dO * O) taken from the
+    # bf16-rounded O (the backward's definition), multiplied by 24 t.
+    N = 300
+    q, k, v, do = draw(1, 2, 2, N, d, seed=11, dtype=torch.bfloat16)
+    q, k = q.float(), k.float()
+    q[..., 0] = 4.0
+    k[..., 0] = 24.0 * (torch.arange(N) // 64).float()[None, :, None]
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    scale = default_scale(d)
+    o, lse, dq, dk, dv = run_fwd_bwd(q, k, v, do, causal, scale)
+    ro, rl, rdq, rdk, rdv = oracle_full(q, k, v, do, causal, scale)
+    check_bf16("o", o, ro)
+    check_abs("lse", lse, rl, BF16_LSE_ABS)
+    for n, g_, r_ in (("dq[..., 1:]", dq[..., 1:], rdq[..., 1:]), ("dk", dk, rdk), ("dv", dv, rdv)):
+        check_rel(n, g_, r_, 1e-2)
+
+
 def test_identical_keys_give_mean_of_values_on_gpu():
     q, k, v, do = draw(1, 2, 2, 256, 64, seed=8, dtype=torch.bfloat16)
     k = k[:, :1].expand(-1, 256, -1, -1).contiguous()
