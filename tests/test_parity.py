@@ -137,6 +137,38 @@ def test_float32_gradients_meet_flat_bar(shape, causal):
                        oracle_full(q, k, v, do, causal, scale))
 
 
+def guarded(t, extra=256):
+    """t (batch 1) in the first rows of a longer device buffer whose other rows
+    hold NaN. Tiles that run past a tensor's last row must read those rows as
+    zeros (the tile loads' range check) or not at all: any read of the buffer's
+    tail brings NaN into the results."""
+    assert t.shape[0] == 1
+    buf = torch.full((1, t.shape[1] + extra) + tuple(t.shape[2:]), float("nan"), dtype=t.dtype, device=DEV)
+    buf[:, : t.shape[1]] = t.to(DEV)
+    view = buf[:, : t.shape[1]]
+    assert view.is_contiguous()
+    return view
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("shape", [(1, 4, 2, 200, 128), (1, 4, 4, 130, 64), (1, 2, 1, 1000, 128)],
+                         ids=lambda s: "B%dH%dKV%dN%dd%d" % s)
+def test_rows_past_the_end_are_not_read(shape, causal, dtype):
+    B, H, Hkv, N, d = shape
+    q, k, v, do = draw(B, H, Hkv, N, d, seed=700 + N, dtype=dtype)
+    scale = default_scale(d)
+    qd, kd, vd, dod = (guarded(t) for t in (q, k, v, do))
+    o = guarded(torch.full(q.shape, float("nan"), dtype=dtype))
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=DEV)
+    mi.fwd(qd, kd, vd, causal, scale, out=o, out_lse=lse)
+    dq, dk, dv = nan_like(qd), nan_like(kd), nan_like(vd)
+    mi.bwd(qd, kd, vd, o, lse, dod, causal, scale, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    gpu = [f64(t) for t in (o, lse, dq, dk, dv)]
+    compare_full(gpu, oracle_full(q, k, v, do, causal, scale), dtype)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_uniform_rows(causal):
     # Q = 0: every score is 0, so each row is the mean of its visible values
