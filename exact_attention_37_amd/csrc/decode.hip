@@ -150,8 +150,10 @@ void fwd_split_kernel(SplitParams p) {
   // covers tensor tile bytes [(s % TILE_KB) KB, +1 KB); lane l fills 16 bytes
   // at 16 l: tile row rr, logical chunk ch (padding from chunk 0), read from
   // byte loff[j] = 2 (rr * row stride + 8 ch) past the tile's first key. Keys
-  // past the cache's last row read as zeros (buffer range check); keys past
-  // k_hi are masked.
+  // past the sequence's valid length read as zeros (buffer range check): a
+  // cache's rows past its length may hold anything, NaN included, and a
+  // masked score's zero weight times such a V row would not be zero. Keys
+  // past k_hi are masked.
   uint32_t loff[NL];
 #pragma unroll
   for (int j = 0; j < NL; ++j) {
@@ -183,7 +185,7 @@ void fwd_split_kernel(SplitParams p) {
     wait_global_loads();
 
     const int ntile = k_hi > k_lo ? (k_hi - k_lo + DBC - 1) / DBC : 0;
-    const uint32_t kbytes = (uint32_t)(((p.Nk - 1) * krs + D) * 2);
+    const uint32_t kbytes = L > 0 ? (uint32_t)(((L - 1) * krs + D) * 2) : 0u;   // rows [0, L)
     const u32x4 rk = rsrc_words(K, kbytes), rv = rsrc_words(V, kbytes);
     auto load_tile = [&](int buf, int key0) {
 #pragma unroll

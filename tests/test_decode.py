@@ -58,6 +58,42 @@ def test_kvcache_matches_oracle(case):
     run_case(q, k, v, lt, causal, d ** -0.5, nsplit)
 
 
+def nan_past_lengths(t, lens, extra=256):
+    """A device copy of cache t [B, Nk, Hkv, d] whose rows at or past each
+    sequence's length hold NaN, inside a buffer that continues with NaN rows
+    past the last sequence: caches hold stale or unwritten rows there, and any
+    use of them (even times a zero weight) shows up as NaN in the output."""
+    B, Nk = t.shape[:2]
+    flat = torch.full((t.numel() + extra * t[0, 0].numel(),), float("nan"), dtype=t.dtype, device=DEV)
+    view = flat[: t.numel()].view(t.shape)
+    view.copy_(t.to(DEV))
+    for b in range(B):
+        view[b, int(lens[b]):] = float("nan")
+    return view
+
+
+@pytest.mark.parametrize("case", [
+    (2, 8, 2, 1, 1000, 128, [1000, 517], True, 0),
+    (3, 4, 4, 3, 300, 64, [300, 45, 2], True, 3),
+    (4, 8, 4, 2, 900, 64, [900, 5, 0, 64], True, 13),
+    (3, 16, 2, 40, 1200, 128, [1200, 300, 77], True, 13),
+    (2, 8, 2, 1, 4000, 128, [4000, 10], False, 200),
+    (1, 32, 8, 1, 4097, 128, [4097], False, 7),
+], ids=lambda c: "B%dH%dKV%dNq%dNk%dd%d" % c[:6])
+def test_kvcache_rows_past_each_length_are_not_used(case):
+    B, H, Hkv, Nq, Nk, d, lens, causal, nsplit = case
+    q, k, v, _ = draw_cache(B, H, Hkv, Nq, Nk, d, seed=300 + Nk)
+    print("case", case, flush=True)
+    kd, vd = nan_past_lengths(k, lens), nan_past_lengths(v, lens)
+    ld = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    o, lse = mi.fwd_kvcache(q.to(DEV), kd, vd, ld, causal, d ** -0.5, nsplit)
+    torch.cuda.synchronize()
+    ro, rl = oracle.forward_kvcache(as_f64(q), as_f64(k), as_f64(v), lens, causal, d ** -0.5)
+    eo = check_bf16("o", f64(o), ro)
+    el = check_abs("lse", f64(lse), rl, BF16_LSE_ABS)
+    print("errors o %.3g lse %.3g" % (eo, el), flush=True)
+
+
 def test_kvcache_split_count_changes_only_rounding():
     q, k, v, lens = draw_cache(2, 8, 2, 2, 3000, 128, seed=9, min_len=1500)
     qd, kd, vd, ld = (t.to(DEV) for t in (q, k, v, lens))

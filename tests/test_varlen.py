@@ -99,6 +99,33 @@ def test_padding_rows_outside_every_sequence_are_untouched():
         check_bf16(name, f64(g[:180]), r[:180])
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_rows_outside_every_sequence_are_not_read(d):
+    # the rows after the last sequence, and a buffer tail past the tensor,
+    # hold NaN: a tile that reads any of them, even under a zero weight,
+    # brings NaN into the outputs of the sequences
+    lengths, cu = [200, 150], torch.tensor([0, 130, 197], dtype=torch.int32)
+    q, k, v, do, _ = draw_varlen(lengths, 4, 2, d, seed=43 + d)
+    dev = []
+    for t in (q, k, v, do):
+        flat = torch.full((t.numel() + 256 * t[0].numel(),), float("nan"), dtype=t.dtype, device=DEV)
+        x = flat[: t.numel()].view(t.shape)
+        x.copy_(t.to(DEV))
+        x[197:] = float("nan")
+        dev.append(x)
+    qd, kd, vd, dod = dev
+    o, lse = mi.fwd_varlen(qd, kd, vd, cu.to(DEV), 130, True, 0.1)
+    dq, dk, dv = mi.bwd_varlen(qd, kd, vd, o, lse, dod, cu.to(DEV), 130, True, 0.1)
+    torch.cuda.synchronize()
+    qq, kk, vv, dd = (as_f64(t) for t in (q, k, v, do))
+    ro, rl = oracle.forward_varlen(qq, kk, vv, cu.numpy(), True, 0.1)
+    check_bf16("o", f64(o[:197]), ro[:197])
+    check_abs("lse", f64(lse[:, :197]), rl[:, :197], BF16_LSE_ABS)
+    rg = oracle.backward_varlen(qq, kk, vv, dd, cu.numpy(), True, 0.1)
+    for name, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), rg):
+        check_bf16(name, f64(g[:197]), r[:197])
+
+
 @pytest.mark.slow
 def test_packed16k_sampled():
     w = VARLEN_WORKLOADS["packed16k"]
