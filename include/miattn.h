@@ -89,8 +89,10 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *   k_cache, v_cache: [B, Nk, Hkv, d] bf16, Nk = cache capacity in rows
  *   k_lens        : device int32 [B], the number of valid cache rows of each
  *                   batch entry (values are clamped to [0, Nk]), or NULL for
- *                   Nk everywhere. Rows at or past k_lens[b] are never read
- *                   into the result.
+ *                   Nk everywhere. Rows at or past k_lens[b] may hold
+ *                   anything (stale or unwritten values, NaN included): the
+ *                   kernels read them as zeros and they never enter the
+ *                   result.
  *   lse           : [B, H, Nq] float32
  *   causal        : 0 = every query row sees all valid cache rows; 1 = query
  *                   row i of batch b sits at position k_lens[b] - Nq + i and
