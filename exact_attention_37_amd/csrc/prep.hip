@@ -100,8 +100,11 @@ __global__ __launch_bounds__(256) void merge_kernel(const TA* o_a, const float* 
   float x[8], y[8], z[8];
   load8(o_a + off, x);
   load8(o_b + off, y);
+  // a partial over an empty key set (lse = -inf) contributes nothing,
+  // whatever its o holds (zeros by convention, but also stale values or NaN)
+  const bool use_a = la != -INFINITY, use_b = lb != -INFINITY;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) z[e] = wa * x[e] + wb * y[e];
+  for (int e = 0; e < 8; ++e) z[e] = (use_a ? wa * x[e] : 0.f) + (use_b ? wb * y[e] : 0.f);
   store8(o + off, z);
   if (part == 0) lse[li] = l;
 }

@@ -259,7 +259,8 @@ int attn_bwd_timed(const void* q, const void* k, const void* v, const void* o, c
  * rebuttal page: partial softmax results are combined across devices):
  *     lse = ln(e^lse_a + e^lse_b)  (computed with the max factored out)
  *     o   = e^(lse_a - lse) o_a + e^(lse_b - lse) o_b
- * Rows where both lse are -inf give o = 0, lse = -inf.
+ * A partial whose lse is -inf (an empty key set) contributes nothing,
+ * whatever its o holds; rows where both lse are -inf give o = 0, lse = -inf.
  * o_a, o_b, o: [B, N, H, d] of `dtype`; lse_a, lse_b, lse: [B, H, N] float32.
  * In-place use is allowed: o may equal o_a or o_b, lse may equal lse_a or
  * lse_b (each element is read before it is written by the same thread).

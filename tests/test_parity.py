@@ -514,6 +514,13 @@ def test_merge_empty_partials():
     o2, l2 = mi.merge(empty_o, empty_l, empty_o, empty_l)
     torch.cuda.synchronize()
     assert torch.all(o2 == 0) and torch.all(torch.isneginf(l2))
+    # an empty partial's o is never used, whatever it holds
+    nan_o = torch.full_like(o_a, float("nan"))
+    o3, l3 = mi.merge(nan_o, empty_l, o_a, l_a)
+    o4, l4 = mi.merge(nan_o, empty_l, nan_o, empty_l)
+    torch.cuda.synchronize()
+    assert torch.equal(o3, o_a) and torch.equal(l3, l_a)
+    assert torch.all(o4 == 0) and torch.all(torch.isneginf(l4))
 
 
 # ---------------------------------------------------------------- accumulate mode
