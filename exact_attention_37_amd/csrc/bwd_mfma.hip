@@ -836,6 +836,8 @@ void bwd_dq_kernel(Params p) {
         },
         [&](auto ic) {
           constexpr int i = decltype(ic)::value;
+          constexpr int NSTEP = 2 * PS + 2 * PD;
+          progress_priority<i, NSTEP / 2, 3 * NSTEP / 4, 7 * NSTEP / 8>();
           if constexpr (i < PS) {                 // phase 0: next tile's direct loads
             constexpr int lo_ = i * NL / PS, hi_ = (i + 1) * NL / PS;
             [&]<int... Ws>(std::integer_sequence<int, Ws...>) {

@@ -358,6 +358,7 @@ void fwd_mfma_kernel(Params p) {
       const int jk = t2 * BC, jv = t1 * BC;
       scores(sn, vb ^ 1, [&](auto ic) {
         constexpr int i = decltype(ic)::value;
+        progress_priority<i, 2 * KS, 2 * KS + 2 * DB, 2 * KS + 3 * DB>();   // steps 0 .. 2 KS - 1 of the tile
         prob_steps(sc, pc, lsb, KB1{}, ic, std::integral_constant<int, 2 * KS>{});
         constexpr int lo = i * NL / (2 * KS), hi = (i + 1) * NL / (2 * KS);
         [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
@@ -385,7 +386,12 @@ void fwd_mfma_kernel(Params p) {
           constexpr int i = decltype(ic)::value, kq = i / DB, db = i % DB;
           acc[db] = mfma32(a, pc[kq], acc[db]);
         },
-        [&](auto ic) { prob_steps(sn, pn, lsa, KB0{}, ic, std::integral_constant<int, 4 * DB>{}); },
+        [&](auto ic) {
+          // the tile's steps 2 KS + i of 2 KS + 4 DB: step-downs at 1/2, 3/4, 7/8
+          static_assert(2 * KS == 4 * DB, "the two phases have equal step counts");
+          progress_priority<2 * KS + decltype(ic)::value, 2 * KS, 2 * KS + 2 * DB, 2 * KS + 3 * DB>();
+          prob_steps(sn, pn, lsa, KB0{}, ic, std::integral_constant<int, 4 * DB>{});
+        },
         std::true_type{});
     t1 = t2;
     t2 = t3;
