@@ -92,6 +92,10 @@ def test_tiny_fp32_matches_oracle(causal):
 SMALL = [
     # B, H, Hkv, N, d
     (1, 1, 1, 1, 64),
+    (2, 2, 1, 1, 128),      # one row and one key per sequence
+    (1, 2, 2, 2, 128),
+    (1, 4, 4, 63, 128),     # one row short of a key tile
+    (2, 2, 2, 65, 128),     # one row past it
     (1, 2, 2, 17, 64),
     (2, 2, 1, 127, 64),
     (1, 4, 2, 129, 128),
