@@ -58,6 +58,28 @@ def test_kvcache_matches_oracle(case):
     run_case(q, k, v, lt, causal, d ** -0.5, nsplit)
 
 
+def random_cache_cases(n=10, seed=2027):
+    """(B, H, Hkv, Nq, Nk, d, lens, causal, nsplit): decode (Nq = 1) and
+    chunked prefill, lengths 0..Nk, split counts from the default to 40."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        Hkv = int(rng.choice([1, 2, 4]))
+        H = Hkv * int(rng.choice([1, 2, 4, 8]))
+        B = int(rng.integers(1, 5))
+        Nq = 1 if rng.random() < 0.5 else int(rng.integers(2, 41))
+        Nk = int(rng.integers(1, 3000))
+        lens = [int(x) for x in rng.integers(0, Nk + 1, size=B)]
+        nsplit = int(rng.choice([0, 1, 3, 17, 40]))
+        cases.append((B, H, Hkv, Nq, Nk, int(rng.choice([64, 128])), lens, bool(rng.integers(0, 2)), nsplit))
+    return cases
+
+
+@pytest.mark.parametrize("case", random_cache_cases(), ids=[str(i) for i in range(10)])
+def test_random_kvcache_match_oracle(case):
+    test_kvcache_matches_oracle(case)
+
+
 def nan_past_lengths(t, lens, extra=256):
     """A device copy of cache t [B, Nk, Hkv, d] whose rows at or past each
     sequence's length hold NaN, inside a buffer that continues with NaN rows

@@ -115,6 +115,77 @@ def test_small_shapes_match_oracle(shape, causal, dtype):
     compare_full(run_fwd_bwd(q, k, v, do, causal, scale), oracle_full(q, k, v, do, causal, scale), dtype)
 
 
+def random_cases(n=48, seed=2024):
+    """Seeded random problem shapes, for combinations the hand-picked cases
+    may miss: head counts and group sizes, lengths on and off tile edges,
+    masks, windows, scales and both dtypes. Each entry:
+    (B, H, Hkv, N, d, causal, window, scale, dtype)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        Hkv = int(rng.choice([1, 2, 3]))
+        H = Hkv * int(rng.choice([1, 2, 4, 5]))
+        B = int(rng.integers(1, 4))
+        N = int(rng.integers(1, 700))
+        d = int(rng.choice([64, 128]))
+        causal = bool(rng.integers(0, 2))
+        window = int(rng.integers(1, N + 64)) if causal and rng.random() < 0.4 else 0
+        scale = float(rng.choice([d ** -0.5, 0.3 * d ** -0.5, -d ** -0.5]))
+        dtype = torch.float32 if rng.random() < 0.25 else torch.bfloat16
+        cases.append((B, H, Hkv, N, d, causal, window, scale, dtype))
+    return cases
+
+
+@pytest.mark.parametrize("case", random_cases(), ids=lambda c: "B%dH%dKV%dN%dd%d-c%d-w%d-%s" % (
+    c[0], c[1], c[2], c[3], c[4], int(c[5]), c[6], "f32" if c[8] == torch.float32 else "bf16"))
+def test_random_shapes_match_oracle(case):
+    B, H, Hkv, N, d, causal, window, scale, dtype = case
+    print("case", case, flush=True)
+    q, k, v, do = draw(B, H, Hkv, N, d, seed=9000 + N + H, dtype=dtype)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    o, lse = nan_like(qd), torch.full((B, H, N), float("nan"), dtype=torch.float32, device=DEV)
+    mi.fwd(qd, kd, vd, causal, scale, out=o, out_lse=lse, window=window)
+    dq, dk, dv = nan_like(qd), nan_like(kd), nan_like(vd)
+    mi.bwd(qd, kd, vd, o, lse, dod, causal, scale, dq=dq, dk=dk, dv=dv, window=window)
+    torch.cuda.synchronize()
+    gpu = [f64(t) for t in (o, lse, dq, dk, dv)]
+    qq, kk, vv, dd = (as_f64(t) for t in (q, k, v, do))
+    ro, rl = oracle.forward(qq, kk, vv, causal, scale, window=window)
+    rdq, rdk, rdv = oracle.backward(qq, kk, vv, dd, causal, scale, window=window)
+    compare_full(gpu, (ro, rl, rdq, rdk, rdv), dtype)
+
+
+def random_chunked_cases(n=10, seed=2025):
+    """(B, H, Hkv, N, d, nchunks, dtype): causal problems cut into an even
+    number of equal chunks (the chunk driver's condition)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        Hkv = int(rng.choice([1, 2]))
+        H = Hkv * int(rng.choice([1, 2, 3]))
+        nch = int(rng.choice([2, 4, 6, 8]))
+        N = nch * int(rng.integers(3, 90))
+        d = int(rng.choice([64, 128]))
+        dtype = torch.float32 if rng.random() < 0.3 else torch.bfloat16
+        cases.append((int(rng.integers(1, 3)), H, Hkv, N, d, nch, dtype))
+    return cases
+
+
+@pytest.mark.parametrize("case", random_chunked_cases(), ids=lambda c: "B%dH%dKV%dN%dd%d-x%d-%s" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], "f32" if c[6] == torch.float32 else "bf16"))
+def test_random_chunked_match_oracle(case):
+    B, H, Hkv, N, d, nch, dtype = case
+    print("case", case, flush=True)
+    q, k, v, do = draw(B, H, Hkv, N, d, seed=9500 + N, dtype=dtype)
+    scale = default_scale(d)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    o, lse = mi.fwd_chunked(qd, kd, vd, nch, scale)
+    dq, dk, dv = mi.bwd_chunked(qd, kd, vd, o, lse, dod, nch, scale)
+    torch.cuda.synchronize()
+    gpu = [f64(t) for t in (o, lse, dq, dk, dv)]
+    compare_full(gpu, oracle_full(q, k, v, do, True, scale), dtype)
+
+
 # A negative scale is folded into Q (forward, dQ) or K (dK/dV) and scale 0 is
 # run as Q = 0 with scale 1: every kernel's sign handling is exercised here.
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])

@@ -56,6 +56,29 @@ def test_varlen_matches_oracle(case):
     print("errors", {k_: "%.3g" % v_ for k_, v_ in errs.items()}, flush=True)
 
 
+def random_varlen_cases(n=10, seed=2026):
+    """(lengths, H, Hkv, d, causal, window, dtype) with 1-7 sequences of
+    0-450 rows each."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        lengths = [int(x) for x in rng.integers(0, 451, size=int(rng.integers(1, 8)))]
+        if sum(lengths) == 0:
+            lengths[0] = 1
+        Hkv = int(rng.choice([1, 2]))
+        H = Hkv * int(rng.choice([1, 2, 4]))
+        causal = bool(rng.integers(0, 2))
+        window = int(rng.integers(1, 300)) if causal and rng.random() < 0.4 else 0
+        dtype = torch.float32 if rng.random() < 0.25 else torch.bfloat16
+        cases.append((lengths, H, Hkv, int(rng.choice([64, 128])), causal, window, dtype))
+    return cases
+
+
+@pytest.mark.parametrize("case", random_varlen_cases(), ids=[str(i) for i in range(10)])
+def test_random_varlen_match_oracle(case):
+    test_varlen_matches_oracle(case)
+
+
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
 def test_equal_lengths_equal_the_batched_entry_points_bitwise(dt):
     # three sequences of 333 rows packed = a batch of three: the same tiles,
