@@ -58,6 +58,24 @@ def test_blocksparse_matches_oracle(case):
     print("errors", {k_: "%.3g" % v_ for k_, v_ in errs.items()}, flush=True)
 
 
+def random_block_cases(n=10, seed=2028):
+    """(B, H, Hkv, N, d, causal, density, keep the diagonal, dtype)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        Hkv = int(rng.choice([1, 2]))
+        H = Hkv * int(rng.choice([1, 2, 4]))
+        cases.append((int(rng.integers(1, 3)), H, Hkv, int(rng.integers(1, 1300)), int(rng.choice([64, 128])),
+                      bool(rng.integers(0, 2)), float(rng.choice([0.1, 0.3, 0.6, 0.9])), bool(rng.integers(0, 2)),
+                      torch.float32 if rng.random() < 0.25 else torch.bfloat16))
+    return cases
+
+
+@pytest.mark.parametrize("case", random_block_cases(), ids=[str(i) for i in range(10)])
+def test_random_blocksparse_match_oracle(case):
+    test_blocksparse_matches_oracle(case)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
 def test_every_block_kept_equals_dense_bitwise(causal, dt):
