@@ -238,9 +238,11 @@ void bwd_dkdv_kernel(Params p) {
   //   phase 2: S, dP of half 1 of tile k       + softmax group 1 of half 0 of tile k
   //   phase 3: dV^T, dK^T over half 0 of k     + softmax group 0 of half 1 of tile k
   // (half = 32 query rows, group = 16 of them). Tile -1 is an all-zero buffer
-  // with LSE = +inf (P = 0), and one empty tile past the last query row
-  // (zero rows, LSE = +inf) drains the pipeline. Each phase prefetches the
-  // LSE / D values the next phase's softmax group needs.
+  // with LSE = +inf (P = 0); the last iteration loads an empty tile past the
+  // last query row (zero rows, LSE = +inf), and a drain after the loop does
+  // what is left of the last tile (its phase-1 products and the softmax they
+  // need). Each phase prefetches the LSE / D values the next phase's softmax
+  // group needs.
   constexpr int PL = D / 8;          // lock steps per phase
   const int empty_q0 = nqt * DKV_BQ; // rows past the end: zeros, LSE = +inf
 
@@ -466,7 +468,38 @@ void bwd_dkdv_kernel(Params p) {
     if constexpr (WIN)
       while (kt_ < base + per_head) iteration(std::true_type{});
   }
-  iteration(std::false_type{});       // the draining tile
+  // Drain: the last tile's dV^T, dK^T over its half 1 (what an iteration's
+  // phase 1 would do), with the softmax of that half's group 1 first (what
+  // its phase 0 would do); the last tile sits in buffer cb - 1. With no
+  // tile at all that is the zero buffer of tile -1, with P = dS = 0.
+  {
+    const int lb = cb == 0 ? 2 : cb - 1;
+    const uint32_t lq = lds_q0 + lb * BUF_BYTES;
+    const uint32_t btl[2] = {lds_opaque(lq + 2 * rd_t[0]), lds_opaque(lq + 2 * rd_t[1])};
+    lockstep_products<PL, 4>(
+        [&](auto ic) {   // step j = (t, db, which), two transposing reads
+          constexpr int j = decltype(ic)::value;
+          constexpr int t = 2 + j / (2 * DB), db = (j >> 1) % DB;
+          constexpr int off = ((j & 1) ? 0 : TILE) + 16 * t * ROW + 32 * db;   // Q^T for dK, dO^T for dV
+          const bf16x4 r0 = lds_read_tr4_at(btl[0] + 2 * off);
+          const bf16x4 r1 = lds_read_tr4_at(btl[1] + 2 * off);
+          return bf16x8{r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+        },
+        [&](auto ic, bf16x8 a) {
+          constexpr int j = decltype(ic)::value;
+          constexpr int t = 2 + j / (2 * DB), db = (j >> 1) % DB;
+          if constexpr (j & 1) mfma32_agpr(dk[db], a, da[t]);
+          else mfma32_agpr(dv[db], a, pa[t]);
+        },
+        [&](auto ic) {   // the group's four softmax sub-steps, before its products (step 2 DB on)
+          constexpr int j = decltype(ic)::value;
+          static_assert(2 * DB >= 4, "sub-steps before the group's first product");
+          if constexpr (j < 4)
+            softmax_sub(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{},
+                        std::integral_constant<int, j>{}, std::integral_constant<int, 0>{});
+        },
+        std::true_type{});
+  }
 
   // ---- store dK^T, dV^T: lane (g, key n), register r <-> column 32 db + 8 (r/4) + 4g + r%4
 #pragma unroll
