@@ -635,3 +635,47 @@ def test_bwd_timed_matches_bwd_and_records_marks(dtype):
         assert torch.equal(a, b), name
     for i in range(3):
         assert ev[i].elapsed_time(ev[i + 1]) >= 0.0
+
+
+# ---------------------------------------------------------------- run-to-run reproducibility
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_outputs_are_bitwise_reproducible(dtype):
+    """No workgroup shares a partial sum with another (no atomics), so every
+    entry point gives the same bits on every call, also with other calls
+    (other shapes, scratch reuse) in between."""
+    from workloads import draw_varlen, draw_cache
+    q, k, v, do = to_dev(*draw(2, 8, 2, 777, 128, seed=77, dtype=dtype))
+    vq, vk, vv, vdo, cu = draw_varlen([300, 0, 129, 400], 4, 2, 64, seed=78, dtype=dtype)
+    vq, vk, vv, vdo, cu = to_dev(vq, vk, vv, vdo, cu)
+    cq, ck, cv, lens = to_dev(*draw_cache(3, 8, 2, 1, 2000, 128, seed=79, min_len=0))
+    xq, xk, xv, xdo = to_dev(*draw(1, 4, 2, 768, 128, seed=81, dtype=dtype))
+    mask = torch.from_numpy(np.ones(mi.block_mask_shape(777), dtype=np.uint8)).to(DEV)
+    mask[::2, 1::3] = 0
+
+    def run_all():
+        out = []
+        o, lse = mi.fwd(q, k, v, True, 0.09)
+        out += [o, lse, *mi.bwd(q, k, v, o, lse, do, True, 0.09)]
+        o, lse = mi.fwd(q, k, v, True, 0.09, window=100)
+        out += [o, lse, *mi.bwd(q, k, v, o, lse, do, True, 0.09, window=100)]
+        o, lse = mi.fwd_chunked(xq, xk, xv, 4, 0.09)
+        out += [o, lse, *mi.bwd_chunked(xq, xk, xv, o, lse, xdo, 4, 0.09)]
+        o, lse = mi.fwd_varlen(vq, vk, vv, cu, 400, True, 0.1)
+        out += [o, lse, *mi.bwd_varlen(vq, vk, vv, o, lse, vdo, cu, 400, True, 0.1)]
+        o, lse = mi.fwd_blocksparse(q, k, v, mask, True, 0.09)
+        out += [o, lse, *mi.bwd_blocksparse(q, k, v, o, lse, do, mask, True, 0.09)]
+        if dtype == torch.bfloat16:
+            out += list(mi.fwd_kvcache(cq, ck, cv, lens, True, 0.088, 13))
+        torch.cuda.synchronize()
+        return [t.clone() for t in out]
+
+    first = run_all()
+    # other work in between: a different shape through the same entry points
+    # and scratch
+    q2, k2, v2, do2 = to_dev(*draw(1, 4, 4, 1500, 64, seed=80, dtype=dtype))
+    o2, l2 = mi.fwd(q2, k2, v2, False, 0.1)
+    mi.bwd(q2, k2, v2, o2, l2, do2, False, 0.1)
+    second = run_all()
+    for i, (a, b) in enumerate(zip(first, second)):
+        assert torch.equal(a, b), "output %d differs between calls" % i
