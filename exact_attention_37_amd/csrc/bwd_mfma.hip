@@ -54,7 +54,9 @@ constexpr int DKV_BQ = 64;           // query rows per streamed tile
 // 4-row transposing reads of dV^T = dO^T P, dK^T = Q^T dS are both free of
 // bank conflicts, and the tile is written by direct global -> LDS loads.
 // Three buffers (previous, current and next tile); within a buffer dO
-// follows Q, so both are reached from one base address.
+// follows Q and the tile's row statistics follow dO, so all three are
+// reached from one base address. A buffer is 512 bytes past a multiple of
+// the 256-byte bank cycle, which keeps the bank pattern of every read.
 template <int D>
 struct DkdvSmem {
   static constexpr int ROW = D + 32;
@@ -62,8 +64,8 @@ struct DkdvSmem {
   struct Buf {
     bf16 q[TILE];
     bf16 o[TILE];              // dO
+    float stat[2][DKV_BQ];     // [0]: LSE * log2(e) (+inf past the last row), [1]: -D
   };
-  float stat[3][2][DKV_BQ];    // [0]: LSE * log2(e) (+inf past the last row), [1]: -D
   Buf buf[3];
 };
 
@@ -184,12 +186,15 @@ void bwd_dkdv_kernel(Params p) {
   // pointer once (buffers follow at sizeof(Buf), dO at + 2 TILE in each)
   const uint32_t lds_q0 = lds_addr(sm.buf[0].q);
   constexpr uint32_t BUF_BYTES = (uint32_t)sizeof(typename DkdvSmem<D>::Buf);
-  auto load_piece = [&](int piece, int buf, int h, int q0) {   // piece < 2 NL: Q then dO
+  constexpr uint32_t STAT_BYTES = 4u * TILE;       // stats past Q and dO in a buffer
+  // piece < 2 NL (Q then dO) of the tile at rows q0 of head h into the
+  // buffer at byte offset bo from buffer 0
+  auto load_piece = [&](int piece, uint32_t bo, int h, int q0) {
     const int i = piece % NL;
     const bool is_o = piece >= NL;
     const uint32_t soff = (uint32_t)(q0 * qrs + h * D) * 2u;
-    buffer_load_lds16_async(is_o ? ro : rq, loff[i], soff,
-                            lds_q0 + buf * BUF_BYTES + (is_o ? 2u * TILE : 0u) + (uint32_t)(wave * NL + i) * 1024u);
+    buffer_load_lds16_async(is_o ? ro : rq, loff[i], soff, bo,
+                            lds_q0 + (is_o ? 2u * TILE : 0u) + (uint32_t)(wave * NL + i) * 1024u);
   };
   float st;          // LSE (tid < 64) or D (64 <= tid < 128) of row q0 + tid % 64
   bool st_valid;
@@ -201,10 +206,10 @@ void bwd_dkdv_kernel(Params p) {
     st_valid = row < p.Nq;
     st = st_base[h * p.N + min(row, p.Nq - 1)];
   };
-  auto stat_store = [&](int buf) {
+  auto stat_store = [&](uint32_t bo) {   // into the buffer at byte offset bo
     if (tid < 128) {
       const float v = (tid < 64) ? (st_valid ? st * kLog2e : INFINITY) : (st_valid ? -st : 0.f);
-      sm.stat[buf][tid >> 6][tid & 63] = v;
+      *(__attribute__((address_space(3))) float*)(lds_q0 + bo + STAT_BYTES + 4 * tid) = v;
     }
   };
 
@@ -253,7 +258,7 @@ void bwd_dkdv_kernel(Params p) {
       *(f32x4*)(sm.buf[2].q + 8 * i) = z;
       *(f32x4*)(sm.buf[2].o + 8 * i) = z;
     }
-    if (tid < 128) sm.stat[2][tid >> 6][tid & 63] = (tid < 64) ? INFINITY : 0.f;
+    if (tid < 128) sm.buf[2].stat[tid >> 6][tid & 63] = (tid < 64) ? INFINITY : 0.f;
   }
   // block-sparse: query tile of the next tile and of the one after (fetched
   // an iteration ahead, so the list reads never stall the tile loads)
@@ -285,7 +290,7 @@ void bwd_dkdv_kernel(Params p) {
   // LSE (log2 units) of the 8 query rows of the group being softmaxed,
   // double-buffered: slot (phase & 1) is consumed, the other one prefetched
   f32x4 st_l[2][2];
-  const uint32_t stat_lane = lds_addr(&sm.stat[0][0][0]) + 32 * g;   // + rows 8g..8g+7
+  const uint32_t stat_lane = lds_q0 + STAT_BYTES + 32 * g;   // buffer 0, + rows 8g..8g+7
   // stb: LDS address of this lane's rows in the stats of one buffer
   auto stat_read = [&](int slot, uint32_t stb, int qb, int g2) {
     const int off = (qb * 32 + g2 * 16) * 4;
@@ -306,7 +311,7 @@ void bwd_dkdv_kernel(Params p) {
       }
     return x;
   };
-  stat_read(0, stat_lane + 2 * (2 * DKV_BQ * 4), 1, 1);   // tile -1, half 1, group 1
+  stat_read(0, stat_lane + 2 * BUF_BYTES, 1, 1);   // tile -1, half 1, group 1
 
   // softmax sub-step k (0..3) of group g2 of half qb: P and dS of elements
   // e = 2k, 2k+1 of the group (register r = 8 g2 + e), stats from `slot`
@@ -343,10 +348,12 @@ void bwd_dkdv_kernel(Params p) {
   // code at all (a mask test inside one loop body is turned into
   // per-element selects that every tile pays for).
   int kt_ = 0;
-  int cb = 0;                          // LDS buffer of tile k (k % 3, kept incrementally)
+  uint32_t cbo = 0;   // byte offset of tile k's LDS buffer (k % 3) from buffer 0
   auto iteration = [&](auto mc) {
     constexpr bool MASKED = decltype(mc)::value;
-      const int pb = cb == 0 ? 2 : cb - 1, nb = cb == 2 ? 0 : cb + 1;
+      // buffers of tiles k - 1 and k + 1
+      const uint32_t pbo = cbo == 0 ? 2 * BUF_BYTES : cbo - BUF_BYTES;
+      const uint32_t nbo = cbo == 2 * BUF_BYTES ? 0 : cbo + BUF_BYTES;
       const bool real = kt_ < niter;
       const int q0 = SPARSE ? q0_cur : (real ? (first + t_cur) * DKV_BQ : empty_q0);
       // the tile after this one
@@ -363,12 +370,12 @@ void bwd_dkdv_kernel(Params p) {
       const int h_ld = nx_real ? h_nx : gkv * p.G;   // a valid head also for the empty tile
       const int mthr = kpos - (p.q_start + q0);     // query index inside the tile < mthr -> masked
       // LDS read bases of this iteration (byte addresses; dO at +TILE from Q)
-      const uint32_t cq = lds_q0 + cb * BUF_BYTES;
-      const uint32_t pq = lds_q0 + pb * BUF_BYTES;
+      const uint32_t cq = lds_q0 + cbo;
+      const uint32_t pq = lds_q0 + pbo;
       const uint32_t bs[2] = {lds_opaque(cq + 2 * rd_s[0]), lds_opaque(cq + 2 * rd_s[1])};
       const uint32_t bt[2] = {lds_opaque(cq + 2 * rd_t[0]), lds_opaque(cq + 2 * rd_t[1])};
       const uint32_t btp[2] = {lds_opaque(pq + 2 * rd_t[0]), lds_opaque(pq + 2 * rd_t[1])};
-      const uint32_t stb = lds_opaque(stat_lane + cb * (2 * DKV_BQ * 4));
+      const uint32_t stb = lds_opaque(stat_lane + cbo);
       // -D of half 0 now; that of half 1 two steps before its first product
       const f32x16 di0 = dinit_read(stb, 0);
       f32x16 di1;
@@ -425,12 +432,12 @@ void bwd_dkdv_kernel(Params p) {
             if constexpr (ph == 0) {            // next tile: direct loads, then its LSE / D
               constexpr int lo = j * (2 * NL) / PL, hi = (j + 1) * (2 * NL) / PL;
               [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
-                (load_piece(lo + Ws, nb, h_ld, q0_nx), ...);
+                (load_piece(lo + Ws, nbo, h_ld, q0_nx), ...);
               }(std::make_integer_sequence<int, hi - lo>{});
               if constexpr (j == PL - 1) stat_load(h_ld, q0_nx);
             }
             if constexpr (ph == 1 && j == PL - 2) di1 = dinit_read(stb, 1);
-            if constexpr (ph == 3 && j == PL - 1) stat_store(nb);
+            if constexpr (ph == 3 && j == PL - 1) stat_store(nbo);
             // diagonal tiles: mask each half's scores once its products are done
             if constexpr ((ph == 0 || ph == 2) && j == PL - 1) {
               if constexpr (MASKED) mask_half(ph == 0 ? s0 : s1, mthr - (ph / 2) * 32);
@@ -443,7 +450,7 @@ void bwd_dkdv_kernel(Params p) {
     t_cur = t_nx;
     q0_cur = q0_nx;
     ++kt_;
-    cb = cb == 2 ? 0 : cb + 1;
+    cbo = nbo;
   };
   // The masked tiles of a head: a prefix whose rows start before this
   // wave's last key (the diagonal) and, under a sliding window, a suffix
@@ -470,11 +477,10 @@ void bwd_dkdv_kernel(Params p) {
   }
   // Drain: the last tile's dV^T, dK^T over its half 1 (what an iteration's
   // phase 1 would do), with the softmax of that half's group 1 first (what
-  // its phase 0 would do); the last tile sits in buffer cb - 1. With no
+  // its phase 0 would do); the last tile sits in the buffer before tile k's. With no
   // tile at all that is the zero buffer of tile -1, with P = dS = 0.
   {
-    const int lb = cb == 0 ? 2 : cb - 1;
-    const uint32_t lq = lds_q0 + lb * BUF_BYTES;
+    const uint32_t lq = lds_q0 + (cbo == 0 ? 2 * BUF_BYTES : cbo - BUF_BYTES);
     const uint32_t btl[2] = {lds_opaque(lq + 2 * rd_t[0]), lds_opaque(lq + 2 * rd_t[1])};
     lockstep_products<PL, 4>(
         [&](auto ic) {   // step j = (t, db, which), two transposing reads

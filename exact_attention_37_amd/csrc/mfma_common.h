@@ -140,6 +140,17 @@ __device__ __forceinline__ void buffer_load_lds16_async(u32x4 rsrc, uint32_t vof
                : "m0");
 }
 
+// The same load with the LDS address given as base + offset (both
+// wave-uniform), summed straight into M0: one scalar instruction fewer per
+// load where the base changes from tile to tile and the offsets do not.
+__device__ __forceinline__ void buffer_load_lds16_async(u32x4 rsrc, uint32_t voff, uint32_t soff,
+                                                        uint32_t lds_base, uint32_t lds_off) {
+  asm volatile("s_add_u32 m0, %0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds"
+               :
+               : "s"(lds_base), "s"(lds_off), "v"(voff), "s"(rsrc), "s"(soff)
+               : "m0", "scc");
+}
+
 // acc += A B with the accumulator held in AGPRs (the matrix cores' own
 // accumulation registers), for accumulators that live through a whole loop
 // and are read only after it: they then take no VGPRs. The compiler does not
