@@ -187,24 +187,26 @@ void bwd_dkdv_kernel(Params p) {
   const uint32_t lds_q0 = lds_addr(sm.buf[0].q);
   constexpr uint32_t BUF_BYTES = (uint32_t)sizeof(typename DkdvSmem<D>::Buf);
   constexpr uint32_t STAT_BYTES = 4u * TILE;       // stats past Q and dO in a buffer
-  // piece < 2 NL (Q then dO) of the tile at rows q0 of head h into the
-  // buffer at byte offset bo from buffer 0
-  auto load_piece = [&](int piece, uint32_t bo, int h, int q0) {
+  // piece < 2 NL (Q then dO) of a tile into the buffer at byte offset bo
+  // from buffer 0; soff = 2 (q0 qrs + h D) for the tile at rows q0 of head h
+  auto load_piece = [&](int piece, uint32_t bo, uint32_t soff) {
     const int i = piece % NL;
     const bool is_o = piece >= NL;
-    const uint32_t soff = (uint32_t)(q0 * qrs + h * D) * 2u;
     buffer_load_lds16_async(is_o ? ro : rq, loff[i], soff, bo,
                             lds_q0 + (is_o ? 2u * TILE : 0u) + (uint32_t)(wave * NL + i) * 1024u);
   };
+  auto tile_soff = [&](int h, int q0) { return (uint32_t)(q0 * qrs + h * D) * 2u; };
   float st;          // LSE (tid < 64) or D (64 <= tid < 128) of row q0 + tid % 64
   bool st_valid;
-  // LSE (tid < 64) or D (64 <= tid < 128) of batch entry b from row q_start
-  // on; a row is h * N + row past it (32-bit: B * H * N < 2^31)
-  const float* st_base = ((tid & 64) ? p.dsum : p.lse) + (long long)b * p.H * p.N + p.q_start;
-  auto stat_load = [&](int h, int q0) {
-    const int row = q0 + (tid & 63);
-    st_valid = row < p.Nq;
-    st = st_base[h * p.N + min(row, p.Nq - 1)];
+  // LSE (wave 0) or D (wave 1) of batch entry b from row q_start on; row q
+  // of head h is element si = h N + q past it (32-bit: B H N < 2^31), read
+  // through a range-checked descriptor over the entry's H N - q_start
+  // elements (zeros past them)
+  const float* st_base = (wave & 1 ? p.dsum : p.lse) + (long long)b * p.H * p.N + p.q_start;
+  const __amdgpu_buffer_rsrc_t rst = make_rsrc(st_base, (uint32_t)(p.H * p.N - p.q_start) * 4u);
+  auto stat_load = [&](int si, int q0) {
+    st_valid = q0 + lane < p.Nq;
+    st = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rst, 4 * lane, 4 * si, 0));
   };
   auto stat_store = [&](uint32_t bo) {   // into the buffer at byte offset bo
     if (tid < 128) {
@@ -243,11 +245,10 @@ void bwd_dkdv_kernel(Params p) {
   //   phase 2: S, dP of half 1 of tile k       + softmax group 1 of half 0 of tile k
   //   phase 3: dV^T, dK^T over half 0 of k     + softmax group 0 of half 1 of tile k
   // (half = 32 query rows, group = 16 of them). Tile -1 is an all-zero buffer
-  // with LSE = +inf (P = 0); the last iteration loads an empty tile past the
-  // last query row (zero rows, LSE = +inf), and a drain after the loop does
-  // what is left of the last tile (its phase-1 products and the softmax they
-  // need). Each phase prefetches the LSE / D values the next phase's softmax
-  // group needs.
+  // with LSE = +inf (P = 0); the last iteration loads one more tile, which
+  // nothing reads, and a drain after the loop does what is left of the last
+  // tile (its phase-1 products and the softmax they need). Each phase
+  // prefetches the LSE / D values the next phase's softmax group needs.
   constexpr int PL = D / 8;          // lock steps per phase
   const int empty_q0 = nqt * DKV_BQ; // rows past the end: zeros, LSE = +inf
 
@@ -271,8 +272,8 @@ void bwd_dkdv_kernel(Params p) {
   {  // tile 0 (the empty tile if this workgroup has none)
     const int h = gkv * p.G, q0 = niter > 0 ? (SPARSE ? uni(tl[0]) : first) * DKV_BQ : empty_q0;
 #pragma unroll
-    for (int piece = 0; piece < 2 * NL; ++piece) load_piece(piece, 0, h, q0);
-    stat_load(h, q0);
+    for (int piece = 0; piece < 2 * NL; ++piece) load_piece(piece, 0, tile_soff(h, q0));
+    stat_load(h * p.N + q0, q0);
     wait_global_loads();
     stat_store(0);
   }
@@ -342,6 +343,13 @@ void bwd_dkdv_kernel(Params p) {
 
   int h_cur = gkv * p.G, t_cur = 0;   // (query head, tile index within the head) of tile k
   int q0_cur = niter > 0 ? (SPARSE ? uni(tl[0]) : first) * DKV_BQ : empty_q0;   // first row of tile k
+  // tile k's Q / dO offset for load_piece() and LSE / D index for
+  // stat_load(), advanced by a tile, or to the next head's first tile
+  uint32_t so_cur = tile_soff(h_cur, q0_cur);
+  int si_cur = h_cur * p.N + q0_cur;
+  const uint32_t so_step = (uint32_t)(DKV_BQ * qrs) * 2u;
+  const uint32_t so_wrap = (uint32_t)D * 2u - (uint32_t)(per_head - 1) * so_step;   // modulo 2^32
+  const int si_wrap = p.N - (per_head - 1) * DKV_BQ;
   // Tile k: one iteration of the pipeline. MASKED iterations apply the
   // causal (and window) mask to the tile's scores; the driver below gives
   // each its own loop, so that tiles clear of the diagonal carry no mask
@@ -354,20 +362,27 @@ void bwd_dkdv_kernel(Params p) {
       // buffers of tiles k - 1 and k + 1
       const uint32_t pbo = cbo == 0 ? 2 * BUF_BYTES : cbo - BUF_BYTES;
       const uint32_t nbo = cbo == 2 * BUF_BYTES ? 0 : cbo + BUF_BYTES;
-      const bool real = kt_ < niter;
-      const int q0 = SPARSE ? q0_cur : (real ? (first + t_cur) * DKV_BQ : empty_q0);
-      // the tile after this one
-      int h_nx = h_cur, t_nx = t_cur + 1;
-      if (t_nx == per_head) { h_nx = h_cur + 1; t_nx = 0; }
-      const bool nx_real = kt_ + 1 < niter;
-      const int q0_nx = nx_real ? (SPARSE ? tq_nx : first + t_nx) * DKV_BQ : empty_q0;
+      const int q0 = q0_cur;           // tile k < niter: the loops below run real tiles only
+      // The tile after this one. After the last tile it is the next (head,
+      // tile) step all the same: its loads are never read, and the range
+      // checks of both descriptors keep them in bounds.
+      const bool wrap = t_cur + 1 == per_head;
+      const int h_nx = wrap ? h_cur + 1 : h_cur, t_nx = wrap ? 0 : t_cur + 1;
+      int q0_nx, si_nx;
+      uint32_t so_nx;
       if constexpr (SPARSE) {            // list entry of tile k + 3, read now for the next iteration
+        q0_nx = tq_nx * DKV_BQ;
         if (++t_nx2 == per_head) t_nx2 = 0;
         const int after = kt_ + 3 < niter ? uni(tl[t_nx2]) : 0;
         tq_nx = tq_nx2;
         tq_nx2 = after;
+        so_nx = tile_soff(h_nx, q0_nx);
+        si_nx = h_nx * p.N + q0_nx;
+      } else {                           // one tile on, or the next head's first
+        q0_nx = wrap ? first * DKV_BQ : q0_cur + DKV_BQ;
+        so_nx = so_cur + (wrap ? so_wrap : so_step);
+        si_nx = si_cur + (wrap ? si_wrap : DKV_BQ);
       }
-      const int h_ld = nx_real ? h_nx : gkv * p.G;   // a valid head also for the empty tile
       const int mthr = kpos - (p.q_start + q0);     // query index inside the tile < mthr -> masked
       // LDS read bases of this iteration (byte addresses; dO at +TILE from Q)
       const uint32_t cq = lds_q0 + cbo;
@@ -432,9 +447,9 @@ void bwd_dkdv_kernel(Params p) {
             if constexpr (ph == 0) {            // next tile: direct loads, then its LSE / D
               constexpr int lo = j * (2 * NL) / PL, hi = (j + 1) * (2 * NL) / PL;
               [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
-                (load_piece(lo + Ws, nbo, h_ld, q0_nx), ...);
+                (load_piece(lo + Ws, nbo, so_nx), ...);
               }(std::make_integer_sequence<int, hi - lo>{});
-              if constexpr (j == PL - 1) stat_load(h_ld, q0_nx);
+              if constexpr (j == PL - 1) stat_load(si_nx, q0_nx);
             }
             if constexpr (ph == 1 && j == PL - 2) di1 = dinit_read(stb, 1);
             if constexpr (ph == 3 && j == PL - 1) stat_store(nbo);
@@ -449,6 +464,8 @@ void bwd_dkdv_kernel(Params p) {
     h_cur = h_nx;
     t_cur = t_nx;
     q0_cur = q0_nx;
+    so_cur = so_nx;
+    si_cur = si_nx;
     ++kt_;
     cbo = nbo;
   };
@@ -715,8 +732,8 @@ void bwd_dq_kernel(Params p) {
     const int sl = wave * NL + i;                  // wave-uniform
     if (TILES_KB % NW != 0 && sl >= TILES_KB) return;
     const bool is_v = sl >= TILE_KB;
-    buffer_load_lds16_async(is_v ? rv : rk, loff[i], (uint32_t)(j0 * krs) * 2u,
-                            lds_addr((is_v ? sm.v[buf] : sm.k[buf]) + (sl % TILE_KB) * 512));
+    buffer_load_lds16_async(is_v ? rv : rk, loff[i], (uint32_t)(j0 * krs) * 2u, (uint32_t)buf * (2u * TILE),
+                            lds_addr((is_v ? sm.v[0] : sm.k[0]) + (sl % TILE_KB) * 512));
   };
 
   // per-lane LDS read offsets (elements). Every row a lane reads has the
