@@ -203,7 +203,8 @@ void bwd_dkdv_kernel(Params p) {
   // through a range-checked descriptor over the entry's H N - q_start
   // elements (zeros past them)
   const float* st_base = (wave & 1 ? p.dsum : p.lse) + (long long)b * p.H * p.N + p.q_start;
-  const __amdgpu_buffer_rsrc_t rst = make_rsrc(st_base, (uint32_t)(p.H * p.N - p.q_start) * 4u);
+  const int st_end = p.H * p.N - p.q_start;
+  const __amdgpu_buffer_rsrc_t rst = make_rsrc(st_base, (uint32_t)st_end * 4u);
   auto stat_load = [&](int si, int q0) {
     st_valid = q0 + lane < p.Nq;
     st = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rst, 4 * lane, 4 * si, 0));
@@ -363,9 +364,9 @@ void bwd_dkdv_kernel(Params p) {
       const uint32_t pbo = cbo == 0 ? 2 * BUF_BYTES : cbo - BUF_BYTES;
       const uint32_t nbo = cbo == 2 * BUF_BYTES ? 0 : cbo + BUF_BYTES;
       const int q0 = q0_cur;           // tile k < niter: the loops below run real tiles only
-      // The tile after this one. After the last tile it is the next (head,
-      // tile) step all the same: its loads are never read, and the range
-      // checks of both descriptors keep them in bounds.
+      // The tile after this one. After the last tile nothing reads it: its
+      // loads then start at the end of both descriptors' ranges, so they
+      // return zeros without touching memory.
       const bool wrap = t_cur + 1 == per_head;
       const int h_nx = wrap ? h_cur + 1 : h_cur, t_nx = wrap ? 0 : t_cur + 1;
       int q0_nx, si_nx;
@@ -383,6 +384,9 @@ void bwd_dkdv_kernel(Params p) {
         so_nx = so_cur + (wrap ? so_wrap : so_step);
         si_nx = si_cur + (wrap ? si_wrap : DKV_BQ);
       }
+      const bool nx_real = kt_ + 1 < niter;
+      const uint32_t so_ld = nx_real ? so_nx : qbytes;
+      const int si_ld = nx_real ? si_nx : st_end;
       const int mthr = kpos - (p.q_start + q0);     // query index inside the tile < mthr -> masked
       // LDS read bases of this iteration (byte addresses; dO at +TILE from Q)
       const uint32_t cq = lds_q0 + cbo;
@@ -447,9 +451,9 @@ void bwd_dkdv_kernel(Params p) {
             if constexpr (ph == 0) {            // next tile: direct loads, then its LSE / D
               constexpr int lo = j * (2 * NL) / PL, hi = (j + 1) * (2 * NL) / PL;
               [&]<int... Ws>(std::integer_sequence<int, Ws...>) {
-                (load_piece(lo + Ws, nbo, so_nx), ...);
+                (load_piece(lo + Ws, nbo, so_ld), ...);
               }(std::make_integer_sequence<int, hi - lo>{});
-              if constexpr (j == PL - 1) stat_load(si_nx, q0_nx);
+              if constexpr (j == PL - 1) stat_load(si_ld, q0_nx);
             }
             if constexpr (ph == 1 && j == PL - 2) di1 = dinit_read(stb, 1);
             if constexpr (ph == 3 && j == PL - 1) stat_store(nbo);
