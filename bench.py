@@ -30,7 +30,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 # rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; calibrated against a plain
 # 1 GiB device copy in the same process), valid only for the kernel sources
 # and build flags whose SHA-1 is recorded with it (profiles/llama16k_causal_bf16_traffic.md).
-DKDV_TRAFFIC = {"sources_sha1": "32d27f9071c8c7d26b2656ac35f0607f3445366c", "bytes": 2849822628}   # fetch 2.581 GB + write 0.269 GB
+DKDV_TRAFFIC = {"sources_sha1": "ac08606f580ebb709b7c85ceb88dcae38c0dda24", "bytes": 2849822628}   # fetch 2.581 GB + write 0.269 GB
 DKDV_SOURCES = ("exact_attention_37_amd/csrc/bwd_mfma.hip", "exact_attention_37_amd/csrc/mfma_common.h",
                 "exact_attention_37_amd/csrc/common.h", "exact_attention_37_amd/build.py")
 

@@ -55,8 +55,8 @@ constexpr int DKV_BQ = 64;           // query rows per streamed tile
 // bank conflicts, and the tile is written by direct global -> LDS loads.
 // Three buffers (previous, current and next tile); within a buffer dO
 // follows Q and the tile's row statistics follow dO, so all three are
-// reached from one base address. A buffer is 512 bytes past a multiple of
-// the 256-byte bank cycle, which keeps the bank pattern of every read.
+// reached from one base address. A buffer's size is a multiple of the
+// 256-byte bank cycle, so every buffer has the same bank pattern.
 template <int D>
 struct DkdvSmem {
   static constexpr int ROW = D + 32;
